@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests compares the oracle with a re-typed copy of itself:
+  * the target-law theorem (SpecTr-GBV page, section 2 "theoretical
+    foundation" and section 3: the output keeps the target distribution),
+    checked by exact black-box enumeration of the oracle's output law;
+  * closed forms for E[tau]: token-level SD, GBV (P(tau >= i) = E_q[w_i]),
+    recursive rejection sampling at L = 1;
+  * invariants: the K-draft upper bound, monotonicity in K (SpecTr-GBV page,
+    section 2 "monotonicity" and section 4 ablation on K), GBV >= token level
+    (GBV is the optimal single-draft verifier, SpecTr-GBV page, section 1), GBV
+    non-decreasing in L (section 4 ablation on L);
+  * special cases: p = q, disjoint supports, one draft = GBV, L = 1 token = GBV;
+  * hand-worked examples (tests/golden/worked_examples.json);
+  * planted mistakes in a copy of the oracle, each of which must fail a pin.
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import lawtools as lt
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LAW_TOL = 2e-6          # float32 bisection of the correction uniform: <= V ulps per leaf
+ETAU_TOL = 1e-10        # E[tau] from exact branch probabilities (fp64)
+
+# exhaustive grid (V, L, K): every corner of V <= 8, L <= 3, K <= 3 that enumerates
+# in seconds; (8, 3, 3) is covered statistically below.
+GRID = [(2, 1, 1), (2, 2, 1), (2, 3, 1), (2, 1, 2), (2, 2, 2), (2, 3, 2), (2, 1, 3),
+        (2, 2, 3), (2, 3, 3), (3, 1, 1), (3, 2, 1), (3, 1, 2), (3, 2, 2), (3, 1, 3),
+        (3, 2, 3), (4, 1, 3), (4, 2, 2), (8, 1, 1), (8, 1, 2), (8, 1, 3), (8, 2, 1),
+        (8, 3, 1), (8, 2, 2)]
+
+
+def _model(V, L, seed, **kw):
+    rng = np.random.default_rng(1000 * V + 100 * L + seed)
+    T = kw.pop("T", [0.7, 1.0, 1.6][seed % 3])
+    zero = kw.pop("zero_frac", 0.25 if seed % 2 else 0.0)
+    mode = kw.pop("draft_mode", ["noisy", "indep"][seed % 2])
+    return lt.TreeModel.random(V, L, rng, T=T, zero_frac=zero, draft_mode=mode, **kw)
+
+
+@pytest.mark.parametrize("V,L,K", GRID)
+def test_multidraft_keeps_target_law(V, L, K):
+    for seed in range(2):
+        m = _model(V, L, seed)
+        law, e_tau, dropped = lt.output_law(m, K, "multidraft")
+        assert dropped < 1e-7
+        assert abs(sum(law.values()) - 1.0) < LAW_TOL
+        assert lt.extended_law_gap(m, law) < LAW_TOL
+        assert e_tau <= lt.expected_tau_bound(m, K) + ETAU_TOL
+        if K == 1:
+            assert abs(e_tau - lt.expected_tau_gbv(m)) < ETAU_TOL
+        if L == 1:
+            assert abs(e_tau - lt.expected_tau_rrs_l1(m, K)) < ETAU_TOL
+
+
+@pytest.mark.parametrize("V,L", [(2, 1), (2, 3), (3, 2), (8, 2), (8, 3)])
+def test_single_draft_rules_keep_target_law(V, L):
+    for seed in range(2):
+        m = _model(V, L, seed)
+        law_t, et_t, _ = lt.output_law(m, 1, "token")
+        law_b, et_b, _ = lt.output_law(m, 1, "block")
+        assert lt.extended_law_gap(m, law_t) < LAW_TOL
+        assert lt.extended_law_gap(m, law_b) < LAW_TOL
+        assert abs(et_t - lt.expected_tau_token(m)) < ETAU_TOL
+        assert abs(et_b - lt.expected_tau_gbv(m)) < ETAU_TOL
+        assert et_b >= et_t - ETAU_TOL          # GBV is optimal among single-draft verifiers
+
+
+@pytest.mark.parametrize("V,L", [(2, 2), (3, 2), (2, 3)])
+def test_expected_length_monotone_in_k(V, L):
+    for seed in range(3):
+        m = _model(V, L, seed)
+        prev = lt.expected_tau_gbv(m)
+        for K in (2, 3):
+            _, e_tau, _ = lt.output_law(m, K, "multidraft")
+            assert e_tau >= prev - ETAU_TOL
+            prev = e_tau
+
+
+def test_gbv_expected_length_monotone_in_l():
+    rng = np.random.default_rng(5)
+    m = lt.TreeModel.random(3, 3, rng, T=0.8)
+    vals = [lt.expected_tau_gbv(m, L) for L in (1, 2, 3)]
+    assert vals[0] <= vals[1] <= vals[2]
+
+
+def _random_batch(rng, B, K, L, V, T=0.8, same_rows=True):
+    """Random tree-consistent batch: drafts with equal prefixes get equal rows."""
+    tgt = rng.standard_normal((B, K, L + 1, V)).astype(np.float32) * 2
+    drf = (tgt[:, :, :L] + rng.standard_normal((B, K, L, V)).astype(np.float32))
+    tok = rng.integers(0, V, (B, K, L)).astype(np.int32)
+    if same_rows:
+        for b in range(B):
+            for k in range(K):
+                for j in range(L + 1):
+                    for c in range(k):
+                        if (tok[b, c, :j] == tok[b, k, :j]).all():
+                            tgt[b, k, j] = tgt[b, c, j]
+                            if j < L:
+                                drf[b, k, j] = drf[b, c, j]
+                            break
+    temps = np.full(B, T, np.float32)
+    ua = rng.random((B, K, L)).astype(np.float32)
+    uc = rng.random(B).astype(np.float32)
+    return tgt, drf, tok, temps, ua, uc
+
+
+def test_extra_draft_never_shortens_accepted_length():
+    """Pathwise monotonicity in K: the walk over drafts 0..K-1 is a prefix of the
+    walk over drafts 0..K, so with the same uniforms tau can only grow."""
+    rng = np.random.default_rng(11)
+    for V in (3, 5, 40):
+        tgt, drf, tok, temps, ua, uc = _random_batch(rng, 300, 4, 3, V)
+        prev = None
+        for K in (1, 2, 3, 4):
+            o = oracle.verify("multidraft", tgt[:, :K], drf[:, :K], tok[:, :K], temps,
+                              ua[:, :K], uc)
+            if prev is not None:
+                assert (o["accept_len"] >= prev).all()
+            prev = o["accept_len"]
+
+
+def test_one_draft_multidraft_equals_block_pathwise():
+    rng = np.random.default_rng(12)
+    for V in (2, 7, 64):
+        tgt, drf, tok, temps, ua, uc = _random_batch(rng, 400, 1, 4, V)
+        a = oracle.verify("block", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+        b = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+        for key in ("accept_len", "draft_index", "correction", "flags"):
+            np.testing.assert_array_equal(a[key], b[key])
+        np.testing.assert_array_equal(a["accept_prob"], b["accept_prob"])
+        np.testing.assert_array_equal(a["resid_mass"], b["resid_mass"])
+
+
+def test_length_one_token_equals_block_pathwise():
+    rng = np.random.default_rng(13)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 500, 1, 1, 9)
+    a = oracle.verify("token", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+    b = oracle.verify("block", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+    for key in ("accept_len", "draft_index", "correction"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_equal_distributions_accept_everything():
+    """p = q at every node: every method accepts the whole block."""
+    rng = np.random.default_rng(14)
+    B, K, L, V = 200, 3, 4, 11
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, B, K, L, V)
+    drf = tgt[:, :, :L].copy()
+    for method, k in (("token", 1), ("block", 1), ("multidraft", K)):
+        o = oracle.verify(method, tgt[:, :k], drf[:, :k], tok[:, :k], temps, ua[:, :k], uc)
+        assert (o["accept_len"] == L).all()
+        assert (o["draft_index"] == 0).all()
+
+
+def test_disjoint_supports_reject_and_sample_target():
+    """supp(p) and supp(q) disjoint at the root: tau = 0 and the correction law is p_0."""
+    V, L = 4, 2
+    rng = np.random.default_rng(15)
+    m = lt.TreeModel.random(V, L, rng, T=1.0)
+    for pre in list(m.tgt):
+        if len(pre) == 0:
+            m.tgt[pre][2:] = -np.inf
+        if pre in m.drf and len(pre) == 0:
+            m.drf[pre][:2] = -np.inf
+    for method, K in (("token", 1), ("block", 1), ("multidraft", 2), ("multidraft", 3)):
+        law, e_tau, _ = lt.output_law(m, K, method)
+        assert e_tau == 0.0
+        p0 = m.p(())
+        for y in range(V):
+            assert abs(law.get((y,), 0.0) - p0[y]) < LAW_TOL
+
+
+def test_non_canonical_rows_are_never_read():
+    """Rows of a draft that shares its prefix with a lower-index draft belong to
+    the same node; overwriting them must not change anything."""
+    rng = np.random.default_rng(16)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 300, 4, 3, 3)
+    a = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+    tgt2, drf2 = tgt.copy(), drf.copy()
+    B, K, L = tok.shape
+    for b in range(B):
+        for k in range(1, K):
+            for j in range(L + 1):
+                if any((tok[b, c, :j] == tok[b, k, :j]).all() for c in range(k)):
+                    tgt2[b, k, j] = np.nan
+                    if j < L:
+                        drf2[b, k, j] = np.nan
+    b2 = oracle.verify("multidraft", tgt2, drf2, tok, temps, ua, uc, diagnostics=True)
+    for key in ("accept_len", "draft_index", "correction", "flags"):
+        np.testing.assert_array_equal(a[key], b2[key])
+
+
+def test_row_lse_matches_library_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(17)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 20, 2, 3, 50, T=0.4, same_rows=False)
+    o = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+    B, K, L = tok.shape
+    for b in range(B):
+        for k in range(K):
+            for j in range(L + 1):
+                c = next(c for c in range(k + 1) if (tok[b, c, :j] == tok[b, k, :j]).all())
+                ref = logsumexp(tgt[b, c, j].astype(np.float64) / np.float64(temps[b]))
+                assert abs(o["row_lse"][b, k, j] - ref) < 1e-12 * max(1, abs(ref))
+            for j in range(L):
+                c = next(c for c in range(k + 1) if (tok[b, c, :j] == tok[b, k, :j]).all())
+                ref = logsumexp(drf[b, c, j].astype(np.float64) / np.float64(temps[b]))
+                assert abs(o["row_lse"][b, k, L + 1 + j] - ref) < 1e-12 * max(1, abs(ref))
+
+
+def test_bf16_bits_are_widened_exactly():
+    rng = np.random.default_rng(18)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 50, 2, 3, 33)
+    # round to bf16 (truncate the mantissa) and pass both as f32 and as bf16 bits
+    t16 = (tgt.view(np.uint32) >> 16).astype(np.uint16)
+    d16 = (drf.view(np.uint32) >> 16).astype(np.uint16)
+    t32 = (t16.astype(np.uint32) << 16).view(np.float32)
+    d32 = (d16.astype(np.uint32) << 16).view(np.float32)
+    a = oracle.verify("multidraft", t32, d32, tok, temps, ua, uc, diagnostics=True)
+    b = oracle.verify("multidraft", t16, d16, tok, temps, ua, uc, diagnostics=True)
+    for key in ("accept_len", "draft_index", "correction", "row_lse", "resid_mass"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_invalid_request_data_is_flagged():
+    rng = np.random.default_rng(19)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 6, 2, 2, 10)
+    tgt[0, 0, 0, 3] = np.nan                 # NaN in a node row
+    tok[1, 1, 1] = 10                        # token outside [0, V)
+    temps[2] = 0.0                           # T must be > 0
+    ua[3, 0, 0] = 1.0                        # u must be < 1
+    drf[4, 0, 1, :] = -np.inf                # a row of zero mass
+    o = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc)
+    assert (o["accept_len"][:5] == -1).all()
+    assert (o["flags"][:5] & oracle.FLAG_INVALID).all()
+    assert o["accept_len"][5] >= 0 and not o["flags"][5] & oracle.FLAG_INVALID
+
+
+def test_golden_worked_examples():
+    with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        K, L, V = e["K"], e["L"], e["V"]
+        tgt = np.log(np.array(e["target_probs"], np.float64)).astype(np.float32)[None]
+        drf = np.log(np.array(e["draft_probs"], np.float64)).astype(np.float32)[None]
+        assert tgt.shape == (1, K, L + 1, V) and drf.shape == (1, K, L, V)
+        tok = np.array(e["tokens"], np.int32)[None]
+        ua = np.array(e["u_accept"], np.float32)[None]
+        uc = np.array([e["u_correct"]], np.float32)
+        temps = np.array([e["T"]], np.float32)
+        for method in e["methods"]:
+            o = oracle.verify(method, tgt, drf, tok, temps, ua, uc, diagnostics=True)
+            exp = e["expect"]
+            assert o["accept_len"][0] == exp["accept_len"], (e["name"], method)
+            assert o["draft_index"][0] == exp["draft_index"], (e["name"], method)
+            assert o["correction"][0] == exp["correction"], (e["name"], method)
+            assert abs(o["resid_mass"][0] - exp["resid_mass"]) < 1e-6, (e["name"], method)
+            want = np.array([[np.nan if v is None else v for v in row]
+                             for row in exp["accept_prob"]])
+            got = o["accept_prob"][0]
+            if method == "token":
+                want = want[:1]
+                got = got[:1]
+            assert np.array_equal(np.isnan(got), np.isnan(want)), (e["name"], method)
+            ok = ~np.isnan(want)
+            assert np.allclose(got[ok], want[ok], atol=1e-6), (e["name"], method)
+
+
+def test_monte_carlo_law_at_v8_l3_k3():
+    """The corner (V, L, K) = (8, 3, 3) of the grid is too large to enumerate
+    (8^9 draft realisations); draw drafts and uniforms instead and compare the
+    law of the extended output with the target law by a chi-square test."""
+    from scipy.stats import chi2
+    V, L, K, n = 8, 3, 3, 60000
+    rng = np.random.default_rng(20)
+    m = lt.TreeModel.random(V, L, rng, T=0.9, sigma=1.0)
+    nodes = {}
+    tgt = np.empty((n, K, L + 1, V), np.float32)
+    drf = np.empty((n, K, L, V), np.float32)
+    tok = np.empty((n, K, L), np.int32)
+    qcache = {}
+    for i in range(n):
+        for k in range(K):
+            pre = ()
+            for j in range(L):
+                tgt[i, k, j] = m.tgt[pre]
+                drf[i, k, j] = m.drf[pre]
+                if pre not in qcache:
+                    qcache[pre] = m.q(pre)
+                x = rng.choice(V, p=qcache[pre])
+                tok[i, k, j] = x
+                pre = pre + (int(x),)
+            tgt[i, k, L] = m.tgt[pre]
+    temps = np.full(n, m.T, np.float32)
+    ua = rng.random((n, K, L)).astype(np.float32)
+    uc = rng.random(n).astype(np.float32)
+    o = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, threads=4)
+    counts = {}
+    pcache = {}
+    for i in range(n):
+        tau, ks, y = int(o["accept_len"][i]), int(o["draft_index"][i]), int(o["correction"][i])
+        z = tuple(int(t) for t in tok[i, ks, :tau]) + (y,)
+        while len(z) < L + 1:                      # extend by the target
+            if z not in pcache:
+                pcache[z] = m.p(z)
+            z = z + (int(rng.choice(V, p=pcache[z])),)
+        nodes[z] = nodes.get(z, 0) + 1
+    # chi-square over the full sequence law, pooling cells with small expectation
+    import itertools
+    exp_, obs = [], []
+    pool_e = pool_o = 0.0
+    for z in itertools.product(range(V), repeat=L + 1):
+        e = n * m.p_seq(z)
+        c = nodes.get(z, 0)
+        if e >= 8:
+            exp_.append(e)
+            obs.append(c)
+        else:
+            pool_e += e
+            pool_o += c
+    exp_.append(pool_e)
+    obs.append(pool_o)
+    exp_, obs = np.array(exp_), np.array(obs)
+    stat = ((obs - exp_) ** 2 / exp_).sum()
+    pval = chi2.sf(stat, len(exp_) - 1)
+    assert pval > 1e-4, (stat, len(exp_), pval)
+
+
+# ------------------------------------------------------------- planted mistakes
+
+MUTANTS = {
+    # the residual does not move after a rejection
+    "no_beta_update": ("                H[nH++] = x;\n                beta += N;",
+                       "                H[nH++] = x;\n                beta += 0.0;"),
+    # R_m with the two rows transposed
+    "R_transposed": ("Rm += fmax(w[m] * r->p[v] - r->q[v], 0.0);",
+                     "Rm += fmax(w[m] * r->q[v] - r->p[v], 0.0);"),
+    # first position not normalised by the residual mass
+    "first_weight_unnormalised": ("svo_chain(1.0, r->om[x] / N, r->q[x])",
+                                  "svo_chain(1.0, r->om[x], r->q[x])"),
+    # GBV's h without the (1 - w) term
+    "h_drops_term": ("double d = Rm + 1.0 - w[m];", "double d = Rm + 1.0;"),
+    # after acceptance the residual state keeps the old weight
+    "accept_state_wrong": ("alpha = w[tau];", "alpha = 1.0;"),
+    # inverse CDF threshold not scaled by the mass Z
+    "icdf_unscaled_threshold": ("double t = r->uc * Z;", "double t = r->uc;"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_libs(tmp_path_factory):
+    d = tmp_path_factory.mktemp("mutants")
+    src = open(oracle.SRC).read()
+    libs = {}
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, name
+        p = d / f"{name}.c"
+        p.write_text(src.replace(old, new))
+        so = d / f"{name}.so"
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC",
+                               "-shared", "-o", str(so), str(p), "-lm"])
+        libs[name] = str(so)
+    return libs
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(mutant_libs, name):
+    """Each planted mistake must break the law, a closed form or the bound on
+    at least one tiny instance."""
+    caught = False
+    for (V, L, K) in [(2, 2, 2), (3, 2, 2), (2, 3, 1), (3, 1, 3), (2, 3, 3)]:
+        for seed in range(2):
+            m = _model(V, L, seed)
+            law, e_tau, _ = lt.output_law(m, K, "multidraft", lib_path=mutant_libs[name])
+            gap = lt.extended_law_gap(m, law)
+            bad = gap > LAW_TOL or e_tau > lt.expected_tau_bound(m, K) + ETAU_TOL
+            if K == 1:
+                bad |= abs(e_tau - lt.expected_tau_gbv(m)) > ETAU_TOL
+            if bad:
+                caught = True
+                break
+        if caught:
+            break
+    assert caught, name
