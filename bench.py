@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark: verified draft tokens per second of batched verification on one MI355X.
+
+One step = one call of the verification entry point over one batch of
+synthetic inputs already resident in HBM (both kernels: row statistics and
+the per-request walk).  Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The roofline object describes the row-statistics kernel (the one that streams
+the logits): achieved = node-row bytes per launch / its mean duration, timed
+with HIP events recorded on the launch stream around that kernel in every
+timed step.  The cpu_baseline object times the CPU oracle (unmodified,
+single-threaded per request) on a bounded sample of the same batch across the
+host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    from draft_token_verification_online_amd import build as svbuild
+    h = hashlib.sha256()
+    for p in sorted(svbuild.DEPS):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.made.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+def node_rows(tokens_host) -> int:
+    """Rows the statistics kernel reads: for every position j < L, one target and
+    one draft row per distinct prefix X[0..j-1] among a request's drafts."""
+    B, K, L = tokens_host.shape
+    n = 0
+    for j in range(L):
+        if j == 0:
+            n += 2 * B
+            continue
+        pre = tokens_host[:, :, :j]
+        for b in range(B):
+            n += 2 * len({bytes(pre[b, k].tobytes()) for k in range(K)})
+    return n
+
+
+def read_traffic(workload: str, launch_bytes: float):
+    """HBM traffic of the statistics kernel from committed rocprofv3 PMC summaries
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy-kernel calibration), or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"rowstats_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return float(d["bytes_per_launch"])
+
+
+def cpu_baseline(method, batch, w, target_cpu_s: float):
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    host1 = synth.to_host(batch, [0])
+    t = time.perf_counter()
+    oracle.verify(method, host1["target"], host1["draft"], host1["tokens"],
+                  host1["temperature"], host1["u_accept"], host1["u_correct"])
+    t_one = max(time.perf_counter() - t, 1e-4)
+    m = int(np.clip(round(target_cpu_s / t_one), threads, w.B))
+    reqs = list(range(m))
+    host = synth.to_host(batch, reqs)
+    t = time.perf_counter()
+    oracle.verify(method, host["target"], host["draft"], host["tokens"], host["temperature"],
+                  host["u_accept"], host["u_correct"], threads=threads)
+    wall = time.perf_counter() - t
+    return {
+        "value": m * w.K * w.L / wall,
+        "unit": "verified draft tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {m} of {w.B} requests of the same batch ({m * w.K * w.L} draft "
+                  f"tokens), fp64 C oracle, one request per thread, {wall:.2f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--method", default=None)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU work (summed over cores) spent on the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run plain device copies of this many MiB (a "
+                         "reference kernel of known traffic for rocprofv3 PMC runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build verifies each request on one "
+              f"device and has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import draft_token_verification_online_amd as sv
+    from draft_token_verification_online_amd import build as svbuild
+
+    if not os.path.exists(svbuild.LIB):
+        log("library not built; building")
+        svbuild.build()
+    if not torch.cuda.is_available():
+        log("no HIP device visible")
+        sys.exit(1)
+
+    name = args.workload or synth.BENCH_DEFAULT
+    w = synth.WORKLOADS[name]
+    method = args.method or w.methods[-1]
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {name} on cuda:0 (seed {args.seed})")
+    batch = synth.generate(w, args.seed, device="cuda")
+    torch.cuda.synchronize()
+    tok_host = batch["tokens"].cpu().numpy()
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    rows = node_rows(tok_host)
+    stats_bytes = rows * w.V * es
+    dense = synth.dense_bytes(w)
+
+    ver = sv.Verifier(method, w.B, w.K, w.L, w.V, w.dtype)
+    args_in = (batch["target"], batch["draft"], batch["tokens"], batch["temperature"],
+               batch["u_accept"], batch["u_correct"])
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        ver(*args_in, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[hip.create() for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps of {method} on {name}")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ver(*args_in, stream=stream, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stats_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    walk_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    hip.close()
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = synth.tokens_per_step(w)
+    value = tokens / (ms_per_step * 1e-3)
+    st_mean = sum(stats_ms) / len(stats_ms)
+    wk_mean = sum(walk_ms) / len(walk_ms)
+    achieved = stats_bytes / (st_mean * 1e-3) / 1e9
+    flags = ver.out["flags"].cpu()
+    log(f"[bench] {ms_per_step:.3f} ms/step, stats {st_mean:.3f} ms, walk {wk_mean:.3f} ms, "
+        f"{achieved:.0f} GB/s node-row stream, {value / 1e6:.2f} M tokens/s")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {n} bytes")
+        del src, dst
+
+    traffic = read_traffic(name, stats_bytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(method, batch, w, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "verified draft tokens/s (B*K*L) + achieved HBM GB/s of verify kernel",
+        "value": value,
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "method": method, "B": w.B, "K": w.K, "L": w.L,
+                   "V": w.V, "logits": "bf16" if es == 2 else "fp32",
+                   "seed": args.seed},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "rowstats_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "detail": {
+            "rowstats_ms": st_mean,
+            "walk_ms": wk_mean,
+            "node_rows_per_launch": rows,
+            "node_row_bytes": stats_bytes,
+            "dense_logit_bytes": dense,
+            "dense_equiv_GBps_per_step": dense / (ms_per_step * 1e-3) / 1e9,
+            "mean_accept_len": float(ver.out["accept_len"].float().mean()),
+            "invalid_requests": int(((flags & 2) != 0).sum()),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

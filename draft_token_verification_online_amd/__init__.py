@@ -1,0 +1,188 @@
+"""Batched draft-token verification on AMD MI355X -- Python binding.
+
+Thin ctypes layer over libspec_verify.so (C ABI in include/spec_verify.h).
+It only marshals arguments: every step of the verification runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.
+There is no CPU fallback: if the library is missing or the tensors are not on
+a HIP device, the calls raise.
+
+    from draft_token_verification_online_amd import spec_verify_multidraft
+    out = spec_verify_multidraft(target, draft, tokens, temperature, u_accept, u_correct)
+    out["accept_len"], out["draft_index"], out["correction"]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspec_verify.so")
+
+SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EHIP, SV_EWORKSPACE = range(5)
+SV_F32, SV_BF16 = 0, 1
+SV_FLAG_DEGENERATE, SV_FLAG_INVALID = 1, 2
+SV_MAX_K, SV_MAX_L, SV_MAX_V = 64, 16, 1 << 22
+
+_vp = ctypes.c_void_p
+
+
+class SvInputs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("target_logits", _vp), ("draft_logits", _vp), ("draft_tokens", _vp),
+                ("temperature", _vp), ("u_accept", _vp), ("u_correct", _vp)]
+
+
+class SvOutputs(ctypes.Structure):
+    _fields_ = [("accept_len", _vp), ("draft_index", _vp), ("correction", _vp),
+                ("flags", _vp), ("row_lse", _vp), ("accept_prob", _vp), ("resid_mass", _vp)]
+
+
+class SvLaunch(ctypes.Structure):
+    _fields_ = [("stream", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("phase_events", _vp * 3)]
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the C ABI library (built by draft_token_verification_online_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SpecVerifyError(
+            f"{path} is missing: build it with `python -m draft_token_verification_online_amd.build`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.sv_workspace_size.restype = ctypes.c_size_t
+    lib.sv_workspace_size.argtypes = [ctypes.c_int32] * 5
+    for name in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.POINTER(SvInputs), ctypes.POINTER(SvOutputs),
+                      ctypes.POINTER(SvLaunch)]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_status_string.argtypes = [ctypes.c_int]
+    lib.sv_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def workspace_size(B, K, L, V, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (SV_BF16 if dtype == torch.bfloat16 else SV_F32)
+    return int(load_library().sv_workspace_size(B, K, L, V, code))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class Verifier:
+    """Holds outputs and workspace for repeated calls on inputs of one shape.
+
+    method: "token", "block" or "multidraft".  diagnostics=True also returns
+    row_lse [B][K][2L+1], accept_prob [B][K][L] and resid_mass [B]."""
+
+    _ENTRY = {"token": "spec_verify_token", "block": "spec_verify_block",
+              "multidraft": "spec_verify_multidraft"}
+
+    def __init__(self, method, B, K, L, V, dtype, device="cuda", diagnostics=False,
+                 with_flags=True):
+        lib = load_library()
+        if method not in self._ENTRY:
+            raise ValueError(f"unknown method {method!r}")
+        self.method, self.shape = method, (B, K, L, V)
+        self.dtype = dtype
+        self._fn = getattr(lib, self._ENTRY[method])
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.out = {"accept_len": torch.empty(B, **i32),
+                    "draft_index": torch.empty(B, **i32),
+                    "correction": torch.empty(B, **i32)}
+        if with_flags or diagnostics:
+            self.out["flags"] = torch.empty(B, **i32)
+        if diagnostics:
+            f32 = dict(dtype=torch.float32, device=dev)
+            self.out["row_lse"] = torch.empty((B, K, 2 * L + 1), **f32)
+            self.out["accept_prob"] = torch.empty((B, K, L), **f32)
+            self.out["resid_mass"] = torch.empty(B, **f32)
+        nbytes = workspace_size(B, K, L, V, _dtype_code(torch.empty((), dtype=dtype)))
+        if nbytes == 0:
+            raise ValueError(f"sizes out of range: B={B} K={K} L={L} V={V}")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self._outs = SvOutputs(*[_ptr(self.out.get(k)) for k in
+                                 ("accept_len", "draft_index", "correction", "flags",
+                                  "row_lse", "accept_prob", "resid_mass")])
+
+    def __call__(self, target, draft, tokens, temperature, u_accept, u_correct, *,
+                 stream=None, events=None):
+        B, K, L, V = self.shape
+        checks = [(target, (B, K, L + 1, V), self.dtype), (draft, (B, K, L, V), self.dtype),
+                  (tokens, (B, K, L), torch.int32), (temperature, (B,), torch.float32),
+                  (u_accept, (B, K, L), torch.float32), (u_correct, (B,), torch.float32)]
+        for t, shp, dt in checks:
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"expected contiguous {dt} tensor of shape {shp}, "
+                                 f"got {t.dtype} {tuple(t.shape)}")
+            if t.device.type != "cuda":
+                raise ValueError("inputs must live in GPU memory")
+        ins = SvInputs(B, K, L, V, _dtype_code(target), target.data_ptr(), draft.data_ptr(),
+                       tokens.data_ptr(), temperature.data_ptr(), u_accept.data_ptr(),
+                       u_correct.data_ptr())
+        if stream is None:
+            stream = torch.cuda.current_stream(target.device).cuda_stream
+        ev = (_vp * 3)(*(events or (None, None, None)))
+        ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
+        rc = self._fn(ctypes.byref(ins), ctypes.byref(self._outs), ctypes.byref(ln))
+        if rc != SV_OK:
+            msg = load_library().sv_status_string(rc).decode()
+            raise SpecVerifyError(f"{self._ENTRY[self.method]} failed: {msg} ({rc})")
+        return self.out
+
+
+def _run(method, target, draft, tokens, temperature, u_accept, u_correct, diagnostics, **kw):
+    B, K, L1, V = target.shape
+    v = Verifier(method, B, K, L1 - 1, V, target.dtype, device=target.device,
+                 diagnostics=diagnostics)
+    return dict(v(target, draft, tokens, temperature, u_accept, u_correct, **kw))
+
+
+def spec_verify_token(target, draft, tokens, temperature, u_accept, u_correct, *,
+                      diagnostics=False, **kw):
+    """Token-level speculative sampling (K = 1).  See include/spec_verify.h."""
+    return _run("token", target, draft, tokens, temperature, u_accept, u_correct,
+                diagnostics, **kw)
+
+
+def spec_verify_block(target, draft, tokens, temperature, u_accept, u_correct, *,
+                      diagnostics=False, **kw):
+    """Greedy block verification of one draft (K = 1).  See include/spec_verify.h."""
+    return _run("block", target, draft, tokens, temperature, u_accept, u_correct,
+                diagnostics, **kw)
+
+
+def spec_verify_multidraft(target, draft, tokens, temperature, u_accept, u_correct, *,
+                           diagnostics=False, **kw):
+    """Block verification over K i.i.d. drafts.  See include/spec_verify.h."""
+    return _run("multidraft", target, draft, tokens, temperature, u_accept, u_correct,
+                diagnostics, **kw)
+
+
+__all__ = ["spec_verify_token", "spec_verify_block", "spec_verify_multidraft", "Verifier",
+           "workspace_size", "load_library", "SpecVerifyError"]

@@ -1,0 +1,168 @@
+// spec_verify.hip -- C ABI of the verification library (see include/spec_verify.h).
+//
+// A call validates everything it can on the host before touching the device,
+// then launches two kernels on the caller's stream:
+//   1. rowstats_kernel  -- one workgroup per node row: softmax statistics;
+//                          this is the kernel that streams the logits from HBM;
+//   2. walk_kernel      -- one workgroup per request: the verification walk.
+// No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/spec_verify.h"
+#include "sv_rowstats.hpp"
+#include "sv_walk.hpp"
+
+namespace {
+
+constexpr int kStatsThreads = 256;
+constexpr int kWalkThreads = 512;
+constexpr long long kMaxStatsGrid = 1LL << 22;
+constexpr int kMaxB = 1 << 24;
+
+static_assert(SV_MAX_K == sv::kMaxK, "K limit");
+static_assert(SV_MAX_L == sv::kMaxL, "L limit");
+static_assert(SV_MAX_V == sv::kMaxV, "V limit");
+static_assert(SV_FLAG_DEGENERATE == sv::kFlagDegenerate, "flag bits");
+static_assert(SV_FLAG_INVALID == sv::kFlagInvalid, "flag bits");
+static_assert(sizeof(sv::RowStat) == 16, "row statistics layout");
+
+size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+bool sizes_ok(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
+    return B >= 0 && B <= kMaxB && K >= 1 && K <= SV_MAX_K && L >= 1 && L <= SV_MAX_L &&
+           V >= 1 && V <= SV_MAX_V && (dtype == SV_F32 || dtype == SV_BF16);
+}
+
+size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
+    return static_cast<size_t>(B) * static_cast<size_t>(K) * static_cast<size_t>(2 * L + 1) *
+           sizeof(sv::RowStat);
+}
+
+template <typename E, bool VEC>
+hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln, int method) {
+    using RD = typename sv::RowOf<E, VEC>::type;
+    hipStream_t stream = static_cast<hipStream_t>(ln->stream);
+    const bool bonus = out->row_lse != nullptr;
+
+    sv::StatsArgs sa;
+    sa.tgt = in->target_logits;
+    sa.drf = in->draft_logits;
+    sa.tok = in->draft_tokens;
+    sa.temp = in->temperature;
+    sa.stats = static_cast<sv::RowStat *>(ln->workspace);
+    sa.B = in->B;
+    sa.K = in->K;
+    sa.L = in->L;
+    sa.V = in->V;
+    sa.rows_per_draft = 2 * in->L + (bonus ? 1 : 0);
+    const long long nrows = static_cast<long long>(in->B) * in->K * sa.rows_per_draft;
+    const unsigned grid = static_cast<unsigned>(nrows < kMaxStatsGrid ? nrows : kMaxStatsGrid);
+
+    sv::WalkArgs wa;
+    wa.tgt = in->target_logits;
+    wa.drf = in->draft_logits;
+    wa.tok = in->draft_tokens;
+    wa.temp = in->temperature;
+    wa.ua = in->u_accept;
+    wa.uc = in->u_correct;
+    wa.stats = sa.stats;
+    wa.B = in->B;
+    wa.K = in->K;
+    wa.L = in->L;
+    wa.V = in->V;
+    wa.method = method;
+    wa.bonus_stats = bonus ? 1 : 0;
+    wa.accept_len = out->accept_len;
+    wa.draft_index = out->draft_index;
+    wa.correction = out->correction;
+    wa.flags = out->flags;
+    wa.row_lse = out->row_lse;
+    wa.accept_prob = out->accept_prob;
+    wa.resid_mass = out->resid_mass;
+
+    hipError_t err;
+    if (ln->phase_events[0] &&
+        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[0]), stream)) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>), dim3(grid),
+                       dim3(kStatsThreads), 0, stream, sa);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ln->phase_events[1] &&
+        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[1]), stream)) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads), 0,
+                       stream, wa);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ln->phase_events[2] &&
+        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[2]), stream)) != hipSuccess)
+        return err;
+    return hipSuccess;
+}
+
+int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
+           bool single_draft) {
+    if (!in || !out || !ln) return SV_EINVAL;
+    if (!sizes_ok(in->B, in->K, in->L, in->V, in->dtype)) return SV_EINVAL;
+    if (single_draft && in->K != 1) return SV_EINVAL;
+    if (in->B == 0) return SV_OK;
+    if (!in->target_logits || !in->draft_logits || !in->draft_tokens || !in->temperature ||
+        !in->u_accept || !in->u_correct)
+        return SV_EINVAL;
+    if (!out->accept_len || !out->draft_index || !out->correction) return SV_EINVAL;
+    const size_t es = in->dtype == SV_F32 ? 4 : 2;
+    const uintptr_t ta = reinterpret_cast<uintptr_t>(in->target_logits);
+    const uintptr_t da = reinterpret_cast<uintptr_t>(in->draft_logits);
+    if (ta % es || da % es) return SV_EINVAL;
+    if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < stats_bytes(in->B, in->K, in->L)) return SV_EWORKSPACE;
+
+    const bool vec = (in->V % 8 == 0) && (ta % 16 == 0) && (da % 16 == 0);
+    hipError_t err;
+    if (in->dtype == SV_BF16)
+        err = vec ? launch<uint16_t, true>(in, out, ln, method)
+                  : launch<uint16_t, false>(in, out, ln, method);
+    else
+        err = vec ? launch<float, true>(in, out, ln, method)
+                  : launch<float, false>(in, out, ln, method);
+    return err == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
+    if (!sizes_ok(B, K, L, V, dtype)) return 0;
+    const size_t n = align_up(stats_bytes(B, K, L), 256);
+    return n ? n : 256;
+}
+
+int spec_verify_token(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
+    return verify(sv::kMethodToken, in, out, ln, true);
+}
+
+int spec_verify_block(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
+    return verify(sv::kMethodBlockWalk, in, out, ln, true);
+}
+
+int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
+    return verify(sv::kMethodBlockWalk, in, out, ln, false);
+}
+
+const char *sv_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_EINVAL: return "invalid argument";
+        case SV_EUNSUPPORTED: return "unsupported dtype or size";
+        case SV_EHIP: return "HIP runtime error";
+        case SV_EWORKSPACE: return "workspace missing, misaligned or too small";
+        default: return "unknown status";
+    }
+}
+
+const char *sv_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// sv_device.hpp -- device-side building blocks for the verification kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Rows of logits are consumed in chunks of 8 consecutive elements: one 16-byte
+// load for bf16, two for fp32, or 8 bounds-checked scalar loads when the row
+// is not 16-byte aligned.  Elements past the end of a row read as -inf, which
+// every consumer maps to probability zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kChunk = 8;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 2^y on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float y) { return __builtin_amdgcn_exp2f(y); }
+
+// Split a positive scale c (= log2(e)/T) into hi + lo floats with hi <= c and
+// lo > 0, so that d*hi + d*lo keeps the sign of d: a -inf logit difference
+// then maps to 2^-inf = 0 instead of -inf + inf = NaN.
+__device__ __forceinline__ void split_scale(double c, float &hi, float &lo) {
+    hi = static_cast<float>(c);
+    if (static_cast<double>(hi) >= c) hi = nextafterf(hi, 0.0f);
+    lo = static_cast<float>(c - static_cast<double>(hi));
+}
+
+// Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7.
+struct RowBf16Vec {
+    const uint4 *p;
+    __device__ RowBf16Vec(const void *row, int) : p(static_cast<const uint4 *>(row)) {}
+    __device__ __forceinline__ uint4 raw(int c) const { return p[c]; }
+    __device__ __forceinline__ static void unpack(const uint4 &w, float x[8]) {
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+        x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+        x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    }
+    __device__ __forceinline__ void load(int c, float x[8]) const { unpack(raw(c), x); }
+    __device__ __forceinline__ float at(int v) const {
+        const uint16_t *s = reinterpret_cast<const uint16_t *>(p);
+        return __uint_as_float(static_cast<uint32_t>(s[v]) << 16);
+    }
+};
+
+struct RowF32Vec {
+    const float4 *p;
+    __device__ RowF32Vec(const void *row, int) : p(static_cast<const float4 *>(row)) {}
+    __device__ __forceinline__ void load(int c, float x[8]) const {
+        float4 a = p[2 * c], b = p[2 * c + 1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    __device__ __forceinline__ float at(int v) const {
+        return reinterpret_cast<const float *>(p)[v];
+    }
+};
+
+struct RowBf16Scalar {
+    const uint16_t *p;
+    int V;
+    __device__ RowBf16Scalar(const void *row, int V_) : p(static_cast<const uint16_t *>(row)), V(V_) {}
+    __device__ __forceinline__ void load(int c, float x[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int v = 8 * c + e;
+            x[e] = v < V ? __uint_as_float(static_cast<uint32_t>(p[v]) << 16) : -INFINITY;
+        }
+    }
+    __device__ __forceinline__ float at(int v) const {
+        return __uint_as_float(static_cast<uint32_t>(p[v]) << 16);
+    }
+};
+
+struct RowF32Scalar {
+    const float *p;
+    int V;
+    __device__ RowF32Scalar(const void *row, int V_) : p(static_cast<const float *>(row)), V(V_) {}
+    __device__ __forceinline__ void load(int c, float x[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int v = 8 * c + e;
+            x[e] = v < V ? p[v] : -INFINITY;
+        }
+    }
+    __device__ __forceinline__ float at(int v) const { return p[v]; }
+};
+
+template <typename E, bool VEC> struct RowOf;
+template <> struct RowOf<uint16_t, true> { using type = RowBf16Vec; };
+template <> struct RowOf<uint16_t, false> { using type = RowBf16Scalar; };
+template <> struct RowOf<float, true> { using type = RowF32Vec; };
+template <> struct RowOf<float, false> { using type = RowF32Scalar; };
+
+__device__ __forceinline__ float max8(const float x[8]) {
+    return fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+}
+
+__device__ __forceinline__ float sum8(const float e[8]) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
+// ---------------------------------------------------------------- reductions
+// Butterfly reductions give every lane the same bits (IEEE + is commutative),
+// so every thread of a block leaves a block reduction with identical values.
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// red[] must hold NT/64 entries; the leading barrier protects its previous use.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double *red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    double t = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) t += red[i];
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_max_int(int v, int *red) {
+    v = wave_max_int(v);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    int t = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) t = max(t, red[i]);
+    return t;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_min_int(int v, int *red) {
+    v = wave_min_int(v);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    int t = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) t = min(t, red[i]);
+    return t;
+}
+
+// Exclusive prefix sum over the block in thread order.
+template <int NT>
+__device__ __forceinline__ double block_exclusive_scan(double v, double *red) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    double s = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double n = __shfl_up(s, o, kWave);
+        if (lane >= o) s += n;
+    }
+    double excl = __shfl_up(s, 1, kWave);
+    if (lane == 0) excl = 0.0;
+    __syncthreads();
+    if (lane == kWave - 1) red[w] = s;
+    __syncthreads();
+    double base = 0.0;
+    for (int i = 0; i < w; ++i) base += red[i];
+    return base + excl;
+}
+
+}  // namespace sv

@@ -1,0 +1,480 @@
+// sv_walk.hpp -- per-request verification walk.
+//
+// One workgroup verifies one request.  Every thread runs the same scalar walk
+// (fp64, identical inputs, hence identical decisions); the O(V) steps run
+// block-wide over one node's row pair:
+//   * residual mass   N = sum_v [v not in H] max(alpha p(v) - beta q(v), 0)
+//   * GBV's R_m       = sum_v max(w_m p_m(v) - q_m(v), 0)
+//   * inverse CDF     y = min{v : C_v > u Z} in token-id order.
+// p and q are rebuilt per element from the row statistics: p(v) =
+// 2^((l_v - M) c) / S.  Drafted-token probabilities come from one gathered
+// logit per row and are kept in log2 form in fp64.
+//
+// Rules (see the header spec_verify.h for the full statement):
+//  token level   -- standard speculative sampling: accept X_j iff
+//                   u_j < min(1, p_j(X_j)/q_j(X_j)), stop at the first
+//                   rejection, resample from norm(max(p - q, 0)), or from the
+//                   target row after the block when all L are accepted.
+//  block / K-draft -- GBV (SpecTr-GBV page, section 1) run draft after draft as
+//                   the SpecTr-GBV page, section 2 ("algorithmic procedure",
+//                   steps 1-5) describes: a draft off the accepted prefix is
+//                   skipped; a draft whose token at the node is in H is rejected
+//                   without a test; otherwise its sub-block is tested from
+//                   position L down to tau+1 against w_m / h_m, where the first
+//                   position's target is the node residual omega/N.
+//                   Acceptance at m sets tau = m and, for m < L, the residual
+//                   (alpha, beta, N) = (w_m, 1, R_m); rejection adds the first
+//                   token to H and N to beta.  One O(V) sweep per selection
+//                   step, no search over a scaling factor (section 3).
+// A test at m < L with u >= w_m is settled without its sweep: R_m <= w_m
+// implies h_m = R_m / (R_m + 1 - w_m) <= w_m, so it rejects either way.
+#pragma once
+
+#include "sv_device.hpp"
+#include "sv_rowstats.hpp"
+
+namespace sv {
+
+constexpr int kMaxK = 64;
+constexpr int kMaxL = 16;
+constexpr int kMaxV = 1 << 22;
+constexpr int kMethodToken = 0;
+constexpr int kMethodBlockWalk = 1;
+constexpr int kFlagDegenerate = 1;
+constexpr int kFlagInvalid = 2;
+
+struct WalkArgs {
+    const void *tgt;        // [B][K][L+1][V]
+    const void *drf;        // [B][K][L][V]
+    const int32_t *tok;     // [B][K][L]
+    const float *temp;      // [B]
+    const float *ua;        // [B][K][L]
+    const float *uc;        // [B]
+    const RowStat *stats;   // [B][K][2L+1]
+    int B, K, L, V;
+    int method;             // kMethodToken or kMethodBlockWalk
+    int bonus_stats;        // stats hold target rows at position L too
+    int32_t *accept_len, *draft_index, *correction, *flags;
+    float *row_lse, *accept_prob, *resid_mass;
+};
+
+// Likelihood ratio from log2-probabilities, with the drafted-token convention:
+// q = 0 gives +inf if p > 0 and 0 otherwise.
+__device__ __forceinline__ double ratio_log2(double lp, double lq) {
+    if (lq == -INFINITY) return lp > -INFINITY ? INFINITY : 0.0;
+    return exp2(lp - lq);
+}
+
+__device__ __forceinline__ double chain_step(double w, double r) {
+    if (w == 0.0) return 0.0;
+    const double t = w * r;
+    return t < 1.0 ? t : 1.0;
+}
+
+// omega(v) for the 8 elements of chunk c: [v not in H] max(a eP - bq eQ, 0),
+// eP = 2^((P_v - MP) c); without a Q row, omega = a eP.
+template <bool HAS_Q>
+__device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MP, float MQ,
+                                       float a, float bq, float chi, float clo, int v0,
+                                       const int *H, int nH, float w[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float dp = xp[e] - MP;
+        const float ep = fast_exp2(fmaf(dp, chi, dp * clo));
+        if (HAS_Q) {
+            const float dq = xq[e] - MQ;
+            const float eq = fast_exp2(fmaf(dq, chi, dq * clo));
+            w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), 0.0f);
+        } else {
+            w[e] = a * ep;
+        }
+    }
+    for (int i = 0; i < nH; ++i) {
+        const unsigned off = static_cast<unsigned>(H[i] - v0);
+        if (off < 8u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (off == static_cast<unsigned>(e)) ? 0.0f : w[e];
+        }
+    }
+}
+
+struct SweepRows {
+    float MP, MQ, a, bq;
+};
+
+// Block-wide sum of omega over a row pair (or a single row when HAS_Q is false).
+template <int NT, typename RD, bool HAS_Q>
+__device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
+                             float clo, const int *H, int nH, double *red) {
+    double acc = 0.0;
+    int c = threadIdx.x;
+    for (; c + NT < nch; c += 2 * NT) {
+        float xp0[8], xq0[8], xp1[8], xq1[8], w[8];
+        P.load(c, xp0);
+        P.load(c + NT, xp1);
+        if (HAS_Q) { Q.load(c, xq0); Q.load(c + NT, xq1); }
+        omega8<HAS_Q>(xp0, xq0, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+        acc += static_cast<double>(sum8(w));
+        omega8<HAS_Q>(xp1, xq1, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * (c + NT), H, nH, w);
+        acc += static_cast<double>(sum8(w));
+    }
+    if (c < nch) {
+        float xp0[8], xq0[8], w[8];
+        P.load(c, xp0);
+        if (HAS_Q) Q.load(c, xq0);
+        omega8<HAS_Q>(xp0, xq0, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+        acc += static_cast<double>(sum8(w));
+    }
+    return block_sum<NT>(acc, red);
+}
+
+// Block-wide inverse-CDF draw over omega in token-id order.  Returns y, or -1
+// when the mass Z is not a positive finite number.  Z is returned in *Z.
+template <int NT, typename RD, bool HAS_Q>
+__device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
+                          float clo, const int *H, int nH, double u, double *Z, double *tile,
+                          double *red, int *ired) {
+    const int ntile = (nch + NT - 1) / NT;
+    int lastpos = -1;
+    for (int t = 0; t < ntile; ++t) {
+        const int c = t * NT + threadIdx.x;
+        double cs = 0.0;
+        if (c < nch) {
+            float xp[8], xq[8], w[8];
+            P.load(c, xp);
+            if (HAS_Q) Q.load(c, xq);
+            omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                cs += static_cast<double>(w[e]);
+                if (w[e] > 0.0f) lastpos = 8 * c + e;
+            }
+        }
+        const double ts = block_sum<NT>(cs, red);
+        if (threadIdx.x == 0) tile[t] = ts;
+    }
+    lastpos = block_max_int<NT>(lastpos, ired);   // its barriers publish tile[]
+    double z = 0.0;
+    for (int t = 0; t < ntile; ++t) z += tile[t];
+    *Z = z;
+    if (!(z > 0.0) || !isfinite(z)) return -1;
+    const double thr = u * z;
+    double base = 0.0;
+    int tc = -1;
+    for (int t = 0; t < ntile; ++t) {
+        if (base + tile[t] > thr) { tc = t; break; }
+        base += tile[t];
+    }
+    if (tc < 0) return lastpos;
+
+    const int c = tc * NT + threadIdx.x;
+    float w[8];
+    double cs = 0.0;
+    if (c < nch) {
+        float xp[8], xq[8];
+        P.load(c, xp);
+        if (HAS_Q) Q.load(c, xq);
+        omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs += static_cast<double>(w[e]);
+    }
+    const double pre = base + block_exclusive_scan<NT>(cs, red);
+    int cand = 0x7fffffff;
+    if (c < nch && pre <= thr && pre + cs > thr) {
+        double C = pre;
+        int last = -1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (cand == 0x7fffffff) {
+                if (w[e] > 0.0f) last = 8 * c + e;
+                C += static_cast<double>(w[e]);
+                if (C > thr) cand = 8 * c + e;
+            }
+        }
+        if (cand == 0x7fffffff && last >= 0) cand = last;
+    }
+    cand = block_min_int<NT>(cand, ired);
+    return cand == 0x7fffffff ? lastpos : cand;
+}
+
+// Block-wide maximum of a row (NaN entries are ignored here; they surface as a
+// NaN mass in the following sweep).
+template <int NT, typename RD>
+__device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
+    float m = -INFINITY;
+    for (int c = threadIdx.x; c < nch; c += NT) {
+        float x[8];
+        P.load(c, x);
+        m = fmaxf(m, max8(x));
+    }
+    return block_max<NT>(m, fred);
+}
+
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
+    constexpr int kMaxTiles = (kMaxV / kChunk + NT - 1) / NT;
+    __shared__ int s_x[kMaxK * kMaxL];
+    __shared__ unsigned char s_can[kMaxK * (kMaxL + 1)];
+    __shared__ double s_lp[kMaxK * kMaxL];
+    __shared__ double s_lq[kMaxK * kMaxL];
+    __shared__ double s_red[NT / kWave];
+    __shared__ float s_fred[NT / kWave];
+    __shared__ int s_ired[NT / kWave];
+    __shared__ double s_tile[kMaxTiles];
+    __shared__ int s_H[kMaxK];
+    __shared__ double s_w[kMaxL + 1];
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int K = A.K, L = A.L, V = A.V, KL = K * L, RS = 2 * L + 1;
+    const int nch = (V + kChunk - 1) / kChunk;
+    const long long bKL = static_cast<long long>(b) * KL;
+    const float T = A.temp[b];
+    const double c64 = 1.4426950408889634 / static_cast<double>(T);
+    float chi, clo;
+    split_scale(c64, chi, clo);
+    const E *tgt = static_cast<const E *>(A.tgt);
+    const E *drf = static_cast<const E *>(A.drf);
+    const RowStat *st = A.stats + static_cast<long long>(b) * K * RS;
+    auto trow = [&](int c, int j) {
+        return tgt + ((static_cast<long long>(b) * K + c) * (L + 1) + j) * V;
+    };
+    auto drow = [&](int c, int j) {
+        return drf + ((static_cast<long long>(b) * K + c) * L + j) * V;
+    };
+
+    // 1. tokens, uniforms, temperature
+    int bad = !(T > 0.0f) || !isfinite(T);
+    for (int i = tid; i < KL; i += NT) {
+        const int x = A.tok[bKL + i];
+        s_x[i] = x;
+        bad |= (x < 0 || x >= V);
+        const float u = A.ua[bKL + i];
+        bad |= !(u >= 0.0f && u < 1.0f);
+        if (A.accept_prob) A.accept_prob[bKL + i] = NAN;
+    }
+    const float ucf = A.uc[b];
+    bad |= !(ucf >= 0.0f && ucf < 1.0f);
+    bad = __syncthreads_or(bad);
+
+    // 2. node (lowest-index draft with the same prefix) of every (k, j), j = 0..L
+    for (int i = tid; i < K * (L + 1); i += NT) {
+        const int k = i / (L + 1), j = i % (L + 1);
+        int c = k;
+        for (int cc = 0; cc < k; ++cc) {
+            int same = 1;
+            for (int t = 0; t < j; ++t) same &= (s_x[cc * L + t] == s_x[k * L + t]);
+            if (same) { c = cc; break; }
+        }
+        s_can[i] = static_cast<unsigned char>(c);
+    }
+    __syncthreads();
+
+    // 3. node rows at positions 0..L-1 must be distributions
+    if (!bad) {
+        for (int i = tid; i < KL; i += NT) {
+            const int k = i / L, j = i % L;
+            if (s_can[k * (L + 1) + j] != k) continue;
+            const RowStat a = st[k * RS + j], q = st[k * RS + L + 1 + j];
+            bad |= !(isfinite(a.shift) && a.sum > 0.0 && isfinite(a.sum));
+            bad |= !(isfinite(q.shift) && q.sum > 0.0 && isfinite(q.sum));
+        }
+    }
+    bad = __syncthreads_or(bad);
+
+    int tau = -1, kstar = -1, y = -1, flags = 0;
+    double Zp = NAN;
+    if (!bad) {
+        // 4. log2 p and log2 q of every drafted token under its node rows
+        for (int i = tid; i < KL; i += NT) {
+            const int k = i / L, j = i % L;
+            const int c = s_can[k * (L + 1) + j];
+            const int x = s_x[i];
+            const RowStat a = st[c * RS + j], q = st[c * RS + L + 1 + j];
+            const float lt = RD(trow(c, j), V).at(x);
+            const float ld = RD(drow(c, j), V).at(x);
+            s_lp[i] = (static_cast<double>(lt) - static_cast<double>(a.shift)) * c64 - log2(a.sum);
+            s_lq[i] = (static_cast<double>(ld) - static_cast<double>(q.shift)) * c64 - log2(q.sum);
+        }
+        __syncthreads();
+
+        int own = 0, nH = 0;
+        double alpha = 1.0, beta = 0.0, N = 1.0;
+        if (A.method == kMethodToken) {
+            tau = L;
+            for (int j = 0; j < L; ++j) {
+                double a = ratio_log2(s_lp[j], s_lq[j]);
+                if (a > 1.0) a = 1.0;
+                const double u = static_cast<double>(A.ua[bKL + j]);
+                if (tid == 0 && A.accept_prob) A.accept_prob[bKL + j] = static_cast<float>(a);
+                if (!(u < a)) { tau = j; break; }
+            }
+            kstar = tau > 0 ? 0 : -1;
+            beta = 1.0;   // token-level residual max(p - q, 0)
+        } else {
+            tau = 0;
+            for (int k = 0; k < K && tau < L; ++k) {
+                int match = 1;
+                for (int t = 0; t < tau; ++t) match &= (s_x[k * L + t] == s_x[own * L + t]);
+                if (!match) continue;
+                const int x = s_x[k * L + tau];
+                int dup = 0;
+                for (int i = 0; i < nH; ++i) dup |= (s_H[i] == x);
+                const int cn = s_can[own * (L + 1) + tau];
+                const RowStat np = st[cn * RS + tau], nq = st[cn * RS + L + 1 + tau];
+                bool rejected = true;
+                if (!dup) {
+                    // weight chain: first position against the node residual omega/N
+                    const double ps = exp2(s_lp[k * L + tau]);
+                    const double qs = exp2(s_lq[k * L + tau]);
+                    const double om = fmax(alpha * ps - beta * qs, 0.0);
+                    __syncthreads();   // previous readers of s_w are done
+                    if (tid == 0) {
+                        double w = (qs > 0.0) ? fmin(om / N / qs, 1.0) : (om > 0.0 ? 1.0 : 0.0);
+                        s_w[tau + 1] = w;
+                        for (int j = tau + 1; j < L; ++j) {
+                            w = chain_step(w, ratio_log2(s_lp[k * L + j], s_lq[k * L + j]));
+                            s_w[j + 1] = w;
+                        }
+                    }
+                    __syncthreads();
+                    int acc = 0;
+                    double Racc = 0.0;
+                    for (int m = L; m > tau; --m) {
+                        const double u = static_cast<double>(A.ua[bKL + k * L + m - 1]);
+                        const double wm = s_w[m];
+                        double h;
+                        if (m == L) {
+                            h = wm;
+                        } else {
+                            if (!(u < wm)) continue;      // h_m <= w_m: rejects without a sweep
+                            const int cm = s_can[k * (L + 1) + m];
+                            const RowStat sp = st[cm * RS + m], sq = st[cm * RS + L + 1 + m];
+                            SweepRows sr;
+                            sr.MP = sp.shift;
+                            sr.MQ = sq.shift;
+                            sr.a = static_cast<float>(wm / sp.sum);
+                            sr.bq = static_cast<float>(1.0 / sq.sum);
+                            const RD P(trow(cm, m), V), Q(drow(cm, m), V);
+                            const double R =
+                                sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, 0, s_red);
+                            const double d = R + 1.0 - wm;
+                            h = d > 0.0 ? R / d : 1.0;
+                            Racc = R;
+                        }
+                        if (tid == 0 && A.accept_prob)
+                            A.accept_prob[bKL + k * L + m - 1] = static_cast<float>(h);
+                        if (u < h) { acc = m; break; }
+                    }
+                    if (acc > 0) {
+                        rejected = false;
+                        tau = acc;
+                        own = k;
+                        kstar = k;
+                        nH = 0;
+                        if (tau < L) {
+                            alpha = s_w[tau];
+                            beta = 1.0;
+                            N = Racc;
+                        }
+                    }
+                }
+                if (rejected) {
+                    if (!dup) {
+                        if (tid == 0) s_H[nH] = x;
+                        ++nH;
+                        __syncthreads();
+                    }
+                    beta += N;
+                    SweepRows sr;
+                    sr.MP = np.shift;
+                    sr.MQ = nq.shift;
+                    sr.a = static_cast<float>(alpha / np.sum);
+                    sr.bq = static_cast<float>(beta / nq.sum);
+                    const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
+                    N = sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, s_red);
+                }
+                if (tau < L && !(N > 0.0)) {
+                    flags |= kFlagDegenerate;   // only rounding empties a residual
+                    alpha = 1.0;
+                    beta = 0.0;
+                    N = 1.0;
+                    nH = 0;
+                }
+            }
+        }
+
+        // 5. correction token
+        const double u = static_cast<double>(ucf);
+        if (tau == L) {
+            const int cb = s_can[(kstar < 0 ? 0 : kstar) * (L + 1) + L];
+            const RD P(trow(cb, L), V);
+            const float M = sweep_rowmax<NT, RD>(P, nch, s_fred);
+            SweepRows sr;
+            sr.MP = M;
+            sr.MQ = 0.0f;
+            sr.a = 1.0f;
+            sr.bq = 0.0f;
+            double Z;
+            y = (M > -INFINITY && M < INFINITY)
+                    ? sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
+                                                s_red, s_ired)
+                    : -1;
+            Zp = 1.0;
+            if (y < 0) bad = 1;   // the target row after the block is not a distribution
+        } else {
+            const int cn = s_can[own * (L + 1) + tau];
+            const RowStat np = st[cn * RS + tau], nq = st[cn * RS + L + 1 + tau];
+            const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
+            SweepRows sr;
+            sr.MP = np.shift;
+            sr.MQ = nq.shift;
+            sr.a = static_cast<float>(alpha / np.sum);
+            sr.bq = static_cast<float>(beta / nq.sum);
+            double Z;
+            y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, u, &Z, s_tile, s_red,
+                                         s_ired);
+            Zp = Z;
+            if (y < 0) {
+                flags |= kFlagDegenerate;
+                sr.a = static_cast<float>(1.0 / np.sum);
+                sr.bq = 0.0f;
+                y = sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
+                                              s_red, s_ired);
+                Zp = Z;
+            }
+        }
+    }
+
+    if (tid == 0) {
+        if (bad) {
+            tau = -1;
+            kstar = -1;
+            y = -1;
+            flags |= kFlagInvalid;
+            Zp = NAN;
+        }
+        A.accept_len[b] = tau;
+        A.draft_index[b] = kstar;
+        A.correction[b] = y;
+        if (A.flags) A.flags[b] = flags;
+        if (A.resid_mass) A.resid_mass[b] = static_cast<float>(Zp);
+    }
+    if (A.row_lse) {
+        float *o = A.row_lse + static_cast<long long>(b) * K * RS;
+        for (int i = tid; i < K * RS; i += NT) {
+            const int k = i / RS, r = i % RS;
+            const int j = r <= L ? r : r - L - 1;
+            const int c = s_can[k * (L + 1) + j];
+            float v = NAN;
+            if (!bad && (r != L || A.bonus_stats)) {
+                const RowStat a = st[c * RS + r];
+                v = static_cast<float>((static_cast<double>(a.shift) * c64 + log2(a.sum)) *
+                                       0.6931471805599453);
+            }
+            o[i] = v;
+        }
+    }
+}
+
+}  // namespace sv

@@ -1,0 +1,163 @@
+/*
+ * spec_verify.h -- batched verification of drafted tokens on AMD MI355X (gfx950).
+ *
+ * Speculative decoding lets a small draft model propose a run of tokens that
+ * the large target model then checks in one parallel pass (MineDraft page,
+ * section 1; SpecTr-GBV page, section 1).  This library implements that check
+ * for a batch of B requests, each with K i.i.d. drafted blocks of length L
+ * over a vocabulary of V tokens, given the target and draft logits:
+ *
+ *   spec_verify_token       token-level speculative sampling (K = 1): accept
+ *                           token x with probability min(1, p(x)/q(x)), stop at
+ *                           the first rejection and resample from the residual
+ *                           norm(max(p - q, 0)) -- the standard rule the
+ *                           speculative-decoding pages build on;
+ *   spec_verify_block       greedy block verification, GBV (K = 1): the whole
+ *                           block is verified jointly, the single-draft method
+ *                           of the SpecTr-GBV page, section 1;
+ *   spec_verify_multidraft  GBV over K i.i.d. drafts as the SpecTr-GBV page,
+ *                           section 2 ("algorithmic procedure", steps 1-5),
+ *                           describes it: walk the drafts, skip rejected
+ *                           sub-blocks, keep the longest accepted prefix tau,
+ *                           draw the correction from the target (tau = L) or
+ *                           from the residual (tau < L), one O(V) sweep per
+ *                           selection step and no search over a scaling factor
+ *                           (section 3, efficiency).
+ *
+ * Every call is asynchronous on the caller's HIP stream: it validates its
+ * arguments on the host, launches kernels and returns without synchronising.
+ * The library never allocates device memory; scratch comes from the caller's
+ * workspace.  Calls that share a workspace must be ordered on one stream.
+ *
+ * Notation.  T_b is request b's temperature; the temperature softmax of a logit
+ * row l is pi(v) = exp(l_v / T_b) / sum_v' exp(l_v' / T_b).  For draft k of
+ * request b, target row j (j = 0..L) and draft row j (j = 0..L-1) are the
+ * target and draft distributions of the token at position j+1, given the
+ * prefix X[b][k][0..j-1]; X[b][k][j] was drawn from draft row j.
+ *
+ * Node rows.  Drafts of one request that share the prefix X[..][0..j-1] stand at
+ * the same node of the draft tree, so their rows j must describe the same
+ * distribution.  The library reads each node's rows from the lowest-index draft
+ * with that prefix and never reads the duplicates, so a caller may leave them
+ * unwritten.  (The pages do not fix this; it is the reading that keeps every
+ * draft at a node tested against one distribution.)
+ *
+ * Decision rules, stated precisely:
+ *  - tests are strict: a test with acceptance probability h accepts iff u < h,
+ *    with u in [0, 1) taken from u_accept[b][k][m-1] for position m of draft k;
+ *  - among several accepted positions of one block the largest wins;
+ *  - the correction is the inverse-CDF draw in token-id order:
+ *    y = min{v : C_v > u_correct[b] * Z}, C_v = sum_{v' <= v} omega(v'),
+ *    Z = C_{V-1}, over the (unnormalised) correction weights omega;
+ *  - the K-draft residual at a node s is omega(v) = [v not in H] *
+ *    max(alpha p_s(v) - beta q_s(v), 0); a rejection adds the residual mass N
+ *    to beta; a draft whose token at s is already in H is rejected without a
+ *    test (its uniforms are not consumed) and still adds N to beta.
+ * Integer outputs match the CPU oracle bit for bit except where a decision lies
+ * within floating-point error of its threshold (|u - h| of order 1e-6).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Nothing is launched when a call returns anything but SV_OK. */
+typedef enum {
+    SV_OK = 0,
+    SV_EINVAL = 1,        /* null pointer, size out of range, K != 1 for token/block */
+    SV_EUNSUPPORTED = 2,  /* dtype or size this build does not handle */
+    SV_EHIP = 3,          /* a HIP runtime call failed (no device, launch error) */
+    SV_EWORKSPACE = 4     /* workspace missing, misaligned or too small */
+} sv_status;
+
+/* Element type of both logit tensors. */
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Limits of this build. */
+#define SV_MAX_K 64
+#define SV_MAX_L 16
+#define SV_MAX_V (1 << 22)
+
+/* Per-request flag bits (sv_outputs.flags). */
+#define SV_FLAG_DEGENERATE 1  /* a residual of zero mass was met (rounding only);
+                                 the node's target distribution was used instead */
+#define SV_FLAG_INVALID 2     /* request data the rules cannot act on: T not a
+                                 positive finite number, a token outside [0, V),
+                                 a uniform outside [0, 1), or a node row that is
+                                 not a distribution (NaN, +inf, all -inf) */
+
+/* Inputs.  All pointers are DEVICE pointers owned by the caller, row-major,
+ * read-only for the library, and must stay valid until the stream reaches the
+ * end of the call.  Logit tensors need 4-byte alignment; the fast path needs
+ * 16-byte alignment of both base pointers and V * sizeof(element) divisible by 16. */
+typedef struct sv_inputs {
+    int32_t B;                    /* requests, >= 0 (B = 0 is a no-op) */
+    int32_t K;                    /* drafts per request, 1..SV_MAX_K */
+    int32_t L;                    /* draft length, 1..SV_MAX_L */
+    int32_t V;                    /* vocabulary size, 1..SV_MAX_V */
+    int32_t dtype;                /* sv_dtype of both logit tensors */
+    const void *target_logits;    /* [B][K][L+1][V] */
+    const void *draft_logits;     /* [B][K][L][V] */
+    const int32_t *draft_tokens;  /* [B][K][L], X[b][k][j] drawn from draft row j */
+    const float *temperature;     /* [B], T_b > 0 */
+    const float *u_accept;        /* [B][K][L], uniforms in [0, 1) */
+    const float *u_correct;       /* [B], uniforms in [0, 1) */
+} sv_inputs;
+
+/* Outputs.  DEVICE pointers owned by the caller; every element of every
+ * non-null output is overwritten.  The three integer outputs are required. */
+typedef struct sv_outputs {
+    int32_t *accept_len;   /* [B] tau in [0, L]; -1 for an invalid request */
+    int32_t *draft_index;  /* [B] the draft whose prefix was accepted, -1 iff tau <= 0 */
+    int32_t *correction;   /* [B] token id in [0, V); -1 for an invalid request */
+    int32_t *flags;        /* optional [B]: SV_FLAG_* bits */
+    float *row_lse;        /* optional [B][K][2L+1]: ln sum_v exp(l_v / T_b) of the node
+                              row read for (k, row); rows 0..L are target rows,
+                              L+1..2L draft rows 0..L-1.  Requesting it adds one
+                              pass over the target rows at position L. */
+    float *accept_prob;    /* optional [B][K][L]: h of each test evaluated exactly,
+                              NaN where no test was made or where the test was
+                              settled by the bound h <= w without computing h */
+    float *resid_mass;     /* optional [B]: mass Z (in probability units) of the
+                              distribution the correction was drawn from */
+} sv_outputs;
+
+/* Launch resources. */
+typedef struct sv_launch {
+    void *stream;          /* hipStream_t to launch on; NULL = the null stream */
+    void *workspace;       /* device scratch, 256-byte aligned, contents need not
+                              be initialised, >= sv_workspace_size(...) bytes */
+    size_t workspace_bytes;
+    void *phase_events[3]; /* optional hipEvent_t: if non-null, recorded on `stream`
+                              before the row-statistics kernel, between it and the
+                              walk kernel, and after the walk kernel (timing) */
+} sv_launch;
+
+/* Workspace bytes a call with these sizes needs (0 on invalid sizes). */
+size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
+
+/* Token-level speculative sampling (K must be 1). */
+int spec_verify_token(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* Greedy block verification of one draft (K must be 1). */
+int spec_verify_block(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* Block verification over K i.i.d. drafts (K >= 1; K = 1 equals spec_verify_block). */
+int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* Static description of a status code. */
+const char *sv_status_string(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char *sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Integer outputs (accept_len, draft_index, correction) must be bit-identical,
+except for requests whose oracle decision log holds a decision within 1e-6 of
+its threshold (or a degenerate residual); those are counted and reported.
+Diagnostics: row ln-partition functions within 1e-5 relative, acceptance
+probabilities within 1e-5 absolute, correction mass within 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paritytools as pt
+import synth
+from draft_token_verification_online_amd import Verifier
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _verify(method, batch, diagnostics=True):
+    t = batch["target"]
+    B, K, L1, V = t.shape
+    v = Verifier(method, B, K, L1 - 1, V, t.dtype, diagnostics=diagnostics)
+    out = v(batch["target"], batch["draft"], batch["tokens"], batch["temperature"],
+            batch["u_accept"], batch["u_correct"])
+    torch.cuda.synchronize()
+    return out
+
+
+def _parity(method, batch, label, requests=None, diagnostics=True):
+    print(f"[case] {label} method={method} shape={tuple(batch['target'].shape)} "
+          f"dtype={batch['target'].dtype}", flush=True)
+    out = _verify(method, batch, diagnostics=diagnostics)
+    B = batch["target"].shape[0]
+    req = list(range(B)) if requests is None else list(requests)
+    host = synth.to_host(batch, req)
+    ref = pt.run_oracle(method, host, diagnostics=diagnostics)
+    rep = pt.compare(method, out, ref, req, diagnostics=diagnostics, label=label)
+    pt.check(rep)
+    return rep, out, ref
+
+
+# ---------------------------------------------------------------- small sizes
+# Several tiles of the walk (512 threads x 8 elements), ragged tails, the
+# scalar path (V not a multiple of 8), every temperature the pages study.
+
+SMALL = [
+    # name, workload, overrides
+    ("tiny_fp32", W["tiny_fp32_b1_k1_l4_v32"], dict(B=64)),
+    ("gbv_bf16_v8200", W["gbv_bf16_b64_k1_l5_v32000"], dict(B=48, V=8200)),
+    ("gbv_bf16_v4099_scalar", W["gbv_bf16_b64_k1_l5_v32000"], dict(B=32, V=4099)),
+    ("multi_k4_v12296", W["multi_bf16_b256_k4_l4_v128256"], dict(B=48, V=12296)),
+    ("multi_zipf_k8_l8_v9000", W["multi_zipf_bf16_b512_k8_l8_v151936"], dict(B=32, V=9000)),
+    ("multi_mixedT_k4_l8_v5003", W["multi_mixedT_bf16_b1024_k4_l8_v151936"], dict(B=40, V=5003)),
+    ("multi_fp32_k3_v777", W["multi_bf16_b256_k4_l4_v128256"],
+     dict(B=40, K=3, V=777, dtype=torch.float32)),
+]
+
+
+@pytest.mark.parametrize("name,w,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(name, w, over):
+    ws = synth.scaled(w, **over)
+    methods = ("token", "block") if ws.K == 1 else ("multidraft",)
+    for seed in (1, 2):
+        batch = pt.gpu_batch(ws, seed)
+        for method in methods:
+            _parity(method, batch, f"{name}/seed{seed}")
+
+
+def test_block_equals_multidraft_with_one_draft():
+    ws = synth.scaled(W["gbv_bf16_b64_k1_l5_v32000"], B=64, V=3000)
+    batch = pt.gpu_batch(ws, 3)
+    a = _verify("block", batch)
+    b = _verify("multidraft", batch)
+    for k in ("accept_len", "draft_index", "correction", "flags"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_temperatures_of_the_ablation():
+    """T in {0.1, 0.4, 0.7} (SpecTr-GBV page, section 4, ablations)."""
+    for T in (0.1, 0.4, 0.7):
+        ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=32, V=4096, temperature=T)
+        _parity("multidraft", pt.gpu_batch(ws, 4), f"multi_T{T}")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_batch_is_a_noop():
+    v = Verifier("multidraft", 0, 2, 3, 64, torch.bfloat16)
+    z = torch.empty(0, device="cuda")
+    out = v(torch.empty((0, 2, 4, 64), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((0, 2, 3, 64), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((0, 2, 3), dtype=torch.int32, device="cuda"), z,
+            torch.empty((0, 2, 3), device="cuda"), z)
+    torch.cuda.synchronize()
+    assert out["accept_len"].numel() == 0
+
+
+def test_invalid_requests_are_flagged():
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=8, V=1024)
+    batch = pt.gpu_batch(ws, 5)
+    batch["target"][0, 0, 0, 7] = float("nan")          # NaN in a node row
+    batch["tokens"][1, 2, 1] = 1024                     # token outside [0, V)
+    batch["temperature"][2] = 0.0                       # T must be > 0
+    batch["u_accept"][3, 0, 0] = 1.0                    # u must be < 1
+    batch["draft"][4, 0, 2] = float("-inf")             # a row of zero mass
+    batch["u_correct"][5] = -0.25                       # u must be >= 0
+    rep, out, ref = _parity("multidraft", batch, "invalid")
+    al = out["accept_len"].cpu().numpy()
+    assert (al[:6] == -1).all()
+    assert (out["flags"].cpu().numpy()[:6] & oracle.FLAG_INVALID).all()
+    assert (al[6:] >= 0).all()
+
+
+def test_equal_rows_accept_whole_block():
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=16, V=2048)
+    batch = pt.gpu_batch(ws, 6)
+    batch["draft"].copy_(batch["target"][:, :, :ws.L])
+    for method, K in (("multidraft", ws.K),):
+        rep, out, _ = _parity(method, batch, "p_equals_q")
+        assert (out["accept_len"] == ws.L).all()
+
+
+def test_single_token_vocabulary():
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=8, V=1)
+    batch = pt.gpu_batch(ws, 7)
+    rep, out, _ = _parity("multidraft", batch, "V1")
+    assert (out["accept_len"] == ws.L).all() and (out["correction"] == 0).all()
+
+
+def test_largest_k_and_l():
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=6, K=64, L=16, V=96,
+                      temperature=1.5)
+    _parity("multidraft", pt.gpu_batch(ws, 8), "K64_L16")
+
+
+def test_duplicate_rows_are_never_read():
+    ws = synth.scaled(W["multi_zipf_bf16_b512_k8_l8_v151936"], B=16, V=2048)
+    batch = pt.gpu_batch(ws, 9)
+    ref = _verify("multidraft", batch)
+    ref = {k: v.clone() for k, v in ref.items()}
+    tok = batch["tokens"].cpu().numpy()
+    B, K, L = tok.shape
+    for b in range(B):
+        for k in range(1, K):
+            for j in range(L + 1):
+                if any((tok[b, c, :j] == tok[b, k, :j]).all() for c in range(k)):
+                    batch["target"][b, k, j] = float("nan")
+                    if j < L:
+                        batch["draft"][b, k, j] = float("nan")
+    out = _verify("multidraft", batch)
+    for k in ("accept_len", "draft_index", "correction", "flags", "row_lse", "resid_mass"):
+        assert torch.equal(out[k].nan_to_num(-7.0), ref[k].nan_to_num(-7.0)), k
+
+
+def test_negative_infinity_entries():
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=24, V=4096)
+    batch = pt.gpu_batch(ws, 10)
+    g = torch.Generator(device="cuda").manual_seed(10)
+    for key in ("target", "draft"):
+        mask = torch.rand(batch[key].shape, generator=g, device="cuda") < 0.3
+        batch[key].masked_fill_(mask, float("-inf"))
+    # redraw nothing: tokens may now sit on zero-probability entries of q
+    _parity("multidraft", batch, "neg_inf_entries")
+
+
+def test_misaligned_rows_take_the_scalar_path():
+    ws = synth.scaled(W["gbv_bf16_b64_k1_l5_v32000"], B=16, V=2048)
+    batch = pt.gpu_batch(ws, 11)
+    for key in ("target", "draft"):
+        t = batch[key]
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        view = buf[1:].view(t.shape)             # 2-byte offset: not 16-byte aligned
+        view.copy_(t)
+        batch[key] = view
+    _parity("block", batch, "misaligned")
+
+
+# ---------------------------------------------------------------- full sizes
+# The five workloads at their full shapes, in the launch configuration the
+# benchmark times (no diagnostics); the oracle checks a sample of requests.
+
+FULL = list(W)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    w = W[name]
+    batch = pt.gpu_batch(w, 1234)
+    rng = np.random.default_rng(5)
+    n = min(w.B, 24)
+    req = sorted(rng.choice(w.B, size=n, replace=False).tolist())
+    for method in w.methods:
+        _parity(method, batch, f"full/{name}", requests=req, diagnostics=False)
+    del batch
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", FULL[2:])
+def test_full_size_diagnostics(name):
+    w = W[name]
+    batch = pt.gpu_batch(w, 99)
+    req = [0, 1, w.B // 2, w.B - 1]
+    for method in w.methods:
+        _parity(method, batch, f"full_diag/{name}", requests=req, diagnostics=True)
+    del batch
+    torch.cuda.empty_cache()
