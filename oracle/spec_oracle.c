@@ -131,10 +131,13 @@ static int svo_row_valid(const svo_req *r, int target, int k, int j)
 /* ------------------------------------------------------------- softmax */
 
 /* Temperature softmax of a node row:
- *   pi(v) = exp((l_v - max) / T) / sum_v' exp((l_v' - max) / T). */
+ *   pi(v) = exp((l_v - max) / T) / sum_v' exp((l_v' - max) / T).
+ * A row that is read but is not a distribution makes the request invalid. */
 static void svo_softmax(svo_req *r, int target, int k, int j, double *out)
 {
     int c = svo_canon(r, k, j);
+    if (!svo_row_valid(r, target, k, j))
+        r->flags |= SVO_FLAG_INVALID;
     r->touched[(target ? j : r->L + 1 + j) * r->K + c] = 1;
     double mx = -INFINITY;
     for (int v = 0; v < r->V; ++v) {
@@ -492,8 +495,8 @@ static void svo_run_multi(svo_req *r, int32_t *tau_o, int32_t *k_o, int32_t *y_o
 /* ------------------------------------------------------------ validation */
 
 /* Request data the rules cannot act on: T not a positive finite number, a
- * token outside [0, V), a uniform outside [0, 1), or a node row at positions
- * 0..L-1 that is not a distribution (NaN, +inf, or all -inf). */
+ * token outside [0, V) or a uniform outside [0, 1).  (A node row that is not a
+ * distribution -- NaN, +inf or all -inf -- is detected when it is read.) */
 static int svo_request_valid(const svo_req *r)
 {
     if (!(r->T > 0.0) || !isfinite(r->T))
@@ -506,13 +509,6 @@ static int svo_request_valid(const svo_req *r)
     }
     if (!(r->uc >= 0.0 && r->uc < 1.0))
         return 0;
-    for (int k = 0; k < r->K; ++k)
-        for (int j = 0; j < r->L; ++j) {
-            if (svo_canon(r, k, j) != k)
-                continue;
-            if (!svo_row_valid(r, 1, k, j) || !svo_row_valid(r, 0, k, j))
-                return 0;
-        }
     return 1;
 }
 
@@ -524,7 +520,8 @@ static int svo_request_valid(const svo_req *r)
  *   tokens [B][K][L], temperature [B], u_accept [B][K][L], u_correct [B].
  * Outputs [B]: accept_len (-1 for invalid request data), draft_index (-1 iff
  * accept_len <= 0), correction, flags (bit 0 degenerate residual, bit 1
- * invalid data).  Optional (NULL to skip): row_lse [B][K][2L+1] (target rows
+ * invalid data: bad T, token or uniform, or a row read by the rules that is
+ * not a distribution).  Optional (NULL to skip): row_lse [B][K][2L+1] (target rows
  * 0..L then draft rows 0..L-1, each the node row's ln-partition function at
  * T), accept_prob [B][K][L] (h of every evaluated test, NaN elsewhere),
  * resid_mass [B] (mass Z of the distribution the correction was drawn from,
@@ -598,13 +595,9 @@ int svo_verify(int method, int B, int K, int L, int V, int dtype,
         } else {
             svo_run_multi(&r, &tau, &ks, &y, &Z);
         }
-        if (y < 0 && !(r.flags & SVO_FLAG_INVALID)) {
-            /* the bonus row of the winning draft is not a distribution */
-            r.flags |= SVO_FLAG_INVALID;
-            tau = -1;
-            ks = -1;
-        }
         if (r.flags & SVO_FLAG_INVALID) {
+            r.flags = SVO_FLAG_INVALID;
+            r.margin = INFINITY;
             tau = -1;
             ks = -1;
             y = -1;

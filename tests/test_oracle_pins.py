@@ -239,8 +239,26 @@ def test_invalid_request_data_is_flagged():
     drf[4, 0, 1, :] = -np.inf                # a row of zero mass
     o = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc)
     assert (o["accept_len"][:5] == -1).all()
-    assert (o["flags"][:5] & oracle.FLAG_INVALID).all()
+    assert (o["flags"][:5] == oracle.FLAG_INVALID).all()
     assert o["accept_len"][5] >= 0 and not o["flags"][5] & oracle.FLAG_INVALID
+
+
+def test_rows_never_read_cannot_invalidate():
+    """Validity is checked where a row is read: NaN in rows past the first
+    token-level rejection changes nothing."""
+    rng = np.random.default_rng(21)
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, 20, 1, 3, 12)
+    tgt[:, 0, 0, tok[:, 0, 0]] = -np.inf      # p(x) = 0: position 1 always rejects
+    a = oracle.verify("token", tgt, drf, tok, temps, ua, uc)
+    assert (a["accept_len"] == 0).all()
+    tgt[:, 0, 1:] = np.nan
+    drf[:, 0, 1:] = np.nan
+    b = oracle.verify("token", tgt, drf, tok, temps, ua, uc)
+    for key in ("accept_len", "draft_index", "correction", "flags"):
+        np.testing.assert_array_equal(a[key], b[key])
+    drf[:, 0, 0, 5] = np.nan                   # a row that is read
+    c = oracle.verify("token", tgt, drf, tok, temps, ua, uc)
+    assert (c["flags"] == oracle.FLAG_INVALID).all()
 
 
 def test_golden_worked_examples():
