@@ -8,9 +8,10 @@ the per-request walk).  Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 The roofline object describes the row-statistics kernel (the one that streams
-the logits): achieved = node-row bytes per launch / its mean duration, timed
-with HIP events recorded on the launch stream around that kernel in every
-timed step.  The cpu_baseline object times the CPU oracle (unmodified,
+the logits): achieved = bytes of the rows it streams per step (rows_streamed *
+V * sizeof(logit), reported by the library) / its time per step (its one or two
+launches), timed with HIP events recorded on the launch stream around those
+launches in every timed step.  The cpu_baseline object times the CPU oracle (unmodified,
 single-threaded per request) on a bounded sample of the same batch across the
 host's cores.
 """
@@ -77,21 +78,6 @@ class HipEvents:
         for e in self.made:
             self.hip.hipEventDestroy(e)
         self.made = []
-
-
-def node_rows(tokens_host) -> int:
-    """Rows the statistics kernel reads: for every position j < L, one target and
-    one draft row per distinct prefix X[0..j-1] among a request's drafts."""
-    B, K, L = tokens_host.shape
-    n = 0
-    for j in range(L):
-        if j == 0:
-            n += 2 * B
-            continue
-        pre = tokens_host[:, :, :j]
-        for b in range(B):
-            n += 2 * len({bytes(pre[b, k].tobytes()) for k in range(K)})
-    return n
 
 
 def read_traffic(workload: str, launch_bytes: float):
@@ -177,10 +163,7 @@ def main():
     log(f"[bench] generating {name} on cuda:0 (seed {args.seed})")
     batch = synth.generate(w, args.seed, device="cuda")
     torch.cuda.synchronize()
-    tok_host = batch["tokens"].cpu().numpy()
     es = 2 if w.dtype == torch.bfloat16 else 4
-    rows = node_rows(tok_host)
-    stats_bytes = rows * w.V * es
     dense = synth.dense_bytes(w)
 
     ver = sv.Verifier(method, w.B, w.K, w.L, w.V, w.dtype)
@@ -191,7 +174,7 @@ def main():
     for _ in range(args.warmup):
         ver(*args_in, stream=stream)
     torch.cuda.synchronize()
-    evs = [[hip.create() for _ in range(3)] for _ in range(args.steps)]
+    evs = [[hip.create() for _ in range(sv.N_PHASE_EVENTS)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps of {method} on {name}")
 
     torch.cuda.synchronize()
@@ -201,9 +184,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    stats_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
-    walk_ms = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    # events: [0] stats launch 1 [1] walk round 1 [2] stats launch 2 [3] walk round 2 [4]
+    phase = [[hip.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in evs]
+    stats_ms = [p[0] + p[2] for p in phase]
+    walk_ms = [p[1] + p[3] for p in phase]
+    phase_mean = [sum(p[i] for p in phase) / len(phase) for i in range(4)]
     hip.close()
+    rows = int(ver.out["rows_streamed"].sum())          # rows the statistics kernel streamed
+    stats_bytes = rows * w.V * es
     ms_per_step = wall * 1e3 / args.steps
     tokens = synth.tokens_per_step(w)
     value = tokens / (ms_per_step * 1e-3)
@@ -260,8 +248,10 @@ def main():
         "detail": {
             "rowstats_ms": st_mean,
             "walk_ms": wk_mean,
-            "node_rows_per_launch": rows,
-            "node_row_bytes": stats_bytes,
+            "phase_ms": {"rowstats_first_visit": phase_mean[0], "walk_round1": phase_mean[1],
+                         "rowstats_after_accept": phase_mean[2], "walk_round2": phase_mean[3]},
+            "rows_streamed_per_step": rows,
+            "rows_streamed_bytes": stats_bytes,
             "dense_logit_bytes": dense,
             "dense_equiv_GBps_per_step": dense / (ms_per_step * 1e-3) / 1e9,
             "mean_accept_len": float(ver.out["accept_len"].float().mean()),

@@ -37,12 +37,16 @@ class SvInputs(ctypes.Structure):
 
 class SvOutputs(ctypes.Structure):
     _fields_ = [("accept_len", _vp), ("draft_index", _vp), ("correction", _vp),
-                ("flags", _vp), ("row_lse", _vp), ("accept_prob", _vp), ("resid_mass", _vp)]
+                ("flags", _vp), ("row_lse", _vp), ("accept_prob", _vp), ("resid_mass", _vp),
+                ("rows_streamed", _vp)]
+
+
+N_PHASE_EVENTS = 5
 
 
 class SvLaunch(ctypes.Structure):
     _fields_ = [("stream", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
-                ("phase_events", _vp * 3)]
+                ("phase_events", _vp * N_PHASE_EVENTS)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -117,6 +121,7 @@ class Verifier:
                     "correction": torch.empty(B, **i32)}
         if with_flags or diagnostics:
             self.out["flags"] = torch.empty(B, **i32)
+            self.out["rows_streamed"] = torch.empty(B, **i32)
         if diagnostics:
             f32 = dict(dtype=torch.float32, device=dev)
             self.out["row_lse"] = torch.empty((B, K, 2 * L + 1), **f32)
@@ -128,7 +133,7 @@ class Verifier:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self._outs = SvOutputs(*[_ptr(self.out.get(k)) for k in
                                  ("accept_len", "draft_index", "correction", "flags",
-                                  "row_lse", "accept_prob", "resid_mass")])
+                                  "row_lse", "accept_prob", "resid_mass", "rows_streamed")])
 
     def __call__(self, target, draft, tokens, temperature, u_accept, u_correct, *,
                  stream=None, events=None):
@@ -147,7 +152,7 @@ class Verifier:
                        u_correct.data_ptr())
         if stream is None:
             stream = torch.cuda.current_stream(target.device).cuda_stream
-        ev = (_vp * 3)(*(events or (None, None, None)))
+        ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
         ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
         rc = self._fn(ctypes.byref(ins), ctypes.byref(self._outs), ctypes.byref(ln))
         if rc != SV_OK:

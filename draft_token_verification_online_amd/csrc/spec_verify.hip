@@ -1,10 +1,14 @@
 // spec_verify.hip -- C ABI of the verification library (see include/spec_verify.h).
 //
 // A call validates everything it can on the host before touching the device,
-// then launches two kernels on the caller's stream:
-//   1. rowstats_kernel  -- one workgroup per node row: softmax statistics;
-//                          this is the kernel that streams the logits from HBM;
-//   2. walk_kernel      -- one workgroup per request: the verification walk.
+// then launches on the caller's stream:
+//   1. rowstats_kernel  -- one workgroup per node row: softmax statistics of the
+//                          rows the walk reads first (streams the logits);
+//   2. walk_kernel      -- one workgroup per request: the verification walk; with
+//                          K > 1 it may stop after an acceptance, flagging the rows
+//                          below the accepted node;
+//   3. rowstats_kernel  -- (K > 1) statistics of the flagged rows;
+//   4. walk_kernel      -- (K > 1) resumes the stopped walks.
 // No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
@@ -20,6 +24,7 @@ namespace {
 constexpr int kStatsThreads = 256;
 constexpr int kWalkThreads = 512;
 constexpr long long kMaxStatsGrid = 1LL << 22;
+constexpr long long kListGrid = 4096;
 constexpr int kMaxB = 1 << 24;
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
@@ -41,25 +46,56 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
            sizeof(sv::RowStat);
 }
 
+// Workspace: row statistics | walk states | node rows flagged for the second
+// round (bytes, then the same rows as a list) | list length.
+struct Layout {
+    size_t stats, state, need, list, count, total;
+};
+
+Layout layout(int32_t B, int32_t K, int32_t L) {
+    Layout l;
+    const size_t bkl = static_cast<size_t>(B) * K * L;
+    l.stats = 0;
+    l.state = align_up(stats_bytes(B, K, L), 256);
+    l.need = l.state + align_up(static_cast<size_t>(B) * sizeof(sv::WalkState), 256);
+    l.list = l.need + align_up(bkl, 256);
+    l.count = l.list + align_up(2 * bkl * sizeof(sv::RowRef), 256);
+    l.total = l.count + 256;
+    return l;
+}
+
+hipError_t record(const sv_launch *ln, int i, hipStream_t stream) {
+    return ln->phase_events[i] ? hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[i]), stream)
+                               : hipSuccess;
+}
+
 template <typename E, bool VEC>
 hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln, int method) {
     using RD = typename sv::RowOf<E, VEC>::type;
     hipStream_t stream = static_cast<hipStream_t>(ln->stream);
-    const bool bonus = out->row_lse != nullptr;
+    const bool diagnostics = out->row_lse != nullptr;
+    // a second round only pays when several drafts can share an accepted prefix
+    const bool two_round = method == sv::kMethodBlockWalk && in->K > 1 && !diagnostics;
+    const Layout lay = layout(in->B, in->K, in->L);
+    char *ws = static_cast<char *>(ln->workspace);
 
     sv::StatsArgs sa;
     sa.tgt = in->target_logits;
     sa.drf = in->draft_logits;
     sa.tok = in->draft_tokens;
     sa.temp = in->temperature;
-    sa.stats = static_cast<sv::RowStat *>(ln->workspace);
+    sa.stats = reinterpret_cast<sv::RowStat *>(ws + lay.stats);
+    sa.list = reinterpret_cast<const sv::RowRef *>(ws + lay.list);
+    sa.list_count = reinterpret_cast<unsigned *>(ws + lay.count);
     sa.B = in->B;
     sa.K = in->K;
     sa.L = in->L;
     sa.V = in->V;
-    sa.rows_per_draft = 2 * in->L + (bonus ? 1 : 0);
-    const long long nrows = static_cast<long long>(in->B) * in->K * sa.rows_per_draft;
-    const unsigned grid = static_cast<unsigned>(nrows < kMaxStatsGrid ? nrows : kMaxStatsGrid);
+    sa.mode = diagnostics ? sv::kSelectAllNodes : sv::kSelectFirstVisit;
+    auto grid_for = [&](int rows_per_draft) {
+        const long long n = static_cast<long long>(in->B) * in->K * rows_per_draft;
+        return static_cast<unsigned>(n < kMaxStatsGrid ? n : kMaxStatsGrid);
+    };
 
     sv::WalkArgs wa;
     wa.tgt = in->target_logits;
@@ -74,32 +110,51 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.L = in->L;
     wa.V = in->V;
     wa.method = method;
-    wa.bonus_stats = bonus ? 1 : 0;
+    wa.all_nodes = diagnostics ? 1 : 0;
+    wa.round = 1;
+    wa.two_round = two_round ? 1 : 0;
+    wa.state = reinterpret_cast<sv::WalkState *>(ws + lay.state);
+    wa.need = reinterpret_cast<unsigned char *>(ws + lay.need);
+    wa.list = reinterpret_cast<sv::RowRef *>(ws + lay.list);
+    wa.list_count = sa.list_count;
     wa.accept_len = out->accept_len;
     wa.draft_index = out->draft_index;
     wa.correction = out->correction;
     wa.flags = out->flags;
+    wa.rows_streamed = out->rows_streamed;
     wa.row_lse = out->row_lse;
     wa.accept_prob = out->accept_prob;
     wa.resid_mass = out->resid_mass;
 
     hipError_t err;
-    if (ln->phase_events[0] &&
-        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[0]), stream)) != hipSuccess)
-        return err;
-    hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>), dim3(grid),
-                       dim3(kStatsThreads), 0, stream, sa);
+    if ((err = record(ln, 0, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>),
+                       dim3(grid_for(2 * in->L + (diagnostics ? 1 : 0))), dim3(kStatsThreads), 0,
+                       stream, sa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ln->phase_events[1] &&
-        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[1]), stream)) != hipSuccess)
-        return err;
+    if ((err = record(ln, 1, stream)) != hipSuccess) return err;
     hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads), 0,
                        stream, wa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ln->phase_events[2] &&
-        (err = hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[2]), stream)) != hipSuccess)
-        return err;
-    return hipSuccess;
+    if ((err = record(ln, 2, stream)) != hipSuccess) return err;
+    if (two_round) {
+        // the listed rows: at most 2*B*K*L, usually a few thousand; each block
+        // takes rows grid-stride from the list
+        sa.mode = sv::kSelectListed;
+        const long long most = 2LL * in->B * in->K * in->L;
+        const unsigned grid2 = static_cast<unsigned>(most < kListGrid ? most : kListGrid);
+        hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>), dim3(grid2),
+                           dim3(kStatsThreads), 0, stream, sa);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if ((err = record(ln, 3, stream)) != hipSuccess) return err;
+    if (two_round) {
+        wa.round = 2;
+        hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads),
+                           0, stream, wa);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return record(ln, 4, stream);
 }
 
 int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
@@ -117,7 +172,7 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
     const uintptr_t da = reinterpret_cast<uintptr_t>(in->draft_logits);
     if (ta % es || da % es) return SV_EINVAL;
     if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
-    if (ln->workspace_bytes < stats_bytes(in->B, in->K, in->L)) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < layout(in->B, in->K, in->L).total) return SV_EWORKSPACE;
 
     const bool vec = (in->V % 8 == 0) && (ta % 16 == 0) && (da % 16 == 0);
     hipError_t err;
@@ -136,7 +191,7 @@ extern "C" {
 
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
     if (!sizes_ok(B, K, L, V, dtype)) return 0;
-    const size_t n = align_up(stats_bytes(B, K, L), 256);
+    const size_t n = layout(B, K, L).total;
     return n ? n : 256;
 }
 

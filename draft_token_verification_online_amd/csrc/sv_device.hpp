@@ -30,12 +30,15 @@ __device__ __forceinline__ void split_scale(double c, float &hi, float &lo) {
     lo = static_cast<float>(c - static_cast<double>(hi));
 }
 
-// Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7.
+// Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7; raw(c) issues
+// the same load into a compact register form that unpack() expands later, so
+// several chunks can be in flight at 4 VGPRs each (bf16).
 struct RowBf16Vec {
+    using Raw = uint4;
     const uint4 *p;
     __device__ RowBf16Vec(const void *row, int) : p(static_cast<const uint4 *>(row)) {}
-    __device__ __forceinline__ uint4 raw(int c) const { return p[c]; }
-    __device__ __forceinline__ static void unpack(const uint4 &w, float x[8]) {
+    __device__ __forceinline__ Raw raw(int c) const { return p[c]; }
+    __device__ __forceinline__ static void unpack(const Raw &w, float x[8]) {
         x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
         x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
         x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
@@ -49,19 +52,26 @@ struct RowBf16Vec {
 };
 
 struct RowF32Vec {
+    struct Raw { float4 a, b; };
     const float4 *p;
     __device__ RowF32Vec(const void *row, int) : p(static_cast<const float4 *>(row)) {}
-    __device__ __forceinline__ void load(int c, float x[8]) const {
-        float4 a = p[2 * c], b = p[2 * c + 1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    __device__ __forceinline__ Raw raw(int c) const { return Raw{p[2 * c], p[2 * c + 1]}; }
+    __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
+    __device__ __forceinline__ void load(int c, float x[8]) const { unpack(raw(c), x); }
     __device__ __forceinline__ float at(int v) const {
         return reinterpret_cast<const float *>(p)[v];
     }
 };
 
+struct Raw8 {
+    float v[8];
+};
+
 struct RowBf16Scalar {
+    using Raw = Raw8;
     const uint16_t *p;
     int V;
     __device__ RowBf16Scalar(const void *row, int V_) : p(static_cast<const uint16_t *>(row)), V(V_) {}
@@ -72,12 +82,18 @@ struct RowBf16Scalar {
             x[e] = v < V ? __uint_as_float(static_cast<uint32_t>(p[v]) << 16) : -INFINITY;
         }
     }
+    __device__ __forceinline__ Raw raw(int c) const { Raw r; load(c, r.v); return r; }
+    __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = r.v[e];
+    }
     __device__ __forceinline__ float at(int v) const {
         return __uint_as_float(static_cast<uint32_t>(p[v]) << 16);
     }
 };
 
 struct RowF32Scalar {
+    using Raw = Raw8;
     const float *p;
     int V;
     __device__ RowF32Scalar(const void *row, int V_) : p(static_cast<const float *>(row)), V(V_) {}
@@ -87,6 +103,11 @@ struct RowF32Scalar {
             int v = 8 * c + e;
             x[e] = v < V ? p[v] : -INFINITY;
         }
+    }
+    __device__ __forceinline__ Raw raw(int c) const { Raw r; load(c, r.v); return r; }
+    __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = r.v[e];
     }
     __device__ __forceinline__ float at(int v) const { return p[v]; }
 };
@@ -157,6 +178,27 @@ __device__ __forceinline__ double block_sum(double v, double *red) {
 #pragma unroll
     for (int i = 1; i < NT / kWave; ++i) t += red[i];
     return t;
+}
+
+// Four independent block sums at once; red[] must hold 4 * NT/64 entries.
+template <int NT>
+__device__ __forceinline__ void block_sum4(double v[4], double *red) {
+    constexpr int NW = NT / kWave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = wave_sum(v[i]);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[i * NW + threadIdx.x / kWave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double t = red[i * NW];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) t += red[i * NW + w];
+        v[i] = t;
+    }
 }
 
 template <int NT>

@@ -1,21 +1,29 @@
-// sv_rowstats.hpp -- temperature-softmax statistics of every node row.
+// sv_rowstats.hpp -- temperature-softmax statistics of node rows.
 //
-// For each row l of logits and the request's temperature T this kernel finds a
+// For a row l of logits and the request's temperature T the statistics are a
 // shift M and S = sum_v 2^((l_v - M) * c) with c = log2(e) / T, so that
 //   p(v) = 2^((l_v - M) * c) / S   and   ln sum_v exp(l_v / T) = M / T + ln S.
 // This is the temperature softmax the speculative-decoding verifiers apply to
 // the target and draft distributions (SpecTr-GBV page, section 2: the
-// acceptance probabilities and the residual are functions of those
-// distributions).  Only node rows are streamed: the row of draft k at position
-// j is skipped when a lower-index draft has the same prefix X[0..j-1].
+// acceptance probabilities and the residual are functions of them).
 //
-// One workgroup streams one row once from HBM, 8 elements per thread per step
-// (one 16-byte load for bf16).  The shift is the block maximum of the first
-// tile; a lane only rescales (in fp64) when a later chunk exceeds its shift by
-// more than 64 binary orders of magnitude, so the steady state costs one
-// exp2 per element and no cross-lane traffic.  Per-chunk sums are formed in
-// fp32 and accumulated in fp64.  NaN or +inf logits make S non-finite and an
-// all -inf row makes S = 0; the walk treats both as invalid request data.
+// rowstats_kernel streams, once, the rows the walk reads first: the root pair
+// of every request, and rows 1..L-1 of every draft whose first token no
+// lower-index draft has (each such draft is examined at the root unless an
+// earlier draft is accepted first).  Rows of drafts that repeat an earlier
+// first token are read only after an acceptance: the walk then stops, lists the
+// rows below the accepted node for every draft that shares it, and a second
+// launch of this kernel streams the listed rows before the walk resumes.  With
+// diagnostics requested the kernel covers every node row in one launch, the
+// target rows at position L included.
+//
+// Each workgroup streams one row, 8 elements per thread per step (one 16-byte
+// load for bf16).  The shift is the block maximum of the first tile; a lane
+// only rescales (in fp64) when a later chunk exceeds its shift by more than 64
+// binary orders of magnitude, so the steady state costs one exp2 per element
+// and no cross-lane traffic.  Per-chunk sums are formed in fp32 and
+// accumulated in fp64.  NaN or +inf logits make S non-finite and an all -inf
+// row makes S = 0; the walk treats both as invalid data when it reads the row.
 #pragma once
 
 #include "sv_device.hpp"
@@ -28,15 +36,72 @@ struct RowStat {
     double sum;    // S
 };
 
+__device__ __forceinline__ bool stat_ok(const RowStat &s) {
+    return isfinite(s.shift) && s.sum > 0.0 && isfinite(s.sum);
+}
+
+// Per-lane online accumulator of one row's statistics.
+struct LaneSoftmax {
+    float m;          // this lane's shift
+    double s;         // sum of 2^((x - m) c) over the lane's elements
+    __device__ __forceinline__ void init(float block_first_max) {
+        m = fmaxf(block_first_max, -3.402823466e38f);
+        s = 0.0;
+    }
+    __device__ __forceinline__ void consume(const float (&x)[8], double c64, float chi, float clo,
+                                            float headroom) {
+        const float cm = max8(x);
+        if (cm > m + headroom) {   // rare: move this lane's shift up, in fp64
+            s *= exp2((static_cast<double>(m) - static_cast<double>(cm)) * c64);
+            m = cm;
+        }
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float d = x[i] - m;
+            e[i] = fast_exp2(fmaf(d, chi, d * clo));
+        }
+        s += static_cast<double>(sum8(e));
+    }
+};
+
+// Combine the lanes of a block into the row's (M, S); every thread gets it.
+template <int NT>
+__device__ __forceinline__ RowStat finish_row(const LaneSoftmax &ls, double c64, float *fred,
+                                              double *red) {
+    const float M = block_max<NT>(ls.m, fred);
+    const double scaled =
+        (ls.m == M) ? ls.s
+                    : ls.s * exp2((static_cast<double>(ls.m) - static_cast<double>(M)) * c64);
+    RowStat st;
+    st.shift = M;
+    st.pad = 0.0f;
+    st.sum = block_sum<NT>(scaled, red);
+    return st;
+}
+
+// A row the walk asked for: request b, draft k, position j, target (1) or draft (0).
+struct RowRef {
+    int b;
+    int kjt;                // (k * L + j) * 2 + is_target
+};
+
 struct StatsArgs {
     const void *tgt;        // [B][K][L+1][V]
     const void *drf;        // [B][K][L][V]
     const int32_t *tok;     // [B][K][L]
     const float *temp;      // [B]
     RowStat *stats;         // [B][K][2L+1]: target rows 0..L, draft rows at L+1..2L
+    const RowRef *list;     // rows the walk asked for (mode kSelectListed)
+    unsigned *list_count;   // their number; the first-visit launch resets it to 0
     int B, K, L, V;
-    int rows_per_draft;     // 2L (positions 0..L-1 of both kinds) or 2L+1 (+ target row L)
+    int mode;               // kSelectAllNodes, kSelectFirstVisit or kSelectListed
 };
+
+constexpr int kSelectFirstVisit = 0;   // root pair + rows 1..L-1 of drafts with a new first token
+constexpr int kSelectAllNodes = 1;     // every node row, target rows at position L included
+constexpr int kSelectListed = 2;       // node rows the walk listed after an acceptance
+constexpr int kDepth = 8;              // 16-byte loads in flight per lane
 
 template <int NT, typename RD, typename E>
 __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
@@ -44,36 +109,52 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
     __shared__ double s_sum[NT / kWave];
 
     const int tid = threadIdx.x;
-    const int K = A.K, L = A.L, V = A.V, NR = A.rows_per_draft;
-    const long long nrows = static_cast<long long>(A.B) * K * NR;
+    const int K = A.K, L = A.L, V = A.V;
+    const int NR = 2 * L + (A.mode == kSelectAllNodes ? 1 : 0);
+    const long long nrows = A.mode == kSelectListed
+                                ? static_cast<long long>(*A.list_count)
+                                : static_cast<long long>(A.B) * K * NR;
     const int nch = (V + kChunk - 1) / kChunk;
+    if (A.mode == kSelectFirstVisit && blockIdx.x == 0 && tid == 0) *A.list_count = 0u;
 
     for (long long r = blockIdx.x; r < nrows; r += gridDim.x) {
-        const int slot = static_cast<int>(r % NR);
-        const long long bk = r / NR;
-        const int k = static_cast<int>(bk % K);
-        const int b = static_cast<int>(bk / K);
-        int j, is_target, row_index;
-        if (slot < L) { is_target = 1; j = slot; row_index = j; }
-        else if (slot < 2 * L) { is_target = 0; j = slot - L; row_index = L + 1 + j; }
-        else { is_target = 1; j = L; row_index = L; }
+        int b, k, j, is_target, row_index;
+        if (A.mode == kSelectListed) {
+            const RowRef ref = A.list[r];
+            b = ref.b;
+            is_target = ref.kjt & 1;
+            k = (ref.kjt >> 1) / L;
+            j = (ref.kjt >> 1) % L;
+            row_index = is_target ? j : L + 1 + j;
+        } else {
+            const int slot = static_cast<int>(r % NR);
+            const long long bk = r / NR;
+            k = static_cast<int>(bk % K);
+            b = static_cast<int>(bk / K);
+            if (slot < L) { is_target = 1; j = slot; row_index = j; }
+            else if (slot < 2 * L) { is_target = 0; j = slot - L; row_index = L + 1 + j; }
+            else { is_target = 1; j = L; row_index = L; }
+        }
 
-        // node rows only: skip when a lower-index draft shares the prefix X[0..j-1]
-        if (k > 0) {
-            int dup = 0;
+        // which rows: every node row (lowest-index draft per prefix X[0..j-1]);
+        // first-visit rows (the root pair; rows j >= 1 of drafts whose first token
+        // is new among drafts 0..k); or the node rows the walk listed
+        if (A.mode != kSelectListed && k > 0) {
+            int skip = 0;
             if (j == 0) {
-                dup = 1;
+                skip = 1;
             } else {
                 const int32_t *xk = A.tok + (static_cast<long long>(b) * K + k) * L;
+                const int n = A.mode == kSelectAllNodes ? j : 1;
                 for (int c = tid; c < k; c += NT) {
                     const int32_t *xc = A.tok + (static_cast<long long>(b) * K + c) * L;
                     int same = 1;
-                    for (int i = 0; i < j; ++i) same &= (xc[i] == xk[i]);
-                    dup |= same;
+                    for (int i = 0; i < n; ++i) same &= (xc[i] == xk[i]);
+                    skip |= same;
                 }
-                dup = __syncthreads_or(dup);
+                skip = __syncthreads_or(skip);
             }
-            if (dup) continue;
+            if (skip) continue;
         }
 
         const E *base = static_cast<const E *>(is_target ? A.tgt : A.drf);
@@ -94,50 +175,29 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x0[e] = -INFINITY;
         }
-        float m_l = fmaxf(block_max<NT>(max8(x0), s_max), -3.402823466e38f);
-        double s = 0.0;
-
-        auto consume = [&](const float (&x)[8]) {
-            const float cm = max8(x);
-            if (cm > m_l + headroom) {   // rare: move this lane's shift up, in fp64
-                s *= exp2((static_cast<double>(m_l) - static_cast<double>(cm)) * c64);
-                m_l = cm;
-            }
-            float e[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float d = x[i] - m_l;
-                e[i] = fast_exp2(fmaf(d, chi, d * clo));
-            }
-            s += static_cast<double>(sum8(e));
-        };
-
-        if (have0) consume(x0);
+        LaneSoftmax ls;
+        ls.init(block_max<NT>(max8(x0), s_max));
+        if (have0) ls.consume(x0, c64, chi, clo, headroom);
         int c = tid + NT;
-        for (; c + NT < nch; c += 2 * NT) {
-            float xa[8], xb[8];
-            row.load(c, xa);
-            row.load(c + NT, xb);
-            consume(xa);
-            consume(xb);
+        for (; c + (kDepth - 1) * NT < nch; c += kDepth * NT) {   // kDepth loads in flight
+            typename RD::Raw r[kDepth];
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) r[i] = row.raw(c + i * NT);
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                float x[8];
+                RD::unpack(r[i], x);
+                ls.consume(x, c64, chi, clo, headroom);
+            }
         }
-        if (c < nch) {
+        for (; c < nch; c += NT) {
             float xa[8];
             row.load(c, xa);
-            consume(xa);
+            ls.consume(xa, c64, chi, clo, headroom);
         }
-
-        const float M = block_max<NT>(m_l, s_max);
-        const double scaled =
-            (m_l == M) ? s : s * exp2((static_cast<double>(m_l) - static_cast<double>(M)) * c64);
-        const double S = block_sum<NT>(scaled, s_sum);
-        if (tid == 0) {
-            RowStat st;
-            st.shift = M;
-            st.pad = 0.0f;
-            st.sum = S;
+        const RowStat st = finish_row<NT>(ls, c64, s_max, s_sum);
+        if (tid == 0)
             A.stats[(static_cast<long long>(b) * K + k) * (2 * L + 1) + row_index] = st;
-        }
     }
 }
 

@@ -53,8 +53,14 @@ struct WalkArgs {
     const RowStat *stats;   // [B][K][2L+1]
     int B, K, L, V;
     int method;             // kMethodToken or kMethodBlockWalk
-    int bonus_stats;        // stats hold target rows at position L too
-    int32_t *accept_len, *draft_index, *correction, *flags;
+    int all_nodes;          // the statistics kernel streamed every node row (diagnostics)
+    int round;              // 1, or 2 to resume the walks the first round suspended
+    int two_round;          // a second round follows: the first may suspend
+    struct WalkState *state;     // [B]
+    unsigned char *need;    // [B][K][L]: node rows flagged for the second round
+    RowRef *list;           // the same rows as a list for the statistics kernel
+    unsigned *list_count;
+    int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
     float *row_lse, *accept_prob, *resid_mass;
 };
 
@@ -103,26 +109,33 @@ struct SweepRows {
 };
 
 // Block-wide sum of omega over a row pair (or a single row when HAS_Q is false).
+// Four chunks per row are in flight per lane.
 template <int NT, typename RD, bool HAS_Q>
 __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
                              float clo, const int *H, int nH, double *red) {
     double acc = 0.0;
     int c = threadIdx.x;
-    for (; c + NT < nch; c += 2 * NT) {
-        float xp0[8], xq0[8], xp1[8], xq1[8], w[8];
-        P.load(c, xp0);
-        P.load(c + NT, xp1);
-        if (HAS_Q) { Q.load(c, xq0); Q.load(c + NT, xq1); }
-        omega8<HAS_Q>(xp0, xq0, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
-        acc += static_cast<double>(sum8(w));
-        omega8<HAS_Q>(xp1, xq1, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * (c + NT), H, nH, w);
-        acc += static_cast<double>(sum8(w));
+    for (; c + 3 * NT < nch; c += 4 * NT) {
+        typename RD::Raw rp[4], rq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rp[i] = P.raw(c + i * NT);
+            if (HAS_Q) rq[i] = Q.raw(c + i * NT);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float xp[8], xq[8], w[8];
+            RD::unpack(rp[i], xp);
+            if (HAS_Q) RD::unpack(rq[i], xq);
+            omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * (c + i * NT), H, nH, w);
+            acc += static_cast<double>(sum8(w));
+        }
     }
-    if (c < nch) {
-        float xp0[8], xq0[8], w[8];
-        P.load(c, xp0);
-        if (HAS_Q) Q.load(c, xq0);
-        omega8<HAS_Q>(xp0, xq0, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+    for (; c < nch; c += NT) {
+        float xp[8], xq[8], w[8];
+        P.load(c, xp);
+        if (HAS_Q) Q.load(c, xq);
+        omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
         acc += static_cast<double>(sum8(w));
     }
     return block_sum<NT>(acc, red);
@@ -130,28 +143,47 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
 
 // Block-wide inverse-CDF draw over omega in token-id order.  Returns y, or -1
 // when the mass Z is not a positive finite number.  Z is returned in *Z.
+// Tiles of NT chunks are summed four at a time into tile[]; the tile holding
+// the threshold is rescanned with a block scan.
 template <int NT, typename RD, bool HAS_Q>
 __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
                           float clo, const int *H, int nH, double u, double *Z, double *tile,
-                          double *red, int *ired) {
+                          double *red, double *red4, int *ired) {
     const int ntile = (nch + NT - 1) / NT;
     int lastpos = -1;
-    for (int t = 0; t < ntile; ++t) {
-        const int c = t * NT + threadIdx.x;
-        double cs = 0.0;
-        if (c < nch) {
-            float xp[8], xq[8], w[8];
-            P.load(c, xp);
-            if (HAS_Q) Q.load(c, xq);
-            omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+    for (int t0 = 0; t0 < ntile; t0 += 4) {
+        typename RD::Raw rp[4], rq[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                cs += static_cast<double>(w[e]);
-                if (w[e] > 0.0f) lastpos = 8 * c + e;
+        for (int i = 0; i < 4; ++i) {
+            const int c = (t0 + i) * NT + threadIdx.x;
+            if (c < nch) {
+                rp[i] = P.raw(c);
+                if (HAS_Q) rq[i] = Q.raw(c);
             }
         }
-        const double ts = block_sum<NT>(cs, red);
-        if (threadIdx.x == 0) tile[t] = ts;
+        double cs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = (t0 + i) * NT + threadIdx.x;
+            cs[i] = 0.0;
+            if (c < nch) {
+                float xp[8], xq[8], w[8];
+                RD::unpack(rp[i], xp);
+                if (HAS_Q) RD::unpack(rq[i], xq);
+                omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    cs[i] += static_cast<double>(w[e]);
+                    if (w[e] > 0.0f) lastpos = 8 * c + e;
+                }
+            }
+        }
+        block_sum4<NT>(cs, red4);
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (t0 + i < ntile) tile[t0 + i] = cs[i];
+        }
     }
     lastpos = block_max_int<NT>(lastpos, ired);   // its barriers publish tile[]
     double z = 0.0;
@@ -202,7 +234,19 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
 template <int NT, typename RD>
 __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
     float m = -INFINITY;
-    for (int c = threadIdx.x; c < nch; c += NT) {
+    int c = threadIdx.x;
+    for (; c + 3 * NT < nch; c += 4 * NT) {
+        typename RD::Raw r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = P.raw(c + i * NT);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x[8];
+            RD::unpack(r[i], x);
+            m = fmaxf(m, max8(x));
+        }
+    }
+    for (; c < nch; c += NT) {
         float x[8];
         P.load(c, x);
         m = fmaxf(m, max8(x));
@@ -210,23 +254,96 @@ __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
     return block_max<NT>(m, fred);
 }
 
+// Block-wide statistics of a node's target row and draft row; the walk's
+// fallback for a row that no launch of the statistics kernel streamed.
+template <int NT, typename RD>
+__device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, double c64, float chi,
+                                 float clo, RowStat &sp, RowStat &sq, float *fred, double *red) {
+    const float headroom = 64.0f / chi;
+    const int tid = threadIdx.x;
+    float xp[8], xq[8];
+    const bool have0 = tid < nch;
+    if (have0) {
+        P.load(tid, xp);
+        Q.load(tid, xq);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xp[e] = xq[e] = -INFINITY;
+    }
+    LaneSoftmax lp, lq;
+    lp.init(block_max<NT>(max8(xp), fred));
+    lq.init(block_max<NT>(max8(xq), fred));
+    if (have0) {
+        lp.consume(xp, c64, chi, clo, headroom);
+        lq.consume(xq, c64, chi, clo, headroom);
+    }
+    int c = tid + NT;
+    for (; c + 3 * NT < nch; c += 4 * NT) {
+        typename RD::Raw rp[4], rq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rp[i] = P.raw(c + i * NT);
+            rq[i] = Q.raw(c + i * NT);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ap[8], aq[8];
+            RD::unpack(rp[i], ap);
+            RD::unpack(rq[i], aq);
+            lp.consume(ap, c64, chi, clo, headroom);
+            lq.consume(aq, c64, chi, clo, headroom);
+        }
+    }
+    for (; c < nch; c += NT) {
+        P.load(c, xp);
+        Q.load(c, xq);
+        lp.consume(xp, c64, chi, clo, headroom);
+        lq.consume(xq, c64, chi, clo, headroom);
+    }
+    sp = finish_row<NT>(lp, c64, fred, red);
+    sq = finish_row<NT>(lq, c64, fred, red);
+}
+
+// Walk state saved when the first round stops for rows below an accepted node.
+struct WalkState {
+    int status;             // kStateDone or kStateSuspended
+    int k_next;             // draft to examine on resumption
+    int tau, own, kstar, nH, flags, rows;
+    double alpha, beta, N;
+    int H[kMaxK];
+};
+constexpr int kStateDone = 0;
+constexpr int kStateSuspended = 1;
+
+// Two 512-thread walks per CU (4 waves per SIMD) keep every request of a
+// 512-request batch resident at once.
 template <int NT, typename RD, typename E>
-__global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void walk_kernel(
+    WalkArgs A) {
     constexpr int kMaxTiles = (kMaxV / kChunk + NT - 1) / NT;
+    constexpr int kMaxRS = 2 * kMaxL + 1;
+    constexpr int NW = NT / kWave;
     __shared__ int s_x[kMaxK * kMaxL];
     __shared__ unsigned char s_can[kMaxK * (kMaxL + 1)];
-    __shared__ double s_lp[kMaxK * kMaxL];
-    __shared__ double s_lq[kMaxK * kMaxL];
-    __shared__ double s_red[NT / kWave];
-    __shared__ float s_fred[NT / kWave];
-    __shared__ int s_ired[NT / kWave];
+    __shared__ unsigned char s_have[kMaxK * (kMaxL + 1)];
+    __shared__ float s_gp[kMaxK * kMaxL];
+    __shared__ float s_gq[kMaxK * kMaxL];
+    __shared__ float s_M[kMaxK * kMaxRS];
+    __shared__ double s_S[kMaxK * kMaxRS];
+    __shared__ double s_red[NW];
+    __shared__ double s_red4[4 * NW];
+    __shared__ float s_fred[NW];
+    __shared__ int s_ired[NW];
     __shared__ double s_tile[kMaxTiles];
     __shared__ int s_H[kMaxK];
     __shared__ double s_w[kMaxL + 1];
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int K = A.K, L = A.L, V = A.V, KL = K * L, RS = 2 * L + 1;
+    const int K = A.K, L = A.L, V = A.V, KL = K * L, RS = 2 * L + 1, L1 = L + 1;
+    WalkState *ws = A.state + b;
+    if (A.round == 2 && ws->status != kStateSuspended) return;   // finished in the first round
+
     const int nch = (V + kChunk - 1) / kChunk;
     const long long bKL = static_cast<long long>(b) * KL;
     const float T = A.temp[b];
@@ -236,8 +353,9 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
     const E *tgt = static_cast<const E *>(A.tgt);
     const E *drf = static_cast<const E *>(A.drf);
     const RowStat *st = A.stats + static_cast<long long>(b) * K * RS;
+    unsigned char *need = A.need + bKL;
     auto trow = [&](int c, int j) {
-        return tgt + ((static_cast<long long>(b) * K + c) * (L + 1) + j) * V;
+        return tgt + ((static_cast<long long>(b) * K + c) * L1 + j) * V;
     };
     auto drow = [&](int c, int j) {
         return drf + ((static_cast<long long>(b) * K + c) * L + j) * V;
@@ -251,15 +369,20 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
         bad |= (x < 0 || x >= V);
         const float u = A.ua[bKL + i];
         bad |= !(u >= 0.0f && u < 1.0f);
-        if (A.accept_prob) A.accept_prob[bKL + i] = NAN;
+        if (A.round == 1) {
+            if (A.accept_prob) A.accept_prob[bKL + i] = NAN;
+            need[i] = 0;
+        }
     }
     const float ucf = A.uc[b];
     bad |= !(ucf >= 0.0f && ucf < 1.0f);
     bad = __syncthreads_or(bad);
 
-    // 2. node (lowest-index draft with the same prefix) of every (k, j), j = 0..L
-    for (int i = tid; i < K * (L + 1); i += NT) {
-        const int k = i / (L + 1), j = i % (L + 1);
+    // 2. node (lowest-index draft with the same prefix) of every (k, j), j = 0..L,
+    //    and the node rows whose statistics a launch of the statistics kernel made
+    int streamed = 0;
+    for (int i = tid; i < K * L1; i += NT) {
+        const int k = i / L1, j = i % L1;
         int c = k;
         for (int cc = 0; cc < k; ++cc) {
             int same = 1;
@@ -267,43 +390,114 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
             if (same) { c = cc; break; }
         }
         s_can[i] = static_cast<unsigned char>(c);
+        int first = 1;
+        for (int cc = 0; cc < k; ++cc) first &= (s_x[cc * L] != s_x[k * L]);
+        int have = 0;
+        if (j < L && c == k) {
+            const int fv = A.all_nodes || (j == 0 && k == 0) || (j > 0 && first);
+            const int nd = A.round == 2 && need[k * L + j];
+            have = fv || nd;
+            streamed += fv ? (A.round == 1 ? 2 : 0) : (nd ? 2 : 0);
+        }
+        if (j == L && c == k && A.all_nodes) streamed += 1;
+        s_have[i] = static_cast<unsigned char>(have);
+    }
+    __syncthreads();
+    streamed = static_cast<int>(block_sum<NT>(static_cast<double>(streamed), s_red));
+
+    // 3. statistics of those rows into LDS; logits at the drafted tokens
+    if (!bad) {
+        for (int i = tid; i < KL; i += NT) {
+            const int k = i / L, j = i % L;
+            const int c = s_can[k * L1 + j];
+            const int x = s_x[i];
+            s_gp[i] = RD(trow(c, j), V).at(x);
+            s_gq[i] = RD(drow(c, j), V).at(x);
+            if (c == k && s_have[k * L1 + j]) {
+                const RowStat a = st[k * RS + j], q = st[k * RS + L1 + j];
+                s_M[k * RS + j] = a.shift;
+                s_S[k * RS + j] = a.sum;
+                s_M[k * RS + L1 + j] = q.shift;
+                s_S[k * RS + L1 + j] = q.sum;
+            }
+        }
     }
     __syncthreads();
 
-    // 3. node rows at positions 0..L-1 must be distributions
-    if (!bad) {
-        for (int i = tid; i < KL; i += NT) {
-            const int k = i / L, j = i % L;
-            if (s_can[k * (L + 1) + j] != k) continue;
-            const RowStat a = st[k * RS + j], q = st[k * RS + L + 1 + j];
-            bad |= !(isfinite(a.shift) && a.sum > 0.0 && isfinite(a.sum));
-            bad |= !(isfinite(q.shift) && q.sum > 0.0 && isfinite(q.sum));
+    // statistics of node (c, j): 1 = present and valid, 0 = not a distribution,
+    // -1 = not streamed yet and the walk may stop for it (first of two rounds);
+    // otherwise they are computed here
+    const bool may_suspend = A.round == 1 && A.two_round;
+    auto ensure = [&](int c, int j) -> int {
+        if (!s_have[c * L1 + j]) {
+            if (may_suspend) return -1;
+            RowStat sp, sq;
+            sweep_stats_pair<NT, RD>(RD(trow(c, j), V), RD(drow(c, j), V), nch, c64, chi, clo, sp,
+                                     sq, s_fred, s_red);
+            if (tid == 0) {
+                s_M[c * RS + j] = sp.shift;
+                s_S[c * RS + j] = sp.sum;
+                s_M[c * RS + L1 + j] = sq.shift;
+                s_S[c * RS + L1 + j] = sq.sum;
+                s_have[c * L1 + j] = 1;
+            }
+            __syncthreads();
         }
-    }
-    bad = __syncthreads_or(bad);
+        RowStat a, q;
+        a.shift = s_M[c * RS + j];
+        a.sum = s_S[c * RS + j];
+        q.shift = s_M[c * RS + L1 + j];
+        q.sum = s_S[c * RS + L1 + j];
+        return (stat_ok(a) && stat_ok(q)) ? 1 : 0;
+    };
+    // log2 p and log2 q of draft k's token at position j under its node rows
+    auto lp2 = [&](int k, int j) {
+        const int c = s_can[k * L1 + j];
+        return (static_cast<double>(s_gp[k * L + j]) - static_cast<double>(s_M[c * RS + j])) * c64 -
+               log2(s_S[c * RS + j]);
+    };
+    auto lq2 = [&](int k, int j) {
+        const int c = s_can[k * L1 + j];
+        return (static_cast<double>(s_gq[k * L + j]) - static_cast<double>(s_M[c * RS + L1 + j])) *
+                   c64 -
+               log2(s_S[c * RS + L1 + j]);
+    };
+    auto node_sweep = [&](int c, int j, double alpha, double beta) {
+        SweepRows sr;
+        sr.MP = s_M[c * RS + j];
+        sr.MQ = s_M[c * RS + L1 + j];
+        sr.a = static_cast<float>(alpha / s_S[c * RS + j]);
+        sr.bq = static_cast<float>(beta / s_S[c * RS + L1 + j]);
+        return sr;
+    };
 
-    int tau = -1, kstar = -1, y = -1, flags = 0;
+    int tau = -1, kstar = -1, y = -1, flags = 0, rows = 0;
     double Zp = NAN;
-    if (!bad) {
-        // 4. log2 p and log2 q of every drafted token under its node rows
-        for (int i = tid; i < KL; i += NT) {
-            const int k = i / L, j = i % L;
-            const int c = s_can[k * (L + 1) + j];
-            const int x = s_x[i];
-            const RowStat a = st[c * RS + j], q = st[c * RS + L + 1 + j];
-            const float lt = RD(trow(c, j), V).at(x);
-            const float ld = RD(drow(c, j), V).at(x);
-            s_lp[i] = (static_cast<double>(lt) - static_cast<double>(a.shift)) * c64 - log2(a.sum);
-            s_lq[i] = (static_cast<double>(ld) - static_cast<double>(q.shift)) * c64 - log2(q.sum);
-        }
+    bool suspend = false;
+    int own = 0, nH = 0, k0 = 0;
+    double alpha = 1.0, beta = 0.0, N = 1.0;
+    if (A.round == 2) {
+        k0 = ws->k_next;
+        tau = ws->tau;
+        own = ws->own;
+        kstar = ws->kstar;
+        nH = ws->nH;
+        flags = ws->flags;
+        rows = ws->rows;
+        alpha = ws->alpha;
+        beta = ws->beta;
+        N = ws->N;
+        for (int i = tid; i < nH; i += NT) s_H[i] = ws->H[i];
         __syncthreads();
+    }
+    rows += streamed;
 
-        int own = 0, nH = 0;
-        double alpha = 1.0, beta = 0.0, N = 1.0;
+    if (!bad) {
         if (A.method == kMethodToken) {
             tau = L;
             for (int j = 0; j < L; ++j) {
-                double a = ratio_log2(s_lp[j], s_lq[j]);
+                if (ensure(0, j) != 1) { bad = 1; break; }
+                double a = ratio_log2(lp2(0, j), lq2(0, j));
                 if (a > 1.0) a = 1.0;
                 const double u = static_cast<double>(A.ua[bKL + j]);
                 if (tid == 0 && A.accept_prob) A.accept_prob[bKL + j] = static_cast<float>(a);
@@ -312,28 +506,31 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
             kstar = tau > 0 ? 0 : -1;
             beta = 1.0;   // token-level residual max(p - q, 0)
         } else {
-            tau = 0;
-            for (int k = 0; k < K && tau < L; ++k) {
+            if (A.round == 1) tau = 0;
+            for (int k = k0; k < K && tau < L; ++k) {
                 int match = 1;
                 for (int t = 0; t < tau; ++t) match &= (s_x[k * L + t] == s_x[own * L + t]);
                 if (!match) continue;
                 const int x = s_x[k * L + tau];
                 int dup = 0;
                 for (int i = 0; i < nH; ++i) dup |= (s_H[i] == x);
-                const int cn = s_can[own * (L + 1) + tau];
-                const RowStat np = st[cn * RS + tau], nq = st[cn * RS + L + 1 + tau];
+                const int cn = s_can[own * L1 + tau];
+                int ok = ensure(cn, tau);
+                for (int j = tau + 1; j < L && ok == 1 && !dup; ++j) ok = ensure(s_can[k * L1 + j], j);
+                if (ok < 0) { suspend = true; k0 = k; break; }
+                if (ok == 0) { bad = 1; break; }
                 bool rejected = true;
                 if (!dup) {
                     // weight chain: first position against the node residual omega/N
-                    const double ps = exp2(s_lp[k * L + tau]);
-                    const double qs = exp2(s_lq[k * L + tau]);
+                    const double ps = exp2(lp2(k, tau));
+                    const double qs = exp2(lq2(k, tau));
                     const double om = fmax(alpha * ps - beta * qs, 0.0);
                     __syncthreads();   // previous readers of s_w are done
                     if (tid == 0) {
                         double w = (qs > 0.0) ? fmin(om / N / qs, 1.0) : (om > 0.0 ? 1.0 : 0.0);
                         s_w[tau + 1] = w;
                         for (int j = tau + 1; j < L; ++j) {
-                            w = chain_step(w, ratio_log2(s_lp[k * L + j], s_lq[k * L + j]));
+                            w = chain_step(w, ratio_log2(lp2(k, j), lq2(k, j)));
                             s_w[j + 1] = w;
                         }
                     }
@@ -348,13 +545,8 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
                             h = wm;
                         } else {
                             if (!(u < wm)) continue;      // h_m <= w_m: rejects without a sweep
-                            const int cm = s_can[k * (L + 1) + m];
-                            const RowStat sp = st[cm * RS + m], sq = st[cm * RS + L + 1 + m];
-                            SweepRows sr;
-                            sr.MP = sp.shift;
-                            sr.MQ = sq.shift;
-                            sr.a = static_cast<float>(wm / sp.sum);
-                            sr.bq = static_cast<float>(1.0 / sq.sum);
+                            const int cm = s_can[k * L1 + m];
+                            const SweepRows sr = node_sweep(cm, m, wm, 1.0);
                             const RD P(trow(cm, m), V), Q(drow(cm, m), V);
                             const double R =
                                 sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, 0, s_red);
@@ -386,11 +578,7 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
                         __syncthreads();
                     }
                     beta += N;
-                    SweepRows sr;
-                    sr.MP = np.shift;
-                    sr.MQ = nq.shift;
-                    sr.a = static_cast<float>(alpha / np.sum);
-                    sr.bq = static_cast<float>(beta / nq.sum);
+                    const SweepRows sr = node_sweep(cn, tau, alpha, beta);
                     const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
                     N = sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, s_red);
                 }
@@ -403,11 +591,56 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
                 }
             }
         }
+    }
 
-        // 5. correction token
+    if (suspend) {
+        // Flag every node row at positions tau..L-1 of the drafts that share the
+        // accepted prefix; the next launch of the statistics kernel streams them.
+        // Every draft examined after this point shares that prefix, so the walk
+        // resumes with all the rows it can read.
+        for (int i = tid; i < KL; i += NT) {
+            const int c = i / L, j = i % L;
+            if (j < tau || s_can[c * L1 + j] != c || s_have[c * L1 + j]) continue;
+            int match = 1;
+            for (int t = 0; t < tau; ++t) match &= (s_x[c * L + t] == s_x[own * L + t]);
+            if (match) need[i] = 1;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int n = 0;
+            for (int i = 0; i < KL; ++i) n += need[i];
+            unsigned base = atomicAdd(A.list_count, static_cast<unsigned>(2 * n));
+            for (int i = 0; i < KL; ++i) {
+                if (!need[i]) continue;
+                A.list[base].b = b;
+                A.list[base].kjt = 2 * i + 1;
+                A.list[base + 1].b = b;
+                A.list[base + 1].kjt = 2 * i;
+                base += 2;
+            }
+        }
+        if (tid == 0) {
+            ws->status = kStateSuspended;
+            ws->k_next = k0;
+            ws->tau = tau;
+            ws->own = own;
+            ws->kstar = kstar;
+            ws->nH = nH;
+            ws->flags = flags;
+            ws->rows = rows;
+            ws->alpha = alpha;
+            ws->beta = beta;
+            ws->N = N;
+        }
+        for (int i = tid; i < nH; i += NT) ws->H[i] = s_H[i];
+        return;
+    }
+
+    // 5. correction token
+    if (!bad) {
         const double u = static_cast<double>(ucf);
         if (tau == L) {
-            const int cb = s_can[(kstar < 0 ? 0 : kstar) * (L + 1) + L];
+            const int cb = s_can[(kstar < 0 ? 0 : kstar) * L1 + L];
             const RD P(trow(cb, L), V);
             const float M = sweep_rowmax<NT, RD>(P, nch, s_fred);
             SweepRows sr;
@@ -418,29 +651,24 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
             double Z;
             y = (M > -INFINITY && M < INFINITY)
                     ? sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
-                                                s_red, s_ired)
+                                                s_red, s_red4, s_ired)
                     : -1;
             Zp = 1.0;
             if (y < 0) bad = 1;   // the target row after the block is not a distribution
         } else {
-            const int cn = s_can[own * (L + 1) + tau];
-            const RowStat np = st[cn * RS + tau], nq = st[cn * RS + L + 1 + tau];
+            const int cn = s_can[own * L1 + tau];
+            SweepRows sr = node_sweep(cn, tau, alpha, beta);
             const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
-            SweepRows sr;
-            sr.MP = np.shift;
-            sr.MQ = nq.shift;
-            sr.a = static_cast<float>(alpha / np.sum);
-            sr.bq = static_cast<float>(beta / nq.sum);
             double Z;
             y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, u, &Z, s_tile, s_red,
-                                         s_ired);
+                                         s_red4, s_ired);
             Zp = Z;
             if (y < 0) {
                 flags |= kFlagDegenerate;
-                sr.a = static_cast<float>(1.0 / np.sum);
+                sr.a = static_cast<float>(1.0 / s_S[cn * RS + tau]);
                 sr.bq = 0.0f;
                 y = sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
-                                              s_red, s_ired);
+                                              s_red, s_red4, s_ired);
                 Zp = Z;
             }
         }
@@ -451,23 +679,26 @@ __global__ __launch_bounds__(NT) void walk_kernel(WalkArgs A) {
             tau = -1;
             kstar = -1;
             y = -1;
-            flags |= kFlagInvalid;
+            flags = kFlagInvalid;
             Zp = NAN;
         }
+        ws->status = kStateDone;
         A.accept_len[b] = tau;
         A.draft_index[b] = kstar;
         A.correction[b] = y;
         if (A.flags) A.flags[b] = flags;
         if (A.resid_mass) A.resid_mass[b] = static_cast<float>(Zp);
+        if (A.rows_streamed) A.rows_streamed[b] = rows;
     }
     if (A.row_lse) {
+        // diagnostics: the statistics kernel streamed every node row
         float *o = A.row_lse + static_cast<long long>(b) * K * RS;
         for (int i = tid; i < K * RS; i += NT) {
             const int k = i / RS, r = i % RS;
             const int j = r <= L ? r : r - L - 1;
-            const int c = s_can[k * (L + 1) + j];
+            const int c = s_can[k * L1 + j];
             float v = NAN;
-            if (!bad && (r != L || A.bonus_stats)) {
+            if (!bad) {
                 const RowStat a = st[c * RS + r];
                 v = static_cast<float>((static_cast<double>(a.shift) * c64 + log2(a.sum)) *
                                        0.6931471805599453);

@@ -29,6 +29,13 @@
  * The library never allocates device memory; scratch comes from the caller's
  * workspace.  Calls that share a workspace must be ordered on one stream.
  *
+ * Work done per request: the softmax statistics of the rows the walk reads
+ * first (the root pair and the rows of each draft with a new first token) are
+ * streamed once from HBM; the walk then runs, and for K > 1 a draft that
+ * continues below an accepted node makes a second round stream the rows
+ * below that node for every draft sharing it.  Rows that the rules never
+ * read are never loaded.
+ *
  * Notation.  T_b is request b's temperature; the temperature softmax of a logit
  * row l is pi(v) = exp(l_v / T_b) / sum_v' exp(l_v' / T_b).  For draft k of
  * request b, target row j (j = 0..L) and draft row j (j = 0..L-1) are the
@@ -88,8 +95,9 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
                                  the node's target distribution was used instead */
 #define SV_FLAG_INVALID 2     /* request data the rules cannot act on: T not a
                                  positive finite number, a token outside [0, V),
-                                 a uniform outside [0, 1), or a node row that is
-                                 not a distribution (NaN, +inf, all -inf) */
+                                 a uniform outside [0, 1), or a node row that the
+                                 rules read and that is not a distribution (NaN,
+                                 +inf, all -inf) */
 
 /* Inputs.  All pointers are DEVICE pointers owned by the caller, row-major,
  * read-only for the library, and must stay valid until the stream reaches the
@@ -117,14 +125,18 @@ typedef struct sv_outputs {
     int32_t *correction;   /* [B] token id in [0, V); -1 for an invalid request */
     int32_t *flags;        /* optional [B]: SV_FLAG_* bits */
     float *row_lse;        /* optional [B][K][2L+1]: ln sum_v exp(l_v / T_b) of the node
-                              row read for (k, row); rows 0..L are target rows,
-                              L+1..2L draft rows 0..L-1.  Requesting it adds one
-                              pass over the target rows at position L. */
+                              row of (k, row); rows 0..L are target rows, L+1..2L
+                              draft rows 0..L-1.  Requesting it makes the
+                              statistics kernel stream every node row (one round,
+                              target rows at position L included). */
     float *accept_prob;    /* optional [B][K][L]: h of each test evaluated exactly,
                               NaN where no test was made or where the test was
                               settled by the bound h <= w without computing h */
     float *resid_mass;     /* optional [B]: mass Z (in probability units) of the
                               distribution the correction was drawn from */
+    int32_t *rows_streamed;/* optional [B]: logit rows whose softmax statistics the
+                              row-statistics kernel computed for the request (its
+                              algorithmic bytes are rows_streamed * V * sizeof(elem)) */
 } sv_outputs;
 
 /* Launch resources. */
@@ -133,9 +145,12 @@ typedef struct sv_launch {
     void *workspace;       /* device scratch, 256-byte aligned, contents need not
                               be initialised, >= sv_workspace_size(...) bytes */
     size_t workspace_bytes;
-    void *phase_events[3]; /* optional hipEvent_t: if non-null, recorded on `stream`
-                              before the row-statistics kernel, between it and the
-                              walk kernel, and after the walk kernel (timing) */
+    void *phase_events[5]; /* optional hipEvent_t, recorded on `stream` when non-null:
+                              [0] before the first row-statistics launch, [1] before the
+                              first walk launch, [2] after it, [3] after the second
+                              row-statistics launch, [4] after the second walk launch
+                              (the second round runs only for K > 1 without
+                              diagnostics; otherwise [2], [3], [4] coincide) */
 } sv_launch;
 
 /* Workspace bytes a call with these sizes needs (0 on invalid sizes). */

@@ -57,6 +57,10 @@ SMALL = [
     ("multi_mixedT_k4_l8_v5003", W["multi_mixedT_bf16_b1024_k4_l8_v151936"], dict(B=40, V=5003)),
     ("multi_fp32_k3_v777", W["multi_bf16_b256_k4_l4_v128256"],
      dict(B=40, K=3, V=777, dtype=torch.float32)),
+    # drafts close to the target at low T: long accepted prefixes, many drafts
+    # sharing them, so the walk computes statistics of rows below accepted nodes
+    ("multi_highaccept_k8_l8_v6000", W["multi_zipf_bf16_b512_k8_l8_v151936"],
+     dict(B=48, V=6000, sigma_draft=0.3, temperature=0.25)),
 ]
 
 
