@@ -48,20 +48,34 @@ struct LaneSoftmax {
         m = fmaxf(block_first_max, -3.402823466e38f);
         s = 0.0;
     }
+    // The overflow check looks at the exponents themselves: their maximum is
+    // taken over FMA results, which needs no NaN canonicalisation, unlike a
+    // maximum over the raw logits.
     __device__ __forceinline__ void consume(const float (&x)[8], double c64, float chi, float clo,
                                             float headroom) {
-        const float cm = max8(x);
-        if (cm > m + headroom) {   // rare: move this lane's shift up, in fp64
-            s *= exp2((static_cast<double>(m) - static_cast<double>(cm)) * c64);
-            m = cm;
-        }
-        float e[8];
+        float y[8];
+        float ymax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float d = x[i] - m;
-            e[i] = fast_exp2(fmaf(d, chi, d * clo));
+            y[i] = fmaf(d, chi, d * clo);
+            ymax = fmaxf(ymax, y[i]);
         }
+        if (ymax > 64.0f) {   // rare: move this lane's shift up, in fp64
+            const float cm = max8(x);
+            s *= exp2((static_cast<double>(m) - static_cast<double>(cm)) * c64);
+            m = cm;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float d = x[i] - m;
+                y[i] = fmaf(d, chi, d * clo);
+            }
+        }
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(y[i]);
         s += static_cast<double>(sum8(e));
+        (void)headroom;
     }
 };
 
