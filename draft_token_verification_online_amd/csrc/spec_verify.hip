@@ -149,7 +149,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     }
     if ((err = record(ln, 3, stream)) != hipSuccess) return err;
     if (two_round) {
-        wa.round = 2;
+        wa.round = 2;   // only the stopped walks run
         hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads),
                            0, stream, wa);
         if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -571,6 +571,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                         }
                     }
                 }
+                bool mass_known = true;
                 if (rejected) {
                     if (!dup) {
                         if (tid == 0) s_H[nH] = x;
@@ -578,11 +579,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                         __syncthreads();
                     }
                     beta += N;
-                    const SweepRows sr = node_sweep(cn, tau, alpha, beta);
-                    const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
-                    N = sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, s_red);
+                    // The new mass is needed only if a later draft is examined at this
+                    // node; otherwise the correction's inverse CDF sums the residual
+                    // itself (and falls back to the node's target on zero mass, as the
+                    // degenerate reset below would).
+                    int later = 0;
+                    for (int k2 = k + 1; k2 < K && !later; ++k2) {
+                        int m2 = 1;
+                        for (int t = 0; t < tau; ++t) m2 &= (s_x[k2 * L + t] == s_x[own * L + t]);
+                        later = m2;
+                    }
+                    if (later) {
+                        const SweepRows sr = node_sweep(cn, tau, alpha, beta);
+                        const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
+                        N = sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, s_red);
+                    } else {
+                        mass_known = false;
+                    }
                 }
-                if (tau < L && !(N > 0.0)) {
+                if (tau < L && mass_known && !(N > 0.0)) {
                     flags |= kFlagDegenerate;   // only rounding empties a residual
                     alpha = 1.0;
                     beta = 0.0;
