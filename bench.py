@@ -80,10 +80,10 @@ class HipEvents:
         self.made = []
 
 
-def read_traffic(workload: str, launch_bytes: float):
-    """HBM traffic of the statistics kernel from committed rocprofv3 PMC summaries
-    (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy-kernel calibration), or
-    None when absent or taken on a different kernel source."""
+def read_traffic(workload: str):
+    """HBM bytes per step of the statistics kernel (its launches in one step) from
+    the committed rocprofv3 PMC summary (FETCH_SIZE and WRITE_SIZE runs, scaled by
+    a copy-kernel calibration), or None when absent or taken on other sources."""
     path = os.path.join(PROFILES, f"rowstats_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -91,7 +91,7 @@ def read_traffic(workload: str, launch_bytes: float):
         d = json.load(f)
     if d.get("source_hash") != kernel_source_hash():
         return None
-    return float(d["bytes_per_launch"])
+    return float(d["bytes_per_step"])
 
 
 def cpu_baseline(method, batch, w, target_cpu_s: float):
@@ -212,7 +212,7 @@ def main():
         log(f"[bench] copy calibration: 3 copies of {n} bytes")
         del src, dst
 
-    traffic = read_traffic(name, stats_bytes)
+    traffic = read_traffic(name)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
