@@ -24,10 +24,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "spec_oracle.c")
 LIB = os.path.join(_HERE, "libsvoracle.so")
 
-TOKEN, BLOCK, MULTI = 0, 1, 2
+TOKEN, BLOCK, MULTI, SPECTR = 0, 1, 2, 3
 F32, BF16 = 0, 1
 FLAG_DEGENERATE, FLAG_INVALID = 1, 2
-METHODS = {"token": TOKEN, "block": BLOCK, "multidraft": MULTI}
+METHODS = {"token": TOKEN, "block": BLOCK, "multidraft": MULTI, "spectr": SPECTR}
 
 _lock = threading.Lock()
 _libs = {}

@@ -20,6 +20,12 @@
  *         optimal for a single draft (SpecTr-GBV page, section 1, second
  *         limitation).  Written from its published definition (Sun et al.,
  *         "Block Verification Accelerates Speculative Decoding", 2024).
+ *  [KS]   SpecTr, the multi-draft baseline: verifies the drafts position by
+ *         position and stops at the first rejection (SpecTr-GBV page, section 1),
+ *         each selection step searching a scaling factor rho by bisection,
+ *         O(V log K) (section 3).  Written from the published k-sequential
+ *         selection of Sun et al., "SpecTr: Fast Speculative Decoding via
+ *         Optimal Transport" (2023), restated from its mathematics.
  *  [MD]   SpecTr-GBV, K i.i.d. drafts of length L (SpecTr-GBV page, section 2,
  *         "algorithmic procedure", steps 1-5): start from accepted length 0 and
  *         an empty rejected set H; walk the drafts; verify each one's sub-block
@@ -57,6 +63,7 @@
 #define SVO_TOKEN 0
 #define SVO_BLOCK 1
 #define SVO_MULTI 2
+#define SVO_SPECTR 3
 
 #define SVO_FLAG_DEGENERATE 1
 #define SVO_FLAG_INVALID 2
@@ -492,6 +499,110 @@ static void svo_run_multi(svo_req *r, int32_t *tau_o, int32_t *k_o, int32_t *y_o
     *y_o = y;
 }
 
+/* --------------------------------------- k-sequential selection [KS] */
+
+/* beta(rho) = sum_v min(q(v), p(v)/rho): the chance that one candidate drawn
+ * from q is accepted with probability min(1, p/(rho q)). */
+static double svo_ks_beta(const svo_req *r, double rho)
+{
+    double b = 0.0;
+    for (int v = 0; v < r->V; ++v)
+        b += fmin(r->q[v], r->p[v] / rho);
+    return b;
+}
+
+/* c = sum_{i<n} (1 - beta)^i = (1 - (1 - beta)^n) / beta: the expected number
+ * of tries when n candidates are tried in turn, each succeeding with
+ * probability beta -- so the mass a token receives from acceptances is
+ * c min(q, p/rho).  The sum form is exact at n = 1 and needs no limit at
+ * beta = 0. */
+static double svo_ks_c(double beta, int n)
+{
+    double c = 0.0, t = 1.0;
+    for (int i = 0; i < n; ++i) {
+        c += t;
+        t *= 1.0 - beta;
+    }
+    return c;
+}
+
+/* The smallest rho in [1, n] with c(beta(rho)) <= rho -- exactly the rho for
+ * which p - c min(q, p/rho) stays non-negative everywhere -- by bisection down
+ * to a bracket of relative width 2^-26, one O(V) pass per step.  The
+ * condition is monotone in rho: wherever rho = c(beta(rho)), the slope of
+ * rho - c(beta(rho)) is at least n x^(n-1) (1 - x) / (1 - x^n) > 0 with
+ * x = 1 - beta, so the condition turns from false to true once. */
+static double svo_ks_rho(svo_req *r, int n)
+{
+    if (n <= 1)
+        return 1.0;
+    r->sweeps += 1;
+    if (svo_ks_c(svo_ks_beta(r, 1.0), n) <= 1.0)
+        return 1.0;
+    double lo = 1.0, hi = (double)n;
+    while (hi - lo > hi * 1.4901161193847656e-08) {
+        double mid = 0.5 * (lo + hi);
+        r->sweeps += 1;
+        if (svo_ks_c(svo_ks_beta(r, mid), n) <= mid)
+            hi = mid;
+        else
+            lo = mid;
+    }
+    return hi;
+}
+
+/* SpecTr over K drafts: at position j the candidates are the tokens X[k][j] of
+ * the drafts whose first j tokens are the accepted prefix, tried in draft
+ * order with u[k][j] < min(1, p(x)/(rho* q(x))); the first success extends the
+ * prefix, no success stops the walk with tau = j and a correction from
+ * norm(max(p - c(rho*) min(q, p/rho*), 0)); with all L accepted the correction
+ * comes from the target row after the block.  The recorded draft is the one
+ * whose candidate was accepted last. */
+static void svo_run_spectr(svo_req *r, int32_t *tau_o, int32_t *k_o, int32_t *y_o,
+                           double *Z_o)
+{
+    const int K = r->K, L = r->L, V = r->V;
+    int own = 0, kacc = -1;
+    for (int j = 0; j < L; ++j) {
+        svo_softmax(r, 1, own, j, r->p);
+        svo_softmax(r, 0, own, j, r->q);
+        int n = 0;
+        for (int k = 0; k < K; ++k)
+            n += svo_same_prefix(r, k, own, j);
+        double rho = svo_ks_rho(r, n);
+        int acc = -1;
+        for (int k = 0; k < K && acc < 0; ++k) {
+            if (!svo_same_prefix(r, k, own, j))
+                continue;
+            int x = r->X[k * L + j];
+            double a = svo_ratio(r->p[x], rho * r->q[x]);
+            if (a > 1.0)
+                a = 1.0;
+            if (svo_test(r, k, j + 1, a))
+                acc = k;
+        }
+        if (acc < 0) {
+            double c = svo_ks_c(svo_ks_beta(r, rho), n);
+            for (int v = 0; v < V; ++v)
+                r->om[v] = fmax(r->p[v] - c * fmin(r->q[v], r->p[v] / rho), 0.0);
+            int y = svo_icdf(r, r->om, Z_o);
+            if (y < 0) {
+                r->flags |= SVO_FLAG_DEGENERATE;
+                y = svo_draw_target(r, own, j, Z_o);
+            }
+            *tau_o = j;
+            *k_o = kacc;
+            *y_o = y;
+            return;
+        }
+        own = acc;
+        kacc = acc;
+    }
+    *tau_o = L;
+    *k_o = kacc;
+    *y_o = svo_draw_target(r, own, L, Z_o);
+}
+
 /* ------------------------------------------------------------ validation */
 
 /* Request data the rules cannot act on: T not a positive finite number, a
@@ -538,10 +649,10 @@ int svo_verify(int method, int B, int K, int L, int V, int dtype,
                int32_t *flags, double *row_lse, double *accept_prob,
                double *resid_mass, double *margin, int64_t *counters)
 {
-    if (method < SVO_TOKEN || method > SVO_MULTI || B < 0 || K < 1 || K > SVO_KMAX ||
+    if (method < SVO_TOKEN || method > SVO_SPECTR || B < 0 || K < 1 || K > SVO_KMAX ||
         L < 1 || L > SVO_LMAX || V < 1 || (dtype != SVO_F32 && dtype != SVO_BF16))
         return -1;
-    if (method != SVO_MULTI && K != 1)
+    if ((method == SVO_TOKEN || method == SVO_BLOCK) && K != 1)
         return -1;
     if (b_begin < 0 || b_end > B || b_begin > b_end)
         return -1;
@@ -592,8 +703,10 @@ int svo_verify(int method, int B, int K, int L, int V, int dtype,
             svo_run_token(&r, &tau, &ks, &y, &Z);
         } else if (method == SVO_BLOCK) {
             svo_run_block(&r, &tau, &ks, &y, &Z);
-        } else {
+        } else if (method == SVO_MULTI) {
             svo_run_multi(&r, &tau, &ks, &y, &Z);
+        } else {
+            svo_run_spectr(&r, &tau, &ks, &y, &Z);
         }
         if (r.flags & SVO_FLAG_INVALID) {
             r.flags = SVO_FLAG_INVALID;

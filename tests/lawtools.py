@@ -195,9 +195,12 @@ def _f32(x):
 
 def _walk_order(method, K, L):
     """Order in which the rules take their decisions: token level tests
-    positions forward; block walks test each draft's positions backward."""
+    positions forward; SpecTr tests position by position, drafts in order;
+    block walks test each draft's positions backward."""
     if method == "token":
         return [(0, j) for j in range(L)]
+    if method == "spectr":
+        return [(k, j) for j in range(L) for k in range(K)]
     return [(k, m - 1) for k in range(K) for m in range(L, 0, -1)]
 
 

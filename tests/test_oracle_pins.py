@@ -10,7 +10,11 @@ None of these tests compares the oracle with a re-typed copy of itself:
     section 2 "monotonicity" and section 4 ablation on K), GBV >= token level
     (GBV is the optimal single-draft verifier, SpecTr-GBV page, section 1), GBV
     non-decreasing in L (section 4 ablation on L);
-  * special cases: p = q, disjoint supports, one draft = GBV, L = 1 token = GBV;
+  * special cases: p = q, disjoint supports, one draft = GBV, L = 1 token = GBV,
+    one-draft SpecTr = token level;
+  * SpecTr's scaling factor: at L = 1 the accepted length brackets the one of
+    the smallest rho that keeps the residual non-negative, found by a grid
+    search over rho;
   * hand-worked examples (tests/golden/worked_examples.json);
   * planted mistakes in a copy of the oracle, each of which must fail a pin.
 """
@@ -57,6 +61,84 @@ def test_multidraft_keeps_target_law(V, L, K):
             assert abs(e_tau - lt.expected_tau_gbv(m)) < ETAU_TOL
         if L == 1:
             assert abs(e_tau - lt.expected_tau_rrs_l1(m, K)) < ETAU_TOL
+
+
+# SpecTr enumerates like the K-draft walk; the two largest corners are left out
+# for time (each K-draft corner above is also run for SpecTr).
+SPECTR_GRID = [g for g in GRID if g not in ((2, 3, 3), (3, 2, 3))]
+
+
+def spectr_l1_bracket(m, K, n_grid=4001):
+    """L = 1 SpecTr, written from its definition rather than the oracle's
+    search: rho* is the smallest rho in [1, K] for which K candidates tried in
+    turn, each accepted with probability min(1, p/(rho q)), leave a
+    non-negative residual p - P(accept with that token).  A grid over rho
+    brackets rho*, and P(tau = 1) = 1 - (1 - beta(rho))^K is decreasing in rho,
+    so the grid cell gives an interval for E[tau]."""
+    p, q = m.p(()), m.q(())
+    rhos = np.linspace(1.0, float(K), n_grid)
+
+    def accept_and_residual(rho):
+        m_ = np.minimum(q, p / rho)                       # per-try acceptance mass
+        beta = m_.sum()
+        tries = sum((1.0 - beta) ** i for i in range(K))  # expected tries that happen
+        return 1.0 - (1.0 - beta) ** K, p - tries * m_
+
+    ok = [accept_and_residual(r)[1].min() >= -1e-12 for r in rhos]
+    g = ok.index(True)
+    hi = accept_and_residual(rhos[g])[0]
+    lo = hi if g == 0 else accept_and_residual(rhos[g - 1])[0]
+    return hi, lo
+
+
+@pytest.mark.parametrize("V,L,K", SPECTR_GRID)
+def test_spectr_keeps_target_law(V, L, K):
+    for seed in range(2):
+        m = _model(V, L, seed)
+        law, e_tau, dropped = lt.output_law(m, K, "spectr")
+        assert dropped < 1e-7
+        assert abs(sum(law.values()) - 1.0) < LAW_TOL
+        assert lt.extended_law_gap(m, law) < LAW_TOL
+        assert e_tau <= lt.expected_tau_bound(m, K) + ETAU_TOL
+        if K == 1:
+            assert abs(e_tau - lt.expected_tau_token(m)) < ETAU_TOL
+        if L == 1:
+            lo, hi = spectr_l1_bracket(m, K)
+            assert lo - 1e-9 <= e_tau <= hi + 1e-9, (lo, e_tau, hi)
+
+
+def test_spectr_l1_scaling_factor_is_the_smallest_feasible():
+    """Larger vocabularies than the enumeration reaches: at L = 1 the oracle's
+    P(tau = 1) over many realisations matches the bracket of the smallest
+    feasible rho (the acceptance probability of each test is reported, so the
+    expected acceptance is computed from h exactly, not sampled)."""
+    rng = np.random.default_rng(31)
+    for V, K in ((16, 2), (40, 4), (40, 8)):
+        m = lt.TreeModel.random(V, 1, rng, T=0.9, draft_mode="noisy")
+        lo, hi = spectr_l1_bracket(m, K, n_grid=20001)
+        p, q = m.p(()), m.q(())
+        B = 4000
+        tok = rng.choice(V, size=(B, K, 1), p=q).astype(np.int32)
+        tgt = np.broadcast_to(np.stack([m.tgt[()], m.tgt[()]])[None, None],
+                              (B, K, 2, V)).astype(np.float32)
+        drf = np.broadcast_to(m.drf[()][None, None, None], (B, K, 1, V)).astype(np.float32)
+        temps = np.full(B, m.T, np.float32)
+        ua = np.full((B, K, 1), 0.9999999, np.float32)   # tests reject unless h ~ 1
+        uc = rng.random(B).astype(np.float32)
+        o = oracle.verify("spectr", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+        h = o["accept_prob"][:, :, 0].astype(np.float64)
+        # a draft goes untested only after a test with h ~ 1 accepted; its factor
+        # in the product below is then irrelevant
+        untested = np.isnan(h)
+        assert (~untested[:, 0]).all()
+        assert all((h[i, :np.argmax(untested[i])] > 0.9999999).any()
+                   for i in np.nonzero(untested.any(axis=1))[0])
+        h = np.where(untested, 0.0, h)
+        # P(accept | drafts) = 1 - prod_k (1 - h_k); its mean over q^K estimates
+        # 1 - (1 - beta)^K with standard error ~1e-3
+        est = (1.0 - np.prod(1.0 - h, axis=1)).mean()
+        se = (1.0 - np.prod(1.0 - h, axis=1)).std() / np.sqrt(B)
+        assert lo - 5 * se - 1e-6 <= est <= hi + 5 * se + 1e-6, (V, K, lo, est, hi)
 
 
 @pytest.mark.parametrize("V,L", [(2, 1), (2, 3), (3, 2), (8, 2), (8, 3)])
@@ -138,6 +220,19 @@ def test_one_draft_multidraft_equals_block_pathwise():
         np.testing.assert_array_equal(a["resid_mass"], b["resid_mass"])
 
 
+def test_one_draft_spectr_equals_token_pathwise():
+    """With one candidate rho* = 1 and c = 1: SpecTr is token-level sampling."""
+    rng = np.random.default_rng(17)
+    for V in (2, 7, 64):
+        tgt, drf, tok, temps, ua, uc = _random_batch(rng, 400, 1, 4, V)
+        a = oracle.verify("token", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+        b = oracle.verify("spectr", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+        for key in ("accept_len", "draft_index", "correction", "flags"):
+            np.testing.assert_array_equal(a[key], b[key])
+        np.testing.assert_array_equal(a["accept_prob"], b["accept_prob"])
+        np.testing.assert_array_equal(a["resid_mass"], b["resid_mass"])
+
+
 def test_length_one_token_equals_block_pathwise():
     rng = np.random.default_rng(13)
     tgt, drf, tok, temps, ua, uc = _random_batch(rng, 500, 1, 1, 9)
@@ -153,7 +248,7 @@ def test_equal_distributions_accept_everything():
     B, K, L, V = 200, 3, 4, 11
     tgt, drf, tok, temps, ua, uc = _random_batch(rng, B, K, L, V)
     drf = tgt[:, :, :L].copy()
-    for method, k in (("token", 1), ("block", 1), ("multidraft", K)):
+    for method, k in (("token", 1), ("block", 1), ("multidraft", K), ("spectr", K)):
         o = oracle.verify(method, tgt[:, :k], drf[:, :k], tok[:, :k], temps, ua[:, :k], uc)
         assert (o["accept_len"] == L).all()
         assert (o["draft_index"] == 0).all()
@@ -169,7 +264,8 @@ def test_disjoint_supports_reject_and_sample_target():
             m.tgt[pre][2:] = -np.inf
         if pre in m.drf and len(pre) == 0:
             m.drf[pre][:2] = -np.inf
-    for method, K in (("token", 1), ("block", 1), ("multidraft", 2), ("multidraft", 3)):
+    for method, K in (("token", 1), ("block", 1), ("multidraft", 2), ("multidraft", 3),
+                      ("spectr", 2), ("spectr", 3)):
         law, e_tau, _ = lt.output_law(m, K, method)
         assert e_tau == 0.0
         p0 = m.p(())
@@ -182,7 +278,8 @@ def test_non_canonical_rows_are_never_read():
     the same node; overwriting them must not change anything."""
     rng = np.random.default_rng(16)
     tgt, drf, tok, temps, ua, uc = _random_batch(rng, 300, 4, 3, 3)
-    a = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, diagnostics=True)
+    a = {m: oracle.verify(m, tgt, drf, tok, temps, ua, uc, diagnostics=True)
+         for m in ("multidraft", "spectr")}
     tgt2, drf2 = tgt.copy(), drf.copy()
     B, K, L = tok.shape
     for b in range(B):
@@ -192,9 +289,10 @@ def test_non_canonical_rows_are_never_read():
                     tgt2[b, k, j] = np.nan
                     if j < L:
                         drf2[b, k, j] = np.nan
-    b2 = oracle.verify("multidraft", tgt2, drf2, tok, temps, ua, uc, diagnostics=True)
-    for key in ("accept_len", "draft_index", "correction", "flags"):
-        np.testing.assert_array_equal(a[key], b2[key])
+    for m in a:
+        b2 = oracle.verify(m, tgt2, drf2, tok, temps, ua, uc, diagnostics=True)
+        for key in ("accept_len", "draft_index", "correction", "flags"):
+            np.testing.assert_array_equal(a[m][key], b2[key])
 
 
 def test_row_lse_matches_library_logsumexp():
@@ -372,12 +470,29 @@ MUTANTS = {
 }
 
 
+SPECTR_MUTANTS = {
+    # no search: rho = n is feasible but not the smallest
+    "spectr_rho_is_n": ("double rho = svo_ks_rho(r, n);", "double rho = (double)n;"),
+    # residual without the expected number of tries
+    "spectr_residual_without_c": ("fmax(r->p[v] - c * fmin(r->q[v], r->p[v] / rho), 0.0)",
+                                  "fmax(r->p[v] - fmin(r->q[v], r->p[v] / rho), 0.0)"),
+    # candidates counted over all drafts, not those on the accepted prefix
+    "spectr_counts_all_drafts": ("n += svo_same_prefix(r, k, own, j);", "n += 1;"),
+    # acceptance ignores the scaling factor
+    "spectr_accept_ignores_rho": ("svo_ratio(r->p[x], rho * r->q[x])",
+                                  "svo_ratio(r->p[x], r->q[x])"),
+    # per-try acceptance mass taken at rho = 1
+    "spectr_beta_unscaled": ("b += fmin(r->q[v], r->p[v] / rho);",
+                             "b += fmin(r->q[v], r->p[v]);"),
+}
+
+
 @pytest.fixture(scope="module")
 def mutant_libs(tmp_path_factory):
     d = tmp_path_factory.mktemp("mutants")
     src = open(oracle.SRC).read()
     libs = {}
-    for name, (old, new) in MUTANTS.items():
+    for name, (old, new) in {**MUTANTS, **SPECTR_MUTANTS}.items():
         assert src.count(old) == 1, name
         p = d / f"{name}.c"
         p.write_text(src.replace(old, new))
@@ -401,6 +516,26 @@ def test_planted_mistake_fails_a_pin(mutant_libs, name):
             bad = gap > LAW_TOL or e_tau > lt.expected_tau_bound(m, K) + ETAU_TOL
             if K == 1:
                 bad |= abs(e_tau - lt.expected_tau_gbv(m)) > ETAU_TOL
+            if bad:
+                caught = True
+                break
+        if caught:
+            break
+    assert caught, name
+
+
+@pytest.mark.parametrize("name", sorted(SPECTR_MUTANTS))
+def test_planted_spectr_mistake_fails_a_pin(mutant_libs, name):
+    caught = False
+    for (V, L, K) in [(3, 1, 3), (2, 2, 2), (3, 2, 2), (8, 1, 3)]:
+        for seed in range(2):
+            m = _model(V, L, seed)
+            law, e_tau, _ = lt.output_law(m, K, "spectr", lib_path=mutant_libs[name])
+            bad = lt.extended_law_gap(m, law) > LAW_TOL
+            bad |= e_tau > lt.expected_tau_bound(m, K) + ETAU_TOL
+            if L == 1:
+                lo, hi = spectr_l1_bracket(m, K)
+                bad |= not (lo - 1e-9 <= e_tau <= hi + 1e-9)
             if bad:
                 caught = True
                 break
