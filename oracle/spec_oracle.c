@@ -526,9 +526,41 @@ static double svo_ks_c(double beta, int n)
     return c;
 }
 
+/* D(rho) = sum_v max(p - rho q, 0): the p-mass that rho q does not cover. */
+static double svo_ks_excess(const svo_req *r, double rho)
+{
+    double d = 0.0;
+    for (int v = 0; v < r->V; ++v)
+        d += fmax(r->p[v] - rho * r->q[v], 0.0);
+    return d;
+}
+
+/* Whether rho is feasible, c(beta(rho)) <= rho.  Multiplied by beta this reads
+ * 1 - rho beta <= (1 - beta)^n, and 1 - rho beta = sum_v p - sum_v min(p, rho q)
+ * = D(rho).  The two forms decide the same thing; each is evaluated where its
+ * two sides do not agree in their leading digits: for beta > 1/2 the gap
+ * rho - c is rho ((1 - beta)^n - D) / (1 - D), far below the rounding of
+ * rho or c when the rows nearly coincide, while D and (1 - beta)^n are each
+ * exact to rounding; for beta <= 1/2, D and (1 - beta)^n both tend to 1 as
+ * the supports separate, while rho - c does not cancel. */
+static int svo_ks_feasible(const svo_req *r, double rho, int n)
+{
+    double beta = svo_ks_beta(r, rho);
+    if (beta <= 0.5)
+        return svo_ks_c(beta, n) <= rho;
+    double x = 1.0 - beta, xn = 1.0;
+    for (int i = 0; i < n; ++i)
+        xn *= x;
+    return svo_ks_excess(r, rho) <= xn;
+}
+
 /* The smallest rho in [1, n] with c(beta(rho)) <= rho -- exactly the rho for
- * which p - c min(q, p/rho) stays non-negative everywhere -- by bisection down
- * to a bracket of relative width 2^-26, one O(V) pass per step.  The
+ * which p - c min(q, p/rho) stays non-negative everywhere -- by bisection until
+ * the bracket holds two adjacent doubles, one O(V) pass per step (about
+ * 52 + log2 n passes).  A bracket this tight makes the oracle return the
+ * definition's rho itself: rho can be badly conditioned (the slope below
+ * tends to 0 as the p-mass of tokens with p/q < rho tends to 1), and the
+ * residual mass (1 - beta)^n is small whenever rejection is rare.  The
  * condition is monotone in rho: wherever rho = c(beta(rho)), the slope of
  * rho - c(beta(rho)) is at least n x^(n-1) (1 - x) / (1 - x^n) > 0 with
  * x = 1 - beta, so the condition turns from false to true once. */
@@ -537,13 +569,15 @@ static double svo_ks_rho(svo_req *r, int n)
     if (n <= 1)
         return 1.0;
     r->sweeps += 1;
-    if (svo_ks_c(svo_ks_beta(r, 1.0), n) <= 1.0)
+    if (svo_ks_feasible(r, 1.0, n))
         return 1.0;
     double lo = 1.0, hi = (double)n;
-    while (hi - lo > hi * 1.4901161193847656e-08) {
+    for (;;) {
         double mid = 0.5 * (lo + hi);
+        if (!(mid > lo && mid < hi))
+            break;
         r->sweeps += 1;
-        if (svo_ks_c(svo_ks_beta(r, mid), n) <= mid)
+        if (svo_ks_feasible(r, mid, n))
             hi = mid;
         else
             lo = mid;

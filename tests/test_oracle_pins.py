@@ -141,6 +141,62 @@ def test_spectr_l1_scaling_factor_is_the_smallest_feasible():
         assert lo - 5 * se - 1e-6 <= est <= hi + 5 * se + 1e-6, (V, K, lo, est, hi)
 
 
+def _spectr_root(K, tgt_logits, drf_logits, tokens, T, u, lib_path=None):
+    """One request per row of u, L = 1, the same rows in every draft."""
+    B = len(u)
+    V = len(tgt_logits)
+    tgt = np.broadcast_to(np.array([tgt_logits, tgt_logits], np.float32)[None, None],
+                          (B, K, 2, V)).copy()
+    drf = np.broadcast_to(np.array([drf_logits], np.float32)[None, None], (B, K, 1, V)).copy()
+    tok = np.full((B, K, 1), tokens, np.int32)
+    ua = np.repeat(np.asarray(u, np.float32)[:, None, None], K, axis=1)
+    return oracle.verify("spectr", tgt, drf, tok, np.full(B, T, np.float32), ua,
+                         np.full(B, 0.5, np.float32), diagnostics=True, lib_path=lib_path)
+
+
+def spectr_near_identical_ok(lib_path=None):
+    """Rows whose total variation is ~1.2e-12 (the draft puts a little more mass
+    on the last token): p > rho q nowhere once rho exceeds 1 + 1.3e-12, so
+    rho* <= 1 + 1.3e-12 and the shared top token is accepted with h = 1 - 1e-12
+    or more, whatever u < 1 is.  (The quotient form c <= rho cannot tell c
+    from rho here: their gap rho (1 - beta)^n stays below double rounding for
+    rho up to ~1.01.)"""
+    o = _spectr_root(8, [0.0, -27.0, -27.0, -27.0], [0.0, -27.0, -27.0, -26.5], 0, 1.0,
+                     [0.9999, 0.99999, 0.999999], lib_path)
+    return bool((o["accept_len"] == 1).all() and (o["accept_prob"][:, 0, 0] >= 1 - 1e-12).all())
+
+
+def spectr_near_disjoint_ok(lib_path=None):
+    """Supports that share one token C with p_C = s, q_C = t: beta(rho) =
+    min(t, s/rho), which is s/rho at the root, so rho* solves
+    rho = sum_{i<n} (1 - s/rho)^i, a scalar equation that does not cancel.  A
+    draft offering C is accepted with h = (s/t)/rho*.  (The product form
+    D <= (1 - beta)^n compares two numbers within ~1e-9 of 1 here.)"""
+    n, s_, t_ = 8, 3e-9, 1e-9
+    tl = np.array([np.log1p(-s_), -np.inf, np.log(s_)], np.float32)
+    dl = np.array([-np.inf, np.log1p(-t_), np.log(t_)], np.float32)
+    p = np.exp(tl.astype(np.float64)); p /= p.sum()
+    q = np.exp(dl.astype(np.float64)); q /= q.sum()
+    s_, t_ = p[2], q[2]
+    lo, hi = s_ / t_, float(n)                     # root lies above the breakpoint s/t
+    f = lambda r: r - sum((1.0 - s_ / r) ** i for i in range(n))
+    assert f(lo) < 0 <= f(hi)
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if f(mid) < 0 else (lo, mid)
+    o = _spectr_root(n, tl, dl, 2, 1.0, [0.9999], lib_path)
+    want = (s_ / t_) / hi
+    return abs(float(o["accept_prob"][0, 0, 0]) - want) < 1e-12 * want
+
+
+def test_spectr_scaling_factor_at_nearly_identical_rows():
+    assert spectr_near_identical_ok()
+
+
+def test_spectr_scaling_factor_at_nearly_disjoint_rows():
+    assert spectr_near_disjoint_ok()
+
+
 @pytest.mark.parametrize("V,L", [(2, 1), (2, 3), (3, 2), (8, 2), (8, 3)])
 def test_single_draft_rules_keep_target_law(V, L):
     for seed in range(2):
@@ -486,13 +542,21 @@ SPECTR_MUTANTS = {
                              "b += fmin(r->q[v], r->p[v]);"),
 }
 
+# the feasibility test evaluated in one form only
+SPECTR_NUMERIC_MUTANTS = {
+    "spectr_quotient_form_only": ("    if (beta <= 0.5)\n        return svo_ks_c(beta, n) <= rho;",
+                                  "    if (1)\n        return svo_ks_c(beta, n) <= rho;"),
+    "spectr_product_form_only": ("    if (beta <= 0.5)\n        return svo_ks_c(beta, n) <= rho;",
+                                 "    if (0)\n        return svo_ks_c(beta, n) <= rho;"),
+}
+
 
 @pytest.fixture(scope="module")
 def mutant_libs(tmp_path_factory):
     d = tmp_path_factory.mktemp("mutants")
     src = open(oracle.SRC).read()
     libs = {}
-    for name, (old, new) in {**MUTANTS, **SPECTR_MUTANTS}.items():
+    for name, (old, new) in {**MUTANTS, **SPECTR_MUTANTS, **SPECTR_NUMERIC_MUTANTS}.items():
         assert src.count(old) == 1, name
         p = d / f"{name}.c"
         p.write_text(src.replace(old, new))
@@ -542,3 +606,9 @@ def test_planted_spectr_mistake_fails_a_pin(mutant_libs, name):
         if caught:
             break
     assert caught, name
+
+
+@pytest.mark.parametrize("name", sorted(SPECTR_NUMERIC_MUTANTS))
+def test_planted_spectr_numeric_mistake_fails_a_pin(mutant_libs, name):
+    lib = mutant_libs[name]
+    assert not (spectr_near_identical_ok(lib) and spectr_near_disjoint_ok(lib)), name
