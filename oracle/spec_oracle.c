@@ -537,16 +537,19 @@ static double svo_ks_excess(const svo_req *r, double rho)
 
 /* Whether rho is feasible, c(beta(rho)) <= rho.  Multiplied by beta this reads
  * 1 - rho beta <= (1 - beta)^n, and 1 - rho beta = sum_v p - sum_v min(p, rho q)
- * = D(rho).  The two forms decide the same thing; each is evaluated where its
- * two sides do not agree in their leading digits: for beta > 1/2 the gap
- * rho - c is rho ((1 - beta)^n - D) / (1 - D), far below the rounding of
- * rho or c when the rows nearly coincide, while D and (1 - beta)^n are each
- * exact to rounding; for beta <= 1/2, D and (1 - beta)^n both tend to 1 as
- * the supports separate, while rho - c does not cancel. */
+ * = D(rho).  The two forms decide the same thing; each is evaluated where the
+ * rounding of its inputs cannot flip it.  The gap rho - c equals
+ * rho ((1 - beta)^n - D) / (1 - D): once (1 - beta)^n is below double
+ * rounding -- nearly identical rows, or many candidates -- the rounding of
+ * beta alone moves c by more than that gap, while D and (1 - beta)^n are each
+ * exact to rounding.  When beta is tiny (nearly disjoint supports) D and
+ * (1 - beta)^n both lie within ~n beta of 1 and the product form cancels,
+ * while rho - c does not.  The quotient form is taken for beta <= 2^-10
+ * (there (1 - beta)^n >= 0.93 for n <= 64), the product form above. */
 static int svo_ks_feasible(const svo_req *r, double rho, int n)
 {
     double beta = svo_ks_beta(r, rho);
-    if (beta <= 0.5)
+    if (beta <= 0x1p-10)
         return svo_ks_c(beta, n) <= rho;
     double x = 1.0 - beta, xn = 1.0;
     for (int i = 0; i < n; ++i)

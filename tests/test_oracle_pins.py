@@ -189,6 +189,26 @@ def spectr_near_disjoint_ok(lib_path=None):
     return abs(float(o["accept_prob"][0, 0, 0]) - want) < 1e-12 * want
 
 
+def spectr_many_candidates_ok(lib_path=None):
+    """K = 64 candidates, p = (0.63, 0.37), q = (0.3, 0.7): for rho >= 2.1 = the
+    largest ratio no token has p > rho q, so every such rho is feasible, and
+    below it D(rho) = 0.63 - 0.3 rho exceeds (1 - beta)^64 < 1e-17 until
+    within ~1e-17 of 2.1: rho* = p_0/q_0 to double precision, and a draft
+    offering token 1 is accepted with h = (p_1/q_1)/rho*.  (Here beta ~ 0.48 and
+    rho - c ~ rho (1 - beta)^64 ~ 1e-18, below the rounding of rho.)"""
+    tl = np.log(np.array([0.63, 0.37])).astype(np.float32)
+    dl = np.log(np.array([0.3, 0.7])).astype(np.float32)
+    p = np.exp(tl.astype(np.float64)); p /= p.sum()
+    q = np.exp(dl.astype(np.float64)); q /= q.sum()
+    o = _spectr_root(64, tl, dl, 1, 1.0, [0.9999], lib_path)
+    want = (p[1] / q[1]) / (p[0] / q[0])
+    return abs(float(o["accept_prob"][0, 0, 0]) - want) < 1e-12
+
+
+def test_spectr_scaling_factor_with_many_candidates():
+    assert spectr_many_candidates_ok()
+
+
 def test_spectr_scaling_factor_at_nearly_identical_rows():
     assert spectr_near_identical_ok()
 
@@ -544,10 +564,13 @@ SPECTR_MUTANTS = {
 
 # the feasibility test evaluated in one form only
 SPECTR_NUMERIC_MUTANTS = {
-    "spectr_quotient_form_only": ("    if (beta <= 0.5)\n        return svo_ks_c(beta, n) <= rho;",
+    "spectr_quotient_form_only": ("    if (beta <= 0x1p-10)\n        return svo_ks_c(beta, n) <= rho;",
                                   "    if (1)\n        return svo_ks_c(beta, n) <= rho;"),
-    "spectr_product_form_only": ("    if (beta <= 0.5)\n        return svo_ks_c(beta, n) <= rho;",
+    "spectr_product_form_only": ("    if (beta <= 0x1p-10)\n        return svo_ks_c(beta, n) <= rho;",
                                  "    if (0)\n        return svo_ks_c(beta, n) <= rho;"),
+    "spectr_quotient_form_to_one_half": (
+        "    if (beta <= 0x1p-10)\n        return svo_ks_c(beta, n) <= rho;",
+        "    if (beta <= 0.5)\n        return svo_ks_c(beta, n) <= rho;"),
 }
 
 
@@ -611,4 +634,5 @@ def test_planted_spectr_mistake_fails_a_pin(mutant_libs, name):
 @pytest.mark.parametrize("name", sorted(SPECTR_NUMERIC_MUTANTS))
 def test_planted_spectr_numeric_mistake_fails_a_pin(mutant_libs, name):
     lib = mutant_libs[name]
-    assert not (spectr_near_identical_ok(lib) and spectr_near_disjoint_ok(lib)), name
+    assert not (spectr_near_identical_ok(lib) and spectr_near_disjoint_ok(lib)
+                and spectr_many_candidates_ok(lib)), name
