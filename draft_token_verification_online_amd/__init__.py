@@ -68,7 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.sv_workspace_size.restype = ctypes.c_size_t
     lib.sv_workspace_size.argtypes = [ctypes.c_int32] * 5
-    for name in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft"):
+    for name in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
+                 "spec_verify_spectr"):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(SvInputs), ctypes.POINTER(SvOutputs),
@@ -100,11 +101,11 @@ def _ptr(t):
 class Verifier:
     """Holds outputs and workspace for repeated calls on inputs of one shape.
 
-    method: "token", "block" or "multidraft".  diagnostics=True also returns
+    method: "token", "block", "multidraft" or "spectr".  diagnostics=True also returns
     row_lse [B][K][2L+1], accept_prob [B][K][L] and resid_mass [B]."""
 
     _ENTRY = {"token": "spec_verify_token", "block": "spec_verify_block",
-              "multidraft": "spec_verify_multidraft"}
+              "multidraft": "spec_verify_multidraft", "spectr": "spec_verify_spectr"}
 
     def __init__(self, method, B, K, L, V, dtype, device="cuda", diagnostics=False,
                  with_flags=True):
@@ -189,5 +190,13 @@ def spec_verify_multidraft(target, draft, tokens, temperature, u_accept, u_corre
                 diagnostics, **kw)
 
 
-__all__ = ["spec_verify_token", "spec_verify_block", "spec_verify_multidraft", "Verifier",
-           "workspace_size", "load_library", "SpecVerifyError"]
+def spec_verify_spectr(target, draft, tokens, temperature, u_accept, u_correct, *,
+                       diagnostics=False, **kw):
+    """SpecTr's position-by-position verification of K i.i.d. drafts.  See
+    include/spec_verify.h."""
+    return _run("spectr", target, draft, tokens, temperature, u_accept, u_correct,
+                diagnostics, **kw)
+
+
+__all__ = ["spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
+           "spec_verify_spectr", "Verifier", "workspace_size", "load_library", "SpecVerifyError"]

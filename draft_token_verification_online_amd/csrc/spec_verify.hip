@@ -4,7 +4,8 @@
 // then launches on the caller's stream:
 //   1. rowstats_kernel  -- one workgroup per node row: softmax statistics of the
 //                          rows the walk reads first (streams the logits);
-//   2. walk_kernel      -- one workgroup per request: the verification walk; with
+//   2. walk_kernel      -- one workgroup per request: the verification walk (the
+//                          block walk, the token rule, or SpecTr's forward walk); with
 //                          K > 1 it may stop after an acceptance, flagging the rows
 //                          below the accepted node;
 //   3. rowstats_kernel  -- (K > 1) statistics of the flagged rows;
@@ -75,7 +76,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     hipStream_t stream = static_cast<hipStream_t>(ln->stream);
     const bool diagnostics = out->row_lse != nullptr;
     // a second round only pays when several drafts can share an accepted prefix
-    const bool two_round = method == sv::kMethodBlockWalk && in->K > 1 && !diagnostics;
+    const bool two_round = method != sv::kMethodToken && in->K > 1 && !diagnostics;
     const Layout lay = layout(in->B, in->K, in->L);
     char *ws = static_cast<char *>(ln->workspace);
 
@@ -133,9 +134,16 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
                        stream, sa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads), 0,
-                       stream, wa);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    auto walk = [&]() {
+        if (method == sv::kMethodSpecTr)
+            hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E, true>), dim3(in->B),
+                               dim3(kWalkThreads), 0, stream, wa);
+        else
+            hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B),
+                               dim3(kWalkThreads), 0, stream, wa);
+        return hipGetLastError();
+    };
+    if ((err = walk()) != hipSuccess) return err;
     if ((err = record(ln, 2, stream)) != hipSuccess) return err;
     if (two_round) {
         // the listed rows: at most 2*B*K*L, usually a few thousand; each block
@@ -150,9 +158,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     if ((err = record(ln, 3, stream)) != hipSuccess) return err;
     if (two_round) {
         wa.round = 2;   // only the stopped walks run
-        hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E>), dim3(in->B), dim3(kWalkThreads),
-                           0, stream, wa);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = walk()) != hipSuccess) return err;
     }
     return record(ln, 4, stream);
 }
@@ -205,6 +211,10 @@ int spec_verify_block(const sv_inputs *in, const sv_outputs *out, const sv_launc
 
 int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
     return verify(sv::kMethodBlockWalk, in, out, ln, false);
+}
+
+int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
+    return verify(sv::kMethodSpecTr, in, out, ln, false);
 }
 
 const char *sv_status_string(int status) {

@@ -180,6 +180,27 @@ __device__ __forceinline__ double block_sum(double v, double *red) {
     return t;
 }
 
+// N independent block sums at once; red[] must hold N * NT/64 entries.
+template <int NT, int N>
+__device__ __forceinline__ void block_sum_n(double (&v)[N], double *red) {
+    constexpr int NW = NT / kWave;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) red[i * NW + threadIdx.x / kWave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        double t = red[i * NW];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) t += red[i * NW + w];
+        v[i] = t;
+    }
+}
+
 // Four independent block sums at once; red[] must hold 4 * NT/64 entries.
 template <int NT>
 __device__ __forceinline__ void block_sum4(double v[4], double *red) {

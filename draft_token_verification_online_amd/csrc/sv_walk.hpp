@@ -26,12 +26,20 @@
 //                   (alpha, beta, N) = (w_m, 1, R_m); rejection adds the first
 //                   token to H and N to beta.  One O(V) sweep per selection
 //                   step, no search over a scaling factor (section 3).
+//  SpecTr        -- the position-by-position multi-draft baseline (SpecTr-GBV
+//                   page, sections 1 and 3): at each position the n drafts on
+//                   the accepted prefix are tried in draft order, each accepted
+//                   with probability min(1, p(x)/(rho* q(x))) (rho* from
+//                   sv_spectr.hpp); the first acceptance extends the prefix,
+//                   none stops the walk with a correction from
+//                   max(p - c q, (1 - c/rho*) p) = max(p - c min(q, p/rho*), 0).
 // A test at m < L with u >= w_m is settled without its sweep: R_m <= w_m
 // implies h_m = R_m / (R_m + 1 - w_m) <= w_m, so it rejects either way.
 #pragma once
 
 #include "sv_device.hpp"
 #include "sv_rowstats.hpp"
+#include "sv_spectr.hpp"
 
 namespace sv {
 
@@ -40,6 +48,7 @@ constexpr int kMaxL = 16;
 constexpr int kMaxV = 1 << 22;
 constexpr int kMethodToken = 0;
 constexpr int kMethodBlockWalk = 1;
+constexpr int kMethodSpecTr = 2;
 constexpr int kFlagDegenerate = 1;
 constexpr int kFlagInvalid = 2;
 
@@ -52,7 +61,7 @@ struct WalkArgs {
     const float *uc;        // [B]
     const RowStat *stats;   // [B][K][2L+1]
     int B, K, L, V;
-    int method;             // kMethodToken or kMethodBlockWalk
+    int method;             // kMethodToken, kMethodBlockWalk or kMethodSpecTr
     int all_nodes;          // the statistics kernel streamed every node row (diagnostics)
     int round;              // 1, or 2 to resume the walks the first round suspended
     int two_round;          // a second round follows: the first may suspend
@@ -78,10 +87,11 @@ __device__ __forceinline__ double chain_step(double w, double r) {
 }
 
 // omega(v) for the 8 elements of chunk c: [v not in H] max(a eP - bq eQ, 0),
-// eP = 2^((P_v - MP) c); without a Q row, omega = a eP.
-template <bool HAS_Q>
+// eP = 2^((P_v - MP) c); without a Q row, omega = a eP.  With FLOOR the lower
+// bound is g eP (g >= 0) instead of 0.
+template <bool HAS_Q, bool FLOOR = false>
 __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MP, float MQ,
-                                       float a, float bq, float chi, float clo, int v0,
+                                       float a, float bq, float g, float chi, float clo, int v0,
                                        const int *H, int nH, float w[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -90,7 +100,7 @@ __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], flo
         if (HAS_Q) {
             const float dq = xq[e] - MQ;
             const float eq = fast_exp2(fmaf(dq, chi, dq * clo));
-            w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), 0.0f);
+            w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), FLOOR ? g * ep : 0.0f);
         } else {
             w[e] = a * ep;
         }
@@ -106,11 +116,12 @@ __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], flo
 
 struct SweepRows {
     float MP, MQ, a, bq;
+    float g = 0.0f;   // floor coefficient (FLOOR sweeps only)
 };
 
 // Block-wide sum of omega over a row pair (or a single row when HAS_Q is false).
 // Four chunks per row are in flight per lane.
-template <int NT, typename RD, bool HAS_Q>
+template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
 __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
                              float clo, const int *H, int nH, double *red) {
     double acc = 0.0;
@@ -127,7 +138,7 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
             float xp[8], xq[8], w[8];
             RD::unpack(rp[i], xp);
             if (HAS_Q) RD::unpack(rq[i], xq);
-            omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * (c + i * NT), H, nH, w);
+            omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * (c + i * NT), H, nH, w);
             acc += static_cast<double>(sum8(w));
         }
     }
@@ -135,7 +146,7 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
         float xp[8], xq[8], w[8];
         P.load(c, xp);
         if (HAS_Q) Q.load(c, xq);
-        omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
         acc += static_cast<double>(sum8(w));
     }
     return block_sum<NT>(acc, red);
@@ -145,7 +156,7 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
 // when the mass Z is not a positive finite number.  Z is returned in *Z.
 // Tiles of NT chunks are summed four at a time into tile[]; the tile holding
 // the threshold is rescanned with a block scan.
-template <int NT, typename RD, bool HAS_Q>
+template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
 __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
                           float clo, const int *H, int nH, double u, double *Z, double *tile,
                           double *red, double *red4, int *ired) {
@@ -170,7 +181,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
                 float xp[8], xq[8], w[8];
                 RD::unpack(rp[i], xp);
                 if (HAS_Q) RD::unpack(rq[i], xq);
-                omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+                omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     cs[i] += static_cast<double>(w[e]);
@@ -206,7 +217,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
         float xp[8], xq[8];
         P.load(c, xp);
         if (HAS_Q) Q.load(c, xq);
-        omega8<HAS_Q>(xp, xq, s.MP, s.MQ, s.a, s.bq, chi, clo, 8 * c, H, nH, w);
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
 #pragma unroll
         for (int e = 0; e < 8; ++e) cs += static_cast<double>(w[e]);
     }
@@ -316,8 +327,9 @@ constexpr int kStateDone = 0;
 constexpr int kStateSuspended = 1;
 
 // Two 512-thread walks per CU (4 waves per SIMD) keep every request of a
-// 512-request batch resident at once.
-template <int NT, typename RD, typename E>
+// 512-request batch resident at once.  SPECTR selects SpecTr's forward walk;
+// otherwise A.method chooses between the token-level rule and the block walk.
+template <int NT, typename RD, typename E, bool SPECTR = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void walk_kernel(
     WalkArgs A) {
     constexpr int kMaxTiles = (kMaxV / kChunk + NT - 1) / NT;
@@ -337,6 +349,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     __shared__ double s_tile[kMaxTiles];
     __shared__ int s_H[kMaxK];
     __shared__ double s_w[kMaxL + 1];
+    __shared__ unsigned s_hist[SPECTR ? 2 * kHistBins : 1];
+    __shared__ double s_red6[SPECTR ? 6 * NW : 1];
+    __shared__ double s_br[4];
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -473,6 +488,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
 
     int tau = -1, kstar = -1, y = -1, flags = 0, rows = 0;
     double Zp = NAN;
+    double rho = 1.0, cc = 1.0;   // SpecTr: scaling factor and tries at the last node
     bool suspend = false;
     int own = 0, nH = 0, k0 = 0;
     double alpha = 1.0, beta = 0.0, N = 1.0;
@@ -492,7 +508,52 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     }
     rows += streamed;
 
-    if (!bad) {
+    if constexpr (SPECTR) {
+        if (!bad) {
+            if (A.round == 1) {
+                tau = 0;
+                own = 0;
+                kstar = -1;
+            }
+            int j = tau;
+            for (; j < L; ++j) {
+                const int cn = s_can[own * L1 + j];
+                const int ok = ensure(cn, j);
+                if (ok < 0) { suspend = true; break; }
+                if (ok == 0) { bad = 1; break; }
+                // candidates: the drafts whose first j tokens are the accepted prefix
+                int n = 0;
+                for (int k = 0; k < K; ++k) {
+                    int m2 = 1;
+                    for (int t = 0; t < j; ++t) m2 &= (s_x[k * L + t] == s_x[own * L + t]);
+                    n += m2;
+                }
+                rho = 1.0;
+                cc = 1.0;
+                if (n > 1)
+                    spectr_scale<NT, RD>(RD(trow(cn, j), V), RD(drow(cn, j), V), nch,
+                                         s_M[cn * RS + j], s_S[cn * RS + j], s_M[cn * RS + L1 + j],
+                                         s_S[cn * RS + L1 + j], chi, clo, n, rho, cc, s_hist,
+                                         s_red6, s_br, s_ired);
+                int acc = -1;
+                for (int k = 0; k < K && acc < 0; ++k) {
+                    int m2 = 1;
+                    for (int t = 0; t < j; ++t) m2 &= (s_x[k * L + t] == s_x[own * L + t]);
+                    if (!m2) continue;
+                    double h = ratio_log2(lp2(k, j), lq2(k, j)) / rho;
+                    if (h > 1.0) h = 1.0;
+                    const double u = static_cast<double>(A.ua[bKL + k * L + j]);
+                    if (tid == 0 && A.accept_prob)
+                        A.accept_prob[bKL + k * L + j] = static_cast<float>(h);
+                    if (u < h) acc = k;
+                }
+                if (acc < 0) break;
+                own = acc;
+                kstar = acc;
+            }
+            tau = j;
+        }
+    } else if (!bad) {
         if (A.method == kMethodToken) {
             tau = L;
             for (int j = 0; j < L; ++j) {
@@ -675,8 +736,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             SweepRows sr = node_sweep(cn, tau, alpha, beta);
             const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
             double Z;
-            y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, u, &Z, s_tile, s_red,
-                                         s_red4, s_ired);
+            if constexpr (SPECTR) {
+                // max(p - c q, (1 - c/rho) p): the residual after n tries
+                sr = node_sweep(cn, tau, 1.0, cc);
+                sr.g = static_cast<float>(fmax(1.0 - cc / rho, 0.0) / s_S[cn * RS + tau]);
+                y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
+                                                   s_red, s_red4, s_ired);
+            } else {
+                y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, u, &Z, s_tile, s_red,
+                                             s_red4, s_ired);
+            }
             Zp = Z;
             if (y < 0) {
                 flags |= kFlagDegenerate;

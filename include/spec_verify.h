@@ -22,7 +22,12 @@
  *                           draw the correction from the target (tau = L) or
  *                           from the residual (tau < L), one O(V) sweep per
  *                           selection step and no search over a scaling factor
- *                           (section 3, efficiency).
+ *                           (section 3, efficiency);
+ *   spec_verify_spectr      SpecTr, the multi-draft baseline the SpecTr-GBV page
+ *                           compares against (sections 1 and 3): the K drafts are
+ *                           verified position by position, each selection step
+ *                           searching a scaling factor rho (k-sequential
+ *                           selection; the rule is stated below).
  *
  * Every call is asynchronous on the caller's HIP stream: it validates its
  * arguments on the host, launches kernels and returns without synchronising.
@@ -59,7 +64,15 @@
  *  - the K-draft residual at a node s is omega(v) = [v not in H] *
  *    max(alpha p_s(v) - beta q_s(v), 0); a rejection adds the residual mass N
  *    to beta; a draft whose token at s is already in H is rejected without a
- *    test (its uniforms are not consumed) and still adds N to beta.
+ *    test (its uniforms are not consumed) and still adds N to beta;
+ *  - SpecTr at position j (node s = the accepted prefix, n = the number of drafts
+ *    on it): beta(rho) = sum_v min(q_s, p_s/rho), c = sum_{i<n} (1 - beta)^i,
+ *    rho* = the smallest rho in [1, n] with c <= rho (rho* = 1, c = 1 for n = 1);
+ *    the drafts on the prefix are tested in index order with
+ *    h = min(1, p_s(x)/(rho* q_s(x))) and u = u_accept[b][k][j]; the first
+ *    success extends the prefix (draft_index = that draft), no success ends the
+ *    walk with tau = j and a correction from max(p_s - c min(q_s, p_s/rho*), 0).
+ *    rho* is found to about 1e-7 relative (fp32 evaluation of the rows).
  * Integer outputs match the CPU oracle bit for bit except where a decision lies
  * within floating-point error of its threshold (|u - h| of order 1e-6).
  */
@@ -164,6 +177,11 @@ int spec_verify_block(const sv_inputs *in, const sv_outputs *out, const sv_launc
 
 /* Block verification over K i.i.d. drafts (K >= 1; K = 1 equals spec_verify_block). */
 int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* SpecTr over K i.i.d. drafts (K >= 1; K = 1 equals spec_verify_token).  Same
+ * inputs, outputs, workspace and events as spec_verify_multidraft; accept_prob
+ * holds h of every test made (NaN for drafts not tested). */
+int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
 
 /* Static description of a status code. */
 const char *sv_status_string(int status);

@@ -31,10 +31,10 @@ def declared_functions():
     return sorted(set(names))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-              "sv_workspace_size", "sv_status_string", "sv_version"):
+              "spec_verify_spectr", "sv_workspace_size", "sv_status_string", "sv_version"):
         assert n in names
 
 
@@ -82,7 +82,7 @@ def _fake(B=2, K=1, L=4, V=32, dtype=sv.SV_F32, align=256):
 
 
 @pytest.mark.parametrize("name", ["spec_verify_token", "spec_verify_block",
-                                  "spec_verify_multidraft"])
+                                  "spec_verify_multidraft", "spec_verify_spectr"])
 def test_host_validation_rejects_bad_arguments(lib, name):
     ins, outs, ln = _fake()
     assert _call(lib, name, None, outs, ln) == sv.SV_EINVAL

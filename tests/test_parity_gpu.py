@@ -67,7 +67,7 @@ SMALL = [
 @pytest.mark.parametrize("name,w,over", SMALL, ids=[s[0] for s in SMALL])
 def test_small_parity(name, w, over):
     ws = synth.scaled(w, **over)
-    methods = ("token", "block") if ws.K == 1 else ("multidraft",)
+    methods = ("token", "block", "spectr") if ws.K == 1 else ("multidraft", "spectr")
     for seed in (1, 2):
         batch = pt.gpu_batch(ws, seed)
         for method in methods:
@@ -83,11 +83,23 @@ def test_block_equals_multidraft_with_one_draft():
         assert torch.equal(a[k], b[k]), k
 
 
+def test_spectr_equals_token_with_one_draft():
+    """One candidate per position: rho* = 1, c = 1, SpecTr is token-level sampling."""
+    ws = synth.scaled(W["gbv_bf16_b64_k1_l5_v32000"], B=64, V=3000)
+    batch = pt.gpu_batch(ws, 3)
+    a = _verify("token", batch)
+    b = _verify("spectr", batch)
+    for k in ("accept_len", "draft_index", "correction", "flags", "resid_mass"):
+        assert torch.equal(a[k].nan_to_num(-7.0), b[k].nan_to_num(-7.0)), k
+
+
 def test_temperatures_of_the_ablation():
     """T in {0.1, 0.4, 0.7} (SpecTr-GBV page, section 4, ablations)."""
     for T in (0.1, 0.4, 0.7):
         ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=32, V=4096, temperature=T)
-        _parity("multidraft", pt.gpu_batch(ws, 4), f"multi_T{T}")
+        batch = pt.gpu_batch(ws, 4)
+        for method in ("multidraft", "spectr"):
+            _parity(method, batch, f"multi_T{T}")
 
 
 # ---------------------------------------------------------------- edge cases
@@ -112,18 +124,23 @@ def test_invalid_requests_are_flagged():
     batch["u_accept"][3, 0, 0] = 1.0                    # u must be < 1
     batch["draft"][4, 0, 2] = float("-inf")             # a row of zero mass
     batch["u_correct"][5] = -0.25                       # u must be >= 0
-    rep, out, ref = _parity("multidraft", batch, "invalid")
-    al = out["accept_len"].cpu().numpy()
-    assert (al[:6] == -1).all()
-    assert (out["flags"].cpu().numpy()[:6] & oracle.FLAG_INVALID).all()
-    assert (al[6:] >= 0).all()
+    for method in ("multidraft", "spectr"):
+        rep, out, ref = _parity(method, batch, "invalid")
+        al = out["accept_len"].cpu().numpy()
+        # the zero-mass row sits below the root: the K-draft walk reads it on this
+        # batch, SpecTr only if its accepted path passes that node (parity above
+        # already checks that the GPU flags exactly what the oracle flags)
+        bad = [0, 1, 2, 3, 4, 5] if method == "multidraft" else [0, 1, 2, 3, 5]
+        assert (al[bad] == -1).all()
+        assert (out["flags"].cpu().numpy()[bad] & oracle.FLAG_INVALID).all()
+        assert (al[6:] >= 0).all()
 
 
 def test_equal_rows_accept_whole_block():
     ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=16, V=2048)
     batch = pt.gpu_batch(ws, 6)
     batch["draft"].copy_(batch["target"][:, :, :ws.L])
-    for method, K in (("multidraft", ws.K),):
+    for method in ("multidraft", "spectr"):
         rep, out, _ = _parity(method, batch, "p_equals_q")
         assert (out["accept_len"] == ws.L).all()
 
@@ -131,20 +148,24 @@ def test_equal_rows_accept_whole_block():
 def test_single_token_vocabulary():
     ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=8, V=1)
     batch = pt.gpu_batch(ws, 7)
-    rep, out, _ = _parity("multidraft", batch, "V1")
-    assert (out["accept_len"] == ws.L).all() and (out["correction"] == 0).all()
+    for method in ("multidraft", "spectr"):
+        rep, out, _ = _parity(method, batch, "V1")
+        assert (out["accept_len"] == ws.L).all() and (out["correction"] == 0).all()
 
 
 def test_largest_k_and_l():
     ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=6, K=64, L=16, V=96,
                       temperature=1.5)
-    _parity("multidraft", pt.gpu_batch(ws, 8), "K64_L16")
+    batch = pt.gpu_batch(ws, 8)
+    for method in ("multidraft", "spectr"):
+        _parity(method, batch, "K64_L16")
 
 
-def test_duplicate_rows_are_never_read():
+@pytest.mark.parametrize("method", ["multidraft", "spectr"])
+def test_duplicate_rows_are_never_read(method):
     ws = synth.scaled(W["multi_zipf_bf16_b512_k8_l8_v151936"], B=16, V=2048)
     batch = pt.gpu_batch(ws, 9)
-    ref = _verify("multidraft", batch)
+    ref = _verify(method, batch)
     ref = {k: v.clone() for k, v in ref.items()}
     tok = batch["tokens"].cpu().numpy()
     B, K, L = tok.shape
@@ -155,7 +176,7 @@ def test_duplicate_rows_are_never_read():
                     batch["target"][b, k, j] = float("nan")
                     if j < L:
                         batch["draft"][b, k, j] = float("nan")
-    out = _verify("multidraft", batch)
+    out = _verify(method, batch)
     for k in ("accept_len", "draft_index", "correction", "flags", "row_lse", "resid_mass"):
         assert torch.equal(out[k].nan_to_num(-7.0), ref[k].nan_to_num(-7.0)), k
 
@@ -168,7 +189,8 @@ def test_negative_infinity_entries():
         mask = torch.rand(batch[key].shape, generator=g, device="cuda") < 0.3
         batch[key].masked_fill_(mask, float("-inf"))
     # redraw nothing: tokens may now sit on zero-probability entries of q
-    _parity("multidraft", batch, "neg_inf_entries")
+    for method in ("multidraft", "spectr"):
+        _parity(method, batch, "neg_inf_entries")
 
 
 def test_misaligned_rows_take_the_scalar_path():
@@ -180,7 +202,8 @@ def test_misaligned_rows_take_the_scalar_path():
         view = buf[1:].view(t.shape)             # 2-byte offset: not 16-byte aligned
         view.copy_(t)
         batch[key] = view
-    _parity("block", batch, "misaligned")
+    for method in ("block", "spectr"):
+        _parity(method, batch, "misaligned")
 
 
 # ---------------------------------------------------------------- full sizes
@@ -197,7 +220,7 @@ def test_full_size_sampled_parity(name):
     rng = np.random.default_rng(5)
     n = min(w.B, 24)
     req = sorted(rng.choice(w.B, size=n, replace=False).tolist())
-    for method in w.methods:
+    for method in w.methods + (("spectr",) if w.K > 1 else ()):
         _parity(method, batch, f"full/{name}", requests=req, diagnostics=False)
     del batch
     torch.cuda.empty_cache()
@@ -208,7 +231,7 @@ def test_full_size_diagnostics(name):
     w = W[name]
     batch = pt.gpu_batch(w, 99)
     req = [0, 1, w.B // 2, w.B - 1]
-    for method in w.methods:
+    for method in w.methods + (("spectr",) if w.K > 1 else ()):
         _parity(method, batch, f"full_diag/{name}", requests=req, diagnostics=True)
     del batch
     torch.cuda.empty_cache()
