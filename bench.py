@@ -80,11 +80,11 @@ class HipEvents:
         self.made = []
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, method: str):
     """HBM bytes per step of the statistics kernel (its launches in one step) from
     the committed rocprofv3 PMC summary (FETCH_SIZE and WRITE_SIZE runs, scaled by
     a copy-kernel calibration), or None when absent or taken on other sources."""
-    path = os.path.join(PROFILES, f"rowstats_{workload}_pmc.json")
+    path = os.path.join(PROFILES, f"rowstats_{method}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -212,7 +212,7 @@ def main():
         log(f"[bench] copy calibration: 3 copies of {n} bytes")
         del src, dst
 
-    traffic = read_traffic(name)
+    traffic = read_traffic(name, method)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
