@@ -53,6 +53,9 @@ def _load(path=None):
             build()
         lib = ctypes.CDLL(key)
         vp, i32 = ctypes.c_void_p, ctypes.c_int
+        lib.svo_draft.restype = ctypes.c_int
+        lib.svo_draft.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, i32,
+                                  vp, vp, vp, vp]
         lib.svo_verify.restype = ctypes.c_int
         lib.svo_verify.argtypes = [i32, i32, i32, i32, i32, i32,
                                    vp, vp, vp, vp, vp, vp,
@@ -133,6 +136,43 @@ def verify(method, target, draft, tokens, temperature, u_accept, u_correct, *,
         return out
     reqs = list(range(B)) if requests is None else sorted(int(b) for b in requests)
     if threads <= 1 or len(reqs) <= 1:
+        for b in reqs:
+            run(b, b + 1)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda b: run(b, b + 1), reqs))
+    return out
+
+
+def draft(draft_logits, temperature, u_draft, *, threads: int = 1, requests=None,
+          lib_path=None) -> dict:
+    """Sample K i.i.d. draft blocks (svo_draft) on a batch held in host memory.
+
+    draft_logits [B][K][L][V]: float32, or bf16 as uint16 bits; temperature
+    float32 [B]; u_draft float32 [B][K][L].  Returns tokens [B][K][L], flags,
+    margin and rows (node rows read) per request; requests outside `requests`
+    keep tokens -2."""
+    lib = _load(lib_path)
+    d, dt = _as_logits(draft_logits)
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    u_draft = np.ascontiguousarray(u_draft, dtype=np.float32)
+    B, K, L, V = d.shape
+    if temperature.shape != (B,) or u_draft.shape != (B, K, L):
+        raise ValueError("inconsistent shapes")
+    out = {"tokens": np.full((B, K, L), -2, np.int32), "flags": np.zeros(B, np.int32),
+           "margin": np.full(B, np.nan, np.float64), "rows": np.zeros(B, np.int32)}
+
+    def run(b0, b1):
+        rc = lib.svo_draft(B, K, L, V, dt, _ptr(d), _ptr(temperature), _ptr(u_draft), b0, b1,
+                           _ptr(out["tokens"]), _ptr(out["flags"]), _ptr(out["margin"]),
+                           _ptr(out["rows"]))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the arguments (rc={rc})")
+
+    reqs = list(range(B)) if requests is None else sorted(int(b) for b in requests)
+    if requests is None and threads <= 1:
+        run(0, B)
+    elif threads <= 1 or len(reqs) <= 1:
         for b in reqs:
             run(b, b + 1)
     else:

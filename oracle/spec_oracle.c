@@ -26,6 +26,9 @@
  *         O(V log K) (section 3).  Written from the published k-sequential
  *         selection of Sun et al., "SpecTr: Fast Speculative Decoding via
  *         Optimal Transport" (2023), restated from its mathematics.
+ *  [DR]   drafting: K i.i.d. blocks sampled position by position from the
+ *         draft rows (SpecTr-GBV page, section 2, step 1), by the same
+ *         inverse CDF as every correction draw.
  *  [MD]   SpecTr-GBV, K i.i.d. drafts of length L (SpecTr-GBV page, section 2,
  *         "algorithmic procedure", steps 1-5): start from accepted length 0 and
  *         an empty rejected set H; walk the drafts; verify each one's sub-block
@@ -658,6 +661,95 @@ static int svo_request_valid(const svo_req *r)
     if (!(r->uc >= 0.0 && r->uc < 1.0))
         return 0;
     return 1;
+}
+
+/* ------------------------------------------------------ drafting [DR] */
+
+/*
+ * Drafting K i.i.d. blocks of length L (SpecTr-GBV page, section 2, step 1),
+ * the other half of the draft-then-verify loop (MineDraft page, section 1).
+ * Position by position, draft k draws X[k][j] from the temperature softmax of
+ * the node row of its prefix X[k][0..j-1] -- the row of the lowest-index draft
+ * with that prefix, so drafts that meet at a node draw from one distribution --
+ * by the inverse CDF of its own uniform u_draft[k][j] (token-id order, strict
+ * ">", as every draw of this oracle).  Each draft's block is therefore an
+ * independent draw from the draft model's sequence distribution.
+ *
+ * Requests [b_begin, b_end) of a batch: draft [B][K][L][V] (SVO_F32 or bf16
+ * bits), temperature [B], u_draft [B][K][L] in, tokens [B][K][L] out.
+ * flags [B]: SVO_FLAG_INVALID when T is not a positive finite number, a
+ * uniform lies outside [0, 1), or a node row read is not a distribution; the
+ * request's tokens are then all -1.  margin [B] (optional): the smallest
+ * distance of a draw's threshold to a CDF boundary, in probability units.
+ * rows [B] (optional): node rows read.  Returns 0, or -1 for bad arguments.
+ */
+int svo_draft(int B, int K, int L, int V, int dtype, const void *draft,
+              const float *temperature, const float *u_draft, int b_begin, int b_end,
+              int32_t *tokens, int32_t *flags, double *margin, int32_t *rows)
+{
+    if (B < 0 || K < 1 || K > SVO_KMAX || L < 1 || L > SVO_LMAX || V < 1 ||
+        (dtype != SVO_F32 && dtype != SVO_BF16) || b_begin < 0 || b_end > B ||
+        b_begin > b_end)
+        return -1;
+    size_t es = dtype == SVO_F32 ? 4 : 2;
+    size_t drow = (size_t)K * (size_t)L * (size_t)V;
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    unsigned char *touched = (unsigned char *)malloc((size_t)(2 * L + 1) * (size_t)K);
+    if (!q || !touched) {
+        free(q);
+        free(touched);
+        return -2;
+    }
+    for (int b = b_begin; b < b_end; ++b) {
+        int32_t *X = tokens + (size_t)b * (size_t)K * (size_t)L;
+        const float *u = u_draft + (size_t)b * (size_t)K * (size_t)L;
+        svo_req r;
+        memset(&r, 0, sizeof r);
+        r.K = K;
+        r.L = L;
+        r.V = V;
+        r.dtype = dtype;
+        r.drf = (const char *)draft + (size_t)b * drow * es;
+        r.X = X;
+        r.T = (double)temperature[b];
+        r.q = q;
+        r.margin = INFINITY;
+        r.touched = touched;
+        memset(touched, 0, (size_t)(2 * L + 1) * (size_t)K);
+        int ok = r.T > 0.0 && isfinite(r.T);
+        for (int i = 0; i < K * L; ++i) {
+            X[i] = -1;
+            ok &= u[i] >= 0.0f && u[i] < 1.0f;
+        }
+        for (int j = 0; j < L && ok; ++j) {
+            for (int k = 0; k < K && ok; ++k) {
+                svo_softmax(&r, 0, k, j, q);     /* node row of k's prefix */
+                if (r.flags & SVO_FLAG_INVALID) {
+                    ok = 0;
+                    break;
+                }
+                r.uc = (double)u[k * L + j];     /* the draw's uniform */
+                double Z;
+                X[k * L + j] = svo_icdf(&r, q, &Z);
+            }
+        }
+        int nrows = 0;
+        for (int i = 0; i < (2 * L + 1) * K; ++i)
+            nrows += touched[i];
+        if (!ok) {
+            for (int i = 0; i < K * L; ++i)
+                X[i] = -1;
+        }
+        if (flags)
+            flags[b] = ok ? 0 : SVO_FLAG_INVALID;
+        if (margin)
+            margin[b] = ok ? r.margin : INFINITY;
+        if (rows)
+            rows[b] = nrows;
+    }
+    free(q);
+    free(touched);
+    return 0;
 }
 
 /* --------------------------------------------------------------- entry */
