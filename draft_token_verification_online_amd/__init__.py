@@ -49,6 +49,16 @@ class SvLaunch(ctypes.Structure):
                 ("phase_events", _vp * N_PHASE_EVENTS)]
 
 
+class SvDraftInputs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("dtype", ctypes.c_int32), ("draft_logits", _vp),
+                ("temperature", _vp), ("u_draft", _vp)]
+
+
+class SvDraftOutputs(ctypes.Structure):
+    _fields_ = [("draft_tokens", _vp), ("flags", _vp), ("rows_streamed", _vp)]
+
+
 class SpecVerifyError(RuntimeError):
     pass
 
@@ -74,6 +84,11 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(SvInputs), ctypes.POINTER(SvOutputs),
                       ctypes.POINTER(SvLaunch)]
+    lib.sv_draft_workspace_size.restype = ctypes.c_size_t
+    lib.sv_draft_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.spec_draft_sample.restype = ctypes.c_int
+    lib.spec_draft_sample.argtypes = [ctypes.POINTER(SvDraftInputs), ctypes.POINTER(SvDraftOutputs),
+                                      ctypes.POINTER(SvLaunch)]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_version.restype = ctypes.c_char_p
@@ -162,6 +177,57 @@ class Verifier:
         return self.out
 
 
+class Drafter:
+    """Holds outputs and workspace for repeated draft sampling on one shape:
+    K i.i.d. draft blocks of length L per request from [B][K][L][V] draft logits
+    (see spec_draft_sample in include/spec_verify.h)."""
+
+    def __init__(self, B, K, L, V, dtype, device="cuda"):
+        lib = load_library()
+        self.shape, self.dtype = (B, K, L, V), dtype
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.out = {"draft_tokens": torch.empty((B, K, L), **i32),
+                    "flags": torch.empty(B, **i32), "rows_streamed": torch.empty(B, **i32)}
+        code = SV_BF16 if dtype == torch.bfloat16 else SV_F32
+        nbytes = int(lib.sv_draft_workspace_size(B, K, L, V, code))
+        if nbytes == 0:
+            raise ValueError(f"sizes out of range: B={B} K={K} L={L} V={V}")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self._outs = SvDraftOutputs(*[_ptr(self.out[k]) for k in
+                                      ("draft_tokens", "flags", "rows_streamed")])
+
+    def __call__(self, draft_logits, temperature, u_draft, *, stream=None, events=None):
+        B, K, L, V = self.shape
+        checks = [(draft_logits, (B, K, L, V), self.dtype), (temperature, (B,), torch.float32),
+                  (u_draft, (B, K, L), torch.float32)]
+        for t, shp, dt in checks:
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"expected contiguous {dt} tensor of shape {shp}, "
+                                 f"got {t.dtype} {tuple(t.shape)}")
+            if t.device.type != "cuda":
+                raise ValueError("inputs must live in GPU memory")
+        ins = SvDraftInputs(B, K, L, V, _dtype_code(draft_logits), draft_logits.data_ptr(),
+                            temperature.data_ptr(), u_draft.data_ptr())
+        if stream is None:
+            stream = torch.cuda.current_stream(draft_logits.device).cuda_stream
+        ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
+        ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
+        lib = load_library()
+        rc = lib.spec_draft_sample(ctypes.byref(ins), ctypes.byref(self._outs), ctypes.byref(ln))
+        if rc != SV_OK:
+            raise SpecVerifyError(f"spec_draft_sample failed: "
+                                  f"{lib.sv_status_string(rc).decode()} ({rc})")
+        return self.out
+
+
+def spec_draft_sample(draft_logits, temperature, u_draft, **kw):
+    """Draw K i.i.d. draft blocks per request.  See include/spec_verify.h."""
+    B, K, L, V = draft_logits.shape
+    d = Drafter(B, K, L, V, draft_logits.dtype, device=draft_logits.device)
+    return dict(d(draft_logits, temperature, u_draft, **kw))
+
+
 def _run(method, target, draft, tokens, temperature, u_accept, u_correct, diagnostics, **kw):
     B, K, L1, V = target.shape
     v = Verifier(method, B, K, L1 - 1, V, target.dtype, device=target.device,
@@ -199,4 +265,5 @@ def spec_verify_spectr(target, draft, tokens, temperature, u_accept, u_correct, 
 
 
 __all__ = ["spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-           "spec_verify_spectr", "Verifier", "workspace_size", "load_library", "SpecVerifyError"]
+           "spec_verify_spectr", "spec_draft_sample", "Verifier", "Drafter", "workspace_size",
+           "load_library", "SpecVerifyError"]

@@ -10,6 +10,8 @@
 //                          below the accepted node;
 //   3. rowstats_kernel  -- (K > 1) statistics of the flagged rows;
 //   4. walk_kernel      -- (K > 1) resumes the stopped walks.
+// spec_draft_sample draws the draft blocks instead: one draft_kernel launch per
+// position between a clearing launch and a final pass over invalid requests.
 // No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
@@ -17,6 +19,7 @@
 #include <cstring>
 
 #include "../../include/spec_verify.h"
+#include "sv_draft.hpp"
 #include "sv_rowstats.hpp"
 #include "sv_walk.hpp"
 
@@ -191,9 +194,81 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
     return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+constexpr int kDraftThreads = 256;
+
+template <typename E, bool VEC>
+hipError_t launch_draft(const sv_draft_inputs *in, const sv_draft_outputs *out,
+                        const sv_launch *ln) {
+    using RD = typename sv::RowOf<E, VEC>::type;
+    hipStream_t stream = static_cast<hipStream_t>(ln->stream);
+    sv::DraftArgs a;
+    a.drf = in->draft_logits;
+    a.temp = in->temperature;
+    a.ud = in->u_draft;
+    a.tok = out->draft_tokens;
+    a.bad = static_cast<unsigned *>(ln->workspace);
+    a.rows = out->rows_streamed;
+    a.B = in->B;
+    a.K = in->K;
+    a.L = in->L;
+    a.V = in->V;
+    hipError_t err;
+    if ((err = record(ln, 0, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL(sv::draft_init_kernel, dim3((in->B + 255) / 256), dim3(256), 0, stream,
+                       a.bad, a.rows, in->B);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    for (int j = 0; j < in->L; ++j) {
+        a.j = j;
+        hipLaunchKernelGGL((sv::draft_kernel<kDraftThreads, RD, E>),
+                           dim3(static_cast<unsigned>(in->B) * static_cast<unsigned>(in->K)),
+                           dim3(kDraftThreads), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const long long n = static_cast<long long>(in->B) * in->K * in->L;
+    hipLaunchKernelGGL(sv::draft_fixup_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, stream, a.bad, out->draft_tokens, out->flags, in->B,
+                       in->K * in->L);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return record(ln, 1, stream);
+}
+
+size_t draft_workspace_bytes(int32_t B) {
+    const size_t n = align_up(static_cast<size_t>(B) * sizeof(unsigned), 256);
+    return n ? n : 256;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
+    if (!sizes_ok(B, K, L, V, dtype)) return 0;
+    return draft_workspace_bytes(B);
+}
+
+int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
+                      const sv_launch *ln) {
+    if (!in || !out || !ln) return SV_EINVAL;
+    if (!sizes_ok(in->B, in->K, in->L, in->V, in->dtype)) return SV_EINVAL;
+    if (in->B == 0) return SV_OK;
+    if (!in->draft_logits || !in->temperature || !in->u_draft || !out->draft_tokens)
+        return SV_EINVAL;
+    const size_t es = in->dtype == SV_F32 ? 4 : 2;
+    const uintptr_t da = reinterpret_cast<uintptr_t>(in->draft_logits);
+    if (da % es) return SV_EINVAL;
+    if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < draft_workspace_bytes(in->B)) return SV_EWORKSPACE;
+    const bool vec = (in->V % 8 == 0) && (da % 16 == 0);
+    hipError_t err;
+    if (in->dtype == SV_BF16)
+        err = vec ? launch_draft<uint16_t, true>(in, out, ln)
+                  : launch_draft<uint16_t, false>(in, out, ln);
+    else
+        err = vec ? launch_draft<float, true>(in, out, ln)
+                  : launch_draft<float, false>(in, out, ln);
+    return err == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
     if (!sizes_ok(B, K, L, V, dtype)) return 0;

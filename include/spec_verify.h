@@ -183,6 +183,47 @@ int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_
  * holds h of every test made (NaN for drafts not tested). */
 int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
 
+/* ------------------------------------------------------------- drafting */
+
+/* Drafting: the other half of the draft-then-verify loop (MineDraft page,
+ * section 1; SpecTr-GBV page, section 2, step 1: K i.i.d. draft blocks of
+ * length L).  Given the draft model's logits, draw the blocks position by
+ * position: draft k draws X[b][k][j] from the temperature softmax of the node
+ * row of its prefix X[b][k][0..j-1] -- the row of the lowest-index draft with
+ * that prefix, the node rule the verifier uses, so drafts that meet at a node
+ * draw from one distribution and a caller may leave the other rows unwritten --
+ * by the inverse CDF of u_draft[b][k][j]: y = min{v : C_v > u Z} in token-id
+ * order (the last token of positive weight if rounding leaves none).  Each
+ * draft's block is then an independent draw.  Tokens match the CPU oracle
+ * except where u Z lies within ~1e-6 Z of a CDF boundary. */
+typedef struct sv_draft_inputs {
+    int32_t B, K, L, V;           /* as in sv_inputs */
+    int32_t dtype;                /* sv_dtype of the logits */
+    const void *draft_logits;     /* [B][K][L][V], device memory */
+    const float *temperature;     /* [B], T_b > 0 */
+    const float *u_draft;         /* [B][K][L], uniforms in [0, 1) */
+} sv_draft_inputs;
+
+typedef struct sv_draft_outputs {
+    int32_t *draft_tokens;        /* [B][K][L], required; all -1 for an invalid request
+                                     (T not positive finite, a uniform outside [0, 1),
+                                     or a node row read that is not a distribution) */
+    int32_t *flags;               /* optional [B]: SV_FLAG_INVALID or 0 */
+    int32_t *rows_streamed;       /* optional [B]: node rows read */
+} sv_draft_outputs;
+
+/* Workspace bytes spec_draft_sample needs (0 on invalid sizes). */
+size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
+
+/* Draw the K draft blocks of every request.  Asynchronous on ln->stream: L + 2
+ * launches (one per position, plus a clear and a final pass that marks invalid
+ * requests).  ln->phase_events[0] and [1], when non-null, are recorded before
+ * and after them; [2..4] are not used.  The tokens of position j are written by
+ * the launch for j and read back by the later ones, so draft_tokens must not
+ * alias the other arguments. */
+int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
+                      const sv_launch *ln);
+
 /* Static description of a status code. */
 const char *sv_status_string(int status);
 

@@ -163,3 +163,11 @@ def dense_bytes(w: Workload) -> int:
 def tokens_per_step(w: Workload) -> int:
     """Verified draft tokens of one batch: B*K*L."""
     return w.B * w.K * w.L
+
+
+def draft_uniforms(w: Workload, seed: int, device="cpu") -> torch.Tensor:
+    """Uniforms in [0, 1) for drafting [B][K][L], from a stream of their own
+    (independent of the verification uniforms of generate())."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(0x5EED0000 + 7919 * seed + 17)
+    return torch.rand((w.B, w.K, w.L), generator=gen, device=device, dtype=torch.float32)

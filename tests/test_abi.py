@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-              "spec_verify_spectr", "sv_workspace_size", "sv_status_string", "sv_version"):
+              "spec_verify_spectr", "spec_draft_sample", "sv_workspace_size",
+              "sv_draft_workspace_size", "sv_status_string", "sv_version"):
         assert n in names
 
 
@@ -142,3 +143,46 @@ def test_missing_library_fails_loudly(tmp_path):
             sv.load_library(str(tmp_path / "nope.so"))
     finally:
         sv._lib = saved
+
+
+def _fake_draft(B=2, K=2, L=3, V=32, dtype=sv.SV_F32):
+    base = 1 << 20
+    ins = sv.SvDraftInputs(B, K, L, V, dtype, base, base + 4096, base + 8192)
+    outs = sv.SvDraftOutputs(base + 12288, None, None)
+    ln = sv.SvLaunch(None, base * 2, 1 << 20, (ctypes.c_void_p * sv.N_PHASE_EVENTS)())
+    return ins, outs, ln
+
+
+def test_draft_host_validation(lib):
+    f = lambda i, o, l: lib.spec_draft_sample(ctypes.byref(i) if i is not None else None,
+                                              ctypes.byref(o) if o is not None else None,
+                                              ctypes.byref(l) if l is not None else None)
+    ins, outs, ln = _fake_draft()
+    assert f(None, outs, ln) == sv.SV_EINVAL
+    assert f(ins, None, ln) == sv.SV_EINVAL
+    assert f(ins, outs, None) == sv.SV_EINVAL
+    for field, value in [("K", 0), ("K", 65), ("L", 0), ("L", 17), ("V", 0), ("B", -1),
+                         ("dtype", 3)]:
+        ins, outs, ln = _fake_draft()
+        setattr(ins, field, value)
+        assert f(ins, outs, ln) == sv.SV_EINVAL, (field, value)
+    for field in ("draft_logits", "temperature", "u_draft"):
+        ins, outs, ln = _fake_draft()
+        setattr(ins, field, None)
+        assert f(ins, outs, ln) == sv.SV_EINVAL, field
+    ins, outs, ln = _fake_draft()
+    outs.draft_tokens = None
+    assert f(ins, outs, ln) == sv.SV_EINVAL
+    ins, outs, ln = _fake_draft()
+    ins.draft_logits += 2
+    assert f(ins, outs, ln) == sv.SV_EINVAL
+    ins, outs, ln = _fake_draft()
+    ln.workspace = None
+    assert f(ins, outs, ln) == sv.SV_EWORKSPACE
+    ins, outs, ln = _fake_draft()
+    ln.workspace_bytes = 4
+    assert f(ins, outs, ln) == sv.SV_EWORKSPACE
+    ins, outs, ln = _fake_draft(B=0)
+    assert f(ins, outs, ln) == sv.SV_OK
+    assert lib.sv_draft_workspace_size(512, 8, 8, 151936, sv.SV_BF16) == 2048
+    assert lib.sv_draft_workspace_size(1, 0, 8, 16, sv.SV_BF16) == 0
