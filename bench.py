@@ -5,7 +5,13 @@ One step = one call of the verification entry point over one batch of
 synthetic inputs already resident in HBM (both kernels: row statistics and
 the per-request walk).  Prints ONE JSON line on stdout; progress goes to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--method M]
+
+M is a verification method (token, block, multidraft -- the default for
+multi-draft workloads --, spectr), or "draft" to time the drafting kernel
+instead (drafted tokens per second).  --pipeline times the one-GPU emulation
+of MineDraft's two-batch schedule: each step verifies one batch on one HIP
+stream while the other batch is drafted on a second stream, roles alternating.
 
 The roofline object describes the row-statistics kernel (the one that streams
 the logits): achieved = bytes of the rows it streams per step (rows_streamed *
@@ -81,10 +87,12 @@ class HipEvents:
 
 
 def read_traffic(workload: str, method: str):
-    """HBM bytes per step of the statistics kernel (its launches in one step) from
-    the committed rocprofv3 PMC summary (FETCH_SIZE and WRITE_SIZE runs, scaled by
-    a copy-kernel calibration), or None when absent or taken on other sources."""
-    path = os.path.join(PROFILES, f"rowstats_{method}_{workload}_pmc.json")
+    """HBM bytes per step of the streaming kernel (the row-statistics kernel, or
+    the drafting kernel for method "draft"; its launches in one step) from the
+    committed rocprofv3 PMC summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a
+    copy-kernel calibration), or None when absent or taken on other sources."""
+    kernel = "draft" if method == "draft" else "rowstats"
+    path = os.path.join(PROFILES, f"{kernel}_{method}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -121,6 +129,194 @@ def cpu_baseline(method, batch, w, target_cpu_s: float):
     }
 
 
+def cpu_baseline_draft(batch, u, w, target_cpu_s: float):
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    host = lambda reqs: (synth.to_host(batch, reqs)["draft"],
+                         batch["temperature"][reqs].cpu().numpy(), u[reqs].cpu().numpy())
+    t = time.perf_counter()
+    oracle.draft(*host([0]))
+    t_one = max(time.perf_counter() - t, 1e-4)
+    m = int(np.clip(round(target_cpu_s / t_one), threads, w.B))
+    args = host(list(range(m)))
+    t = time.perf_counter()
+    oracle.draft(*args, threads=threads)
+    wall = time.perf_counter() - t
+    return {
+        "value": m * w.K * w.L / wall,
+        "unit": "drafted tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {m} of {w.B} requests of the same batch ({m * w.K * w.L} draws), "
+                  f"fp64 C oracle, one request per thread, {wall:.2f} s wall",
+    }
+
+
+def copy_calibration(torch, mib):
+    if not mib:
+        return
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 copies of {n} bytes")
+
+
+def run_draft(args, w, name):
+    """Time spec_draft_sample: B*K*L draws per step from the workload's draft logits."""
+    import torch
+    import synth
+    import draft_token_verification_online_amd as sv
+    log(f"[bench] generating {name} on cuda:0 (seed {args.seed})")
+    batch = synth.generate(w, args.seed, device="cuda")
+    u = synth.draft_uniforms(w, args.seed, device="cuda")
+    torch.cuda.synchronize()
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    dr = sv.Drafter(w.B, w.K, w.L, w.V, w.dtype)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        dr(batch["draft"], batch["temperature"], u, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[hip.create(), hip.create()] + [None] * (sv.N_PHASE_EVENTS - 2)
+           for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps of draft sampling on {name}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dr(batch["draft"], batch["temperature"], u, stream=stream, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    hip.close()
+    ms_per_step = wall * 1e3 / args.steps
+    k_mean = sum(kern) / len(kern)
+    rows = int(dr.out["rows_streamed"].sum())
+    byts = rows * w.V * es
+    achieved = byts / (k_mean * 1e-3) / 1e9
+    value = synth.tokens_per_step(w) / (ms_per_step * 1e-3)
+    log(f"[bench] {ms_per_step:.3f} ms/step, kernels {k_mean:.3f} ms, {achieved:.0f} GB/s, "
+        f"{value / 1e6:.2f} M drafted tokens/s")
+    copy_calibration(torch, args.copy_calibration_mib)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline_draft(batch, u, w, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+    return {
+        "metric": "drafted tokens/s (B*K*L) + achieved HBM GB/s of the drafting kernel",
+        "value": value,
+        "unit": "drafted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "method": "draft", "B": w.B, "K": w.K, "L": w.L,
+                   "V": w.V, "logits": "bf16" if es == 2 else "fp32", "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "draft_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": read_traffic(name, "draft")},
+        "cpu_baseline": cpu,
+        "detail": {"kernels_ms": k_mean, "rows_streamed_per_step": rows,
+                   "rows_streamed_bytes": byts,
+                   "invalid_requests": int((dr.out["flags"] != 0).sum())},
+    }
+
+
+def run_pipeline(args, w, name, method):
+    """MineDraft's two-batch schedule on one GPU: step i verifies batch i%2 on
+    one stream while batch (i+1)%2 is drafted on another.  Verification of a
+    batch waits for its drafting in the previous step, and drafting waits for
+    that batch's verification in the previous step."""
+    import torch
+    import synth
+    import draft_token_verification_online_amd as sv
+    log(f"[bench] generating two batches of {name} on cuda:0")
+    batches = [synth.generate(w, args.seed + i, device="cuda") for i in range(2)]
+    us = [synth.draft_uniforms(w, args.seed + i, device="cuda") for i in range(2)]
+    torch.cuda.synchronize()
+    drs = [sv.Drafter(w.B, w.K, w.L, w.V, w.dtype) for _ in range(2)]
+    vers = [sv.Verifier(method, w.B, w.K, w.L, w.V, w.dtype) for _ in range(2)]
+    s_ver, s_dra = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+
+    def draft(i, stream):
+        b = batches[i]
+        drs[i](b["draft"], b["temperature"], us[i], stream=stream.cuda_stream)
+
+    def verify(i, stream):
+        b = batches[i]
+        vers[i](b["target"], b["draft"], drs[i].out["draft_tokens"], b["temperature"],
+                b["u_accept"], b["u_correct"], stream=stream.cuda_stream)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / n
+
+    # each piece alone, on one stream
+    for i in range(2):
+        draft(i, s_ver)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        verify(0, s_ver)
+    t_verify = timed(lambda: verify(0, s_ver), args.steps)
+    t_draft = timed(lambda: draft(1, s_ver), args.steps)
+    # serial schedule: verify A, then draft B, on one stream
+    t_serial = timed(lambda: (verify(0, s_ver), draft(1, s_ver)), args.steps)
+
+    # overlapped: two streams, cross-stream events carry the dependencies
+    ev_drafted = [torch.cuda.Event(), torch.cuda.Event()]
+    ev_verified = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def step(i):
+        a, b = i % 2, (i + 1) % 2
+        s_ver.wait_event(ev_drafted[a])
+        verify(a, s_ver)
+        ev_verified[a].record(s_ver)
+        s_dra.wait_event(ev_verified[b])
+        draft(b, s_dra)
+        ev_drafted[b].record(s_dra)
+
+    for i in range(2):
+        draft(i, s_dra)
+        ev_drafted[i].record(s_dra)
+        ev_verified[i].record(s_ver)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_over = (time.perf_counter() - t0) * 1e3 / args.steps
+    tokens = synth.tokens_per_step(w)
+    log(f"[bench] pipeline: verify {t_verify:.3f} ms, draft {t_draft:.3f} ms, serial "
+        f"{t_serial:.3f} ms/step, overlapped {t_over:.3f} ms/step "
+        f"({t_serial / t_over:.2f}x)")
+    return {
+        "metric": "verified draft tokens/s with drafting of the other batch overlapped "
+                  "(two-batch schedule, two HIP streams)",
+        "value": tokens / (t_over * 1e-3),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_over, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "method": method, "pipeline": "verify A | draft B",
+                   "B": w.B, "K": w.K, "L": w.L, "V": w.V, "seed": args.seed},
+        "roofline": None,
+        "cpu_baseline": None,
+        "detail": {"verify_ms": t_verify, "draft_ms": t_draft, "serial_ms": t_serial,
+                   "overlapped_ms": t_over, "overlap_speedup": t_serial / t_over,
+                   "ideal_ms": max(t_verify, t_draft)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +328,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work (summed over cores) spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time the two-batch verify/draft overlap on two streams")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this many MiB (a "
                          "reference kernel of known traffic for rocprofv3 PMC runs)")
@@ -160,6 +358,12 @@ def main():
     w = synth.WORKLOADS[name]
     method = args.method or w.methods[-1]
     torch.cuda.set_device(0)
+    if method == "draft":
+        print(json.dumps(run_draft(args, w, name)), flush=True)
+        return
+    if args.pipeline:
+        print(json.dumps(run_pipeline(args, w, name, method)), flush=True)
+        return
     log(f"[bench] generating {name} on cuda:0 (seed {args.seed})")
     batch = synth.generate(w, args.seed, device="cuda")
     torch.cuda.synchronize()
@@ -202,15 +406,7 @@ def main():
     log(f"[bench] {ms_per_step:.3f} ms/step, stats {st_mean:.3f} ms, walk {wk_mean:.3f} ms, "
         f"{achieved:.0f} GB/s node-row stream, {value / 1e6:.2f} M tokens/s")
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 copies of {n} bytes")
-        del src, dst
+    copy_calibration(torch, args.copy_calibration_mib)
 
     traffic = read_traffic(name, method)
     cpu = None

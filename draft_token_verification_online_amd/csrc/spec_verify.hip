@@ -10,8 +10,9 @@
 //                          below the accepted node;
 //   3. rowstats_kernel  -- (K > 1) statistics of the flagged rows;
 //   4. walk_kernel      -- (K > 1) resumes the stopped walks.
-// spec_draft_sample draws the draft blocks instead: one draft_kernel launch per
-// position between a clearing launch and a final pass over invalid requests.
+// spec_draft_sample draws the draft blocks instead: per position, the node rows
+// are listed, streamed into tile sums and drawn from (three launches), between
+// a clearing launch and a final pass over invalid requests.
 // No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
@@ -194,34 +195,73 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
     return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 
-constexpr int kDraftThreads = 256;
+constexpr long long kDraftTileGrid = 16384;
+
+// Drafting workspace: request flags | per-position list lengths | listed rows |
+// each draft's list slot | tile shifts | tile sums.
+struct DraftLayout {
+    size_t bad, count, list, slot, tmax, tsum, total;
+    int ntiles;
+};
+
+DraftLayout draft_layout(int32_t B, int32_t K, int32_t V) {
+    DraftLayout l;
+    const int nch = (V + sv::kChunk - 1) / sv::kChunk;
+    l.ntiles = (nch + sv::kDraftTileChunks - 1) / sv::kDraftTileChunks;
+    const size_t bk = static_cast<size_t>(B) * K;
+    l.bad = 0;
+    l.count = align_up(static_cast<size_t>(B) * sizeof(unsigned), 256);
+    l.list = l.count + 256;
+    l.slot = l.list + align_up(bk * sizeof(int32_t), 256);
+    l.tmax = l.slot + align_up(bk * sizeof(int32_t), 256);
+    l.tsum = l.tmax + align_up(bk * l.ntiles * sizeof(float), 256);
+    l.total = l.tsum + align_up(bk * l.ntiles * sizeof(double), 256);
+    return l;
+}
 
 template <typename E, bool VEC>
 hipError_t launch_draft(const sv_draft_inputs *in, const sv_draft_outputs *out,
                         const sv_launch *ln) {
     using RD = typename sv::RowOf<E, VEC>::type;
+    constexpr int NT = 256;
     hipStream_t stream = static_cast<hipStream_t>(ln->stream);
+    const DraftLayout lay = draft_layout(in->B, in->K, in->V);
+    char *ws = static_cast<char *>(ln->workspace);
     sv::DraftArgs a;
     a.drf = in->draft_logits;
     a.temp = in->temperature;
     a.ud = in->u_draft;
     a.tok = out->draft_tokens;
-    a.bad = static_cast<unsigned *>(ln->workspace);
+    a.bad = reinterpret_cast<unsigned *>(ws + lay.bad);
+    a.count = reinterpret_cast<unsigned *>(ws + lay.count);
+    a.list = reinterpret_cast<int32_t *>(ws + lay.list);
+    a.slot = reinterpret_cast<int32_t *>(ws + lay.slot);
+    a.tmax = reinterpret_cast<float *>(ws + lay.tmax);
+    a.tsum = reinterpret_cast<double *>(ws + lay.tsum);
     a.rows = out->rows_streamed;
     a.B = in->B;
     a.K = in->K;
     a.L = in->L;
     a.V = in->V;
+    a.ntiles = lay.ntiles;
+    const unsigned bk = static_cast<unsigned>(in->B) * static_cast<unsigned>(in->K);
+    const long long blocks = (static_cast<long long>(bk) * lay.ntiles + 3) / 4;   // 4 waves each
+    const unsigned tile_grid = static_cast<unsigned>(blocks < kDraftTileGrid ? blocks : kDraftTileGrid);
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL(sv::draft_init_kernel, dim3((in->B + 255) / 256), dim3(256), 0, stream,
-                       a.bad, a.rows, in->B);
+    const int n0 = in->B > in->L ? in->B : in->L;
+    hipLaunchKernelGGL(sv::draft_init_kernel, dim3((n0 + 255) / 256), dim3(256), 0, stream, a.bad,
+                       a.rows, a.count, in->B, in->L);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int j = 0; j < in->L; ++j) {
         a.j = j;
-        hipLaunchKernelGGL((sv::draft_kernel<kDraftThreads, RD, E>),
-                           dim3(static_cast<unsigned>(in->B) * static_cast<unsigned>(in->K)),
-                           dim3(kDraftThreads), 0, stream, a);
+        hipLaunchKernelGGL(sv::draft_nodes_kernel, dim3((in->B + 3) / 4), dim3(256), 0, stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((sv::draft_tiles_kernel<NT, RD, E>), dim3(tile_grid), dim3(NT), 0,
+                           stream, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((sv::draft_pick_kernel<NT, RD, E>), dim3((bk + 3) / 4), dim3(NT), 0,
+                           stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const long long n = static_cast<long long>(in->B) * in->K * in->L;
@@ -232,9 +272,8 @@ hipError_t launch_draft(const sv_draft_inputs *in, const sv_draft_outputs *out,
     return record(ln, 1, stream);
 }
 
-size_t draft_workspace_bytes(int32_t B) {
-    const size_t n = align_up(static_cast<size_t>(B) * sizeof(unsigned), 256);
-    return n ? n : 256;
+size_t draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+    return draft_layout(B, K, V).total;
 }
 
 }  // namespace
@@ -243,7 +282,7 @@ extern "C" {
 
 size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
     if (!sizes_ok(B, K, L, V, dtype)) return 0;
-    return draft_workspace_bytes(B);
+    return draft_workspace_bytes(B, K, V);
 }
 
 int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
@@ -257,7 +296,7 @@ int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
     const uintptr_t da = reinterpret_cast<uintptr_t>(in->draft_logits);
     if (da % es) return SV_EINVAL;
     if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
-    if (ln->workspace_bytes < draft_workspace_bytes(in->B)) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < draft_workspace_bytes(in->B, in->K, in->V)) return SV_EWORKSPACE;
     const bool vec = (in->V % 8 == 0) && (da % 16 == 0);
     hipError_t err;
     if (in->dtype == SV_BF16)

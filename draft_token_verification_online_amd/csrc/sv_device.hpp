@@ -246,6 +246,19 @@ __device__ __forceinline__ int block_min_int(int v, int *red) {
     return t;
 }
 
+// Exclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_exclusive_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double s = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double n = __shfl_up(s, o, kWave);
+        if (lane >= o) s += n;
+    }
+    const double excl = __shfl_up(s, 1, kWave);
+    return lane == 0 ? 0.0 : excl;
+}
+
 // Exclusive prefix sum over the block in thread order.
 template <int NT>
 __device__ __forceinline__ double block_exclusive_scan(double v, double *red) {

@@ -8,19 +8,26 @@
 // of its own uniform u[k][j]: y = min{v : C_v > u Z} in token-id order, or the
 // last token of positive weight if rounding leaves none.
 //
-// One launch per position (the node of a draft at position j depends on the
-// tokens drawn before).  A workgroup per (request, draft) returns at once unless
-// the draft is the lowest index at its node; otherwise it makes one pass over
-// the node row, summing the weights 2^((l - M0) c) of each tile of NT chunks
-// into LDS (M0: the maximum of the first tile; the pass is redone with the
-// row maximum if any exponent exceeds 64), and then serves every draft at that
-// node: the tile holding u Z is found from the tile sums and rescanned with a
-// block scan.  The row is read once from HBM; the rescans touch one tile each.
+// The node of a draft at position j depends on the tokens drawn before, so each
+// position takes three launches:
+//   1. draft_nodes_kernel -- one wave per request: the node of every draft, the
+//      list of node rows to read (one per node, appended with one atomic per
+//      wave) and, per draft, the list slot of its node's row;
+//   2. draft_tiles_kernel -- grid-stride over (listed row, tile of 512 chunks),
+//      one 64-lane wave per tile (8 chunks per lane): the tile's maximum M_t and
+//      the sum of 2^((l - M_t) c) over it, by wave reductions only (no barrier).
+//      Every row is streamed once, by as many waves as it has tiles, so a
+//      position with few nodes still fills the chip;
+//   3. draft_pick_kernel  -- one wave per draft: rescale the tile sums of its
+//      node's row to the row maximum, find the tile holding u Z and rescan it
+//      with the tiles kernel's own per-chunk arithmetic (wave reductions only).
 #pragma once
 
 #include "sv_device.hpp"
 
 namespace sv {
+
+constexpr int kDraftTileChunks = 512;                // chunks per tile (8 per lane of a wave)
 
 struct DraftArgs {
     const void *drf;        // [B][K][L][V]
@@ -28,17 +35,23 @@ struct DraftArgs {
     const float *ud;        // [B][K][L]
     int32_t *tok;           // [B][K][L]: drawn tokens (positions < j are read back)
     unsigned *bad;          // [B]: request data the rule cannot act on
+    unsigned *count;        // [L]: node rows listed at each position
+    int32_t *list;          // [B*K]: listed node rows, b*K + k
+    int32_t *slot;          // [B*K]: list slot of each draft's node row
+    float *tmax;            // [B*K][ntiles]: shift of each tile (its maximum)
+    double *tsum;           // [B*K][ntiles]: tile sums under their shift
     int32_t *rows;          // [B] or null: node rows read
-    int B, K, L, V, j;
+    int B, K, L, V, j, ntiles;
 };
 
-// Zero the per-request flags and row counts before the first position.
-__global__ void draft_init_kernel(unsigned *bad, int32_t *rows, int B) {
+// Zero the per-request flags, row counts and per-position list lengths.
+__global__ void draft_init_kernel(unsigned *bad, int32_t *rows, unsigned *count, int B, int L) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b < B) {
         bad[b] = 0u;
         if (rows) rows[b] = 0;
     }
+    if (b < L) count[b] = 0u;
 }
 
 // After the last position: every token of an invalid request becomes -1.
@@ -51,181 +64,215 @@ __global__ void draft_fixup_kernel(const unsigned *bad, int32_t *tok, int32_t *f
     if (flags && i % KL == 0) flags[b] = bad[b] ? 2 : 0;
 }
 
-// Tile sums of one row's weights 2^((x - M0) c) in fp64, one entry per tile of
-// NT chunks, into tile[]; returns their total, sets *lastpos to the last token
-// of positive weight and *ovf when an exponent exceeded 64 (the sums are then
-// not usable).
-template <int NT, typename RD>
-__device__ double draft_tiles(const RD &P, int nch, float M0, float chi, float clo, double *tile,
-                              int *lastpos, int *ovf, double *red, int *ired) {
-    const int ntile = (nch + NT - 1) / NT;
-    int last = -1, over = 0;
-    for (int t0 = 0; t0 < ntile; t0 += 4) {
-        typename RD::Raw r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = (t0 + i) * NT + threadIdx.x;
-            if (c < nch) r[i] = P.raw(c);
-        }
-        double v[5];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = (t0 + i) * NT + threadIdx.x;
-            v[i] = 0.0;
-            if (c < nch) {
-                float x[8];
-                RD::unpack(r[i], x);
-                float e[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float d = x[k] - M0;
-                    const float y = fmaf(d, chi, d * clo);
-                    over |= y > 64.0f;
-                    e[k] = fast_exp2(y);
-                    if (e[k] > 0.0f) last = 8 * c + k;
-                }
-                v[i] = static_cast<double>(sum8(e));
-            }
-        }
-        v[4] = static_cast<double>(over);
-        block_sum_n<NT, 5>(v, red);   // also publishes the previous tile[] writes
-        if (threadIdx.x == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (t0 + i < ntile) tile[t0 + i] = v[i];
-        }
-        if (v[4] > 0.0) break;        // block-uniform: redo with the row maximum
+// 1. One 64-lane wave per request, lane k = draft k (K <= 64).
+__global__ __launch_bounds__(256) void draft_nodes_kernel(DraftArgs A) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (b >= A.B) return;                      // whole waves only
+    const int K = A.K, L = A.L, j = A.j;
+    const int32_t *X = A.tok + static_cast<long long>(b) * K * L;
+    const float T = A.temp[b];
+    if (!(T > 0.0f) || !isfinite(T)) {
+        if (lane == 0) A.bad[b] = 1u;
+        return;
     }
-    *ovf = block_max_int<NT>(over, ired);   // its barriers publish tile[]
-    *lastpos = block_max_int<NT>(last, ired);
-    double z = 0.0;
-    for (int t = 0; t < ntile; ++t) z += tile[t];
-    return z;
+    int canon = lane;
+    if (lane < K) {
+        for (int c = 0; c < lane; ++c) {
+            int same = 1;
+            for (int t = 0; t < j; ++t) same &= (X[c * L + t] == X[lane * L + t]);
+            if (same) { canon = c; break; }
+        }
+    }
+    const bool head = lane < K && canon == lane;
+    const unsigned long long heads = __ballot(head);
+    unsigned base = 0;
+    if (lane == 0) base = atomicAdd(A.count + j, static_cast<unsigned>(__popcll(heads)));
+    base = __shfl(base, 0, kWave);
+    const unsigned rank = __popcll(heads & ((1ull << lane) - 1ull));
+    const int my_slot = static_cast<int>(base + rank);
+    if (head) A.list[my_slot] = b * K + lane;
+    const int node_slot = __shfl(my_slot, canon, kWave);
+    if (lane < K) A.slot[b * K + lane] = node_slot;
+    if (head && A.rows) atomicAdd(A.rows + b, 1);
 }
 
-// The inverse-CDF pick for threshold thr = u Z from the tile sums; the tile
-// holding it is rescanned with the same per-chunk arithmetic as draft_tiles.
-template <int NT, typename RD>
-__device__ int draft_pick(const RD &P, int nch, float M0, float chi, float clo,
-                          const double *tile, double thr, int lastpos, double *red, int *ired) {
-    const int ntile = (nch + NT - 1) / NT;
-    double base = 0.0;
-    int tc = -1;
-    for (int t = 0; t < ntile; ++t) {
-        if (base + tile[t] > thr) { tc = t; break; }
-        base += tile[t];
+// 2. Tile sums of the listed rows, one wave per tile.
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
+    constexpr int kPerLane = kDraftTileChunks / kWave;
+    constexpr int WPB = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int K = A.K, L = A.L, V = A.V, j = A.j, ntiles = A.ntiles;
+    const int nch = (V + kChunk - 1) / kChunk;
+    const long long nitems = static_cast<long long>(A.count[j]) * ntiles;
+    const E *base = static_cast<const E *>(A.drf);
+    for (long long it = static_cast<long long>(blockIdx.x) * WPB + threadIdx.x / kWave;
+         it < nitems; it += static_cast<long long>(gridDim.x) * WPB) {
+        const int slot = static_cast<int>(it / ntiles);
+        const int t = static_cast<int>(it % ntiles);
+        const int bk = A.list[slot];
+        const int b = bk / K, k = bk % K;
+        const RD P(base + ((static_cast<long long>(b) * K + k) * L + j) * V, V);
+        typename RD::Raw r[kPerLane];
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int c = t * kDraftTileChunks + i * kWave + lane;
+            if (c < nch) {
+                r[i] = P.raw(c);
+                float x[8];
+                RD::unpack(r[i], x);
+                m = fmaxf(m, max8(x));
+            }
+        }
+        const float M = fmaxf(wave_max(m), -3.402823466e38f);
+        const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+        float chi, clo;
+        split_scale(c64, chi, clo);
+        double sum = 0.0;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int c = t * kDraftTileChunks + i * kWave + lane;
+            if (c < nch) {
+                float x[8], e[8];
+                RD::unpack(r[i], x);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float d = x[q] - M;
+                    e[q] = fast_exp2(fmaf(d, chi, d * clo));
+                }
+                sum += static_cast<double>(sum8(e));
+            }
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) {
+            A.tmax[static_cast<long long>(slot) * ntiles + t] = M;
+            A.tsum[static_cast<long long>(slot) * ntiles + t] = sum;
+        }
     }
-    if (tc < 0) return lastpos;
-    const int c = tc * NT + threadIdx.x;
-    float e[8];
-    double cs = 0.0;
-    if (c < nch) {
+}
+
+// 3. One 64-lane wave per draft: the inverse-CDF draw from its node row's tiles.
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
+    constexpr int kPerLane = kDraftTileChunks / kWave;   // rescanned chunks per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long d = static_cast<long long>(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
+    const int K = A.K, L = A.L, V = A.V, j = A.j;
+    if (d >= static_cast<long long>(A.B) * K) return;          // whole waves
+    const int b = static_cast<int>(d / K), k = static_cast<int>(d % K);
+    if (A.bad[b]) return;     // one load for the wave; a flag set meanwhile changes nothing
+    const int slot = A.slot[b * K + k];
+    const int c0 = A.list[slot] % K;           // the draft whose row is the node's
+    const int nch = (V + kChunk - 1) / kChunk;
+    const int ntiles = A.ntiles;
+    const float *tm = A.tmax + static_cast<long long>(slot) * ntiles;
+    const double *ts = A.tsum + static_cast<long long>(slot) * ntiles;
+    const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+
+    // row maximum over the tile shifts; each tile's weight in the row's scale
+    float m = -INFINITY;
+    for (int t = lane; t < ntiles; t += kWave) m = fmaxf(m, tm[t]);
+    const float M = wave_max(m);
+    auto wt = [&](int t) {
+        return ts[t] * exp2((static_cast<double>(tm[t]) - static_cast<double>(M)) * c64);
+    };
+    // lane l owns the contiguous tiles [l*per, (l+1)*per)
+    const int per = (ntiles + kWave - 1) / kWave;
+    const int t0 = min(lane * per, ntiles), t1 = min(t0 + per, ntiles);
+    double own = 0.0;
+    int last_tile = -1;
+    for (int t = t0; t < t1; ++t) {
+        const double w = wt(t);
+        own += w;
+        if (w > 0.0) last_tile = t;
+    }
+    const double pre = wave_exclusive_scan(own);
+    const double Z = wave_sum(own);
+    last_tile = wave_max_int(last_tile);
+    const float u = A.ud[(static_cast<long long>(b) * K + k) * L + j];
+    if (!(Z > 0.0) || !isfinite(Z) || !(u >= 0.0f && u < 1.0f)) {
+        if (lane == 0) A.bad[b] = 1u;
+        return;
+    }
+    const double thr = static_cast<double>(u) * Z;
+    int tc = 0x7fffffff;
+    if (pre <= thr && pre + own > thr) {
+        double acc = pre;
+        for (int t = t0; t < t1; ++t) {
+            const double w = wt(t);
+            if (acc + w > thr) { tc = t; break; }
+            acc += w;
+        }
+    }
+    tc = wave_min_int(tc);
+    const bool fallback = tc == 0x7fffffff;    // rounding left no crossing: last positive token
+    if (fallback) tc = last_tile;
+    // the mass before tile tc, from the lane that owns it
+    double tb = 0.0;
+    if (tc >= t0 && tc < t1) {
+        tb = pre;
+        for (int t = t0; t < tc; ++t) tb += wt(t);
+    }
+    const double tbase = __shfl(tb, per > 0 ? tc / per : 0, kWave);
+
+    // rescan tile tc with the tiles kernel's arithmetic; lane l takes chunks
+    // [8l, 8l+8) of the tile, so the wave scan runs in token order
+    const E *base = static_cast<const E *>(A.drf);
+    const RD P(base + ((static_cast<long long>(b) * K + c0) * L + j) * V, V);
+    const float Mg = tm[tc];
+    const double f = exp2((static_cast<double>(Mg) - static_cast<double>(M)) * c64);
+    float chi, clo;
+    split_scale(c64, chi, clo);
+    const int c1 = tc * kDraftTileChunks + lane * kPerLane;
+    auto weights = [&](int c, float (&e)[8]) {
         float x[8];
         P.load(c, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float d = x[k] - M0;
-            e[k] = fast_exp2(fmaf(d, chi, d * clo));
+        for (int q = 0; q < 8; ++q) {
+            const float dd = x[q] - Mg;
+            e[q] = fast_exp2(fmaf(dd, chi, dd * clo));
         }
-        cs = static_cast<double>(sum8(e));
+    };
+    double cs = 0.0;
+    int lastp = -1;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int c = c1 + i;
+        if (c < nch) {
+            float e[8];
+            weights(c, e);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (e[q] > 0.0f) lastp = 8 * c + q;
+            cs += static_cast<double>(sum8(e));
+        }
     }
-    const double pre = base + block_exclusive_scan<NT>(cs, red);
+    const double cpre = wave_exclusive_scan(cs);
     int cand = 0x7fffffff;
-    if (c < nch && pre <= thr && pre + cs > thr) {
-        double C = pre;
-        int lastp = -1;
+    if (!fallback && c1 < nch) {
+        const double lo = tbase + f * cpre, hi = tbase + f * (cpre + cs);
+        if (lo <= thr && hi > thr) {   // the crossing lane: recompute its weights in order
+            double C = cpre;
+            for (int i = 0; i < kPerLane && c1 + i < nch && cand == 0x7fffffff; ++i) {
+                float e[8];
+                weights(c1 + i, e);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (cand == 0x7fffffff) {
-                if (e[k] > 0.0f) lastp = 8 * c + k;
-                C += static_cast<double>(e[k]);
-                if (C > thr) cand = 8 * c + k;
+                for (int q = 0; q < 8; ++q) {
+                    if (cand == 0x7fffffff) {
+                        C += static_cast<double>(e[q]);
+                        if (tbase + f * C > thr) cand = 8 * (c1 + i) + q;
+                    }
+                }
             }
-        }
-        if (cand == 0x7fffffff && lastp >= 0) cand = lastp;
-    }
-    cand = block_min_int<NT>(cand, ired);
-    return cand == 0x7fffffff ? lastpos : cand;
-}
-
-template <int NT, typename RD, typename E>
-__global__ __launch_bounds__(NT) void draft_kernel(DraftArgs A) {
-    constexpr int NW = NT / kWave;
-    constexpr int kMaxTiles = ((1 << 22) / kChunk + NT - 1) / NT;
-    __shared__ double s_tile[kMaxTiles];
-    __shared__ double s_red[5 * NW];
-    __shared__ float s_fred[NW];
-    __shared__ int s_ired[NW];
-
-    const int K = A.K, L = A.L, V = A.V, j = A.j;
-    const int b = blockIdx.x / K, k = blockIdx.x % K;
-    const int tid = threadIdx.x;
-    const int32_t *X = A.tok + static_cast<long long>(b) * K * L;
-
-    // the lowest-index draft at this node does the work for all of them
-    int skip = 0;
-    for (int c = tid; c < k; c += NT) {
-        int same = 1;
-        for (int t = 0; t < j; ++t) same &= (X[c * L + t] == X[k * L + t]);
-        skip |= same;
-    }
-    if (__syncthreads_or(skip)) return;
-
-    const float T = A.temp[b];
-    if (!(T > 0.0f) || !isfinite(T)) {
-        if (tid == 0) A.bad[b] = 1u;
-        return;
-    }
-    const double c64 = 1.4426950408889634 / static_cast<double>(T);
-    float chi, clo;
-    split_scale(c64, chi, clo);
-    const int nch = (V + kChunk - 1) / kChunk;
-    const E *base = static_cast<const E *>(A.drf);
-    const RD P(base + ((static_cast<long long>(b) * K + k) * L + j) * V, V);
-
-    // pass over the row with the first tile's maximum as shift, again with the
-    // row maximum if an exponent overflowed
-    float x0[8];
-    if (tid < nch) P.load(tid, x0);
-    else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x0[e] = -INFINITY;
-    }
-    float M0 = fmaxf(block_max<NT>(max8(x0), s_fred), -3.402823466e38f);
-    int lastpos, ovf;
-    double Z = draft_tiles<NT, RD>(P, nch, M0, chi, clo, s_tile, &lastpos, &ovf, s_red, s_ired);
-    if (ovf) {
-        float m = -INFINITY;
-        for (int c = tid; c < nch; c += NT) {
-            float x[8];
-            P.load(c, x);
-            m = fmaxf(m, max8(x));
-        }
-        M0 = fmaxf(block_max<NT>(m, s_fred), -3.402823466e38f);
-        Z = draft_tiles<NT, RD>(P, nch, M0, chi, clo, s_tile, &lastpos, &ovf, s_red, s_ired);
-    }
-    if (tid == 0 && A.rows) atomicAdd(A.rows + b, 1);
-    if (!(Z > 0.0) || !isfinite(Z) || ovf) {   // not a distribution
-        if (tid == 0) A.bad[b] = 1u;
-        return;
-    }
-
-    // every draft at this node: k itself and the higher drafts with its prefix
-    for (int k2 = k; k2 < K; ++k2) {
-        int same = 1;
-        for (int t = 0; t < j; ++t) same &= (X[k2 * L + t] == X[k * L + t]);
-        if (!same) continue;
-        const long long at = (static_cast<long long>(b) * K + k2) * L + j;
-        const float u = A.ud[at];
-        int y = -1;
-        if (u >= 0.0f && u < 1.0f)
-            y = draft_pick<NT, RD>(P, nch, M0, chi, clo, s_tile, static_cast<double>(u) * Z,
-                                   lastpos, s_red, s_ired);
-        if (tid == 0) {
-            A.tok[at] = y;
-            if (y < 0) A.bad[b] = 1u;
+            if (cand == 0x7fffffff) cand = lastp;
         }
     }
+    cand = wave_min_int(cand);
+    const int lastrow = wave_max_int(lastp);
+    if (lane == 0)
+        A.tok[(static_cast<long long>(b) * K + k) * L + j] = cand == 0x7fffffff ? lastrow : cand;
 }
 
 }  // namespace sv

@@ -215,9 +215,9 @@ typedef struct sv_draft_outputs {
 /* Workspace bytes spec_draft_sample needs (0 on invalid sizes). */
 size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
 
-/* Draw the K draft blocks of every request.  Asynchronous on ln->stream: L + 2
- * launches (one per position, plus a clear and a final pass that marks invalid
- * requests).  ln->phase_events[0] and [1], when non-null, are recorded before
+/* Draw the K draft blocks of every request.  Asynchronous on ln->stream:
+ * 3L + 2 launches (per position: list the node rows, stream them into tile
+ * sums, draw; plus a clear and a final pass that marks invalid requests).  ln->phase_events[0] and [1], when non-null, are recorded before
  * and after them; [2..4] are not used.  The tokens of position j are written by
  * the launch for j and read back by the later ones, so draft_tokens must not
  * alias the other arguments. */
