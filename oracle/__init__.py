@@ -179,3 +179,25 @@ def draft(draft_logits, temperature, u_draft, *, threads: int = 1, requests=None
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda b: run(b, b + 1), reqs))
     return out
+
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) widened exactly to float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def lm_head(hidden_bits, weight_bits, temperature):
+    """Logits and their row statistics, the step that produces the verifier's
+    inputs: logits[r][v] = sum_i h[r][i] w[v][i] over the bf16 hidden states
+    [R][d] and the bf16 LM-head weight [V][d] (bit patterns, widened exactly),
+    in float64 by a library matrix product; lse[r] = ln sum_v exp(l_rv / T_r),
+    the natural-log partition function of the temperature softmax of each row
+    (written out as max/T + ln sum exp((l - max)/T)).  Returns (logits, lse)."""
+    h = bf16_bits_to_f64(hidden_bits)
+    w = bf16_bits_to_f64(weight_bits)
+    logits = h @ w.T
+    T = np.asarray(temperature, np.float64).reshape(-1, 1)
+    m = logits.max(axis=1, keepdims=True)
+    lse = (m / T + np.log(np.exp((logits - m) / T).sum(axis=1, keepdims=True)))[:, 0]
+    return logits, lse
