@@ -32,7 +32,8 @@ class SvInputs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("target_logits", _vp), ("draft_logits", _vp), ("draft_tokens", _vp),
-                ("temperature", _vp), ("u_accept", _vp), ("u_correct", _vp)]
+                ("temperature", _vp), ("u_accept", _vp), ("u_correct", _vp),
+                ("row_stats", _vp)]
 
 
 class SvOutputs(ctypes.Structure):
@@ -57,6 +58,16 @@ class SvDraftInputs(ctypes.Structure):
 
 class SvDraftOutputs(ctypes.Structure):
     _fields_ = [("draft_tokens", _vp), ("flags", _vp), ("rows_streamed", _vp)]
+
+
+class SvLmInputs(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_int32), ("d", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("hidden", _vp), ("weight", _vp), ("temperature", _vp)]
+
+
+class SvLmOutputs(ctypes.Structure):
+    _fields_ = [("logits", _vp), ("row_stats", _vp), ("stats_group", ctypes.c_int32),
+                ("stats_stride", ctypes.c_int32), ("stats_offset", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -89,6 +100,11 @@ def load_library(path: str = LIB_PATH):
     lib.spec_draft_sample.restype = ctypes.c_int
     lib.spec_draft_sample.argtypes = [ctypes.POINTER(SvDraftInputs), ctypes.POINTER(SvDraftOutputs),
                                       ctypes.POINTER(SvLaunch)]
+    lib.sv_lm_workspace_size.restype = ctypes.c_size_t
+    lib.sv_lm_workspace_size.argtypes = [ctypes.c_int32] * 3
+    lib.spec_lm_head.restype = ctypes.c_int
+    lib.spec_lm_head.argtypes = [ctypes.POINTER(SvLmInputs), ctypes.POINTER(SvLmOutputs),
+                                 ctypes.POINTER(SvLaunch)]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_version.restype = ctypes.c_char_p
@@ -152,7 +168,9 @@ class Verifier:
                                   "row_lse", "accept_prob", "resid_mass", "rows_streamed")])
 
     def __call__(self, target, draft, tokens, temperature, u_accept, u_correct, *,
-                 stream=None, events=None):
+                 stream=None, events=None, row_stats=None):
+        """row_stats: optional uint8 device tensor holding [B][K][2L+1] statistics
+        (16 bytes each, e.g. from LmHead); the statistics pass is then skipped."""
         B, K, L, V = self.shape
         checks = [(target, (B, K, L + 1, V), self.dtype), (draft, (B, K, L, V), self.dtype),
                   (tokens, (B, K, L), torch.int32), (temperature, (B,), torch.float32),
@@ -163,9 +181,13 @@ class Verifier:
                                  f"got {t.dtype} {tuple(t.shape)}")
             if t.device.type != "cuda":
                 raise ValueError("inputs must live in GPU memory")
+        if row_stats is not None and (row_stats.device.type != "cuda" or
+                                      row_stats.numel() * row_stats.element_size()
+                                      < B * K * (2 * L + 1) * 16):
+            raise ValueError("row_stats must be a device buffer of B*K*(2L+1) statistics")
         ins = SvInputs(B, K, L, V, _dtype_code(target), target.data_ptr(), draft.data_ptr(),
                        tokens.data_ptr(), temperature.data_ptr(), u_accept.data_ptr(),
-                       u_correct.data_ptr())
+                       u_correct.data_ptr(), _ptr(row_stats))
         if stream is None:
             stream = torch.cuda.current_stream(target.device).cuda_stream
         ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
@@ -221,6 +243,49 @@ class Drafter:
         return self.out
 
 
+class LmHead:
+    """The LM head logits = h W^T (bf16 in, fp32 logits out) with every row's
+    temperature-softmax statistics computed in the same kernel (spec_lm_head in
+    include/spec_verify.h).  Holds the logits output and the workspace."""
+
+    STAT_BYTES = 16
+
+    def __init__(self, R, d, V, device="cuda"):
+        lib = load_library()
+        self.shape = (R, d, V)
+        dev = torch.device(device)
+        self.logits = torch.empty((R, V), dtype=torch.float32, device=dev)
+        nbytes = int(lib.sv_lm_workspace_size(R, d, V))
+        if nbytes == 0:
+            raise ValueError(f"sizes out of range: R={R} d={d} V={V} (d a multiple of 64)")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def __call__(self, hidden, weight, temperature, *, stats=None, group=1, stride=1, offset=0,
+                 stream=None, events=None):
+        """hidden [R][d] and weight [V][d] bf16, temperature [R] fp32 (the row's
+        request temperature).  stats: optional uint8 device tensor receiving
+        row r's statistics at slot (r // group) * stride + offset + r % group."""
+        R, d, V = self.shape
+        for t, shp, dt in [(hidden, (R, d), torch.bfloat16), (weight, (V, d), torch.bfloat16),
+                           (temperature, (R,), torch.float32)]:
+            if tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"expected contiguous {dt} tensor of shape {shp}, "
+                                 f"got {t.dtype} {tuple(t.shape)}")
+            if t.device.type != "cuda":
+                raise ValueError("inputs must live in GPU memory")
+        ins = SvLmInputs(R, d, V, hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr())
+        outs = SvLmOutputs(self.logits.data_ptr(), _ptr(stats), group, stride, offset)
+        if stream is None:
+            stream = torch.cuda.current_stream(hidden.device).cuda_stream
+        ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
+        ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
+        lib = load_library()
+        rc = lib.spec_lm_head(ctypes.byref(ins), ctypes.byref(outs), ctypes.byref(ln))
+        if rc != SV_OK:
+            raise SpecVerifyError(f"spec_lm_head failed: {lib.sv_status_string(rc).decode()} ({rc})")
+        return self.logits
+
+
 def spec_draft_sample(draft_logits, temperature, u_draft, **kw):
     """Draw K i.i.d. draft blocks per request.  See include/spec_verify.h."""
     B, K, L, V = draft_logits.shape
@@ -265,5 +330,5 @@ def spec_verify_spectr(target, draft, tokens, temperature, u_accept, u_correct, 
 
 
 __all__ = ["spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-           "spec_verify_spectr", "spec_draft_sample", "Verifier", "Drafter", "workspace_size",
-           "load_library", "SpecVerifyError"]
+           "spec_verify_spectr", "spec_draft_sample", "Verifier", "Drafter", "LmHead",
+           "workspace_size", "load_library", "SpecVerifyError"]

@@ -16,11 +16,13 @@
 // No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 
 #include "../../include/spec_verify.h"
 #include "sv_draft.hpp"
+#include "sv_lmhead.hpp"
 #include "sv_rowstats.hpp"
 #include "sv_walk.hpp"
 
@@ -38,6 +40,8 @@ static_assert(SV_MAX_V == sv::kMaxV, "V limit");
 static_assert(SV_FLAG_DEGENERATE == sv::kFlagDegenerate, "flag bits");
 static_assert(SV_FLAG_INVALID == sv::kFlagInvalid, "flag bits");
 static_assert(sizeof(sv::RowStat) == 16, "row statistics layout");
+static_assert(sizeof(sv_row_stat) == sizeof(sv::RowStat) && offsetof(sv_row_stat, sum) == 8,
+              "sv_row_stat is the library's row statistics layout");
 
 size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -79,8 +83,9 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     using RD = typename sv::RowOf<E, VEC>::type;
     hipStream_t stream = static_cast<hipStream_t>(ln->stream);
     const bool diagnostics = out->row_lse != nullptr;
+    const bool given = in->row_stats != nullptr;
     // a second round only pays when several drafts can share an accepted prefix
-    const bool two_round = method != sv::kMethodToken && in->K > 1 && !diagnostics;
+    const bool two_round = method != sv::kMethodToken && in->K > 1 && !diagnostics && !given;
     const Layout lay = layout(in->B, in->K, in->L);
     char *ws = static_cast<char *>(ln->workspace);
 
@@ -109,13 +114,14 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.temp = in->temperature;
     wa.ua = in->u_accept;
     wa.uc = in->u_correct;
-    wa.stats = sa.stats;
+    wa.stats = given ? static_cast<sv::RowStat *>(const_cast<void *>(in->row_stats)) : sa.stats;
     wa.B = in->B;
     wa.K = in->K;
     wa.L = in->L;
     wa.V = in->V;
     wa.method = method;
-    wa.all_nodes = diagnostics ? 1 : 0;
+    wa.all_nodes = (diagnostics || given) ? 1 : 0;
+    wa.stats_given = given ? 1 : 0;
     wa.round = 1;
     wa.two_round = two_round ? 1 : 0;
     wa.state = reinterpret_cast<sv::WalkState *>(ws + lay.state);
@@ -133,10 +139,12 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
 
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>),
-                       dim3(grid_for(2 * in->L + (diagnostics ? 1 : 0))), dim3(kStatsThreads), 0,
-                       stream, sa);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (!given) {
+        hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>),
+                           dim3(grid_for(2 * in->L + (diagnostics ? 1 : 0))), dim3(kStatsThreads),
+                           0, stream, sa);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
     auto walk = [&]() {
         if (method == sv::kMethodSpecTr)
@@ -181,6 +189,7 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
     const uintptr_t ta = reinterpret_cast<uintptr_t>(in->target_logits);
     const uintptr_t da = reinterpret_cast<uintptr_t>(in->draft_logits);
     if (ta % es || da % es) return SV_EINVAL;
+    if (in->row_stats && reinterpret_cast<uintptr_t>(in->row_stats) % 16) return SV_EINVAL;
     if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
     if (ln->workspace_bytes < layout(in->B, in->K, in->L).total) return SV_EWORKSPACE;
 
@@ -272,6 +281,29 @@ hipError_t launch_draft(const sv_draft_inputs *in, const sv_draft_outputs *out,
     return record(ln, 1, stream);
 }
 
+// LM-head workspace: per row and column block, the partial maximum and sum.
+struct LmLayout {
+    size_t pmax, psum, total;
+    int nbm, nbn;
+};
+
+LmLayout lm_layout(int32_t R, int32_t V) {
+    LmLayout l;
+    l.nbm = (R + sv::kLmBM - 1) / sv::kLmBM;
+    l.nbn = (V + sv::kLmBN - 1) / sv::kLmBN;
+    const size_t n = static_cast<size_t>(R) * l.nbn;
+    l.pmax = 0;
+    l.psum = align_up(n * sizeof(float), 256);
+    l.total = l.psum + align_up(n * sizeof(double), 256);
+    if (l.total == 0) l.total = 256;
+    return l;
+}
+
+bool lm_sizes_ok(int32_t R, int32_t d, int32_t V) {
+    return R >= 0 && R <= (1 << 26) && d >= sv::kLmBK && d <= 65536 && d % sv::kLmBK == 0 &&
+           V >= 1 && V <= SV_MAX_V;
+}
+
 size_t draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
     return draft_layout(B, K, V).total;
 }
@@ -279,6 +311,60 @@ size_t draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
 }  // namespace
 
 extern "C" {
+
+size_t sv_lm_workspace_size(int32_t R, int32_t d, int32_t V) {
+    if (!lm_sizes_ok(R, d, V)) return 0;
+    return lm_layout(R, V).total;
+}
+
+int spec_lm_head(const sv_lm_inputs *in, const sv_lm_outputs *out, const sv_launch *ln) {
+    if (!in || !out || !ln) return SV_EINVAL;
+    if (!lm_sizes_ok(in->R, in->d, in->V)) return SV_EINVAL;
+    if (in->R == 0) return SV_OK;
+    if (!in->hidden || !in->weight || !in->temperature || !out->logits) return SV_EINVAL;
+    if (reinterpret_cast<uintptr_t>(in->hidden) % 16 || reinterpret_cast<uintptr_t>(in->weight) % 16)
+        return SV_EINVAL;
+    if (out->row_stats && (out->stats_group < 1 || out->stats_stride < out->stats_group ||
+                           out->stats_offset < 0 ||
+                           reinterpret_cast<uintptr_t>(out->row_stats) % 16))
+        return SV_EINVAL;
+    const LmLayout lay = lm_layout(in->R, in->V);
+    if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < lay.total) return SV_EWORKSPACE;
+    hipStream_t stream = static_cast<hipStream_t>(ln->stream);
+    char *ws = static_cast<char *>(ln->workspace);
+    sv::LmArgs a;
+    a.h = static_cast<const uint16_t *>(in->hidden);
+    a.w = static_cast<const uint16_t *>(in->weight);
+    a.temp = in->temperature;
+    a.logits = out->logits;
+    a.pmax = reinterpret_cast<float *>(ws + lay.pmax);
+    a.psum = reinterpret_cast<double *>(ws + lay.psum);
+    a.R = in->R;
+    a.d = in->d;
+    a.V = in->V;
+    a.nbm = lay.nbm;
+    a.nbn = lay.nbn;
+    if (record(ln, 0, stream) != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL(sv::lm_head_kernel, dim3(static_cast<unsigned>(lay.nbm) * lay.nbn),
+                       dim3(sv::kLmThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (out->row_stats) {
+        sv::LmStatsArgs s;
+        s.pmax = a.pmax;
+        s.psum = a.psum;
+        s.temp = in->temperature;
+        s.stats = out->row_stats;
+        s.R = in->R;
+        s.nbn = lay.nbn;
+        s.group = out->stats_group;
+        s.stride = out->stats_stride;
+        s.offset = out->stats_offset;
+        hipLaunchKernelGGL(sv::lm_stats_kernel, dim3((in->R + 3) / 4), dim3(256), 0, stream, s);
+        if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
+    return record(ln, 1, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
 
 size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
     if (!sizes_ok(B, K, L, V, dtype)) return 0;
@@ -342,6 +428,6 @@ const char *sv_status_string(int status) {
     }
 }
 
-const char *sv_version(void) { return "0.1.0"; }
+const char *sv_version(void) { return "0.2.0"; }
 
 }  // extern "C"

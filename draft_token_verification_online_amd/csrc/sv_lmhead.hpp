@@ -1,0 +1,231 @@
+// sv_lmhead.hpp -- the LM head with the verifier's row statistics in its epilogue.
+//
+// The verifier's inputs are logit rows, produced by the target and draft
+// models' LM heads: logits = h W^T over hidden states h [R][d] and the
+// vocabulary projection W [V][d] (bf16).  Verification is a large share of a
+// speculative-decoding step (the performance study's page, section 1); here
+// the first thing the verifier does with a row -- its temperature-softmax
+// statistics (shift M, sum S = sum_v 2^((l_v - M) log2(e)/T)) -- is computed
+// while the row is still in registers, so the statistics pass over the logits
+// disappears.  The logits are still written (fp32): the walk's residual sweeps
+// and correction draws read whole rows.
+//
+// lm_head_kernel: one 256-thread workgroup per 128 x 128 output tile, four waves
+// in a 2 x 2 arrangement each owning 64 x 64 (4 x 4 MFMA 16x16x32 bf16 tiles),
+// K stepped by 64 through double-buffered LDS (rows padded by 16 bytes against
+// bank conflicts).  Blocks are ordered in groups of row-blocks so a group
+// reuses each vocabulary tile from L2, and remapped so that consecutive
+// blocks of the order land on the same XCD.  The epilogue writes the fp32
+// tile and, per row, the partial (max, sum) over its 128 columns; a combine
+// kernel folds the partials of a row into (M, S).
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLmBM = 128, kLmBN = 128, kLmBK = 64;
+constexpr int kLmThreads = 256;
+constexpr int kLmStride = kLmBK + 8;     // LDS row stride in bf16 elements
+constexpr int kLmGroupM = 16;            // row-blocks per group of the block order
+constexpr int kXcds = 8;
+
+struct LmArgs {
+    const uint16_t *h;      // [R][d] bf16 bits
+    const uint16_t *w;      // [V][d] bf16 bits
+    const float *temp;      // [R]: temperature of each row
+    float *logits;          // [R][V]
+    float *pmax;            // [R][nbn]: per column block, the row's maximum
+    double *psum;           // [R][nbn]: and sum_v 2^((l_v - max) c) over the block
+    int R, d, V, nbm, nbn;
+};
+
+__device__ __forceinline__ void lm_block_coords(int pid, int nbm, int nbn, int *bm, int *bn) {
+    const int n = nbm * nbn;
+    if (n % kXcds == 0) {                 // blocks go to XCDs round-robin: make runs local
+        const int per = n / kXcds;
+        pid = (pid % kXcds) * per + pid / kXcds;
+    }
+    const int in_group = kLmGroupM * nbn;
+    const int g = pid / in_group;
+    const int first = g * kLmGroupM;
+    const int gsize = min(kLmGroupM, nbm - first);
+    const int r = pid % in_group;
+    *bm = first + r % gsize;
+    *bn = r / gsize;
+}
+
+__global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kLmBM * kLmStride];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kLmBN * kLmStride];
+    __shared__ float s_m[2][kLmBM];
+    __shared__ double s_s[2][kLmBM];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    int bm, bn;
+    lm_block_coords(blockIdx.x, A.nbm, A.nbn, &bm, &bn);
+    const int row0 = bm * kLmBM, col0 = bn * kLmBN;
+    const int R = A.R, d = A.d, V = A.V;
+
+    // a 128 x 64 bf16 tile is 1024 chunks of 16 bytes: 4 per thread
+    auto load_tile = [&](const uint16_t *base, int rows, int r0, int k0, uint4 (&buf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + kLmThreads * i;
+            const int r = q >> 3, kc = q & 7;
+            const int gr = r0 + r;
+            buf[i] = gr < rows ? *reinterpret_cast<const uint4 *>(base + static_cast<long long>(gr) * d +
+                                                                   k0 + kc * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_tile = [&](uint16_t *s, const uint4 (&buf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + kLmThreads * i;
+            const int r = q >> 3, kc = q & 7;
+            *reinterpret_cast<uint4 *>(s + r * kLmStride + kc * 8) = buf[i];
+        }
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint4 ra[4], rb[4];
+    load_tile(A.h, R, row0, 0, ra);
+    load_tile(A.w, V, col0, 0, rb);
+    store_tile(sA[0], ra);
+    store_tile(sB[0], rb);
+    __syncthreads();
+    const int nk = d / kLmBK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            load_tile(A.h, R, row0, (kt + 1) * kLmBK, ra);
+            load_tile(A.w, V, col0, (kt + 1) * kLmBK, rb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kLmBK; kk += 32) {
+            bf16x8 af[4], bfr[4];
+            const int ko = kk + (lane >> 4) * 8;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = wm * 64 + t * 16 + (lane & 15);
+                af[t] = *reinterpret_cast<const bf16x8 *>(sA[cur] + r * kLmStride + ko);
+                const int c = wn * 64 + t * 16 + (lane & 15);
+                bfr[t] = *reinterpret_cast<const bf16x8 *>(sB[cur] + c * kLmStride + ko);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], acc[a][b], 0,
+                                                                       0, 0);
+        }
+        if (kt + 1 < nk) {
+            store_tile(sA[cur ^ 1], ra);
+            store_tile(sB[cur ^ 1], rb);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds C[4*(lane/16) + i][lane%16] of each 16 x 16 tile
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rloc = wm * 64 + a * 16 + 4 * (lane >> 4) + i;
+            const int row = row0 + rloc;
+            const bool rok = row < R;
+            float v[4];
+            float m = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int col = col0 + wn * 64 + b * 16 + (lane & 15);
+                v[b] = col < V ? acc[a][b][i] : -INFINITY;
+                if (rok && col < V) A.logits[static_cast<long long>(row) * V + col] = v[b];
+                m = fmaxf(m, v[b]);
+            }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            const double c64 = 1.4426950408889634 / static_cast<double>(rok ? A.temp[row] : 1.0f);
+            float chi, clo;
+            split_scale(c64, chi, clo);
+            const float ms = fmaxf(m, -3.402823466e38f);
+            float e = 0.0f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float dd = v[b] - ms;
+                e += fast_exp2(fmaf(dd, chi, dd * clo));
+            }
+            double s = static_cast<double>(e);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
+            if ((lane & 15) == 0) {
+                s_m[wn][rloc] = m;
+                s_s[wn][rloc] = s;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < kLmBM) {
+        const int row = row0 + tid;
+        if (row < R) {
+            const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[row]);
+            const float m0 = s_m[0][tid], m1 = s_m[1][tid];
+            const float M = fmaxf(m0, m1);
+            const double Mc = fmax(static_cast<double>(M), -3.402823466e38);
+            double S = 0.0;
+            if (m0 > -INFINITY) S += s_s[0][tid] * exp2((static_cast<double>(fmaxf(m0, -3.402823466e38f)) - Mc) * c64);
+            if (m1 > -INFINITY) S += s_s[1][tid] * exp2((static_cast<double>(fmaxf(m1, -3.402823466e38f)) - Mc) * c64);
+            A.pmax[static_cast<long long>(row) * A.nbn + bn] = M;
+            A.psum[static_cast<long long>(row) * A.nbn + bn] = S;
+        }
+    }
+}
+
+// The partials of row r folded into its statistics, written to slot
+// (r / group) * stride + offset + r % group of a 16-byte {float M; float pad;
+// double S} array (the verifier's node-row statistics layout).  One wave per row.
+struct LmStatsArgs {
+    const float *pmax;
+    const double *psum;
+    const float *temp;
+    void *stats;
+    int R, nbn, group, stride, offset;
+};
+
+__global__ __launch_bounds__(256) void lm_stats_kernel(LmStatsArgs A) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (r >= A.R) return;
+    const float *pm = A.pmax + static_cast<long long>(r) * A.nbn;
+    const double *ps = A.psum + static_cast<long long>(r) * A.nbn;
+    float m = -INFINITY;
+    for (int i = lane; i < A.nbn; i += kWave) m = fmaxf(m, pm[i]);
+    m = wave_max(m);
+    const double Mc = fmax(static_cast<double>(m), -3.402823466e38);
+    const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[r]);
+    double s = 0.0;
+    for (int i = lane; i < A.nbn; i += kWave)
+        if (pm[i] > -INFINITY)
+            s += ps[i] * exp2((static_cast<double>(fmaxf(pm[i], -3.402823466e38f)) - Mc) * c64);
+    s = wave_sum(s);
+    if (lane == 0) {
+        const long long slot =
+            static_cast<long long>(r / A.group) * A.stride + A.offset + r % A.group;
+        char *p = static_cast<char *>(A.stats) + slot * 16;
+        *reinterpret_cast<float *>(p) = fmaxf(m, -3.402823466e38f);
+        *reinterpret_cast<float *>(p + 4) = 0.0f;
+        *reinterpret_cast<double *>(p + 8) = s;
+    }
+}
+
+}  // namespace sv

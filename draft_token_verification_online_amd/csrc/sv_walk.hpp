@@ -62,7 +62,8 @@ struct WalkArgs {
     const RowStat *stats;   // [B][K][2L+1]
     int B, K, L, V;
     int method;             // kMethodToken, kMethodBlockWalk or kMethodSpecTr
-    int all_nodes;          // the statistics kernel streamed every node row (diagnostics)
+    int all_nodes;          // statistics of every node row are present (diagnostics, or given)
+    int stats_given;        // they came from the caller: no row was streamed here
     int round;              // 1, or 2 to resume the walks the first round suspended
     int two_round;          // a second round follows: the first may suspend
     struct WalkState *state;     // [B]
@@ -418,6 +419,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         s_have[i] = static_cast<unsigned char>(have);
     }
     __syncthreads();
+    if (A.stats_given) streamed = 0;
     streamed = static_cast<int>(block_sum<NT>(static_cast<double>(streamed), s_red));
 
     // 3. statistics of those rows into LDS; logits at the drafted tokens

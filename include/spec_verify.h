@@ -128,7 +128,20 @@ typedef struct sv_inputs {
     const float *temperature;     /* [B], T_b > 0 */
     const float *u_accept;        /* [B][K][L], uniforms in [0, 1) */
     const float *u_correct;       /* [B], uniforms in [0, 1) */
+    const void *row_stats;        /* optional [B][K][2L+1] node-row statistics (sv_row_stat,
+                                     rows as in sv_outputs.row_lse), e.g. from spec_lm_head;
+                                     when set the library streams no rows for statistics
+                                     and runs one walk (no second round); NULL: computed */
 } sv_inputs;
+
+/* Statistics of one logit row l at its request's temperature T: shift M and
+ * sum S = sum_v 2^((l_v - M) log2(e) / T), so that the temperature softmax is
+ * pi(v) = 2^((l_v - M) log2(e) / T) / S. */
+typedef struct sv_row_stat {
+    float shift;
+    float pad;
+    double sum;
+} sv_row_stat;
 
 /* Outputs.  DEVICE pointers owned by the caller; every element of every
  * non-null output is overwritten.  The three integer outputs are required. */
@@ -224,10 +237,46 @@ size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32
 int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
                       const sv_launch *ln);
 
+/* ------------------------------------------------------- fused LM head */
+
+/* The step that produces the verifier's inputs: logits = h W^T for bf16 hidden
+ * states h [R][d] and a bf16 vocabulary projection W [V][d] (row-major, so both
+ * operands are contiguous along d), fp32 accumulation on the matrix cores, fp32
+ * logits out.  The temperature-softmax statistics of every row (the verifier's
+ * first step) are computed in the same kernel while the row is in registers,
+ * so passing them to a verification call (sv_inputs.row_stats) removes the
+ * statistics pass over the logits.  Verification is a large share of a
+ * speculative-decoding step (the performance study's page, section 1). */
+typedef struct sv_lm_inputs {
+    int32_t R;                    /* rows, >= 0 */
+    int32_t d;                    /* hidden size, a positive multiple of 64, <= 65536 */
+    int32_t V;                    /* vocabulary size, 1..SV_MAX_V */
+    const void *hidden;           /* [R][d] bf16, 16-byte aligned, device memory */
+    const void *weight;           /* [V][d] bf16, 16-byte aligned, device memory */
+    const float *temperature;     /* [R]: the temperature of each row's request */
+} sv_lm_inputs;
+
+typedef struct sv_lm_outputs {
+    float *logits;                /* [R][V] fp32, required */
+    void *row_stats;              /* optional sv_row_stat array: row r is written to slot
+                                     (r / stats_group) * stats_stride + stats_offset
+                                     + r % stats_group.  Target rows [B][K][L+1] go to
+                                     group L+1, stride 2L+1, offset 0; draft rows
+                                     [B][K][L] to group L, stride 2L+1, offset L+1. */
+    int32_t stats_group, stats_stride, stats_offset;
+} sv_lm_outputs;
+
+/* Workspace bytes spec_lm_head needs (0 on invalid sizes). */
+size_t sv_lm_workspace_size(int32_t R, int32_t d, int32_t V);
+
+/* Compute the logits (and statistics) asynchronously on ln->stream; events [0]
+ * and [1], when non-null, are recorded before and after. */
+int spec_lm_head(const sv_lm_inputs *in, const sv_lm_outputs *out, const sv_launch *ln);
+
 /* Static description of a status code. */
 const char *sv_status_string(int status);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, e.g. "0.2.0". */
 const char *sv_version(void);
 
 #ifdef __cplusplus

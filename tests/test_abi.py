@@ -34,8 +34,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-              "spec_verify_spectr", "spec_draft_sample", "sv_workspace_size",
-              "sv_draft_workspace_size", "sv_status_string", "sv_version"):
+              "spec_verify_spectr", "spec_draft_sample", "spec_lm_head", "sv_workspace_size",
+              "sv_draft_workspace_size", "sv_lm_workspace_size", "sv_status_string",
+              "sv_version"):
         assert n in names
 
 
@@ -76,7 +77,7 @@ def _fake(B=2, K=1, L=4, V=32, dtype=sv.SV_F32, align=256):
     base = 1 << 20
     ins = sv.SvInputs(B, K, L, V, dtype, base, base + 4096, base + 8192, base + 8448,
                       base + 8704, base + 8960)
-    outs = sv.SvOutputs(base + 9216, base + 9472, base + 9728, None, None, None, None)
+    outs = sv.SvOutputs(base + 9216, base + 9472, base + 9728, None, None, None, None, None)
     ln = sv.SvLaunch(None, base * 2 + (0 if align == 256 else align), 1 << 20,
                      (ctypes.c_void_p * sv.N_PHASE_EVENTS)())
     return ins, outs, ln
@@ -188,3 +189,51 @@ def test_draft_host_validation(lib):
     big = lib.sv_draft_workspace_size(512, 8, 8, 151936, sv.SV_BF16)
     assert big % 256 == 0 and 4096 * 38 * 12 <= big < 4096 * 38 * 12 + 65536
     assert lib.sv_draft_workspace_size(1, 0, 8, 16, sv.SV_BF16) == 0
+
+
+def test_row_stats_must_be_aligned(lib):
+    ins, outs, ln = _fake(K=2)
+    ins.row_stats = (1 << 20) + 8
+    assert _call(lib, "spec_verify_multidraft", ins, outs, ln) == sv.SV_EINVAL
+
+
+def test_lm_head_host_validation(lib):
+    base = 1 << 20
+    f = lambda i, o, l: lib.spec_lm_head(ctypes.byref(i) if i is not None else None,
+                                         ctypes.byref(o) if o is not None else None,
+                                         ctypes.byref(l) if l is not None else None)
+
+    def fake(R=4, d=128, V=100):
+        ins = sv.SvLmInputs(R, d, V, base, base + 4096, base + 8192)
+        outs = sv.SvLmOutputs(base + 12288, None, 1, 1, 0)
+        ln = sv.SvLaunch(None, base * 2, 1 << 24, (ctypes.c_void_p * sv.N_PHASE_EVENTS)())
+        return ins, outs, ln
+
+    ins, outs, ln = fake()
+    assert f(None, outs, ln) == sv.SV_EINVAL and f(ins, None, ln) == sv.SV_EINVAL
+    assert f(ins, outs, None) == sv.SV_EINVAL
+    for field, value in [("d", 0), ("d", 96), ("d", 70000), ("V", 0), ("R", -1)]:
+        ins, outs, ln = fake()
+        setattr(ins, field, value)
+        assert f(ins, outs, ln) == sv.SV_EINVAL, (field, value)
+    for field in ("hidden", "weight", "temperature"):
+        ins, outs, ln = fake()
+        setattr(ins, field, None)
+        assert f(ins, outs, ln) == sv.SV_EINVAL, field
+    ins, outs, ln = fake()
+    ins.hidden += 8                                  # not 16-byte aligned
+    assert f(ins, outs, ln) == sv.SV_EINVAL
+    ins, outs, ln = fake()
+    outs.logits = None
+    assert f(ins, outs, ln) == sv.SV_EINVAL
+    ins, outs, ln = fake()
+    outs.row_stats, outs.stats_group, outs.stats_stride = base + 20480, 3, 2   # stride < group
+    assert f(ins, outs, ln) == sv.SV_EINVAL
+    ins, outs, ln = fake()
+    ln.workspace_bytes = 16
+    assert f(ins, outs, ln) == sv.SV_EWORKSPACE
+    ins, outs, ln = fake(R=0)
+    assert f(ins, outs, ln) == sv.SV_OK
+    # partial (max, sum) per row and 128-column block
+    assert lib.sv_lm_workspace_size(36864, 3584, 151936) >= 36864 * 1187 * 12
+    assert lib.sv_lm_workspace_size(4, 100, 16) == 0

@@ -1,0 +1,127 @@
+"""GPU parity of the fused LM head (spec_lm_head) against the oracle's float64
+matrix product, and of verification fed by its statistics.
+
+Tolerances come from the arithmetic: every bf16 x bf16 product is exact in fp32
+and each of the at most d/32 + 32 fp32 additions that form a logit rounds once,
+so |logit - exact| <= (d/32 + 34) 2^-24 sum_i |h_i w_i| (a bound per element,
+computed here in float64).  A row's log-partition function moves by at most the
+largest logit error over T, plus the fp32 exponentials (< 1e-6 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paritytools as pt
+from draft_token_verification_online_amd import LmHead, Verifier
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _make(R, d, V, seed, scale=4.0):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    h = torch.randn((R, d), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((V, d), generator=g, device="cuda") * (scale / d ** 0.5)).to(torch.bfloat16)
+    return h, w
+
+
+def _bound(hb, wb):
+    d = hb.shape[1]
+    a = np.abs(oracle.bf16_bits_to_f64(hb)) @ np.abs(oracle.bf16_bits_to_f64(wb)).T
+    return (d / 32 + 34) * 2.0 ** -24 * a
+
+
+def _stats_lse(buf, rows, temps):
+    raw = buf.cpu().numpy()
+    shift = raw.view(np.float32).reshape(-1, 4)[:rows, 0].astype(np.float64)
+    ssum = raw.view(np.float64).reshape(-1, 2)[:rows, 1]
+    return shift / temps + np.log(ssum)
+
+
+@pytest.mark.parametrize("R,d,V,T", [(1, 64, 1, 1.0), (130, 64, 1000, 0.7), (257, 128, 4099, 0.4),
+                                     (300, 896, 8192, 1.0), (128, 3584, 2048, 0.25)])
+def test_logits_and_statistics(R, d, V, T):
+    print(f"[case] lm_head R={R} d={d} V={V} T={T}", flush=True)
+    h, w = _make(R, d, V, 100 + R)
+    temps = torch.full((R,), T, device="cuda") * (1 + 0.5 * (torch.arange(R, device="cuda") % 3))
+    stats = torch.zeros(R * 16, dtype=torch.uint8, device="cuda")
+    lm = LmHead(R, d, V)
+    logits = lm(h, w, temps, stats=stats)
+    torch.cuda.synchronize()
+    hb, wb, tt = _bits(h), _bits(w), temps.cpu().numpy().astype(np.float64)
+    ref, lse = oracle.lm_head(hb, wb, tt)
+    bound = _bound(hb, wb)
+    err = np.abs(logits.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= bound).all(), float((err / np.maximum(bound, 1e-300)).max())
+    got = _stats_lse(stats, R, tt)
+    tol = bound.max(axis=1) / tt + 1e-6 * np.maximum(1.0, np.abs(lse))
+    assert (np.abs(got - lse) <= tol).all(), float(np.abs(got - lse).max())
+    print(f"[parity] lm_head R={R} d={d} V={V}: max logit err {err.max():.2e} "
+          f"(bound {bound.max():.2e}), max lse err {np.abs(got - lse).max():.2e}", flush=True)
+
+
+@pytest.mark.parametrize("method", ["multidraft", "spectr"])
+def test_lm_head_statistics_feed_verification(method):
+    """Target and draft LM heads write fp32 logits and their statistics straight
+    into the verifier's [B][K][2L+1] layout; verification skips its statistics
+    pass.  The oracle does the same from its float64 logits (rounded to fp32).
+    Decisions are compared except where a threshold lies within the logits' own
+    error band of the oracle's value."""
+    B, K, L, V, d = 12, 4, 4, 4096, 256
+    print(f"[case] lm_head->verify {method} B={B} K={K} L={L} V={V} d={d}", flush=True)
+    ht, wt = _make(B * K * (L + 1), d, V, 7)
+    g = torch.Generator(device="cuda").manual_seed(8)
+    hd = (ht.view(B, K, L + 1, d)[:, :, :L].float()
+          + 0.5 * torch.randn((B, K, L, d), generator=g, device="cuda")).to(torch.bfloat16)
+    hd = hd.reshape(B * K * L, d).contiguous()
+    wd = (wt.float() + 0.3 * (4 / d ** 0.5) * torch.randn((V, d), generator=g, device="cuda")
+          ).to(torch.bfloat16)
+    T = (0.5 + 0.5 * (torch.arange(B, device="cuda") % 3)).float()
+    Tt = T.repeat_interleave(K * (L + 1))
+    Td = T.repeat_interleave(K * L)
+    stats = torch.zeros(B * K * (2 * L + 1) * 16, dtype=torch.uint8, device="cuda")
+    lt = LmHead(B * K * (L + 1), d, V)(ht, wt, Tt, stats=stats, group=L + 1, stride=2 * L + 1,
+                                       offset=0)
+    ld = LmHead(B * K * L, d, V)(hd, wd, Td, stats=stats, group=L, stride=2 * L + 1,
+                                 offset=L + 1)
+    torch.cuda.synchronize()
+
+    # the oracle's own logits and tokens
+    ref_t, _ = oracle.lm_head(_bits(ht), _bits(wt), Tt.cpu().numpy())
+    ref_d, _ = oracle.lm_head(_bits(hd), _bits(wd), Td.cpu().numpy())
+    bnd = max(_bound(_bits(ht), _bits(wt)).max(), _bound(_bits(hd), _bits(wd)).max())
+    tgt32 = ref_t.astype(np.float32).reshape(B, K, L + 1, V)
+    drf32 = ref_d.astype(np.float32).reshape(B, K, L, V)
+    rng = np.random.default_rng(9)
+    Th = T.cpu().numpy()
+    tok = oracle.draft(drf32, Th, rng.random((B, K, L)).astype(np.float32))["tokens"]
+    ua = rng.random((B, K, L)).astype(np.float32)
+    uc = rng.random(B).astype(np.float32)
+    ref = oracle.verify(method, tgt32, drf32, tok, Th, ua, uc, diagnostics=True)
+
+    v = Verifier(method, B, K, L, V, torch.float32, diagnostics=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = v(lt.view(B, K, L + 1, V), ld.view(B, K, L, V), dev(tok), T, dev(ua), dev(uc),
+            row_stats=stats)
+    torch.cuda.synchronize()
+    assert (out["rows_streamed"] == 0).all()
+    band = 4 * bnd / float(Th.min())          # |dh| from the logit errors, in u units
+    excused, bad = 0, []
+    for b in range(B):
+        same = all(int(out[k][b]) == int(ref[k][b]) for k in ("accept_len", "draft_index",
+                                                               "correction"))
+        if same:
+            continue
+        if ref["margin"][b] < band:
+            excused += 1
+        else:
+            bad.append((b, float(ref["margin"][b])))
+    lse_err = np.nanmax(np.abs(out["row_lse"].cpu().numpy().astype(np.float64) - ref["row_lse"]))
+    print(f"[parity] lm_head->verify {method}: n={B} excused={excused} (band {band:.1e}) "
+          f"lse err {lse_err:.2e}", flush=True)
+    assert not bad, bad
+    assert lse_err <= bnd / float(Th.min()) + 1e-5
