@@ -8,8 +8,10 @@ the per-request walk).  Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--method M]
 
 M is a verification method (token, block, multidraft -- the default for
-multi-draft workloads --, spectr), or "draft" to time the drafting kernel
-instead (drafted tokens per second).  --pipeline times the one-GPU emulation
+multi-draft workloads --, spectr), "draft" to time the drafting kernel
+instead (drafted tokens per second), or "lmhead" to time the fused LM heads
+(synthetic target and draft projections, --d-target and --d-draft) feeding
+verification, against the same with the statistics left to the verifier.  --pipeline times the one-GPU emulation
 of MineDraft's two-batch schedule: each step verifies one batch on one HIP
 stream while the other batch is drafted on a second stream, roles alternating.
 
@@ -36,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -91,7 +94,7 @@ def read_traffic(workload: str, method: str):
     the drafting kernel for method "draft"; its launches in one step) from the
     committed rocprofv3 PMC summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a
     copy-kernel calibration), or None when absent or taken on other sources."""
-    kernel = "draft" if method == "draft" else "rowstats"
+    kernel = {"draft": "draft", "lmhead": "lmhead"}.get(method, "rowstats")
     path = os.path.join(PROFILES, f"{kernel}_{method}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -317,6 +320,123 @@ def run_pipeline(args, w, name, method):
     }
 
 
+def run_lmhead(args, w, name):
+    """Target and draft LM heads (logits + statistics) feeding a verification call
+    that skips its statistics pass, against the unfused sequence."""
+    import torch
+    import synth
+    import draft_token_verification_online_amd as sv
+    B, K, L, V = w.B, w.K, w.L, w.V
+    dt, dd = args.d_target, args.d_draft
+    Rt, Rd = B * K * (L + 1), B * K * L
+    method = "multidraft" if w.K > 1 else "block"
+    log(f"[bench] synthetic LM heads d={dt}/{dd} for {name} ({Rt}+{Rd} rows, V={V})")
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    ht = torch.randn((Rt, dt), generator=g, device="cuda").to(torch.bfloat16)
+    wt = (torch.randn((V, dt), generator=g, device="cuda") * (4 / dt ** 0.5)).to(torch.bfloat16)
+    hd = torch.randn((Rd, dd), generator=g, device="cuda").to(torch.bfloat16)
+    wd = (torch.randn((V, dd), generator=g, device="cuda") * (4 / dd ** 0.5)).to(torch.bfloat16)
+    base = synth.generate(synth.scaled(w, V=8), args.seed, device="cuda")   # temperatures, uniforms
+    T = base["temperature"]
+    Tt, Td = T.repeat_interleave(K * (L + 1)), T.repeat_interleave(K * L)
+    lt, ld = sv.LmHead(Rt, dt, V), sv.LmHead(Rd, dd, V)
+    stats = torch.empty(B * K * (2 * L + 1) * 16, dtype=torch.uint8, device="cuda")
+    ver = sv.Verifier(method, B, K, L, V, torch.float32)
+    ld(hd, wd, Td)
+    drafter = sv.Drafter(B, K, L, V, torch.float32)
+    tok = drafter(ld.logits.view(B, K, L, V), T,
+                  synth.draft_uniforms(w, args.seed, device="cuda"))["draft_tokens"].clone()
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def fused(ev=None):
+        lt(ht, wt, Tt, stats=stats, group=L + 1, stride=2 * L + 1, offset=0, stream=stream,
+           events=ev)
+        ld(hd, wd, Td, stats=stats, group=L, stride=2 * L + 1, offset=L + 1, stream=stream)
+        ver(lt.logits.view(B, K, L + 1, V), ld.logits.view(B, K, L, V), tok, T,
+            base["u_accept"], base["u_correct"], stream=stream, row_stats=stats)
+
+    def unfused():
+        lt(ht, wt, Tt, stream=stream)
+        ld(hd, wd, Td, stream=stream)
+        ver(lt.logits.view(B, K, L + 1, V), ld.logits.view(B, K, L, V), tok, T,
+            base["u_accept"], base["u_correct"], stream=stream)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / n
+
+    for _ in range(args.warmup):
+        fused()
+        unfused()
+    evs = [[hip.create(), hip.create()] + [None] * (sv.N_PHASE_EVENTS - 2)
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused(evs[i])
+    torch.cuda.synchronize()
+    t_fused = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_lm = sum(hip.elapsed_ms(e[0], e[1]) for e in evs) / args.steps   # target LM head
+    hip.close()
+    t_unfused = timed(unfused, args.steps)
+    t_lmd = timed(lambda: ld(hd, wd, Td, stream=stream), args.steps)
+    t_ver_given = timed(lambda: ver(lt.logits.view(B, K, L + 1, V), ld.logits.view(B, K, L, V),
+                                    tok, T, base["u_accept"], base["u_correct"], stream=stream,
+                                    row_stats=stats), args.steps)
+    t_ver_own = timed(lambda: ver(lt.logits.view(B, K, L + 1, V), ld.logits.view(B, K, L, V),
+                                  tok, T, base["u_accept"], base["u_correct"], stream=stream),
+                      args.steps)
+    flops = 2.0 * Rt * V * dt
+    tflops = flops / (t_lm * 1e-3) / 1e12
+    log(f"[bench] target LM head {t_lm:.3f} ms ({tflops:.0f} TFLOP/s), draft LM head "
+        f"{t_lmd:.3f} ms; verify given stats {t_ver_given:.3f} ms, own stats {t_ver_own:.3f} ms; "
+        f"fused step {t_fused:.3f} ms, unfused {t_unfused:.3f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        from threadpoolctl import threadpool_info
+        n = 32
+        hb = lambda x: x[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        wbt = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+        wbd = wd.view(torch.int16).cpu().numpy().view(np.uint16)
+        t = time.perf_counter()
+        oracle.lm_head(hb(ht), wbt, Tt[:n].cpu().numpy())
+        ct = (time.perf_counter() - t) / n
+        t = time.perf_counter()
+        oracle.lm_head(hb(hd), wbd, Td[:n].cpu().numpy())
+        cd = (time.perf_counter() - t) / n
+        step_s = Rt * ct + Rd * cd
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cpu = {"value": B * K * L / step_s, "unit": "verified draft tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"oracle LM heads (float64 BLAS product) on {n} target and {n} draft rows, "
+                         f"scaled to the {Rt}+{Rd} rows of a step; verification not included"}
+    return {
+        "metric": "verified draft tokens/s through fused LM heads + verification",
+        "value": B * K * L / (t_fused * 1e-3),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_fused, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "method": "lmhead+" + method, "B": B, "K": K, "L": L,
+                   "V": V, "d_target": dt, "d_draft": dd, "seed": args.seed},
+        "roofline": {"bound": "mfma", "kernel": "lm_head_kernel (target)", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": read_traffic(name, "lmhead")},
+        "cpu_baseline": cpu,
+        "detail": {"lm_target_ms": t_lm, "lm_draft_ms": t_lmd, "verify_given_stats_ms": t_ver_given,
+                   "verify_own_stats_ms": t_ver_own, "fused_ms": t_fused, "unfused_ms": t_unfused,
+                   "target_gemm_tflop": flops / 1e12},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +448,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work (summed over cores) spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--d-target", type=int, default=3584, help="hidden size of the target LM head")
+    ap.add_argument("--d-draft", type=int, default=896, help="hidden size of the draft LM head")
     ap.add_argument("--pipeline", action="store_true",
                     help="time the two-batch verify/draft overlap on two streams")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -360,6 +482,9 @@ def main():
     torch.cuda.set_device(0)
     if method == "draft":
         print(json.dumps(run_draft(args, w, name)), flush=True)
+        return
+    if method == "lmhead":
+        print(json.dumps(run_lmhead(args, w, name)), flush=True)
         return
     if args.pipeline:
         print(json.dumps(run_pipeline(args, w, name, method)), flush=True)

@@ -13,9 +13,10 @@
 // lm_head_kernel: one 256-thread workgroup per 128 x 128 output tile, four waves
 // in a 2 x 2 arrangement each owning 64 x 64 (4 x 4 MFMA 16x16x32 bf16 tiles),
 // K stepped by 64 through double-buffered LDS (rows padded by 16 bytes against
-// bank conflicts).  Blocks are ordered in groups of row-blocks so a group
-// reuses each vocabulary tile from L2, and remapped so that consecutive
-// blocks of the order land on the same XCD.  The epilogue writes the fp32
+// bank conflicts), with the global loads three steps ahead in registers.
+// Blocks are ordered in groups of row-blocks so a group reuses each vocabulary
+// tile from L2, and remapped so that consecutive blocks of the order land on
+// the same XCD.  The epilogue writes the fp32
 // tile and, per row, the partial (max, sum) over its 128 columns; a combine
 // kernel folds the partials of a row into (M, S).
 #pragma once
@@ -98,19 +99,25 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 ra[4], rb[4];
-    load_tile(A.h, R, row0, 0, ra);
-    load_tile(A.w, V, col0, 0, rb);
-    store_tile(sA[0], ra);
-    store_tile(sB[0], rb);
-    __syncthreads();
+    // three register stages: tile t lives in stage t % 3 from its load until it is
+    // stored to LDS, two compute steps later, so each load has two steps to land
     const int nk = d / kLmBK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            load_tile(A.h, R, row0, (kt + 1) * kLmBK, ra);
-            load_tile(A.w, V, col0, (kt + 1) * kLmBK, rb);
-        }
+    uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4];
+    load_tile(A.h, R, row0, 0, a0);
+    load_tile(A.w, V, col0, 0, b0);
+    if (nk > 1) {
+        load_tile(A.h, R, row0, kLmBK, a1);
+        load_tile(A.w, V, col0, kLmBK, b1);
+    }
+    if (nk > 2) {
+        load_tile(A.h, R, row0, 2 * kLmBK, a2);
+        load_tile(A.w, V, col0, 2 * kLmBK, b2);
+    }
+    store_tile(sA[0], a0);
+    store_tile(sB[0], b0);
+    __syncthreads();
+
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < kLmBK; kk += 32) {
             bf16x8 af[4], bfr[4];
@@ -118,9 +125,9 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = wm * 64 + t * 16 + (lane & 15);
-                af[t] = *reinterpret_cast<const bf16x8 *>(sA[cur] + r * kLmStride + ko);
+                af[t] = *reinterpret_cast<const bf16x8 *>(sA[buf] + r * kLmStride + ko);
                 const int c = wn * 64 + t * 16 + (lane & 15);
-                bfr[t] = *reinterpret_cast<const bf16x8 *>(sB[cur] + c * kLmStride + ko);
+                bfr[t] = *reinterpret_cast<const bf16x8 *>(sB[buf] + c * kLmStride + ko);
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -129,11 +136,25 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], acc[a][b], 0,
                                                                        0, 0);
         }
-        if (kt + 1 < nk) {
-            store_tile(sA[cur ^ 1], ra);
-            store_tile(sB[cur ^ 1], rb);
+    };
+    // step t: compute tile t, store tile t+1 (stage (t+1) % 3), load tile t+3 into
+    // stage t % 3
+    auto step = [&](int t, uint4 (&la)[4], uint4 (&lb)[4], uint4 (&sa)[4], uint4 (&sb)[4]) {
+        compute(t & 1);
+        if (t + 1 < nk) {
+            store_tile(sA[(t + 1) & 1], sa);
+            store_tile(sB[(t + 1) & 1], sb);
+        }
+        if (t + 3 < nk) {
+            load_tile(A.h, R, row0, (t + 3) * kLmBK, la);
+            load_tile(A.w, V, col0, (t + 3) * kLmBK, lb);
         }
         __syncthreads();
+    };
+    for (int t = 0; t < nk; t += 3) {
+        step(t, a0, b0, a1, b1);
+        if (t + 1 < nk) step(t + 1, a1, b1, a2, b2);
+        if (t + 2 < nk) step(t + 2, a2, b2, a0, b0);
     }
 
     // epilogue: lane holds C[4*(lane/16) + i][lane%16] of each 16 x 16 tile
