@@ -391,6 +391,7 @@ def run_lmhead(args, w, name):
     t_ver_own = timed(lambda: ver(lt.logits.view(B, K, L + 1, V), ld.logits.view(B, K, L, V),
                                   tok, T, base["u_accept"], base["u_correct"], stream=stream),
                       args.steps)
+    copy_calibration(torch, args.copy_calibration_mib)
     flops = 2.0 * Rt * V * dt
     tflops = flops / (t_lm * 1e-3) / 1e12
     log(f"[bench] target LM head {t_lm:.3f} ms ({tflops:.0f} TFLOP/s), draft LM head "
