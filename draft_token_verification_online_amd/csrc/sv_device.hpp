@@ -21,13 +21,21 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // 2^y on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float y) { return __builtin_amdgcn_exp2f(y); }
 
-// Split a positive scale c (= log2(e)/T) into hi + lo floats with hi <= c and
-// lo > 0, so that d*hi + d*lo keeps the sign of d: a -inf logit difference
-// then maps to 2^-inf = 0 instead of -inf + inf = NaN.
-__device__ __forceinline__ void split_scale(double c, float &hi, float &lo) {
-    hi = static_cast<float>(c);
-    if (static_cast<double>(hi) >= c) hi = nextafterf(hi, 0.0f);
-    lo = static_cast<float>(c - static_cast<double>(hi));
+// Base-2 exponents of temperature-scaled logits.  For a row with shift M and
+// c = log2(e)/T, every kernel forms y = x c - M c as fmaf(x, c, -Mc) with c
+// rounded once to fp32 (temp_scale) and Mc = M c rounded once to fp32
+// (shift_term; clamped at -FLT_MAX, so a -inf logit still gives 2^-inf = 0 when
+// the shift is -inf).  x c is exact inside the FMA, so y carries one rounding,
+// and the rounding of Mc is a constant of the row: it cancels from every
+// normalised probability because every reader of a row's statistics forms Mc
+// from the stored shift in the same way.  Rounding c to fp32 changes the
+// temperature by at most 2^-25 relative.  In fp64 the same exponent is
+// x (double)c - (double)Mc, with the product exact.
+__device__ __forceinline__ float temp_scale(float T) {
+    return static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+}
+__device__ __forceinline__ float shift_term(float M, float c) {
+    return fmaxf(M * c, -3.402823466e38f);
 }
 
 // Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7; raw(c) issues
@@ -37,6 +45,9 @@ struct RowBf16Vec {
     using Raw = uint4;
     const uint4 *p;
     __device__ RowBf16Vec(const void *row, int) : p(static_cast<const uint4 *>(row)) {}
+    __device__ RowBf16Vec(const uint4 *q) : p(q) {}
+    // the same row from chunk n on
+    __device__ __forceinline__ RowBf16Vec advanced(int n) const { return RowBf16Vec(p + n); }
     __device__ __forceinline__ Raw raw(int c) const { return p[c]; }
     __device__ __forceinline__ static void unpack(const Raw &w, float x[8]) {
         x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
@@ -55,6 +66,7 @@ struct RowF32Vec {
     struct Raw { float4 a, b; };
     const float4 *p;
     __device__ RowF32Vec(const void *row, int) : p(static_cast<const float4 *>(row)) {}
+    __device__ __forceinline__ RowF32Vec advanced(int n) const { return RowF32Vec(p + 2 * n, 0); }
     __device__ __forceinline__ Raw raw(int c) const { return Raw{p[2 * c], p[2 * c + 1]}; }
     __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
@@ -75,6 +87,9 @@ struct RowBf16Scalar {
     const uint16_t *p;
     int V;
     __device__ RowBf16Scalar(const void *row, int V_) : p(static_cast<const uint16_t *>(row)), V(V_) {}
+    __device__ __forceinline__ RowBf16Scalar advanced(int n) const {
+        return RowBf16Scalar(p + kChunk * n, V - kChunk * n);
+    }
     __device__ __forceinline__ void load(int c, float x[8]) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -97,6 +112,9 @@ struct RowF32Scalar {
     const float *p;
     int V;
     __device__ RowF32Scalar(const void *row, int V_) : p(static_cast<const float *>(row)), V(V_) {}
+    __device__ __forceinline__ RowF32Scalar advanced(int n) const {
+        return RowF32Scalar(p + kChunk * n, V - kChunk * n);
+    }
     __device__ __forceinline__ void load(int c, float x[8]) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -117,6 +135,52 @@ template <> struct RowOf<uint16_t, true> { using type = RowBf16Vec; };
 template <> struct RowOf<uint16_t, false> { using type = RowBf16Scalar; };
 template <> struct RowOf<float, true> { using type = RowF32Vec; };
 template <> struct RowOf<float, false> { using type = RowF32Scalar; };
+
+// Stream the chunks c0, c0 + NT, ... (c0 = this thread's index, all < nch) of
+// one row, or of a row pair when HAS_Q, through f(xp, xq, c).  D chunks per row
+// stay in flight per lane: once a chunk is unpacked its register slot is
+// refilled with the chunk D NT further on, so loads overlap the arithmetic of
+// the chunks before them instead of being issued and drained group by group.
+// Refill addresses are clamped into the row (nch >= 1); the refills issued in
+// the last full group are discarded and the remainder is read one chunk at a
+// time.  Without HAS_Q, xq is left unset and Q is not read.
+template <int NT, int D, bool HAS_Q, typename RD, typename F>
+__device__ __forceinline__ void stream_rows(const RD &P, const RD &Q, int nch, F &&f) {
+    int c = threadIdx.x;
+    if (c + (D - 1) * NT < nch) {
+        typename RD::Raw rp[D], rq[D];
+        // issued in the order they are consumed (the scheduler would otherwise
+        // be free to permute them, and the static waits in the loop then cover
+        // the worst order)
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            rp[i] = P.raw(c + i * NT);
+            if (HAS_Q) rq[i] = Q.raw(c + i * NT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (;;) {
+            const int cn = c + D * NT;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                float xp[8], xq[8];
+                RD::unpack(rp[i], xp);
+                if (HAS_Q) RD::unpack(rq[i], xq);
+                const int cl = min(cn + i * NT, nch - 1);
+                rp[i] = P.raw(cl);
+                if (HAS_Q) rq[i] = Q.raw(cl);
+                f(xp, xq, c + i * NT);
+            }
+            c = cn;
+            if (c + (D - 1) * NT >= nch) break;
+        }
+    }
+    for (; c < nch; c += NT) {
+        float xp[8], xq[8];
+        P.load(c, xp);
+        if (HAS_Q) Q.load(c, xq);
+        f(xp, xq, c);
+    }
+}
 
 __device__ __forceinline__ float max8(const float x[8]) {
     return fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),

@@ -15,7 +15,8 @@
 //      wave) and, per draft, the list slot of its node's row;
 //   2. draft_tiles_kernel -- grid-stride over (listed row, tile of 512 chunks),
 //      one 64-lane wave per tile (8 chunks per lane): the tile's maximum M_t and
-//      the sum of 2^((l - M_t) c) over it, by wave reductions only (no barrier).
+//      the sum of 2^(l c - M_t c) over it (the product M_t c rounded to fp32, as
+//      every kernel here forms it), by wave reductions only (no barrier).
 //      Every row is streamed once, by as many waves as it has tiles, so a
 //      position with few nodes still fills the chip;
 //   3. draft_pick_kernel  -- one wave per draft: rescale the tile sums of its
@@ -127,9 +128,8 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
             }
         }
         const float M = fmaxf(wave_max(m), -3.402823466e38f);
-        const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[b]);
-        float chi, clo;
-        split_scale(c64, chi, clo);
+        const float sc = temp_scale(A.temp[b]);
+        const float Mc = shift_term(M, sc);
         double sum = 0.0;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
@@ -138,10 +138,7 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
                 float x[8], e[8];
                 RD::unpack(r[i], x);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float d = x[q] - M;
-                    e[q] = fast_exp2(fmaf(d, chi, d * clo));
-                }
+                for (int q = 0; q < 8; ++q) e[q] = fast_exp2(fmaf(x[q], sc, -Mc));
                 sum += static_cast<double>(sum8(e));
             }
         }
@@ -169,14 +166,15 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     const int ntiles = A.ntiles;
     const float *tm = A.tmax + static_cast<long long>(slot) * ntiles;
     const double *ts = A.tsum + static_cast<long long>(slot) * ntiles;
-    const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+    const float sc = temp_scale(A.temp[b]);
 
     // row maximum over the tile shifts; each tile's weight in the row's scale
     float m = -INFINITY;
     for (int t = lane; t < ntiles; t += kWave) m = fmaxf(m, tm[t]);
     const float M = wave_max(m);
+    const double Mcd = static_cast<double>(shift_term(M, sc));
     auto wt = [&](int t) {
-        return ts[t] * exp2((static_cast<double>(tm[t]) - static_cast<double>(M)) * c64);
+        return ts[t] * exp2(static_cast<double>(shift_term(tm[t], sc)) - Mcd);
     };
     // lane l owns the contiguous tiles [l*per, (l+1)*per)
     const int per = (ntiles + kWave - 1) / kWave;
@@ -221,19 +219,14 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     // [8l, 8l+8) of the tile, so the wave scan runs in token order
     const E *base = static_cast<const E *>(A.drf);
     const RD P(base + ((static_cast<long long>(b) * K + c0) * L + j) * V, V);
-    const float Mg = tm[tc];
-    const double f = exp2((static_cast<double>(Mg) - static_cast<double>(M)) * c64);
-    float chi, clo;
-    split_scale(c64, chi, clo);
+    const float Mgc = shift_term(tm[tc], sc);
+    const double f = exp2(static_cast<double>(Mgc) - Mcd);
     const int c1 = tc * kDraftTileChunks + lane * kPerLane;
     auto weights = [&](int c, float (&e)[8]) {
         float x[8];
         P.load(c, x);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float dd = x[q] - Mg;
-            e[q] = fast_exp2(fmaf(dd, chi, dd * clo));
-        }
+        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(fmaf(x[q], sc, -Mgc));
     };
     double cs = 0.0;
     int lastp = -1;

@@ -5,7 +5,8 @@
 // vocabulary projection W [V][d] (bf16).  Verification is a large share of a
 // speculative-decoding step (the performance study's page, section 1); here
 // the first thing the verifier does with a row -- its temperature-softmax
-// statistics (shift M, sum S = sum_v 2^((l_v - M) log2(e)/T)) -- is computed
+// statistics (shift M, sum S = sum_v 2^(l_v c - M c), c = log2(e)/T, with c and
+// the product M c each rounded to fp32 as in every kernel here) -- is computed
 // while the row is still in registers, so the statistics pass over the logits
 // disappears.  The logits are still written (fp32): the walk's residual sweeps
 // and correction draws read whole rows.
@@ -176,16 +177,11 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
             }
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-            const double c64 = 1.4426950408889634 / static_cast<double>(rok ? A.temp[row] : 1.0f);
-            float chi, clo;
-            split_scale(c64, chi, clo);
-            const float ms = fmaxf(m, -3.402823466e38f);
+            const float sc = temp_scale(rok ? A.temp[row] : 1.0f);
+            const float msc = shift_term(m, sc);
             float e = 0.0f;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float dd = v[b] - ms;
-                e += fast_exp2(fmaf(dd, chi, dd * clo));
-            }
+            for (int b = 0; b < 4; ++b) e += fast_exp2(fmaf(v[b], sc, -msc));
             double s = static_cast<double>(e);
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
@@ -199,13 +195,13 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
     if (tid < kLmBM) {
         const int row = row0 + tid;
         if (row < R) {
-            const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[row]);
+            const float sc = temp_scale(A.temp[row]);
             const float m0 = s_m[0][tid], m1 = s_m[1][tid];
             const float M = fmaxf(m0, m1);
-            const double Mc = fmax(static_cast<double>(M), -3.402823466e38);
+            const double Mc = static_cast<double>(shift_term(M, sc));
             double S = 0.0;
-            if (m0 > -INFINITY) S += s_s[0][tid] * exp2((static_cast<double>(fmaxf(m0, -3.402823466e38f)) - Mc) * c64);
-            if (m1 > -INFINITY) S += s_s[1][tid] * exp2((static_cast<double>(fmaxf(m1, -3.402823466e38f)) - Mc) * c64);
+            if (m0 > -INFINITY) S += s_s[0][tid] * exp2(static_cast<double>(shift_term(m0, sc)) - Mc);
+            if (m1 > -INFINITY) S += s_s[1][tid] * exp2(static_cast<double>(shift_term(m1, sc)) - Mc);
             A.pmax[static_cast<long long>(row) * A.nbn + bn] = M;
             A.psum[static_cast<long long>(row) * A.nbn + bn] = S;
         }
@@ -232,12 +228,11 @@ __global__ __launch_bounds__(256) void lm_stats_kernel(LmStatsArgs A) {
     float m = -INFINITY;
     for (int i = lane; i < A.nbn; i += kWave) m = fmaxf(m, pm[i]);
     m = wave_max(m);
-    const double Mc = fmax(static_cast<double>(m), -3.402823466e38);
-    const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[r]);
+    const float sc = temp_scale(A.temp[r]);
+    const double Mc = static_cast<double>(shift_term(m, sc));
     double s = 0.0;
     for (int i = lane; i < A.nbn; i += kWave)
-        if (pm[i] > -INFINITY)
-            s += ps[i] * exp2((static_cast<double>(fmaxf(pm[i], -3.402823466e38f)) - Mc) * c64);
+        if (pm[i] > -INFINITY) s += ps[i] * exp2(static_cast<double>(shift_term(pm[i], sc)) - Mc);
     s = wave_sum(s);
     if (lane == 0) {
         const long long slot =

@@ -40,53 +40,49 @@ __device__ __forceinline__ bool stat_ok(const RowStat &s) {
     return isfinite(s.shift) && s.sum > 0.0 && isfinite(s.sum);
 }
 
-// Per-lane online accumulator of one row's statistics.
+// Per-lane online accumulator of one row's statistics under scale c.
 struct LaneSoftmax {
     float m;          // this lane's shift
-    double s;         // sum of 2^((x - m) c) over the lane's elements
-    __device__ __forceinline__ void init(float block_first_max) {
+    float mc;         // shift_term(m, c)
+    double s;         // sum of 2^(x c - mc) over the lane's elements
+    __device__ __forceinline__ void init(float block_first_max, float c) {
         m = fmaxf(block_first_max, -3.402823466e38f);
+        mc = shift_term(m, c);
         s = 0.0;
     }
-    // The overflow check looks at the exponents themselves: their maximum is
-    // taken over FMA results, which needs no NaN canonicalisation, unlike a
-    // maximum over the raw logits.
-    __device__ __forceinline__ void consume(const float (&x)[8], double c64, float chi, float clo,
-                                            float headroom) {
-        float y[8];
-        float ymax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float d = x[i] - m;
-            y[i] = fmaf(d, chi, d * clo);
-            ymax = fmaxf(ymax, y[i]);
-        }
-        if (ymax > 64.0f) {   // rare: move this lane's shift up, in fp64
-            const float cm = max8(x);
-            s *= exp2((static_cast<double>(m) - static_cast<double>(cm)) * c64);
-            m = cm;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float d = x[i] - m;
-                y[i] = fmaf(d, chi, d * clo);
-            }
-        }
+    // The chunk sum is checked instead of every exponent: it exceeds 2^64 (or is
+    // +inf) whenever an element lies more than 64 binary orders above the lane's
+    // shift, and then (rarely) the lane moves its shift up to the chunk maximum,
+    // rescaling its sum in fp64, and sums the chunk again.  A NaN sum fails the
+    // test and makes S NaN.
+    __device__ __forceinline__ void consume(const float (&x)[8], float c) {
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(y[i]);
-        s += static_cast<double>(sum8(e));
-        (void)headroom;
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -mc));
+        float t = sum8(e);
+        if (t > 0x1p64f) {
+            const float cm = max8(x);
+            const float cmc = shift_term(cm, c);
+            s *= exp2(static_cast<double>(mc) - static_cast<double>(cmc));
+            m = cm;
+            mc = cmc;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -mc));
+            t = sum8(e);
+        }
+        s += static_cast<double>(t);
     }
 };
 
 // Combine the lanes of a block into the row's (M, S); every thread gets it.
 template <int NT>
-__device__ __forceinline__ RowStat finish_row(const LaneSoftmax &ls, double c64, float *fred,
+__device__ __forceinline__ RowStat finish_row(const LaneSoftmax &ls, float c, float *fred,
                                               double *red) {
     const float M = block_max<NT>(ls.m, fred);
     const double scaled =
         (ls.m == M) ? ls.s
-                    : ls.s * exp2((static_cast<double>(ls.m) - static_cast<double>(M)) * c64);
+                    : ls.s * exp2(static_cast<double>(ls.mc) -
+                                  static_cast<double>(shift_term(M, c)));
     RowStat st;
     st.shift = M;
     st.pad = 0.0f;
@@ -177,10 +173,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
             : ((static_cast<long long>(b) * K + k) * L + j) * V;
         const RD row(base + row_off, V);
 
-        const double c64 = 1.4426950408889634 / static_cast<double>(A.temp[b]);
-        float chi, clo;
-        split_scale(c64, chi, clo);
-        const float headroom = 64.0f / chi;   // logit units kept below 2^64
+        const float c = temp_scale(A.temp[b]);
 
         float x0[8];
         const bool have0 = tid < nch;
@@ -190,26 +183,16 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
             for (int e = 0; e < 8; ++e) x0[e] = -INFINITY;
         }
         LaneSoftmax ls;
-        ls.init(block_max<NT>(max8(x0), s_max));
-        if (have0) ls.consume(x0, c64, chi, clo, headroom);
-        int c = tid + NT;
-        for (; c + (kDepth - 1) * NT < nch; c += kDepth * NT) {   // kDepth loads in flight
-            typename RD::Raw r[kDepth];
-#pragma unroll
-            for (int i = 0; i < kDepth; ++i) r[i] = row.raw(c + i * NT);
-#pragma unroll
-            for (int i = 0; i < kDepth; ++i) {
-                float x[8];
-                RD::unpack(r[i], x);
-                ls.consume(x, c64, chi, clo, headroom);
-            }
-        }
-        for (; c < nch; c += NT) {
-            float xa[8];
-            row.load(c, xa);
-            ls.consume(xa, c64, chi, clo, headroom);
-        }
-        const RowStat st = finish_row<NT>(ls, c64, s_max, s_sum);
+        ls.init(block_max<NT>(max8(x0), s_max), c);
+        if (have0) ls.consume(x0, c);
+        // chunks NT.. of the row (the first tile is consumed above)
+        const RD rest = row.advanced(NT);
+        if (nch > NT)
+            stream_rows<NT, kDepth, false>(rest, rest, nch - NT,
+                                           [&](const float (&x)[8], const float (&)[8], int) {
+                                               ls.consume(x, c);
+                                           });
+        const RowStat st = finish_row<NT>(ls, c, s_max, s_sum);
         if (tid == 0)
             A.stats[(static_cast<long long>(b) * K + k) * (2 * L + 1) + row_index] = st;
     }

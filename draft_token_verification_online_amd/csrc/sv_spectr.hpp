@@ -53,14 +53,15 @@ constexpr double kRhoTol = 1e-7;
 constexpr double kQuotientFormBeta = 0x1p-10;
 
 // Histogram of log2(p/q) over [0, log2 n): hist[b] and hist[kHistBins + b] hold
-// the p and q mass (2^31 fixed point, p = 2^((l_p - MP) c) ap) of tokens in
+// the p and q mass (2^31 fixed point, p = 2^(l_p c - MPc) ap, MPc the shift term
+// of the target row, likewise q) of tokens in
 // bin b.  out[] receives, as sums of the unscaled exponentials e_p, e_q: e_p and
 // e_q over tokens with p/q >= n, e_p over tokens with p/q < 1, then
 // D(1) = sum max(p - q, 0), and e_p, e_q over all tokens.
 template <int NT, typename RD>
-__device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MP, float MQ, float ap,
-                                float aq, float off, float scale, float chi, float clo,
-                                unsigned *hist, double (&out)[6], double *red) {
+__device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MPc, float MQc, float ap,
+                                float aq, float off, float scale, float c, unsigned *hist,
+                                double (&out)[6], double *red) {
     for (int i = threadIdx.x; i < 2 * kHistBins; i += NT) hist[i] = 0u;
     __syncthreads();
     double s[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
@@ -68,8 +69,7 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MP, flo
         float cp = 0.0f, cq = 0.0f, cl = 0.0f, cd = 0.0f, ta = 0.0f, tb = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float dp = xp[e] - MP, dq = xq[e] - MQ;
-            const float yp = fmaf(dp, chi, dp * clo), yq = fmaf(dq, chi, dq * clo);
+            const float yp = fmaf(xp[e], c, -MPc), yq = fmaf(xq[e], c, -MQc);
             const float ep = fast_exp2(yp), eq = fast_exp2(yq);
             ta += ep;
             tb += eq;
@@ -93,28 +93,8 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MP, flo
         s[4] += static_cast<double>(ta);
         s[5] += static_cast<double>(tb);
     };
-    int c = threadIdx.x;
-    for (; c + 3 * NT < nch; c += 4 * NT) {
-        typename RD::Raw rp[4], rq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rp[i] = P.raw(c + i * NT);
-            rq[i] = Q.raw(c + i * NT);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float xp[8], xq[8];
-            RD::unpack(rp[i], xp);
-            RD::unpack(rq[i], xq);
-            chunk(xp, xq);
-        }
-    }
-    for (; c < nch; c += NT) {
-        float xp[8], xq[8];
-        P.load(c, xp);
-        Q.load(c, xq);
-        chunk(xp, xq);
-    }
+    stream_rows<NT, 4, true>(P, Q, nch,
+                             [&](const float xp[8], const float xq[8], int) { chunk(xp, xq); });
     block_sum_n<NT, 6>(s, red);   // its barriers also publish hist[]
 #pragma unroll
     for (int i = 0; i < 6; ++i) out[i] = s[i];
@@ -124,16 +104,15 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MP, flo
 // bq = rho aq in fp32: out = {sum_{p > rho q} (p - rho q), then e_q over
 // p > rho q, e_q over p <= rho q, e_p over p > rho q, e_p over p <= rho q}.
 template <int NT, typename RD>
-__device__ void sweep_excess(const RD &P, const RD &Q, int nch, float MP, float MQ, float ap,
-                             float bq, float chi, float clo, double (&out)[5], double *red) {
+__device__ void sweep_excess(const RD &P, const RD &Q, int nch, float MPc, float MQc, float ap,
+                             float bq, float c, double (&out)[5], double *red) {
     double s[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
     auto chunk = [&](const float xp[8], const float xq[8]) {
         float cd = 0.0f, qa = 0.0f, qb = 0.0f, pa = 0.0f, pb = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float dp = xp[e] - MP, dq = xq[e] - MQ;
-            const float ep = fast_exp2(fmaf(dp, chi, dp * clo));
-            const float eq = fast_exp2(fmaf(dq, chi, dq * clo));
+            const float ep = fast_exp2(fmaf(xp[e], c, -MPc));
+            const float eq = fast_exp2(fmaf(xq[e], c, -MQc));
             const float d = fmaf(ap, ep, -(bq * eq));
             const bool pos = d > 0.0f;
             cd += pos ? d : 0.0f;
@@ -148,28 +127,8 @@ __device__ void sweep_excess(const RD &P, const RD &Q, int nch, float MP, float 
         s[3] += static_cast<double>(pa);
         s[4] += static_cast<double>(pb);
     };
-    int c = threadIdx.x;
-    for (; c + 3 * NT < nch; c += 4 * NT) {
-        typename RD::Raw rp[4], rq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rp[i] = P.raw(c + i * NT);
-            rq[i] = Q.raw(c + i * NT);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float xp[8], xq[8];
-            RD::unpack(rp[i], xp);
-            RD::unpack(rq[i], xq);
-            chunk(xp, xq);
-        }
-    }
-    for (; c < nch; c += NT) {
-        float xp[8], xq[8];
-        P.load(c, xp);
-        Q.load(c, xq);
-        chunk(xp, xq);
-    }
+    stream_rows<NT, 4, true>(P, Q, nch,
+                             [&](const float xp[8], const float xq[8], int) { chunk(xp, xq); });
     block_sum_n<NT, 5>(s, red);
 #pragma unroll
     for (int i = 0; i < 5; ++i) out[i] = s[i];
@@ -229,14 +188,15 @@ __device__ __forceinline__ double edge_gap(double e, double Pge, double Qge, dou
 }
 
 // rho* and c = sum_{i<n} x^i at rho* for the node rows P (target) and Q
-// (draft) with statistics (MP, SP), (MQ, SQ); n >= 2 candidates.  Both are
+// (draft) with shift terms MPc, MQc and sums SP, SQ under scale c2; n >= 2
+// candidates.  Both are
 // returned in the normalisation of (SP, SQ): acceptance min(1, p/(rho q)) and
 // residual max(p - c q, (1 - c/rho) p) with p, q from those statistics.  Every
 // thread of the block returns the same values.  hist[] holds 2 * kHistBins
 // entries, red[] 6 * NT/64, br[] 4, ired[] NT/64.
 template <int NT, typename RD>
-__device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MP, double SP, float MQ,
-                             double SQ, float chi, float clo, int n, double &rho_out,
+__device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MPc, double SP, float MQc,
+                             double SQ, float c2, int n, double &rho_out,
                              double &c_out, unsigned *hist, double *red, double *br,
                              int *ired) {
     static_assert(2 * NT == kHistBins, "two histogram bins per thread");
@@ -246,8 +206,8 @@ __device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MP, double
     const double scale = kHistBins / log2(static_cast<double>(n));
     const float off = static_cast<float>(log2(SQ) - log2(SP));
     double hs[6];
-    ratio_histogram<NT, RD>(P, Q, nch, MP, MQ, ap, aq, off, static_cast<float>(scale), chi, clo,
-                            hist, hs, red);
+    ratio_histogram<NT, RD>(P, Q, nch, MPc, MQc, ap, aq, off, static_cast<float>(scale), c2, hist,
+                            hs, red);
     if (!(hs[3] > 0.0)) {   // D(1) = 0: p = q, every token is accepted, rho* = 1
         rho_out = 1.0;
         c_out = 1.0;
@@ -300,8 +260,7 @@ __device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MP, double
     double rho_fin = hi, c_fin = static_cast<double>(n);
     for (int it = 0; it < 64; ++it) {
         double sw[5];
-        sweep_excess<NT, RD>(P, Q, nch, MP, MQ, ap, static_cast<float>(rho / SQ), chi, clo, sw,
-                             red);
+        sweep_excess<NT, RD>(P, Q, nch, MPc, MQc, ap, static_cast<float>(rho / SQ), c2, sw, red);
         const double EPt = sw[3] + sw[4], EQt = sw[1] + sw[2];
         const double kap = (aqd * EQt) / (apd * EPt);
         const double rh = rho * kap;

@@ -87,107 +87,117 @@ __device__ __forceinline__ double chain_step(double w, double r) {
     return t < 1.0 ? t : 1.0;
 }
 
-// omega(v) for the 8 elements of chunk c: [v not in H] max(a eP - bq eQ, 0),
-// eP = 2^((P_v - MP) c); without a Q row, omega = a eP.  With FLOOR the lower
-// bound is g eP (g >= 0) instead of 0.
+// The chunks of the rejected-token set H that this thread reads (chunk c is
+// read by thread c mod NT in every sweep): up to two are kept, and a third
+// sets `many`, after which every chunk of the thread is checked.
+struct HLanes {
+    int c0, c1;
+    bool many;
+};
+template <int NT>
+__device__ __forceinline__ HLanes h_lanes(const int *H, int nH) {
+    HLanes h{-1, -1, false};
+    for (int i = 0; i < nH; ++i) {
+        const int hc = H[i] / kChunk;
+        if (hc % NT != static_cast<int>(threadIdx.x) || hc == h.c0 || hc == h.c1) continue;
+        if (h.c0 < 0) h.c0 = hc;
+        else if (h.c1 < 0) h.c1 = hc;
+        else h.many = true;
+    }
+    return h;
+}
+
+// omega(v) for the 8 elements of chunk ch: [v not in H] max(a eP - bq eQ, 0),
+// eP = 2^(x c - MPc) (MPc = shift_term of the row's shift); without a Q row,
+// omega = a eP.  With FLOOR the lower bound is g eP (g >= 0) instead of 0.
 template <bool HAS_Q, bool FLOOR = false>
-__device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MP, float MQ,
-                                       float a, float bq, float g, float chi, float clo, int v0,
-                                       const int *H, int nH, float w[8]) {
+__device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MPc, float MQc,
+                                       float a, float bq, float g, float c, int ch, const int *H,
+                                       int nH, const HLanes &hl, float w[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float dp = xp[e] - MP;
-        const float ep = fast_exp2(fmaf(dp, chi, dp * clo));
+        const float ep = fast_exp2(fmaf(xp[e], c, -MPc));
         if (HAS_Q) {
-            const float dq = xq[e] - MQ;
-            const float eq = fast_exp2(fmaf(dq, chi, dq * clo));
+            const float eq = fast_exp2(fmaf(xq[e], c, -MQc));
             w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), FLOOR ? g * ep : 0.0f);
         } else {
             w[e] = a * ep;
         }
     }
-    for (int i = 0; i < nH; ++i) {
-        const unsigned off = static_cast<unsigned>(H[i] - v0);
-        if (off < 8u) {
+    if (ch == hl.c0 || ch == hl.c1 || hl.many) {
+        for (int i = 0; i < nH; ++i) {
+            const unsigned off = static_cast<unsigned>(H[i] - kChunk * ch);
+            if (off < 8u) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (off == static_cast<unsigned>(e)) ? 0.0f : w[e];
+                for (int e = 0; e < 8; ++e) w[e] = (off == static_cast<unsigned>(e)) ? 0.0f : w[e];
+            }
         }
     }
 }
 
 struct SweepRows {
-    float MP, MQ, a, bq;
+    float MPc, MQc;   // shift terms of the target and draft rows
+    float a, bq;
     float g = 0.0f;   // floor coefficient (FLOOR sweeps only)
 };
 
-// Block-wide sum of omega over a row pair (or a single row when HAS_Q is false).
-// Four chunks per row are in flight per lane.
+// Block-wide sum of omega over a row pair (or a single row when HAS_Q is false),
+// four chunks per row in flight per lane.
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
-__device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
-                             float clo, const int *H, int nH, double *red) {
+__device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
+                             const int *H, int nH, double *red) {
+    const HLanes hl = h_lanes<NT>(H, nH);
     double acc = 0.0;
-    int c = threadIdx.x;
-    for (; c + 3 * NT < nch; c += 4 * NT) {
-        typename RD::Raw rp[4], rq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rp[i] = P.raw(c + i * NT);
-            if (HAS_Q) rq[i] = Q.raw(c + i * NT);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float xp[8], xq[8], w[8];
-            RD::unpack(rp[i], xp);
-            if (HAS_Q) RD::unpack(rq[i], xq);
-            omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * (c + i * NT), H, nH, w);
-            acc += static_cast<double>(sum8(w));
-        }
-    }
-    for (; c < nch; c += NT) {
-        float xp[8], xq[8], w[8];
-        P.load(c, xp);
-        if (HAS_Q) Q.load(c, xq);
-        omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
+    stream_rows<NT, 4, HAS_Q>(P, Q, nch, [&](const float xp[8], const float xq[8], int ch) {
+        float w[8];
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
         acc += static_cast<double>(sum8(w));
-    }
+    });
     return block_sum<NT>(acc, red);
 }
 
 // Block-wide inverse-CDF draw over omega in token-id order.  Returns y, or -1
 // when the mass Z is not a positive finite number.  Z is returned in *Z.
-// Tiles of NT chunks are summed four at a time into tile[]; the tile holding
-// the threshold is rescanned with a block scan.
+// Tiles of NT chunks are summed four at a time into tile[] (per-chunk sums in
+// fp32, accumulated in fp64); the tile holding the threshold is rescanned with
+// a block scan, element by element in fp64 inside the crossing chunk.  When
+// rounding leaves the threshold past every crossing, the draw is the last
+// token of positive weight, found from the last chunk with positive weight.
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
-__device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float chi,
-                          float clo, const int *H, int nH, double u, double *Z, double *tile,
-                          double *red, double *red4, int *ired) {
+__device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
+                          const int *H, int nH, double u, double *Z, double *tile, double *red,
+                          double *red4, int *ired) {
+    const HLanes hl = h_lanes<NT>(H, nH);
     const int ntile = (nch + NT - 1) / NT;
-    int lastpos = -1;
-    for (int t0 = 0; t0 < ntile; t0 += 4) {
-        typename RD::Raw rp[4], rq[4];
+    int lastc = -1;
+    // four tiles per group; each chunk's register slot is refilled with the same
+    // lane's chunk of the next group (clamped into the row) once it is unpacked,
+    // so the next group's loads overlap this group's arithmetic and block sum
+    typename RD::Raw rp[4], rq[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = (t0 + i) * NT + threadIdx.x;
-            if (c < nch) {
-                rp[i] = P.raw(c);
-                if (HAS_Q) rq[i] = Q.raw(c);
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int cl = min(i * NT + static_cast<int>(threadIdx.x), nch - 1);
+        rp[i] = P.raw(cl);
+        if (HAS_Q) rq[i] = Q.raw(cl);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int t0 = 0; t0 < ntile; t0 += 4) {
         double cs[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = (t0 + i) * NT + threadIdx.x;
+            const int ch = (t0 + i) * NT + threadIdx.x;
             cs[i] = 0.0;
-            if (c < nch) {
-                float xp[8], xq[8], w[8];
-                RD::unpack(rp[i], xp);
-                if (HAS_Q) RD::unpack(rq[i], xq);
-                omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    cs[i] += static_cast<double>(w[e]);
-                    if (w[e] > 0.0f) lastpos = 8 * c + e;
-                }
+            float xp[8], xq[8], w[8];
+            RD::unpack(rp[i], xp);
+            if (HAS_Q) RD::unpack(rq[i], xq);
+            const int cl = min(ch + 4 * NT, nch - 1);
+            rp[i] = P.raw(cl);
+            if (HAS_Q) rq[i] = Q.raw(cl);
+            if (ch < nch) {
+                omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
+                const float t = sum8(w);
+                cs[i] = static_cast<double>(t);
+                if (t > 0.0f) lastc = ch;
             }
         }
         block_sum4<NT>(cs, red4);
@@ -197,11 +207,30 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
                 if (t0 + i < ntile) tile[t0 + i] = cs[i];
         }
     }
-    lastpos = block_max_int<NT>(lastpos, ired);   // its barriers publish tile[]
+    lastc = block_max_int<NT>(lastc, ired);   // its barriers publish tile[]
     double z = 0.0;
     for (int t = 0; t < ntile; ++t) z += tile[t];
     *Z = z;
     if (!(z > 0.0) || !isfinite(z)) return -1;
+    // the last token of positive weight (block-uniform call)
+    auto last_positive = [&]() {
+        __syncthreads();   // readers of ired[] in the reductions above are done
+        if (static_cast<int>(threadIdx.x) == lastc % NT) {
+            float xp[8], xq[8], w[8];
+            P.load(lastc, xp);
+            if (HAS_Q) Q.load(lastc, xq);
+            omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, lastc, H, nH, hl, w);
+            int last = kChunk * lastc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (w[e] > 0.0f) last = kChunk * lastc + e;
+            ired[0] = last;
+        }
+        __syncthreads();
+        const int y = ired[0];
+        __syncthreads();
+        return y;
+    };
     const double thr = u * z;
     double base = 0.0;
     int tc = -1;
@@ -209,36 +238,35 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
         if (base + tile[t] > thr) { tc = t; break; }
         base += tile[t];
     }
-    if (tc < 0) return lastpos;
+    if (tc < 0) return last_positive();
 
-    const int c = tc * NT + threadIdx.x;
+    const int ch = tc * NT + threadIdx.x;
     float w[8];
     double cs = 0.0;
-    if (c < nch) {
+    if (ch < nch) {
         float xp[8], xq[8];
-        P.load(c, xp);
-        if (HAS_Q) Q.load(c, xq);
-        omega8<HAS_Q, FLOOR>(xp, xq, s.MP, s.MQ, s.a, s.bq, s.g, chi, clo, 8 * c, H, nH, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs += static_cast<double>(w[e]);
+        P.load(ch, xp);
+        if (HAS_Q) Q.load(ch, xq);
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
+        cs = static_cast<double>(sum8(w));
     }
     const double pre = base + block_exclusive_scan<NT>(cs, red);
     int cand = 0x7fffffff;
-    if (c < nch && pre <= thr && pre + cs > thr) {
+    if (ch < nch && pre <= thr && pre + cs > thr) {
         double C = pre;
         int last = -1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if (cand == 0x7fffffff) {
-                if (w[e] > 0.0f) last = 8 * c + e;
+                if (w[e] > 0.0f) last = kChunk * ch + e;
                 C += static_cast<double>(w[e]);
-                if (C > thr) cand = 8 * c + e;
+                if (C > thr) cand = kChunk * ch + e;
             }
         }
         if (cand == 0x7fffffff && last >= 0) cand = last;
     }
     cand = block_min_int<NT>(cand, ired);
-    return cand == 0x7fffffff ? lastpos : cand;
+    return cand == 0x7fffffff ? last_positive() : cand;
 }
 
 // Block-wide maximum of a row (NaN entries are ignored here; they surface as a
@@ -246,32 +274,16 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
 template <int NT, typename RD>
 __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
     float m = -INFINITY;
-    int c = threadIdx.x;
-    for (; c + 3 * NT < nch; c += 4 * NT) {
-        typename RD::Raw r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = P.raw(c + i * NT);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x[8];
-            RD::unpack(r[i], x);
-            m = fmaxf(m, max8(x));
-        }
-    }
-    for (; c < nch; c += NT) {
-        float x[8];
-        P.load(c, x);
-        m = fmaxf(m, max8(x));
-    }
+    stream_rows<NT, 4, false>(P, P, nch,
+                              [&](const float x[8], const float *, int) { m = fmaxf(m, max8(x)); });
     return block_max<NT>(m, fred);
 }
 
 // Block-wide statistics of a node's target row and draft row; the walk's
 // fallback for a row that no launch of the statistics kernel streamed.
 template <int NT, typename RD>
-__device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, double c64, float chi,
-                                 float clo, RowStat &sp, RowStat &sq, float *fred, double *red) {
-    const float headroom = 64.0f / chi;
+__device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, float c, RowStat &sp,
+                                 RowStat &sq, float *fred, double *red) {
     const int tid = threadIdx.x;
     float xp[8], xq[8];
     const bool have0 = tid < nch;
@@ -283,37 +295,22 @@ __device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, double c64, 
         for (int e = 0; e < 8; ++e) xp[e] = xq[e] = -INFINITY;
     }
     LaneSoftmax lp, lq;
-    lp.init(block_max<NT>(max8(xp), fred));
-    lq.init(block_max<NT>(max8(xq), fred));
+    lp.init(block_max<NT>(max8(xp), fred), c);
+    lq.init(block_max<NT>(max8(xq), fred), c);
     if (have0) {
-        lp.consume(xp, c64, chi, clo, headroom);
-        lq.consume(xq, c64, chi, clo, headroom);
+        lp.consume(xp, c);
+        lq.consume(xq, c);
     }
-    int c = tid + NT;
-    for (; c + 3 * NT < nch; c += 4 * NT) {
-        typename RD::Raw rp[4], rq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rp[i] = P.raw(c + i * NT);
-            rq[i] = Q.raw(c + i * NT);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float ap[8], aq[8];
-            RD::unpack(rp[i], ap);
-            RD::unpack(rq[i], aq);
-            lp.consume(ap, c64, chi, clo, headroom);
-            lq.consume(aq, c64, chi, clo, headroom);
-        }
+    if (nch > NT) {
+        const RD P1 = P.advanced(NT), Q1 = Q.advanced(NT);
+        stream_rows<NT, 4, true>(P1, Q1, nch - NT,
+                                 [&](const float (&ap)[8], const float (&aq)[8], int) {
+                                     lp.consume(ap, c);
+                                     lq.consume(aq, c);
+                                 });
     }
-    for (; c < nch; c += NT) {
-        P.load(c, xp);
-        Q.load(c, xq);
-        lp.consume(xp, c64, chi, clo, headroom);
-        lq.consume(xq, c64, chi, clo, headroom);
-    }
-    sp = finish_row<NT>(lp, c64, fred, red);
-    sq = finish_row<NT>(lq, c64, fred, red);
+    sp = finish_row<NT>(lp, c, fred, red);
+    sq = finish_row<NT>(lq, c, fred, red);
 }
 
 // Walk state saved when the first round stops for rows below an accepted node.
@@ -363,9 +360,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     const int nch = (V + kChunk - 1) / kChunk;
     const long long bKL = static_cast<long long>(b) * KL;
     const float T = A.temp[b];
-    const double c64 = 1.4426950408889634 / static_cast<double>(T);
-    float chi, clo;
-    split_scale(c64, chi, clo);
+    const float sc = temp_scale(T);           // exponent scale of this request
+    const double scd = static_cast<double>(sc);
     const E *tgt = static_cast<const E *>(A.tgt);
     const E *drf = static_cast<const E *>(A.drf);
     const RowStat *st = A.stats + static_cast<long long>(b) * K * RS;
@@ -449,8 +445,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         if (!s_have[c * L1 + j]) {
             if (may_suspend) return -1;
             RowStat sp, sq;
-            sweep_stats_pair<NT, RD>(RD(trow(c, j), V), RD(drow(c, j), V), nch, c64, chi, clo, sp,
-                                     sq, s_fred, s_red);
+            sweep_stats_pair<NT, RD>(RD(trow(c, j), V), RD(drow(c, j), V), nch, sc, sp, sq, s_fred,
+                                     s_red);
             if (tid == 0) {
                 s_M[c * RS + j] = sp.shift;
                 s_S[c * RS + j] = sp.sum;
@@ -468,21 +464,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         return (stat_ok(a) && stat_ok(q)) ? 1 : 0;
     };
     // log2 p and log2 q of draft k's token at position j under its node rows
+    // (the exponent x sc - shift_term(M, sc) in fp64, as the sweeps form it in fp32)
     auto lp2 = [&](int k, int j) {
         const int c = s_can[k * L1 + j];
-        return (static_cast<double>(s_gp[k * L + j]) - static_cast<double>(s_M[c * RS + j])) * c64 -
-               log2(s_S[c * RS + j]);
+        return static_cast<double>(s_gp[k * L + j]) * scd -
+               static_cast<double>(shift_term(s_M[c * RS + j], sc)) - log2(s_S[c * RS + j]);
     };
     auto lq2 = [&](int k, int j) {
         const int c = s_can[k * L1 + j];
-        return (static_cast<double>(s_gq[k * L + j]) - static_cast<double>(s_M[c * RS + L1 + j])) *
-                   c64 -
+        return static_cast<double>(s_gq[k * L + j]) * scd -
+               static_cast<double>(shift_term(s_M[c * RS + L1 + j], sc)) -
                log2(s_S[c * RS + L1 + j]);
     };
     auto node_sweep = [&](int c, int j, double alpha, double beta) {
         SweepRows sr;
-        sr.MP = s_M[c * RS + j];
-        sr.MQ = s_M[c * RS + L1 + j];
+        sr.MPc = shift_term(s_M[c * RS + j], sc);
+        sr.MQc = shift_term(s_M[c * RS + L1 + j], sc);
         sr.a = static_cast<float>(alpha / s_S[c * RS + j]);
         sr.bq = static_cast<float>(beta / s_S[c * RS + L1 + j]);
         return sr;
@@ -534,9 +531,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 cc = 1.0;
                 if (n > 1)
                     spectr_scale<NT, RD>(RD(trow(cn, j), V), RD(drow(cn, j), V), nch,
-                                         s_M[cn * RS + j], s_S[cn * RS + j], s_M[cn * RS + L1 + j],
-                                         s_S[cn * RS + L1 + j], chi, clo, n, rho, cc, s_hist,
-                                         s_red6, s_br, s_ired);
+                                         shift_term(s_M[cn * RS + j], sc), s_S[cn * RS + j],
+                                         shift_term(s_M[cn * RS + L1 + j], sc),
+                                         s_S[cn * RS + L1 + j], sc, n, rho, cc, s_hist, s_red6,
+                                         s_br, s_ired);
                 int acc = -1;
                 for (int k = 0; k < K && acc < 0; ++k) {
                     int m2 = 1;
@@ -612,7 +610,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                             const SweepRows sr = node_sweep(cm, m, wm, 1.0);
                             const RD P(trow(cm, m), V), Q(drow(cm, m), V);
                             const double R =
-                                sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, 0, s_red);
+                                sweep_mass<NT, RD, true>(P, Q, nch, sr, sc, s_H, 0, s_red);
                             const double d = R + 1.0 - wm;
                             h = d > 0.0 ? R / d : 1.0;
                             Racc = R;
@@ -655,7 +653,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     if (later) {
                         const SweepRows sr = node_sweep(cn, tau, alpha, beta);
                         const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
-                        N = sweep_mass<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, s_red);
+                        N = sweep_mass<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, s_red);
                     } else {
                         mass_known = false;
                     }
@@ -722,14 +720,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             const RD P(trow(cb, L), V);
             const float M = sweep_rowmax<NT, RD>(P, nch, s_fred);
             SweepRows sr;
-            sr.MP = M;
-            sr.MQ = 0.0f;
+            sr.MPc = shift_term(M, sc);
+            sr.MQc = 0.0f;
             sr.a = 1.0f;
             sr.bq = 0.0f;
             double Z;
             y = (M > -INFINITY && M < INFINITY)
-                    ? sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
-                                                s_red, s_red4, s_ired)
+                    ? sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
+                                                s_red4, s_ired)
                     : -1;
             Zp = 1.0;
             if (y < 0) bad = 1;   // the target row after the block is not a distribution
@@ -742,10 +740,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 // max(p - c q, (1 - c/rho) p): the residual after n tries
                 sr = node_sweep(cn, tau, 1.0, cc);
                 sr.g = static_cast<float>(fmax(1.0 - cc / rho, 0.0) / s_S[cn * RS + tau]);
-                y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
-                                                   s_red, s_red4, s_ired);
+                y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
+                                                   s_red4, s_ired);
             } else {
-                y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, chi, clo, s_H, nH, u, &Z, s_tile, s_red,
+                y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, u, &Z, s_tile, s_red,
                                              s_red4, s_ired);
             }
             Zp = Z;
@@ -753,8 +751,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 flags |= kFlagDegenerate;
                 sr.a = static_cast<float>(1.0 / s_S[cn * RS + tau]);
                 sr.bq = 0.0f;
-                y = sweep_icdf<NT, RD, false>(P, P, nch, sr, chi, clo, s_H, 0, u, &Z, s_tile,
-                                              s_red, s_red4, s_ired);
+                y = sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
+                                              s_red4, s_ired);
                 Zp = Z;
             }
         }
@@ -786,7 +784,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             float v = NAN;
             if (!bad) {
                 const RowStat a = st[c * RS + r];
-                v = static_cast<float>((static_cast<double>(a.shift) * c64 + log2(a.sum)) *
+                // ln sum_v exp(l_v / T): the shift in the exact scale plus the
+                // rounding of its fp32 product, which the sum carries
+                const double M = static_cast<double>(a.shift);
+                const double off = static_cast<double>(shift_term(a.shift, sc)) - M * scd;
+                v = static_cast<float>((M * (1.4426950408889634 / static_cast<double>(T)) + off +
+                                        log2(a.sum)) *
                                        0.6931471805599453);
             }
             o[i] = v;
