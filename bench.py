@@ -46,12 +46,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# sources of each profiled kernel family (besides the shared device helpers, the
+# launch code and the C header): a summary stays valid while these are unchanged
+KERNEL_SOURCES = {"rowstats": ("sv_rowstats.hpp", "sv_walk.hpp", "sv_spectr.hpp"),
+                  "draft": ("sv_draft.hpp",),
+                  "lmhead": ("sv_lmhead.hpp",)}
+
+
+def kernel_source_hash(kernel: str = "rowstats") -> str:
     from draft_token_verification_online_amd import build as svbuild
+    own = KERNEL_SOURCES[kernel] + ("sv_device.hpp", "spec_verify.hip", "spec_verify.h")
     h = hashlib.sha256()
     for p in sorted(svbuild.DEPS):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        if os.path.basename(p) in own:
+            with open(p, "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -100,7 +109,7 @@ def read_traffic(workload: str, method: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(kernel):
         return None
     return float(d["bytes_per_step"])
 

@@ -136,6 +136,15 @@ template <> struct RowOf<uint16_t, false> { using type = RowBf16Scalar; };
 template <> struct RowOf<float, true> { using type = RowF32Vec; };
 template <> struct RowOf<float, false> { using type = RowF32Scalar; };
 
+// Chunks of a row kept in flight per lane for a given number of bytes: four
+// 16-byte bf16 chunks or two 32-byte fp32 chunks in 64 bytes.
+template <typename RD, int BYTES>
+constexpr int depth_for() {
+    return BYTES / static_cast<int>(sizeof(typename RD::Raw)) > 0
+               ? BYTES / static_cast<int>(sizeof(typename RD::Raw))
+               : 1;
+}
+
 // Stream the chunks c0, c0 + NT, ... (c0 = this thread's index, all < nch) of
 // one row, or of a row pair when HAS_Q, through f(xp, xq, c).  D chunks per row
 // stay in flight per lane: once a chunk is unpacked its register slot is

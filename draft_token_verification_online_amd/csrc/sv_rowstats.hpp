@@ -111,7 +111,7 @@ struct StatsArgs {
 constexpr int kSelectFirstVisit = 0;   // root pair + rows 1..L-1 of drafts with a new first token
 constexpr int kSelectAllNodes = 1;     // every node row, target rows at position L included
 constexpr int kSelectListed = 2;       // node rows the walk listed after an acceptance
-constexpr int kDepth = 8;              // 16-byte loads in flight per lane
+constexpr int kStreamBytes = 128;      // bytes of a row in flight per lane (8 bf16 chunks)
 
 template <int NT, typename RD, typename E>
 __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
         // chunks NT.. of the row (the first tile is consumed above)
         const RD rest = row.advanced(NT);
         if (nch > NT)
-            stream_rows<NT, kDepth, false>(rest, rest, nch - NT,
+            stream_rows<NT, depth_for<RD, kStreamBytes>(), false>(rest, rest, nch - NT,
                                            [&](const float (&x)[8], const float (&)[8], int) {
                                                ls.consume(x, c);
                                            });

@@ -142,13 +142,14 @@ struct SweepRows {
 };
 
 // Block-wide sum of omega over a row pair (or a single row when HAS_Q is false),
-// four chunks per row in flight per lane.
+// 64 bytes per row in flight per lane.
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
 __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
                              const int *H, int nH, double *red) {
     const HLanes hl = h_lanes<NT>(H, nH);
     double acc = 0.0;
-    stream_rows<NT, 4, HAS_Q>(P, Q, nch, [&](const float xp[8], const float xq[8], int ch) {
+    stream_rows<NT, depth_for<RD, 64>(), HAS_Q>(P, Q, nch,
+                                               [&](const float xp[8], const float xq[8], int ch) {
         float w[8];
         omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
         acc += static_cast<double>(sum8(w));
@@ -170,18 +171,25 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
     const HLanes hl = h_lanes<NT>(H, nH);
     const int ntile = (nch + NT - 1) / NT;
     int lastc = -1;
-    // four tiles per group; each chunk's register slot is refilled with the same
-    // lane's chunk of the next group (clamped into the row) once it is unpacked,
-    // so the next group's loads overlap this group's arithmetic and block sum
+    // four tiles per group.  With 16-byte chunks each chunk's register slot is
+    // refilled with the same lane's chunk of the next group (clamped into the
+    // row) once it is unpacked, so the next group's loads overlap this group's
+    // arithmetic and block sum; wider chunks are loaded group by group (the
+    // rolling form would double their registers).
+    constexpr bool kRoll = sizeof(typename RD::Raw) <= 16;
     typename RD::Raw rp[4], rq[4];
+    auto load_group = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int cl = min(i * NT + static_cast<int>(threadIdx.x), nch - 1);
-        rp[i] = P.raw(cl);
-        if (HAS_Q) rq[i] = Q.raw(cl);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int cl = min((t0 + i) * NT + static_cast<int>(threadIdx.x), nch - 1);
+            rp[i] = P.raw(cl);
+            if (HAS_Q) rq[i] = Q.raw(cl);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (kRoll) load_group(0);
     for (int t0 = 0; t0 < ntile; t0 += 4) {
+        if (!kRoll) load_group(t0);
         double cs[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -190,9 +198,11 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
             float xp[8], xq[8], w[8];
             RD::unpack(rp[i], xp);
             if (HAS_Q) RD::unpack(rq[i], xq);
-            const int cl = min(ch + 4 * NT, nch - 1);
-            rp[i] = P.raw(cl);
-            if (HAS_Q) rq[i] = Q.raw(cl);
+            if (kRoll) {
+                const int cl = min(ch + 4 * NT, nch - 1);
+                rp[i] = P.raw(cl);
+                if (HAS_Q) rq[i] = Q.raw(cl);
+            }
             if (ch < nch) {
                 omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
                 const float t = sum8(w);
@@ -274,8 +284,8 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
 template <int NT, typename RD>
 __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
     float m = -INFINITY;
-    stream_rows<NT, 4, false>(P, P, nch,
-                              [&](const float x[8], const float *, int) { m = fmaxf(m, max8(x)); });
+    stream_rows<NT, depth_for<RD, 64>(), false>(
+        P, P, nch, [&](const float x[8], const float *, int) { m = fmaxf(m, max8(x)); });
     return block_max<NT>(m, fred);
 }
 
@@ -303,7 +313,7 @@ __device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, float c, Row
     }
     if (nch > NT) {
         const RD P1 = P.advanced(NT), Q1 = Q.advanced(NT);
-        stream_rows<NT, 4, true>(P1, Q1, nch - NT,
+        stream_rows<NT, depth_for<RD, 64>(), true>(P1, Q1, nch - NT,
                                  [&](const float (&ap)[8], const float (&aq)[8], int) {
                                      lp.consume(ap, c);
                                      lq.consume(aq, c);
