@@ -35,6 +35,18 @@ constexpr int kLmStride = kLmBK + 8;     // LDS row stride in bf16 elements
 constexpr int kLmGroupM = 16;            // row-blocks per group of the block order
 constexpr int kXcds = 8;
 
+template <int N> struct Stage { static constexpr int value = N; };
+
+// Buffer resource over rows r0.. of a [rows][d] bf16 matrix (byte range clamped
+// to 32 bits; the kernel's offsets within a tile stay below 128 rows).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *m, int r0, int rows,
+                                                            int d) {
+    const long long bytes = static_cast<long long>(rows - r0) * d * 2;
+    const int n = static_cast<int>(bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(m + static_cast<long long>(r0) * d), 0, n, 0x00020000);
+}
+
 struct LmArgs {
     const uint16_t *h;      // [R][d] bf16 bits
     const uint16_t *w;      // [V][d] bf16 bits
@@ -60,7 +72,8 @@ __device__ __forceinline__ void lm_block_coords(int pid, int nbm, int nbn, int *
     *bn = r / gsize;
 }
 
-__global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
+__global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_kernel(
+    LmArgs A) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][kLmBM * kLmStride];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][kLmBN * kLmStride];
     __shared__ float s_m[2][kLmBM];
@@ -73,16 +86,19 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
     const int row0 = bm * kLmBM, col0 = bn * kLmBN;
     const int R = A.R, d = A.d, V = A.V;
 
-    // a 128 x 64 bf16 tile is 1024 chunks of 16 bytes: 4 per thread
-    auto load_tile = [&](const uint16_t *base, int rows, int r0, int k0, uint4 (&buf)[4]) {
+    // a 128 x 64 bf16 tile is 1024 chunks of 16 bytes: 4 per thread.  The loads
+    // are buffer loads over the rows from the tile's first row to the end of the
+    // matrix: the hardware range check returns zeros past the end, so partial
+    // tiles need no branch in the loop.
+    const __amdgpu_buffer_rsrc_t rsA = tile_rsrc(A.h, row0, R, d);
+    const __amdgpu_buffer_rsrc_t rsB = tile_rsrc(A.w, col0, V, d);
+    auto load_tile = [&](const __amdgpu_buffer_rsrc_t &rs, int k0, uint4 (&buf)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = tid + kLmThreads * i;
             const int r = q >> 3, kc = q & 7;
-            const int gr = r0 + r;
-            buf[i] = gr < rows ? *reinterpret_cast<const uint4 *>(base + static_cast<long long>(gr) * d +
-                                                                   k0 + kc * 8)
-                               : make_uint4(0u, 0u, 0u, 0u);
+            buf[i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r * d + k0 + kc * 8) * 2, 0, 0));
         }
     };
     auto store_tile = [&](uint16_t *s, const uint4 (&buf)[4]) {
@@ -102,20 +118,21 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
 
     // three register stages: tile t lives in stage t % 3 from its load until it is
     // stored to LDS, two compute steps later, so each load has two steps to land
+    // (stage indices are compile-time constants, so the stages stay in registers)
     const int nk = d / kLmBK;
-    uint4 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4];
-    load_tile(A.h, R, row0, 0, a0);
-    load_tile(A.w, V, col0, 0, b0);
+    uint4 ra[3][4], rb[3][4];
+    load_tile(rsA, 0, ra[0]);
+    load_tile(rsB, 0, rb[0]);
     if (nk > 1) {
-        load_tile(A.h, R, row0, kLmBK, a1);
-        load_tile(A.w, V, col0, kLmBK, b1);
+        load_tile(rsA, kLmBK, ra[1]);
+        load_tile(rsB, kLmBK, rb[1]);
     }
     if (nk > 2) {
-        load_tile(A.h, R, row0, 2 * kLmBK, a2);
-        load_tile(A.w, V, col0, 2 * kLmBK, b2);
+        load_tile(rsA, 2 * kLmBK, ra[2]);
+        load_tile(rsB, 2 * kLmBK, rb[2]);
     }
-    store_tile(sA[0], a0);
-    store_tile(sB[0], b0);
+    store_tile(sA[0], ra[0]);
+    store_tile(sB[0], rb[0]);
     __syncthreads();
 
     auto compute = [&](int buf) {
@@ -138,24 +155,43 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(LmArgs A) {
                                                                        0, 0);
         }
     };
-    // step t: compute tile t, store tile t+1 (stage (t+1) % 3), load tile t+3 into
-    // stage t % 3
-    auto step = [&](int t, uint4 (&la)[4], uint4 (&lb)[4], uint4 (&sa)[4], uint4 (&sb)[4]) {
+    // step t (stage S = t % 3): compute tile t, store tile t+1 (stage S+1), load
+    // tile t+3 into stage S
+    auto step = [&](int t, auto stage) {
+        constexpr int S = decltype(stage)::value, S1 = (S + 1) % 3;
         compute(t & 1);
         if (t + 1 < nk) {
-            store_tile(sA[(t + 1) & 1], sa);
-            store_tile(sB[(t + 1) & 1], sb);
+            store_tile(sA[(t + 1) & 1], ra[S1]);
+            store_tile(sB[(t + 1) & 1], rb[S1]);
         }
         if (t + 3 < nk) {
-            load_tile(A.h, R, row0, (t + 3) * kLmBK, la);
-            load_tile(A.w, V, col0, (t + 3) * kLmBK, lb);
+            load_tile(rsA, (t + 3) * kLmBK, ra[S]);
+            load_tile(rsB, (t + 3) * kLmBK, rb[S]);
         }
         __syncthreads();
     };
-    for (int t = 0; t < nk; t += 3) {
-        step(t, a0, b0, a1, b1);
-        if (t + 1 < nk) step(t + 1, a1, b1, a2, b2);
-        if (t + 2 < nk) step(t + 2, a2, b2, a0, b0);
+    // the same step where the next tile and the load three ahead both exist:
+    // no condition, so the steps of the main loop form one scheduling region
+    // apart from their barriers
+    auto full_step = [&](int t, auto stage) {
+        constexpr int S = decltype(stage)::value, S1 = (S + 1) % 3;
+        compute(t & 1);
+        store_tile(sA[(t + 1) & 1], ra[S1]);
+        store_tile(sB[(t + 1) & 1], rb[S1]);
+        load_tile(rsA, (t + 3) * kLmBK, ra[S]);
+        load_tile(rsB, (t + 3) * kLmBK, rb[S]);
+        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 5 < nk; t += 3) {
+        full_step(t, Stage<0>{});
+        full_step(t + 1, Stage<1>{});
+        full_step(t + 2, Stage<2>{});
+    }
+    for (; t < nk; t += 3) {
+        step(t, Stage<0>{});
+        if (t + 1 < nk) step(t + 1, Stage<1>{});
+        if (t + 2 < nk) step(t + 2, Stage<2>{});
     }
 
     // epilogue: lane holds C[4*(lane/16) + i][lane%16] of each 16 x 16 tile
