@@ -136,8 +136,8 @@ template <> struct RowOf<uint16_t, false> { using type = RowBf16Scalar; };
 template <> struct RowOf<float, true> { using type = RowF32Vec; };
 template <> struct RowOf<float, false> { using type = RowF32Scalar; };
 
-// Chunks of a row kept in flight per lane for a given number of bytes: four
-// 16-byte bf16 chunks or two 32-byte fp32 chunks in 64 bytes.
+// Chunks of a row kept in flight per lane for a given number of bytes: two
+// 16-byte bf16 chunks or one 32-byte fp32 chunk in 32 bytes.
 template <typename RD, int BYTES>
 constexpr int depth_for() {
     return BYTES / static_cast<int>(sizeof(typename RD::Raw)) > 0

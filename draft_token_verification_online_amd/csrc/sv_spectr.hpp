@@ -93,7 +93,7 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MPc, fl
         s[4] += static_cast<double>(ta);
         s[5] += static_cast<double>(tb);
     };
-    stream_rows<NT, depth_for<RD, 64>(), true>(P, Q, nch,
+    stream_rows<NT, depth_for<RD, 32>(), true>(P, Q, nch,
                              [&](const float xp[8], const float xq[8], int) { chunk(xp, xq); });
     block_sum_n<NT, 6>(s, red);   // its barriers also publish hist[]
 #pragma unroll
@@ -127,7 +127,7 @@ __device__ void sweep_excess(const RD &P, const RD &Q, int nch, float MPc, float
         s[3] += static_cast<double>(pa);
         s[4] += static_cast<double>(pb);
     };
-    stream_rows<NT, depth_for<RD, 64>(), true>(P, Q, nch,
+    stream_rows<NT, depth_for<RD, 32>(), true>(P, Q, nch,
                              [&](const float xp[8], const float xq[8], int) { chunk(xp, xq); });
     block_sum_n<NT, 5>(s, red);
 #pragma unroll

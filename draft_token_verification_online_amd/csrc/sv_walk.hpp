@@ -142,13 +142,14 @@ struct SweepRows {
 };
 
 // Block-wide sum of omega over a row pair (or a single row when HAS_Q is false),
-// 64 bytes per row in flight per lane.
+// 32 bytes per row in flight per lane (more costs the walk registers it
+// spills elsewhere).
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
 __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
                              const int *H, int nH, double *red) {
     const HLanes hl = h_lanes<NT>(H, nH);
     double acc = 0.0;
-    stream_rows<NT, depth_for<RD, 64>(), HAS_Q>(P, Q, nch,
+    stream_rows<NT, depth_for<RD, 32>(), HAS_Q>(P, Q, nch,
                                                [&](const float xp[8], const float xq[8], int ch) {
         float w[8];
         omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
@@ -284,7 +285,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
 template <int NT, typename RD>
 __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
     float m = -INFINITY;
-    stream_rows<NT, depth_for<RD, 64>(), false>(
+    stream_rows<NT, depth_for<RD, 32>(), false>(
         P, P, nch, [&](const float x[8], const float *, int) { m = fmaxf(m, max8(x)); });
     return block_max<NT>(m, fred);
 }
@@ -313,7 +314,7 @@ __device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, float c, Row
     }
     if (nch > NT) {
         const RD P1 = P.advanced(NT), Q1 = Q.advanced(NT);
-        stream_rows<NT, depth_for<RD, 64>(), true>(P1, Q1, nch - NT,
+        stream_rows<NT, depth_for<RD, 32>(), true>(P1, Q1, nch - NT,
                                  [&](const float (&ap)[8], const float (&aq)[8], int) {
                                      lp.consume(ap, c);
                                      lq.consume(aq, c);
