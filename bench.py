@@ -128,9 +128,11 @@ def cpu_baseline(method, batch, w, target_cpu_s: float):
     reqs = list(range(m))
     host = synth.to_host(batch, reqs)
     t = time.perf_counter()
-    oracle.verify(method, host["target"], host["draft"], host["tokens"], host["temperature"],
-                  host["u_accept"], host["u_correct"], threads=threads)
+    res = oracle.verify(method, host["target"], host["draft"], host["tokens"],
+                        host["temperature"], host["u_accept"], host["u_correct"], threads=threads)
     wall = time.perf_counter() - t
+    # rows whose logits the method reads, as the oracle counts them (A_visit)
+    visit_rows = float(res["counters"][:m, 2].mean())
     return {
         "value": m * w.K * w.L / wall,
         "unit": "verified draft tokens/s",
@@ -138,7 +140,7 @@ def cpu_baseline(method, batch, w, target_cpu_s: float):
         "kind": "oracle",
         "sample": f"first {m} of {w.B} requests of the same batch ({m * w.K * w.L} draft "
                   f"tokens), fp64 C oracle, one request per thread, {wall:.2f} s wall",
-    }
+    }, {"requests": m, "oracle_rows_per_request": visit_rows}
 
 
 def cpu_baseline_draft(batch, u, w, target_cpu_s: float):
@@ -545,10 +547,23 @@ def main():
 
     traffic = read_traffic(name, method)
     cpu = None
+    a_visit = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(method, batch, w, args.cpu_seconds)
+        cpu, visit = cpu_baseline(method, batch, w, args.cpu_seconds)
         log(f"[bench] cpu baseline {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+        # the method's own floor: the rows it must read (oracle count on the sample, scaled
+        # to the batch) over the step time, next to the rows the GPU streamed for the same
+        # requests
+        m = visit["requests"]
+        gpu_rows = float(ver.out["rows_streamed"][:m].float().mean())
+        est = visit["oracle_rows_per_request"] * w.B * w.V * es
+        a_visit = {"sample_requests": m,
+                   "oracle_rows_per_request": visit["oracle_rows_per_request"],
+                   "gpu_rows_streamed_per_request": gpu_rows,
+                   "est_bytes_per_step": est,
+                   "est_GBps": est / (ms_per_step * 1e-3) / 1e9,
+                   "frac_of_peak": est / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
     line = {
         "metric": "verified draft tokens/s (B*K*L) + achieved HBM GB/s of verify kernel",
@@ -587,6 +602,7 @@ def main():
             "dense_equiv_GBps_per_step": dense / (ms_per_step * 1e-3) / 1e9,
             "mean_accept_len": float(ver.out["accept_len"].float().mean()),
             "invalid_requests": int(((flags & 2) != 0).sum()),
+            "a_visit": a_visit,
         },
     }
     print(json.dumps(line), flush=True)
