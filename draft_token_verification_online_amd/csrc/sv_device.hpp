@@ -22,20 +22,37 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float fast_exp2(float y) { return __builtin_amdgcn_exp2f(y); }
 
 // Base-2 exponents of temperature-scaled logits.  For a row with shift M and
-// c = log2(e)/T, every kernel forms y = x c - M c as fmaf(x, c, -Mc) with c
-// rounded once to fp32 (temp_scale) and Mc = M c rounded once to fp32
-// (shift_term; clamped at -FLT_MAX, so a -inf logit still gives 2^-inf = 0 when
-// the shift is -inf).  x c is exact inside the FMA, so y carries one rounding,
-// and the rounding of Mc is a constant of the row: it cancels from every
-// normalised probability because every reader of a row's statistics forms Mc
-// from the stored shift in the same way.  Rounding c to fp32 changes the
-// temperature by at most 2^-25 relative.  In fp64 the same exponent is
-// x (double)c - (double)Mc, with the product exact.
-__device__ __forceinline__ float temp_scale(float T) {
-    return static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+// c = log2(e)/T, every kernel forms the exponent of logit x as
+//   y = fmaf(x, c_lo, fmaf(x, c_hi, -K)),   K = shift_term(M) = M c_hi in fp32,
+// where c = c_hi + c_lo holds c to ~2^-48 (c_hi rounded down, c_lo > 0, so a
+// -inf logit still gives 2^-inf = 0).  Both products are exact inside their
+// FMAs, so y is x c - K with two roundings at the scale of y itself.  K is a
+// constant of the row (K clamped at -FLT_MAX): whatever its rounding, it
+// cancels from every normalised probability, because every reader of a row's
+// statistics forms K from the stored shift the same way.  In fp64 the same
+// exponent is x (c_hi + c_lo) - K.
+struct Scale {
+    float hi, lo;
+};
+__device__ __forceinline__ Scale temp_scale(float T) {
+    const double c = 1.4426950408889634 / static_cast<double>(T);
+    float hi = static_cast<float>(c);
+    if (static_cast<double>(hi) >= c) hi = nextafterf(hi, 0.0f);
+    float lo = static_cast<float>(c - static_cast<double>(hi));
+    if (!(lo > 0.0f)) {   // c within a rounding of a float: keep the sign of d * lo
+        hi = nextafterf(hi, 0.0f);
+        lo = static_cast<float>(c - static_cast<double>(hi));
+    }
+    return Scale{hi, lo};
 }
-__device__ __forceinline__ float shift_term(float M, float c) {
-    return fmaxf(M * c, -3.402823466e38f);
+__device__ __forceinline__ double scale64(const Scale &c) {
+    return static_cast<double>(c.hi) + static_cast<double>(c.lo);
+}
+__device__ __forceinline__ float shift_term(float M, const Scale &c) {
+    return fmaxf(M * c.hi, -3.402823466e38f);
+}
+__device__ __forceinline__ float expo(float x, const Scale &c, float K) {
+    return fmaf(x, c.lo, fmaf(x, c.hi, -K));
 }
 
 // Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7; raw(c) issues

@@ -15,8 +15,8 @@
 //      wave) and, per draft, the list slot of its node's row;
 //   2. draft_tiles_kernel -- grid-stride over (listed row, tile of 512 chunks),
 //      one 64-lane wave per tile (8 chunks per lane): the tile's maximum M_t and
-//      the sum of 2^(l c - M_t c) over it (the product M_t c rounded to fp32, as
-//      every kernel here forms it), by wave reductions only (no barrier).
+//      the sum of 2^(l c - K_t) over it (K_t = shift_term(M_t), the exponent
+//      convention of every kernel here), by wave reductions only (no barrier).
 //      Every row is streamed once, by as many waves as it has tiles, so a
 //      position with few nodes still fills the chip;
 //   3. draft_pick_kernel  -- one wave per draft: rescale the tile sums of its
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
             }
         }
         const float M = fmaxf(wave_max(m), -3.402823466e38f);
-        const float sc = temp_scale(A.temp[b]);
+        const Scale sc = temp_scale(A.temp[b]);
         const float Mc = shift_term(M, sc);
         double sum = 0.0;
 #pragma unroll
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
                 float x[8], e[8];
                 RD::unpack(r[i], x);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) e[q] = fast_exp2(fmaf(x[q], sc, -Mc));
+                for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mc));
                 sum += static_cast<double>(sum8(e));
             }
         }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     const int ntiles = A.ntiles;
     const float *tm = A.tmax + static_cast<long long>(slot) * ntiles;
     const double *ts = A.tsum + static_cast<long long>(slot) * ntiles;
-    const float sc = temp_scale(A.temp[b]);
+    const Scale sc = temp_scale(A.temp[b]);
 
     // row maximum over the tile shifts; each tile's weight in the row's scale
     float m = -INFINITY;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
         float x[8];
         P.load(c, x);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(fmaf(x[q], sc, -Mgc));
+        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
     };
     double cs = 0.0;
     int lastp = -1;

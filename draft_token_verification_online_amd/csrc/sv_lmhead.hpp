@@ -5,8 +5,8 @@
 // vocabulary projection W [V][d] (bf16).  Verification is a large share of a
 // speculative-decoding step (the performance study's page, section 1); here
 // the first thing the verifier does with a row -- its temperature-softmax
-// statistics (shift M, sum S = sum_v 2^(l_v c - M c), c = log2(e)/T, with c and
-// the product M c each rounded to fp32 as in every kernel here) -- is computed
+// statistics (shift M, sum S = sum_v 2^(l_v c - K), c = log2(e)/T, K the row
+// constant of the shift, in the exponent convention of every kernel here) -- is computed
 // while the row is still in registers, so the statistics pass over the logits
 // disappears.  The logits are still written (fp32): the walk's residual sweeps
 // and correction draws read whole rows.
@@ -213,11 +213,11 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-            const float sc = temp_scale(rok ? A.temp[row] : 1.0f);
+            const Scale sc = temp_scale(rok ? A.temp[row] : 1.0f);
             const float msc = shift_term(m, sc);
             float e = 0.0f;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) e += fast_exp2(fmaf(v[b], sc, -msc));
+            for (int b = 0; b < 4; ++b) e += fast_exp2(expo(v[b], sc, msc));
             double s = static_cast<double>(e);
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     if (tid < kLmBM) {
         const int row = row0 + tid;
         if (row < R) {
-            const float sc = temp_scale(A.temp[row]);
+            const Scale sc = temp_scale(A.temp[row]);
             const float m0 = s_m[0][tid], m1 = s_m[1][tid];
             const float M = fmaxf(m0, m1);
             const double Mc = static_cast<double>(shift_term(M, sc));
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void lm_stats_kernel(LmStatsArgs A) {
     float m = -INFINITY;
     for (int i = lane; i < A.nbn; i += kWave) m = fmaxf(m, pm[i]);
     m = wave_max(m);
-    const float sc = temp_scale(A.temp[r]);
+    const Scale sc = temp_scale(A.temp[r]);
     const double Mc = static_cast<double>(shift_term(m, sc));
     double s = 0.0;
     for (int i = lane; i < A.nbn; i += kWave)

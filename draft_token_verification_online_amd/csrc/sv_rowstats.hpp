@@ -1,8 +1,9 @@
 // sv_rowstats.hpp -- temperature-softmax statistics of node rows.
 //
 // For a row l of logits and the request's temperature T the statistics are a
-// shift M and S = sum_v 2^((l_v - M) * c) with c = log2(e) / T, so that
-//   p(v) = 2^((l_v - M) * c) / S   and   ln sum_v exp(l_v / T) = M / T + ln S.
+// shift M and S = sum_v 2^(l_v c - K) with c = log2(e) / T and the row
+// constant K = shift_term(M) (sv_device.hpp), so that
+//   p(v) = 2^(l_v c - K) / S   and   ln sum_v exp(l_v / T) = (K + log2 S) ln 2.
 // This is the temperature softmax the speculative-decoding verifiers apply to
 // the target and draft distributions (SpecTr-GBV page, section 2: the
 // acceptance probabilities and the residual are functions of them).
@@ -45,7 +46,7 @@ struct LaneSoftmax {
     float m;          // this lane's shift
     float mc;         // shift_term(m, c)
     double s;         // sum of 2^(x c - mc) over the lane's elements
-    __device__ __forceinline__ void init(float block_first_max, float c) {
+    __device__ __forceinline__ void init(float block_first_max, const Scale &c) {
         m = fmaxf(block_first_max, -3.402823466e38f);
         mc = shift_term(m, c);
         s = 0.0;
@@ -55,10 +56,10 @@ struct LaneSoftmax {
     // shift, and then (rarely) the lane moves its shift up to the chunk maximum,
     // rescaling its sum in fp64, and sums the chunk again.  A NaN sum fails the
     // test and makes S NaN.
-    __device__ __forceinline__ void consume(const float (&x)[8], float c) {
+    __device__ __forceinline__ void consume(const float (&x)[8], const Scale &c) {
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -mc));
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(expo(x[i], c, mc));
         float t = sum8(e);
         if (t > 0x1p64f) {
             const float cm = max8(x);
@@ -67,7 +68,7 @@ struct LaneSoftmax {
             m = cm;
             mc = cmc;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(x[i], c, -mc));
+            for (int i = 0; i < 8; ++i) e[i] = fast_exp2(expo(x[i], c, mc));
             t = sum8(e);
         }
         s += static_cast<double>(t);
@@ -76,7 +77,7 @@ struct LaneSoftmax {
 
 // Combine the lanes of a block into the row's (M, S); every thread gets it.
 template <int NT>
-__device__ __forceinline__ RowStat finish_row(const LaneSoftmax &ls, float c, float *fred,
+__device__ __forceinline__ RowStat finish_row(const LaneSoftmax &ls, const Scale &c, float *fred,
                                               double *red) {
     const float M = block_max<NT>(ls.m, fred);
     const double scaled =
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
             : ((static_cast<long long>(b) * K + k) * L + j) * V;
         const RD row(base + row_off, V);
 
-        const float c = temp_scale(A.temp[b]);
+        const Scale c = temp_scale(A.temp[b]);
 
         float x0[8];
         const bool have0 = tid < nch;

@@ -60,7 +60,7 @@ constexpr double kQuotientFormBeta = 0x1p-10;
 // D(1) = sum max(p - q, 0), and e_p, e_q over all tokens.
 template <int NT, typename RD>
 __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MPc, float MQc, float ap,
-                                float aq, float off, float scale, float c, unsigned *hist,
+                                float aq, float off, float scale, const Scale &c, unsigned *hist,
                                 double (&out)[6], double *red) {
     for (int i = threadIdx.x; i < 2 * kHistBins; i += NT) hist[i] = 0u;
     __syncthreads();
@@ -69,7 +69,7 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MPc, fl
         float cp = 0.0f, cq = 0.0f, cl = 0.0f, cd = 0.0f, ta = 0.0f, tb = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float yp = fmaf(xp[e], c, -MPc), yq = fmaf(xq[e], c, -MQc);
+            const float yp = expo(xp[e], c, MPc), yq = expo(xq[e], c, MQc);
             const float ep = fast_exp2(yp), eq = fast_exp2(yq);
             ta += ep;
             tb += eq;
@@ -105,14 +105,14 @@ __device__ void ratio_histogram(const RD &P, const RD &Q, int nch, float MPc, fl
 // p > rho q, e_q over p <= rho q, e_p over p > rho q, e_p over p <= rho q}.
 template <int NT, typename RD>
 __device__ void sweep_excess(const RD &P, const RD &Q, int nch, float MPc, float MQc, float ap,
-                             float bq, float c, double (&out)[5], double *red) {
+                             float bq, const Scale &c, double (&out)[5], double *red) {
     double s[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
     auto chunk = [&](const float xp[8], const float xq[8]) {
         float cd = 0.0f, qa = 0.0f, qb = 0.0f, pa = 0.0f, pb = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ep = fast_exp2(fmaf(xp[e], c, -MPc));
-            const float eq = fast_exp2(fmaf(xq[e], c, -MQc));
+            const float ep = fast_exp2(expo(xp[e], c, MPc));
+            const float eq = fast_exp2(expo(xq[e], c, MQc));
             const float d = fmaf(ap, ep, -(bq * eq));
             const bool pos = d > 0.0f;
             cd += pos ? d : 0.0f;
@@ -196,7 +196,7 @@ __device__ __forceinline__ double edge_gap(double e, double Pge, double Qge, dou
 // entries, red[] 6 * NT/64, br[] 4, ired[] NT/64.
 template <int NT, typename RD>
 __device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MPc, double SP, float MQc,
-                             double SQ, float c2, int n, double &rho_out,
+                             double SQ, const Scale &c2, int n, double &rho_out,
                              double &c_out, unsigned *hist, double *red, double *br,
                              int *ired) {
     static_assert(2 * NT == kHistBins, "two histogram bins per thread");

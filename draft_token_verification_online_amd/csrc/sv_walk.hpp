@@ -112,13 +112,13 @@ __device__ __forceinline__ HLanes h_lanes(const int *H, int nH) {
 // omega = a eP.  With FLOOR the lower bound is g eP (g >= 0) instead of 0.
 template <bool HAS_Q, bool FLOOR = false>
 __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MPc, float MQc,
-                                       float a, float bq, float g, float c, int ch, const int *H,
+                                       float a, float bq, float g, const Scale &c, int ch, const int *H,
                                        int nH, const HLanes &hl, float w[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float ep = fast_exp2(fmaf(xp[e], c, -MPc));
+        const float ep = fast_exp2(expo(xp[e], c, MPc));
         if (HAS_Q) {
-            const float eq = fast_exp2(fmaf(xq[e], c, -MQc));
+            const float eq = fast_exp2(expo(xq[e], c, MQc));
             w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), FLOOR ? g * ep : 0.0f);
         } else {
             w[e] = a * ep;
@@ -145,7 +145,7 @@ struct SweepRows {
 // 32 bytes per row in flight per lane (more costs the walk registers it
 // spills elsewhere).
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
-__device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
+__device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows &s, const Scale &c,
                              const int *H, int nH, double *red) {
     const HLanes hl = h_lanes<NT>(H, nH);
     double acc = 0.0;
@@ -166,7 +166,7 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
 // rounding leaves the threshold past every crossing, the draw is the last
 // token of positive weight, found from the last chunk with positive weight.
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
-__device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, float c,
+__device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, const Scale &c,
                           const int *H, int nH, double u, double *Z, double *tile, double *red,
                           double *red4, int *ired) {
     const HLanes hl = h_lanes<NT>(H, nH);
@@ -293,7 +293,7 @@ __device__ float sweep_rowmax(const RD &P, int nch, float *fred) {
 // Block-wide statistics of a node's target row and draft row; the walk's
 // fallback for a row that no launch of the statistics kernel streamed.
 template <int NT, typename RD>
-__device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, float c, RowStat &sp,
+__device__ void sweep_stats_pair(const RD &P, const RD &Q, int nch, const Scale &c, RowStat &sp,
                                  RowStat &sq, float *fred, double *red) {
     const int tid = threadIdx.x;
     float xp[8], xq[8];
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     const int nch = (V + kChunk - 1) / kChunk;
     const long long bKL = static_cast<long long>(b) * KL;
     const float T = A.temp[b];
-    const float sc = temp_scale(T);           // exponent scale of this request
-    const double scd = static_cast<double>(sc);
+    const Scale sc = temp_scale(T);           // exponent scale of this request
+    const double scd = scale64(sc);
     const E *tgt = static_cast<const E *>(A.tgt);
     const E *drf = static_cast<const E *>(A.drf);
     const RowStat *st = A.stats + static_cast<long long>(b) * K * RS;

@@ -64,6 +64,32 @@ SMALL = [
 ]
 
 
+# Row lengths at the edges of the streaming loops: the statistics kernel (256
+# threads) consumes a first tile of 256 chunks and then groups of 8 x 256 bf16
+# chunks (4 x 256 fp32); the walk's sweeps (512 threads) groups of 2 x 512 bf16
+# chunks; the inverse CDF groups of 4 tiles of 512 chunks.  V = 8 * chunks.
+STREAM_EDGES = [
+    ("v8184", 8184, torch.bfloat16),     # 1023 chunks: one short of a sweep group
+    ("v8192", 8192, torch.bfloat16),     # exactly one sweep group
+    ("v16384", 16384, torch.bfloat16),   # two sweep groups, one inverse-CDF group
+    ("v16392", 16392, torch.bfloat16),   # and one chunk more
+    ("v18424", 18424, torch.bfloat16),   # statistics: first tile + group minus one chunk
+    ("v18432", 18432, torch.bfloat16),   # first tile + exactly one group
+    ("v18440", 18440, torch.bfloat16),   # and one chunk more
+    ("v34816", 34816, torch.bfloat16),   # first tile + two groups
+    ("v10240_fp32", 10240, torch.float32),   # first tile + one fp32 group
+    ("v10248_fp32", 10248, torch.float32),
+]
+
+
+@pytest.mark.parametrize("name,V,dtype", STREAM_EDGES, ids=[s[0] for s in STREAM_EDGES])
+def test_streaming_group_edges(name, V, dtype):
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=16, V=V, dtype=dtype)
+    batch = pt.gpu_batch(ws, 3)
+    for method in ("multidraft", "spectr"):
+        _parity(method, batch, f"edges_{name}")
+
+
 @pytest.mark.parametrize("name,w,over", SMALL, ids=[s[0] for s in SMALL])
 def test_small_parity(name, w, over):
     ws = synth.scaled(w, **over)
