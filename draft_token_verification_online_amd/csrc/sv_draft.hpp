@@ -115,17 +115,20 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
         const int bk = A.list[slot];
         const int b = bk / K, k = bk % K;
         const RD P(base + ((static_cast<long long>(b) * K + k) * L + j) * V, V);
+        // all eight loads are issued before any is used (addresses clamped into
+        // the row; chunks past its end are loaded but not counted), so they are
+        // in flight together instead of one after another
         typename RD::Raw r[kPerLane];
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+            r[i] = P.raw(min(t * kDraftTileChunks + i * kWave + lane, nch - 1));
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const int c = t * kDraftTileChunks + i * kWave + lane;
-            if (c < nch) {
-                r[i] = P.raw(c);
-                float x[8];
-                RD::unpack(r[i], x);
-                m = fmaxf(m, max8(x));
-            }
+            float x[8];
+            RD::unpack(r[i], x);
+            if (c < nch) m = fmaxf(m, max8(x));
         }
         const float M = fmaxf(wave_max(m), -3.402823466e38f);
         const Scale sc = temp_scale(A.temp[b]);
@@ -230,16 +233,25 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     };
     double cs = 0.0;
     int lastp = -1;
+    {
+        // the lane's eight chunks are loaded before any is used (clamped
+        // addresses; chunks past the row are not counted)
+        typename RD::Raw r[kPerLane];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const int c = c1 + i;
-        if (c < nch) {
-            float e[8];
-            weights(c, e);
+        for (int i = 0; i < kPerLane; ++i) r[i] = P.raw(min(c1 + i, nch - 1));
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (e[q] > 0.0f) lastp = 8 * c + q;
-            cs += static_cast<double>(sum8(e));
+        for (int i = 0; i < kPerLane; ++i) {
+            const int c = c1 + i;
+            if (c < nch) {
+                float x[8], e[8];
+                RD::unpack(r[i], x);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (e[q] > 0.0f) lastp = 8 * c + q;
+                cs += static_cast<double>(sum8(e));
+            }
         }
     }
     const double cpre = wave_exclusive_scan(cs);
