@@ -107,21 +107,23 @@ __device__ __forceinline__ HLanes h_lanes(const int *H, int nH) {
     return h;
 }
 
-// omega(v) for the 8 elements of chunk ch: [v not in H] max(a eP - bq eQ, 0),
-// eP = 2^(x c - MPc) (MPc = shift_term of the row's shift); without a Q row,
-// omega = a eP.  With FLOOR the lower bound is g eP (g >= 0) instead of 0.
+// omega(v) / a for the 8 elements of chunk ch, where omega(v) = [v not in H]
+// max(a eP - bq eQ, 0), eP = 2^(x c - MPc) (MPc = shift_term of the row's
+// shift): computed as max(eP - r eQ, 0) with r = bq / a, so one FMA and one
+// max per element; the sweeps scale their sums by a once.  Without a Q row,
+// omega / a = eP.  With FLOOR the lower bound is g eP (g >= 0) instead of 0.
 template <bool HAS_Q, bool FLOOR = false>
 __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], float MPc, float MQc,
-                                       float a, float bq, float g, const Scale &c, int ch, const int *H,
+                                       float r, float g, const Scale &c, int ch, const int *H,
                                        int nH, const HLanes &hl, float w[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float ep = fast_exp2(expo(xp[e], c, MPc));
         if (HAS_Q) {
             const float eq = fast_exp2(expo(xq[e], c, MQc));
-            w[e] = fmaxf(fmaf(a, ep, -(bq * eq)), FLOOR ? g * ep : 0.0f);
+            w[e] = fmaxf(fmaf(-r, eq, ep), FLOOR ? g * ep : 0.0f);
         } else {
-            w[e] = a * ep;
+            w[e] = ep;
         }
     }
     if (ch == hl.c0 || ch == hl.c1 || hl.many) {
@@ -135,10 +137,18 @@ __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], flo
     }
 }
 
+// The residual a eP - bq eQ of a sweep, held as a (max(eP - r eQ, 0)) with
+// r = bq / a.
 struct SweepRows {
     float MPc, MQc;   // shift terms of the target and draft rows
-    float a, bq;
-    float g = 0.0f;   // floor coefficient (FLOOR sweeps only)
+    double a;         // > 0
+    float r;          // bq / a, >= 0, finite
+    float g = 0.0f;   // floor coefficient over a (FLOOR sweeps only)
+    // a = alpha / S_P, bq = beta / S_Q (S = the rows' sums)
+    __device__ void set(double alpha, double SP, double beta, double SQ) {
+        a = alpha / SP;
+        r = static_cast<float>(fmin(beta * SP / (alpha * SQ), 3.402823466e38));
+    }
 };
 
 // Block-wide sum of omega over a row pair (or a single row when HAS_Q is false),
@@ -152,10 +162,10 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
     stream_rows<NT, depth_for<RD, 32>(), HAS_Q>(P, Q, nch,
                                                [&](const float xp[8], const float xq[8], int ch) {
         float w[8];
-        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.r, s.g, c, ch, H, nH, hl, w);
         acc += static_cast<double>(sum8(w));
     });
-    return block_sum<NT>(acc, red);
+    return s.a * block_sum<NT>(acc, red);
 }
 
 // Block-wide inverse-CDF draw over omega in token-id order.  Returns y, or -1
@@ -205,7 +215,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
                 if (HAS_Q) rq[i] = Q.raw(cl);
             }
             if (ch < nch) {
-                omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
+                omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.r, s.g, c, ch, H, nH, hl, w);
                 const float t = sum8(w);
                 cs[i] = static_cast<double>(t);
                 if (t > 0.0f) lastc = ch;
@@ -219,9 +229,11 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
         }
     }
     lastc = block_max_int<NT>(lastc, ired);   // its barriers publish tile[]
+    // the tiles hold omega / a: the threshold u z and every comparison with it
+    // are taken at that scale
     double z = 0.0;
     for (int t = 0; t < ntile; ++t) z += tile[t];
-    *Z = z;
+    *Z = s.a * z;
     if (!(z > 0.0) || !isfinite(z)) return -1;
     // the last token of positive weight (block-uniform call)
     auto last_positive = [&]() {
@@ -230,7 +242,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
             float xp[8], xq[8], w[8];
             P.load(lastc, xp);
             if (HAS_Q) Q.load(lastc, xq);
-            omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, lastc, H, nH, hl, w);
+            omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.r, s.g, c, lastc, H, nH, hl, w);
             int last = kChunk * lastc;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -258,7 +270,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
         float xp[8], xq[8];
         P.load(ch, xp);
         if (HAS_Q) Q.load(ch, xq);
-        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.a, s.bq, s.g, c, ch, H, nH, hl, w);
+        omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.r, s.g, c, ch, H, nH, hl, w);
         cs = static_cast<double>(sum8(w));
     }
     const double pre = base + block_exclusive_scan<NT>(cs, red);
@@ -491,8 +503,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         SweepRows sr;
         sr.MPc = shift_term(s_M[c * RS + j], sc);
         sr.MQc = shift_term(s_M[c * RS + L1 + j], sc);
-        sr.a = static_cast<float>(alpha / s_S[c * RS + j]);
-        sr.bq = static_cast<float>(beta / s_S[c * RS + L1 + j]);
+        sr.set(alpha, s_S[c * RS + j], beta, s_S[c * RS + L1 + j]);
         return sr;
     };
 
@@ -733,8 +744,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             SweepRows sr;
             sr.MPc = shift_term(M, sc);
             sr.MQc = 0.0f;
-            sr.a = 1.0f;
-            sr.bq = 0.0f;
+            sr.a = 1.0;
+            sr.r = 0.0f;
             double Z;
             y = (M > -INFINITY && M < INFINITY)
                     ? sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
@@ -750,7 +761,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             if constexpr (SPECTR) {
                 // max(p - c q, (1 - c/rho) p): the residual after n tries
                 sr = node_sweep(cn, tau, 1.0, cc);
-                sr.g = static_cast<float>(fmax(1.0 - cc / rho, 0.0) / s_S[cn * RS + tau]);
+                sr.g = static_cast<float>(fmax(1.0 - cc / rho, 0.0));   // over a = 1 / S_P
                 y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
                                                    s_red4, s_ired);
             } else {
@@ -760,8 +771,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             Zp = Z;
             if (y < 0) {
                 flags |= kFlagDegenerate;
-                sr.a = static_cast<float>(1.0 / s_S[cn * RS + tau]);
-                sr.bq = 0.0f;
+                sr.a = 1.0 / s_S[cn * RS + tau];
+                sr.r = 0.0f;
                 y = sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
                                               s_red4, s_ired);
                 Zp = Z;
