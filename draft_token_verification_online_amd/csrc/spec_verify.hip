@@ -102,6 +102,13 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     sa.L = in->L;
     sa.V = in->V;
     sa.mode = diagnostics ? sv::kSelectAllNodes : sv::kSelectFirstVisit;
+    // First-visit depth.  The block walk examines a draft's whole sub-block at
+    // once, so it streams the chains of every draft with a new first token.
+    // SpecTr stops at its first rejected position and reaches position j only
+    // through acceptances at every position before it: with several drafts it
+    // streams the root pair and the position-1 node of every first token, and
+    // a walk that gets further stops and lists the rest (the second round).
+    sa.depth = (method == sv::kMethodSpecTr && two_round) ? (in->L < 2 ? in->L : 2) : in->L;
     auto grid_for = [&](int rows_per_draft) {
         const long long n = static_cast<long long>(in->B) * in->K * rows_per_draft;
         return static_cast<unsigned>(n < kMaxStatsGrid ? n : kMaxStatsGrid);
@@ -121,6 +128,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.V = in->V;
     wa.method = method;
     wa.all_nodes = (diagnostics || given) ? 1 : 0;
+    wa.fv_depth = sa.depth;
     wa.stats_given = given ? 1 : 0;
     wa.round = 1;
     wa.two_round = two_round ? 1 : 0;
@@ -141,7 +149,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
     if (!given) {
         hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>),
-                           dim3(grid_for(2 * in->L + (diagnostics ? 1 : 0))), dim3(kStatsThreads),
+                           dim3(grid_for(diagnostics ? 2 * in->L + 1 : 2 * sa.depth)), dim3(kStatsThreads),
                            0, stream, sa);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }

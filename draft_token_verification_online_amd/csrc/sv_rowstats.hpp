@@ -107,9 +107,10 @@ struct StatsArgs {
     unsigned *list_count;   // their number; the first-visit launch resets it to 0
     int B, K, L, V;
     int mode;               // kSelectAllNodes, kSelectFirstVisit or kSelectListed
+    int depth;              // first-visit rows are at positions j < depth (1 <= depth <= L)
 };
 
-constexpr int kSelectFirstVisit = 0;   // root pair + rows 1..L-1 of drafts with a new first token
+constexpr int kSelectFirstVisit = 0;   // root pair + rows 1..depth-1 of drafts with a new first token
 constexpr int kSelectAllNodes = 1;     // every node row, target rows at position L included
 constexpr int kSelectListed = 2;       // node rows the walk listed after an acceptance
 constexpr int kStreamBytes = 128;      // bytes of a row in flight per lane (8 bf16 chunks)
@@ -121,7 +122,10 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
 
     const int tid = threadIdx.x;
     const int K = A.K, L = A.L, V = A.V;
-    const int NR = 2 * L + (A.mode == kSelectAllNodes ? 1 : 0);
+    // row slots per (request, draft): target rows then draft rows at positions
+    // 0..D-1, and with every node row the target row at position L
+    const int D = A.mode == kSelectFirstVisit ? A.depth : L;
+    const int NR = 2 * D + (A.mode == kSelectAllNodes ? 1 : 0);
     const long long nrows = A.mode == kSelectListed
                                 ? static_cast<long long>(*A.list_count)
                                 : static_cast<long long>(A.B) * K * NR;
@@ -142,14 +146,14 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
             const long long bk = r / NR;
             k = static_cast<int>(bk % K);
             b = static_cast<int>(bk / K);
-            if (slot < L) { is_target = 1; j = slot; row_index = j; }
-            else if (slot < 2 * L) { is_target = 0; j = slot - L; row_index = L + 1 + j; }
+            if (slot < D) { is_target = 1; j = slot; row_index = j; }
+            else if (slot < 2 * D) { is_target = 0; j = slot - D; row_index = L + 1 + j; }
             else { is_target = 1; j = L; row_index = L; }
         }
 
         // which rows: every node row (lowest-index draft per prefix X[0..j-1]);
-        // first-visit rows (the root pair; rows j >= 1 of drafts whose first token
-        // is new among drafts 0..k); or the node rows the walk listed
+        // first-visit rows (the root pair; rows 1 <= j < depth of drafts whose
+        // first token is new among drafts 0..k); or the node rows the walk listed
         if (A.mode != kSelectListed && k > 0) {
             int skip = 0;
             if (j == 0) {

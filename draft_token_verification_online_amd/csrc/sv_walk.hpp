@@ -63,6 +63,7 @@ struct WalkArgs {
     int B, K, L, V;
     int method;             // kMethodToken, kMethodBlockWalk or kMethodSpecTr
     int all_nodes;          // statistics of every node row are present (diagnostics, or given)
+    int fv_depth;           // otherwise the first-visit rows are at positions j < fv_depth
     int stats_given;        // they came from the caller: no row was streamed here
     int round;              // 1, or 2 to resume the walks the first round suspended
     int two_round;          // a second round follows: the first may suspend
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         for (int cc = 0; cc < k; ++cc) first &= (s_x[cc * L] != s_x[k * L]);
         int have = 0;
         if (j < L && c == k) {
-            const int fv = A.all_nodes || (j == 0 && k == 0) || (j > 0 && first);
+            const int fv = A.all_nodes || (j == 0 && k == 0) || (j > 0 && j < A.fv_depth && first);
             const int nd = A.round == 2 && need[k * L + j];
             have = fv || nd;
             streamed += fv ? (A.round == 1 ? 2 : 0) : (nd ? 2 : 0);
