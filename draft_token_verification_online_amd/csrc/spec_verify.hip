@@ -56,9 +56,12 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
 }
 
 // Workspace: row statistics | walk states | node rows flagged for the second
-// round (bytes, then the same rows as a list) | list length.
+// round (bytes, then the same rows as a list) | list length | node lists of
+// the walk (K >= 3 only: a node sees a second mass sweep only with three or
+// more drafts).
 struct Layout {
-    size_t stats, state, need, list, count, total;
+    size_t stats, state, need, list, count, nodes, total;
+    bool has_nodes;
 };
 
 Layout layout(int32_t B, int32_t K, int32_t L) {
@@ -69,7 +72,11 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.need = l.state + align_up(static_cast<size_t>(B) * sizeof(sv::WalkState), 256);
     l.list = l.need + align_up(bkl, 256);
     l.count = l.list + align_up(2 * bkl * sizeof(sv::RowRef), 256);
-    l.total = l.count + 256;
+    l.nodes = l.count + 256;
+    l.has_nodes = K >= 3;
+    l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
+                                           static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
+                                     : 0);
     return l;
 }
 
@@ -136,6 +143,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.need = reinterpret_cast<unsigned char *>(ws + lay.need);
     wa.list = reinterpret_cast<sv::RowRef *>(ws + lay.list);
     wa.list_count = sa.list_count;
+    wa.nodes = (lay.has_nodes && method == sv::kMethodBlockWalk) ? ws + lay.nodes : nullptr;
     wa.accept_len = out->accept_len;
     wa.draft_index = out->draft_index;
     wa.correction = out->correction;

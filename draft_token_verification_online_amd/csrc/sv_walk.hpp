@@ -51,6 +51,10 @@ constexpr int kMethodBlockWalk = 1;
 constexpr int kMethodSpecTr = 2;
 constexpr int kFlagDegenerate = 1;
 constexpr int kFlagInvalid = 2;
+// Node lists: entries per wave, and the cutoff 2^-kListCut below which a
+// token's residual weight omega(v) / alpha leaves the list.
+constexpr int kWaveList = 2048;
+constexpr int kListCut = 50;
 
 struct WalkArgs {
     const void *tgt;        // [B][K][L+1][V]
@@ -71,6 +75,7 @@ struct WalkArgs {
     unsigned char *need;    // [B][K][L]: node rows flagged for the second round
     RowRef *list;           // the same rows as a list for the statistics kernel
     unsigned *list_count;
+    void *nodes;            // [B] node lists (node_list_bytes each), or null
     int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
     float *row_lse, *accept_prob, *resid_mass;
 };
@@ -108,6 +113,19 @@ __device__ __forceinline__ HLanes h_lanes(const int *H, int nH) {
     return h;
 }
 
+// Zero the weights of chunk ch's tokens that are in H.
+__device__ __forceinline__ void h_zero8(int ch, const int *H, int nH, const HLanes &hl, float w[8]) {
+    if (ch == hl.c0 || ch == hl.c1 || hl.many) {
+        for (int i = 0; i < nH; ++i) {
+            const unsigned off = static_cast<unsigned>(H[i] - kChunk * ch);
+            if (off < 8u) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = (off == static_cast<unsigned>(e)) ? 0.0f : w[e];
+            }
+        }
+    }
+}
+
 // omega(v) / a for the 8 elements of chunk ch, where omega(v) = [v not in H]
 // max(a eP - bq eQ, 0), eP = 2^(x c - MPc) (MPc = shift_term of the row's
 // shift): computed as max(eP - r eQ, 0) with r = bq / a, so one FMA and one
@@ -127,15 +145,7 @@ __device__ __forceinline__ void omega8(const float xp[8], const float xq[8], flo
             w[e] = ep;
         }
     }
-    if (ch == hl.c0 || ch == hl.c1 || hl.many) {
-        for (int i = 0; i < nH; ++i) {
-            const unsigned off = static_cast<unsigned>(H[i] - kChunk * ch);
-            if (off < 8u) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = (off == static_cast<unsigned>(e)) ? 0.0f : w[e];
-            }
-        }
-    }
+    h_zero8(ch, H, nH, hl, w);
 }
 
 // The residual a eP - bq eQ of a sweep, held as a (max(eP - r eQ, 0)) with
@@ -166,6 +176,164 @@ __device__ double sweep_mass(const RD &P, const RD &Q, int nch, const SweepRows 
         omega8<HAS_Q, FLOOR>(xp, xq, s.MPc, s.MQc, s.r, s.g, c, ch, H, nH, hl, w);
         acc += static_cast<double>(sum8(w));
     });
+    return s.a * block_sum<NT>(acc, red);
+}
+
+// Node list: the tokens of one node whose residual weight can matter to a
+// later mass sweep at that node.  While the walk stays at a node, alpha is
+// fixed, beta only grows and H only gains tokens, so omega(v) = [v not in H]
+// max(alpha p(v) - beta q(v), 0) never grows: a token whose weight is below
+// alpha 2^-kListCut at the sweep that builds the list stays below it, and the
+// weight the list leaves out (summed exactly by that sweep) bounds what any
+// later sweep misses.  Each wave keeps its own list of up to kWaveList entries
+// (token, eP, eQ: the sweep's own fp32 exponentials) in token order, compacted
+// with wave ballots so the stores and the later loads are contiguous.
+template <int NT>
+struct NodeList {
+    int *idx;
+    float *ep, *eq;
+    __device__ NodeList(void *base, long long b) {
+        constexpr long long n = static_cast<long long>(NT / kWave) * kWaveList;
+        char *p = static_cast<char *>(base) + b * (3 * n * 4);
+        const long long w = static_cast<long long>(threadIdx.x / kWave) * kWaveList;
+        idx = reinterpret_cast<int *>(p) + w;
+        ep = reinterpret_cast<float *>(p + n * 4) + w;
+        eq = reinterpret_cast<float *>(p + 2 * n * 4) + w;
+    }
+};
+
+template <int NT>
+constexpr long long node_list_bytes() {
+    return 3LL * (NT / kWave) * kWaveList * 4;
+}
+
+// Rank of this lane among the lanes of the wave set in m.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<unsigned>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0u)));
+}
+
+// sweep_mass over a row pair that also writes the node list: a token enters
+// it when omega / a > keep (keep = S_P 2^-kListCut, i.e. omega > alpha
+// 2^-kListCut).  Returns the mass; *cnt is the entry count of this lane's wave,
+// *out the weight left out (omega units), *overflow whether any wave ran out
+// of room.  Every lane runs the same tiles of NT chunks (chunk t NT + tid,
+// masked past the row), so the ballots see the whole wave and each wave's list
+// is in token order; two tiles of each row stay in flight per lane.  A wave
+// whose list is full stops compacting (flat rows keep most tokens) and sweeps
+// on as sweep_mass does.
+template <int NT, typename RD>
+__device__ double sweep_mass_build(const RD &P, const RD &Q, int nch, const SweepRows &s,
+                                   const Scale &c, const int *H, int nH, float keep,
+                                   const NodeList<NT> &nl, int *cnt, double *out, bool *overflow,
+                                   double *red2) {
+    const HLanes hl = h_lanes<NT>(H, nH);
+    const int tid = threadIdx.x;
+    const int ntile = (nch + NT - 1) / NT;
+    double acc = 0.0, exc = 0.0;
+    int n = 0;   // entries of this wave so far (wave-uniform)
+    typename RD::Raw rp[2], rq[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int cl = min(i * NT + tid, nch - 1);
+        rp[i] = P.raw(cl);
+        rq[i] = Q.raw(cl);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int t0 = 0; t0 < ntile; t0 += 2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ch = (t0 + i) * NT + tid;
+            float xp[8], xq[8];
+            RD::unpack(rp[i], xp);
+            RD::unpack(rq[i], xq);
+            const int cl = min(ch + 2 * NT, nch - 1);   // refill with the tile two on
+            rp[i] = P.raw(cl);
+            rq[i] = Q.raw(cl);
+            if (t0 + i >= ntile) break;                 // wave-uniform
+            const bool valid = ch < nch;
+            float ep[8], eq[8], w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ep[e] = fast_exp2(expo(xp[e], c, s.MPc));
+                eq[e] = fast_exp2(expo(xq[e], c, s.MQc));
+                w[e] = valid ? fmaxf(fmaf(-s.r, eq[e], ep[e]), 0.0f) : 0.0f;
+            }
+            h_zero8(ch, H, nH, hl, w);
+            acc += static_cast<double>(sum8(w));
+            if (n > kWaveList) continue;   // this wave's list is full: a plain sweep from here
+            float ex = 0.0f;
+            unsigned long long any = 0;
+            unsigned long long m[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool k = w[e] > keep;
+                if (!k) ex += w[e];
+                m[e] = __ballot(k);
+                any |= m[e];
+            }
+            exc += static_cast<double>(ex);
+            if (any) {
+                // slot of (lane, e): the wave's entries so far, the kept tokens
+                // of lower lanes in this tile, then this lane's kept tokens before e
+                int slot = n, tot = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    slot += lanes_below(m[e]);
+                    tot += __popcll(m[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (w[e] > keep) {
+                        if (slot < kWaveList) {
+                            nl.idx[slot] = kChunk * ch + e;
+                            nl.ep[slot] = ep[e];
+                            nl.eq[slot] = eq[e];
+                        }
+                        ++slot;
+                    }
+                }
+                n += tot;
+            }
+        }
+    }
+    *cnt = n;
+    *overflow = __syncthreads_or(n > kWaveList) != 0;
+    double v[2] = {acc, exc};
+    block_sum_n<NT, 2>(v, red2);
+    *out = s.a * v[1];
+    return s.a * v[0];
+}
+
+// The mass of the residual over a node list (cnt entries in this lane's wave;
+// lane l takes entries l, l + 64, ...).  A lane's loads for eight entries go
+// out before any is used: a typical list (a few hundred entries per wave) is
+// then one round trip.
+template <int NT>
+__device__ double sweep_mass_list(const NodeList<NT> &nl, int cnt, const SweepRows &s,
+                                  const int *H, int nH, double *red) {
+    constexpr int U = 8;
+    const int lane = threadIdx.x & (kWave - 1);
+    double acc = 0.0;
+    for (int i0 = 0; i0 < cnt; i0 += U * kWave) {
+        float p[U], q[U];
+        int x[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int i = i0 + j * kWave + lane;
+            const int ic = i < cnt ? i : cnt - 1;
+            p[j] = nl.ep[ic];
+            q[j] = nl.eq[ic];
+            x[j] = nl.idx[ic];
+            if (i >= cnt) p[j] = q[j] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float v = fmaxf(fmaf(-s.r, q[j], p[j]), 0.0f);
+            for (int h = 0; h < nH; ++h) v = (H[h] == x[j]) ? 0.0f : v;
+            acc += static_cast<double>(v);
+        }
+    }
     return s.a * block_sum<NT>(acc, red);
 }
 
@@ -342,6 +510,7 @@ struct WalkState {
     int status;             // kStateDone or kStateSuspended
     int k_next;             // draft to examine on resumption
     int tau, own, kstar, nH, flags, rows;
+    int list_tries;         // node lists the request may still build
     double alpha, beta, N;
     int H[kMaxK];
 };
@@ -500,6 +669,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                static_cast<double>(shift_term(s_M[c * RS + L1 + j], sc)) -
                log2(s_S[c * RS + L1 + j]);
     };
+    // Whether node (c, j)'s list is likely to fit: of NT tokens spread evenly
+    // over the target row, at most a tenth have p >= 2^-kListCut (a list keeps
+    // a subset of those).  Flat rows (high temperature) keep most tokens and
+    // would only fill their lists and overflow.
+    auto sparse_row = [&](int c, int j) {
+        const float lim = static_cast<float>(log2(s_S[c * RS + j]) - kListCut);
+        const int v = static_cast<int>(static_cast<long long>(tid) * V / NT);
+        const float y = expo(RD(trow(c, j), V).at(v), sc, shift_term(s_M[c * RS + j], sc));
+        return __syncthreads_count(y >= lim) <= NT / 10;
+    };
     auto node_sweep = [&](int c, int j, double alpha, double beta) {
         SweepRows sr;
         sr.MPc = shift_term(s_M[c * RS + j], sc);
@@ -512,7 +691,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     double Zp = NAN;
     double rho = 1.0, cc = 1.0;   // SpecTr: scaling factor and tries at the last node
     bool suspend = false;
-    int own = 0, nH = 0, k0 = 0;
+    int own = 0, nH = 0, k0 = 0, list_tries = 1;
     double alpha = 1.0, beta = 0.0, N = 1.0;
     if (A.round == 2) {
         k0 = ws->k_next;
@@ -522,6 +701,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         nH = ws->nH;
         flags = ws->flags;
         rows = ws->rows;
+        list_tries = ws->list_tries;
         alpha = ws->alpha;
         beta = ws->beta;
         N = ws->N;
@@ -591,6 +771,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             beta = 1.0;   // token-level residual max(p - q, 0)
         } else {
             if (A.round == 1) tau = 0;
+            // node list of the current node (list_node: the node it serves, -1 none);
+            // list_built: the node a list was last built at; a request stops
+            // building (list_tries, kept across rounds) once its sampled row
+            // looked flat or a list overflowed: its rows share one temperature
+            const NodeList<NT> nl(A.nodes, b);
+            int lcnt = 0, list_node = -1, list_built = -1;
+            double list_out = 0.0;
             for (int k = k0; k < K && tau < L; ++k) {
                 int match = 1;
                 for (int t = 0; t < tau; ++t) match &= (s_x[k * L + t] == s_x[own * L + t]);
@@ -668,15 +855,44 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     // itself (and falls back to the node's target on zero mass, as the
                     // degenerate reset below would).
                     int later = 0;
-                    for (int k2 = k + 1; k2 < K && !later; ++k2) {
+                    for (int k2 = k + 1; k2 < K && later < 2; ++k2) {
                         int m2 = 1;
                         for (int t = 0; t < tau; ++t) m2 &= (s_x[k2 * L + t] == s_x[own * L + t]);
-                        later = m2;
+                        later += m2;
                     }
                     if (later) {
                         const SweepRows sr = node_sweep(cn, tau, alpha, beta);
-                        const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
-                        N = sweep_mass<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, s_red);
+                        const int node = cn * L1 + tau;
+                        bool have = false;
+                        if (list_node == node) {
+                            // the list's left-out weight must stay below 2^-30 of the mass
+                            const double Nl = sweep_mass_list<NT>(nl, lcnt, sr, s_H, nH, s_red);
+                            have = list_out <= 0x1p-30 * Nl;
+                            if (have) N = Nl;
+                            else list_node = -1;
+                        }
+                        if (!have) {
+                            const RD P(trow(cn, tau), V), Q(drow(cn, tau), V);
+                            bool build = A.nodes && later > 1 && list_tries > 0 && node != list_built;
+                            if (build && !sparse_row(cn, tau)) {
+                                build = false;
+                                list_tries = 0;   // the request's rows share a temperature
+                            }
+                            if (build) {
+                                // two or more drafts still to come at this node: keep a list
+                                // of the tokens that can still carry weight
+                                const float keep =
+                                    static_cast<float>(ldexp(s_S[cn * RS + tau], -kListCut));
+                                bool ovf;
+                                N = sweep_mass_build<NT, RD>(P, Q, nch, sr, sc, s_H, nH, keep, nl,
+                                                             &lcnt, &list_out, &ovf, s_red4);
+                                list_built = node;
+                                if (ovf) --list_tries;
+                                else list_node = node;
+                            } else {
+                                N = sweep_mass<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, s_red);
+                            }
+                        }
                     } else {
                         mass_known = false;
                     }
@@ -687,6 +903,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     beta = 0.0;
                     N = 1.0;
                     nH = 0;
+                    list_node = -1;   // beta fell: the list's bound no longer holds
+                    list_built = -1;
                 }
             }
         }
@@ -727,6 +945,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             ws->nH = nH;
             ws->flags = flags;
             ws->rows = rows;
+            ws->list_tries = list_tries;
             ws->alpha = alpha;
             ws->beta = beta;
             ws->N = N;

@@ -179,7 +179,11 @@ typedef struct sv_launch {
                               diagnostics; otherwise [2], [3], [4] coincide) */
 } sv_launch;
 
-/* Workspace bytes a call with these sizes needs (0 on invalid sizes). */
+/* Workspace bytes a call with these sizes needs (0 on invalid sizes): row
+ * statistics (16 bytes per node row), one saved walk state per request, the
+ * rows listed for the second round and, for K >= 3, one node list per request
+ * (196 608 bytes: the tokens a node's repeated residual-mass sweeps still need,
+ * so those sweeps read a few thousand entries instead of two rows of V). */
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
 
 /* Token-level speculative sampling (K must be 1). */
