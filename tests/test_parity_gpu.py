@@ -219,6 +219,42 @@ def test_negative_infinity_entries():
         _parity(method, batch, "neg_inf_entries")
 
 
+def _root_rejections(flat, seed):
+    """K = 8 drafts whose first tokens (three distinct ones) have p ~ e^-100 and
+    a large q at the root, so every draft is rejected there and each rejection but the last
+    is followed by a residual-mass sweep of the root pair (duplicates included).
+    The root's target row is -100 at the tokens the walk samples to judge
+    whether a node list fits (every 128th token at V = 65536), so the row
+    samples as sparse either way.  flat: every other logit ~ N(0, 0.5^2) at
+    T = 1, so about half the tokens keep residual weight and every wave's list
+    overflows (the walk falls back to full sweeps); otherwise logits ~ N(0, 5^2)
+    at T = 0.4 and the lists are used."""
+    B, K, L, V = 16, 8, 2, 65536
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    sig, T = (0.5, 1.0) if flat else (5.0, 0.4)
+    tgt = torch.randn((B, K, L + 1, V), generator=g, device="cuda") * sig
+    tgt[..., ::128] = -100.0
+    drf = tgt[:, :, :L] + torch.randn((B, K, L, V), generator=g, device="cuda")
+    drf[..., ::128] = 5.0 if flat else 30.0     # q(x) >> p(x) at the drafted first tokens
+    firsts = 128 * torch.randint(0, V // 128, (B, 3), generator=g, device="cuda")
+    pick = torch.randint(0, 3, (B, K), generator=g, device="cuda")
+    tokens = torch.randint(0, V, (B, K, L), generator=g, device="cuda", dtype=torch.int32)
+    tokens[:, :, 0] = torch.gather(firsts, 1, pick).to(torch.int32)
+    return {"target": tgt.to(torch.bfloat16).contiguous(),
+            "draft": drf.to(torch.bfloat16).contiguous(), "tokens": tokens.contiguous(),
+            "temperature": torch.full((B,), T, device="cuda"),
+            "u_accept": torch.rand((B, K, L), generator=g, device="cuda"),
+            "u_correct": torch.rand((B,), generator=g, device="cuda")}
+
+
+@pytest.mark.parametrize("flat", [False, True], ids=["lists_used", "lists_overflow"])
+def test_repeated_root_rejections(flat):
+    batch = _root_rejections(flat, 11)
+    rep, out, ref = _parity("multidraft", batch, f"root_rejections_flat{int(flat)}")
+    assert (out["accept_len"] == 0).all(), "every draft is rejected at the root"
+
+
 def test_misaligned_rows_take_the_scalar_path():
     ws = synth.scaled(W["gbv_bf16_b64_k1_l5_v32000"], B=16, V=2048)
     batch = pt.gpu_batch(ws, 11)
