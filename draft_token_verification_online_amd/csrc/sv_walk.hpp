@@ -337,6 +337,137 @@ __device__ double sweep_mass_list(const NodeList<NT> &nl, int cnt, const SweepRo
     return s.a * block_sum<NT>(acc, red);
 }
 
+// Node-list draws cover rows of at most this many tiles of NT chunks.
+constexpr int kListTiles = 64;
+
+// Inverse-CDF draw over a node list, in token-id order: y = min{v : C_v > u Z}
+// over the listed tokens, or the last listed token of positive weight when
+// rounding leaves no crossing.  Token order across the lists is tile-major,
+// then wave (wave w holds chunks 64 w .. 64 w + 63 of each tile), then the
+// order inside a wave's list.  Each wave sums its entries per tile into
+// seg[t NW + w] (runs of one tile are contiguous in its list, which also gives
+// their first entry, segstart); wave 0 scans the segments for the crossing; the
+// wave that owns it rescans that run.  Returns -1 when Z is not a positive
+// finite number; Z (omega units) in *Z.
+template <int NT>
+__device__ int sweep_icdf_list(const NodeList<NT> &nl, int cnt, const SweepRows &s, const int *H,
+                               int nH, double u, int ntile, double *Z, double *seg, int *segstart,
+                               int *ired, double *red) {
+    constexpr int NW = NT / kWave;
+    constexpr int kTileTokens = kChunk * NT;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    auto entry = [&](int i, int &x) {   // omega / a of entry i (0 for tokens in H)
+        x = nl.idx[i];
+        float f = fmaxf(fmaf(-s.r, nl.eq[i], nl.ep[i]), 0.0f);
+        for (int h = 0; h < nH; ++h) f = (H[h] == x) ? 0.0f : f;
+        return static_cast<double>(f);
+    };
+    for (int t = lane; t < ntile; t += kWave) {
+        seg[t * NW + w] = 0.0;
+        segstart[t * NW + w] = -1;
+    }
+    int tcarry = -1;   // tile of the previous batch's last entry
+    for (int i0 = 0; i0 < cnt; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool valid = i < cnt;
+        int x = 0, t = 0x7fffffff;
+        double v = 0.0;
+        if (valid) {
+            v = entry(i, x);
+            t = x / kTileTokens;
+        }
+        int tp = __shfl_up(t, 1, kWave);
+        if (lane == 0) tp = tcarry;
+        if (valid && t != tp) segstart[t * NW + w] = i;   // first entry of tile t
+        // first lane of this lane's run inside the batch
+        int f = (valid && (lane == 0 || t != tp)) ? lane : -1;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int g = __shfl_up(f, o, kWave);
+            if (lane >= o) f = max(f, g);
+        }
+        const double inc = wave_exclusive_scan(v) + v;
+        const double b0 = __shfl(inc, f > 0 ? f - 1 : 0, kWave);
+        const double before = f > 0 ? b0 : 0.0;
+        const int tn = __shfl_down(t, 1, kWave);
+        if (valid && (lane == kWave - 1 || i + 1 >= cnt || tn != t)) seg[t * NW + w] += inc - before;
+        tcarry = __shfl(t, kWave - 1, kWave);
+    }
+    __syncthreads();
+    if (w == 0) {
+        const int nq = ntile * NW;
+        const int per = (nq + kWave - 1) / kWave;
+        const int q0 = lane * per, q1 = min(q0 + per, nq);
+        double ls = 0.0;
+        for (int q = q0; q < q1; ++q) ls += seg[q];
+        const double ex = wave_exclusive_scan(ls);
+        const double z = __shfl(ex + ls, kWave - 1, kWave);
+        const double thr = u * z;
+        int qc = 0x7fffffff, ql = -1;
+        double bc = 0.0, cum = ex;
+        for (int q = q0; q < q1; ++q) {
+            if (qc == 0x7fffffff && cum + seg[q] > thr) {
+                qc = q;
+                bc = cum;
+            }
+            cum += seg[q];
+            if (seg[q] > 0.0) ql = q;
+        }
+        const int qmin = wave_min_int(qc);
+        const double base = __shfl(bc, qmin == 0x7fffffff ? 0 : qmin / per, kWave);
+        ql = wave_max_int(ql);
+        if (lane == 0) {
+            ired[0] = qmin;
+            ired[1] = ql;
+            red[0] = base;
+            red[1] = z;
+        }
+    }
+    __syncthreads();
+    const int qs = ired[0], ql = ired[1];
+    const double base = red[0], z = red[1];
+    *Z = s.a * z;
+    if (!(z > 0.0) || !isfinite(z) || ql < 0) {
+        __syncthreads();
+        return -1;
+    }
+    const double thr = u * z;
+    const bool past = qs == 0x7fffffff;   // rounding left the threshold past every crossing
+    const int q = past ? ql : qs;
+    const int tq = q / NW;
+    if (w == q % NW) {   // wave-uniform
+        double carry = base;
+        int found = -1, lastpos = -1;
+        for (int i0 = segstart[q]; i0 >= 0; i0 += kWave) {
+            const int i = i0 + lane;
+            int x = 0;
+            double v = 0.0;
+            bool in = i < cnt;
+            if (in) {
+                v = entry(i, x);
+                in = x / kTileTokens == tq;
+                if (!in) v = 0.0;
+            }
+            const double inc = wave_exclusive_scan(v) + v + carry;
+            const unsigned long long mc = __ballot(in && inc > thr);
+            if (!past && mc) {
+                found = __shfl(x, __ffsll(static_cast<long long>(mc)) - 1, kWave);
+                break;
+            }
+            const unsigned long long mp = __ballot(in && v > 0.0);
+            if (mp) lastpos = __shfl(x, 63 - __clzll(static_cast<long long>(mp)), kWave);
+            carry = __shfl(inc, kWave - 1, kWave);
+            if (__ballot(in) != ~0ull) break;   // the run ends in this batch
+        }
+        if (lane == 0) ired[2] = found >= 0 ? found : lastpos;
+    }
+    __syncthreads();
+    const int y = ired[2];
+    __syncthreads();
+    return y;
+}
+
 // Block-wide inverse-CDF draw over omega in token-id order.  Returns y, or -1
 // when the mass Z is not a positive finite number.  Z is returned in *Z.
 // Tiles of NT chunks are summed four at a time into tile[] (per-chunk sums in
@@ -543,6 +674,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     __shared__ unsigned s_hist[SPECTR ? 2 * kHistBins : 1];
     __shared__ double s_red6[SPECTR ? 6 * NW : 1];
     __shared__ double s_br[4];
+    __shared__ double s_lseg[SPECTR ? 1 : kListTiles * NW];   // node-list draw: tile x wave sums
+    __shared__ int s_lstart[SPECTR ? 1 : kListTiles * NW];
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -710,6 +843,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     }
     rows += streamed;
 
+    // node list of the current node (list_node: the node it serves, -1 none);
+    // list_built: the node a list was last built at; a request stops building
+    // (list_tries, kept across rounds) once its sampled row looked flat or a
+    // list overflowed: its rows share one temperature
+    const NodeList<NT> nl(A.nodes, b);
+    int lcnt = 0, list_node = -1, list_built = -1;
+    double list_out = 0.0;
     if constexpr (SPECTR) {
         if (!bad) {
             if (A.round == 1) {
@@ -771,13 +911,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             beta = 1.0;   // token-level residual max(p - q, 0)
         } else {
             if (A.round == 1) tau = 0;
-            // node list of the current node (list_node: the node it serves, -1 none);
-            // list_built: the node a list was last built at; a request stops
-            // building (list_tries, kept across rounds) once its sampled row
-            // looked flat or a list overflowed: its rows share one temperature
-            const NodeList<NT> nl(A.nodes, b);
-            int lcnt = 0, list_node = -1, list_built = -1;
-            double list_out = 0.0;
             for (int k = k0; k < K && tau < L; ++k) {
                 int match = 1;
                 for (int t = 0; t < tau; ++t) match &= (s_x[k * L + t] == s_x[own * L + t]);
@@ -985,8 +1118,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
                                                    s_red4, s_ired);
             } else {
-                y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, u, &Z, s_tile, s_red,
-                                             s_red4, s_ired);
+                // from the node's list when it has one, its left-out weight is below
+                // 2^-30 of the mass and the row fits the draw's segment table
+                const int ntile = (nch + NT - 1) / NT;
+                y = -1;
+                if (list_node == cn * L1 + tau && ntile <= kListTiles) {
+                    y = sweep_icdf_list<NT>(nl, lcnt, sr, s_H, nH, u, ntile, &Z, s_lseg,
+                                            s_lstart, s_ired, s_red);
+                    if (!(list_out <= 0x1p-30 * Z)) y = -1;
+                }
+                if (y < 0)
+                    y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, u, &Z, s_tile, s_red,
+                                                 s_red4, s_ired);
             }
             Zp = Z;
             if (y < 0) {
