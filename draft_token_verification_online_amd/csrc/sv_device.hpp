@@ -57,7 +57,12 @@ __device__ __forceinline__ float expo(float x, const Scale &c, float K) {
 
 // Row readers: load(c, x) fills x[0..7] with elements 8c..8c+7; raw(c) issues
 // the same load into a compact register form that unpack() expands later, so
-// several chunks can be in flight at 4 VGPRs each (bf16).
+// several chunks can be in flight at 4 VGPRs each (bf16).  raw_once(c) is raw(c)
+// as a non-temporal load, for a pass that reads each chunk once and never again
+// (the statistics kernel): it streams faster than a cached load, where a pass
+// that re-reads rows (the walk's sweeps) loses by it.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 struct RowBf16Vec {
     using Raw = uint4;
     const uint4 *p;
@@ -66,6 +71,10 @@ struct RowBf16Vec {
     // the same row from chunk n on
     __device__ __forceinline__ RowBf16Vec advanced(int n) const { return RowBf16Vec(p + n); }
     __device__ __forceinline__ Raw raw(int c) const { return p[c]; }
+    __device__ __forceinline__ Raw raw_once(int c) const {
+        const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p) + c);
+        return Raw{v.x, v.y, v.z, v.w};
+    }
     __device__ __forceinline__ static void unpack(const Raw &w, float x[8]) {
         x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
         x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
@@ -85,6 +94,11 @@ struct RowF32Vec {
     __device__ RowF32Vec(const void *row, int) : p(static_cast<const float4 *>(row)) {}
     __device__ __forceinline__ RowF32Vec advanced(int n) const { return RowF32Vec(p + 2 * n, 0); }
     __device__ __forceinline__ Raw raw(int c) const { return Raw{p[2 * c], p[2 * c + 1]}; }
+    __device__ __forceinline__ Raw raw_once(int c) const {
+        const f32x4_nt *q = reinterpret_cast<const f32x4_nt *>(p) + 2 * c;
+        const f32x4_nt a = __builtin_nontemporal_load(q), b = __builtin_nontemporal_load(q + 1);
+        return Raw{make_float4(a.x, a.y, a.z, a.w), make_float4(b.x, b.y, b.z, b.w)};
+    }
     __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
         x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
@@ -115,6 +129,7 @@ struct RowBf16Scalar {
         }
     }
     __device__ __forceinline__ Raw raw(int c) const { Raw r; load(c, r.v); return r; }
+    __device__ __forceinline__ Raw raw_once(int c) const { return raw(c); }
     __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = r.v[e];
@@ -140,6 +155,7 @@ struct RowF32Scalar {
         }
     }
     __device__ __forceinline__ Raw raw(int c) const { Raw r; load(c, r.v); return r; }
+    __device__ __forceinline__ Raw raw_once(int c) const { return raw(c); }
     __device__ __forceinline__ static void unpack(const Raw &r, float x[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = r.v[e];
@@ -169,9 +185,11 @@ constexpr int depth_for() {
 // the chunks before them instead of being issued and drained group by group.
 // Refill addresses are clamped into the row (nch >= 1); the refills issued in
 // the last full group are discarded and the remainder is read one chunk at a
-// time.  Without HAS_Q, xq is left unset and Q is not read.
-template <int NT, int D, bool HAS_Q, typename RD, typename F>
+// time.  Without HAS_Q, xq is left unset and Q is not read.  ONCE: the pass
+// reads these rows once (non-temporal loads).
+template <int NT, int D, bool HAS_Q, bool ONCE = false, typename RD, typename F>
 __device__ __forceinline__ void stream_rows(const RD &P, const RD &Q, int nch, F &&f) {
+    auto rd = [](const RD &R, int c) { return ONCE ? R.raw_once(c) : R.raw(c); };
     int c = threadIdx.x;
     if (c + (D - 1) * NT < nch) {
         typename RD::Raw rp[D], rq[D];
@@ -180,8 +198,8 @@ __device__ __forceinline__ void stream_rows(const RD &P, const RD &Q, int nch, F
         // the worst order)
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            rp[i] = P.raw(c + i * NT);
-            if (HAS_Q) rq[i] = Q.raw(c + i * NT);
+            rp[i] = rd(P, c + i * NT);
+            if (HAS_Q) rq[i] = rd(Q, c + i * NT);
             __builtin_amdgcn_sched_barrier(0);
         }
         for (;;) {
@@ -192,8 +210,8 @@ __device__ __forceinline__ void stream_rows(const RD &P, const RD &Q, int nch, F
                 RD::unpack(rp[i], xp);
                 if (HAS_Q) RD::unpack(rq[i], xq);
                 const int cl = min(cn + i * NT, nch - 1);
-                rp[i] = P.raw(cl);
-                if (HAS_Q) rq[i] = Q.raw(cl);
+                rp[i] = rd(P, cl);
+                if (HAS_Q) rq[i] = rd(Q, cl);
                 f(xp, xq, c + i * NT);
             }
             c = cn;
@@ -202,8 +220,8 @@ __device__ __forceinline__ void stream_rows(const RD &P, const RD &Q, int nch, F
     }
     for (; c < nch; c += NT) {
         float xp[8], xq[8];
-        P.load(c, xp);
-        if (HAS_Q) Q.load(c, xq);
+        RD::unpack(rd(P, c), xp);
+        if (HAS_Q) RD::unpack(rd(Q, c), xq);
         f(xp, xq, c);
     }
 }

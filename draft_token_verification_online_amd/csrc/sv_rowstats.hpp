@@ -182,7 +182,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
 
         float x0[8];
         const bool have0 = tid < nch;
-        if (have0) row.load(tid, x0);
+        if (have0) RD::unpack(row.raw_once(tid), x0);
         else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x0[e] = -INFINITY;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
         // chunks NT.. of the row (the first tile is consumed above)
         const RD rest = row.advanced(NT);
         if (nch > NT)
-            stream_rows<NT, depth_for<RD, kStreamBytes>(), false>(rest, rest, nch - NT,
+            stream_rows<NT, depth_for<RD, kStreamBytes>(), false, true>(rest, rest, nch - NT,
                                            [&](const float (&x)[8], const float (&)[8], int) {
                                                ls.consume(x, c);
                                            });
