@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
         typename RD::Raw r[kPerLane];
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i)
-            r[i] = P.raw(min(t * kDraftTileChunks + i * kWave + lane, nch - 1));
+            r[i] = P.raw_once(min(t * kDraftTileChunks + i * kWave + lane, nch - 1));
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
