@@ -219,7 +219,7 @@ def test_negative_infinity_entries():
         _parity(method, batch, "neg_inf_entries")
 
 
-def _root_rejections(flat, seed):
+def _root_rejections(flat, seed, V=65536, B=16):
     """K = 8 drafts whose first tokens (three distinct ones) have p ~ e^-100 and
     a large q at the root, so every draft is rejected there and each rejection but the last
     is followed by a residual-mass sweep of the root pair (duplicates included).
@@ -228,8 +228,10 @@ def _root_rejections(flat, seed):
     samples as sparse either way.  flat: every other logit ~ N(0, 0.5^2) at
     T = 1, so about half the tokens keep residual weight and every wave's list
     overflows (the walk falls back to full sweeps); otherwise logits ~ N(0, 5^2)
-    at T = 0.4 and the lists are used."""
-    B, K, L, V = 16, 8, 2, 65536
+    at T = 0.4 and the lists are used.  Rows of more than 64 tiles of 4096 tokens
+    (V = 300 000) keep the lists for the mass sweeps, but the correction draw
+    takes the full sweep."""
+    K, L = 8, 2
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     sig, T = (0.5, 1.0) if flat else (5.0, 0.4)
@@ -248,10 +250,11 @@ def _root_rejections(flat, seed):
             "u_correct": torch.rand((B,), generator=g, device="cuda")}
 
 
-@pytest.mark.parametrize("flat", [False, True], ids=["lists_used", "lists_overflow"])
-def test_repeated_root_rejections(flat):
-    batch = _root_rejections(flat, 11)
-    rep, out, ref = _parity("multidraft", batch, f"root_rejections_flat{int(flat)}")
+@pytest.mark.parametrize("flat,V,B", [(False, 65536, 16), (True, 65536, 16), (False, 300000, 8)],
+                         ids=["lists_used", "lists_overflow", "lists_used_long_rows"])
+def test_repeated_root_rejections(flat, V, B):
+    batch = _root_rejections(flat, 11, V, B)
+    rep, out, ref = _parity("multidraft", batch, f"root_rejections_flat{int(flat)}_v{V}")
     assert (out["accept_len"] == 0).all(), "every draft is rejected at the root"
 
 
