@@ -222,8 +222,9 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
 
 constexpr long long kDraftTileGrid = 16384;
 
-// Drafting workspace: request flags | per-position list lengths | listed rows |
-// each draft's list slot | tile shifts | tile sums.
+// Drafting workspace: request flags | per-position list lengths | listed rows
+// (two buffers, by position parity) | each draft's list slot | tile shifts |
+// tile sums.
 struct DraftLayout {
     size_t bad, count, list, slot, tmax, tsum, total;
     int ntiles;
@@ -237,7 +238,7 @@ DraftLayout draft_layout(int32_t B, int32_t K, int32_t V) {
     l.bad = 0;
     l.count = align_up(static_cast<size_t>(B) * sizeof(unsigned), 256);
     l.list = l.count + 256;
-    l.slot = l.list + align_up(bk * sizeof(int32_t), 256);
+    l.slot = l.list + align_up(2 * bk * sizeof(int32_t), 256);
     l.tmax = l.slot + align_up(bk * sizeof(int32_t), 256);
     l.tsum = l.tmax + align_up(bk * l.ntiles * sizeof(float), 256);
     l.total = l.tsum + align_up(bk * l.ntiles * sizeof(double), 256);
@@ -278,15 +279,25 @@ hipError_t launch_draft(const sv_draft_inputs *in, const sv_draft_outputs *out,
     hipLaunchKernelGGL(sv::draft_init_kernel, dim3((n0 + 255) / 256), dim3(256), 0, stream, a.bad,
                        a.rows, a.count, in->B, in->L);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    // with K <= 16 the draws of position j and the node rows of position j + 1
+    // share a launch (one workgroup per request)
+    const bool fused = in->K <= sv::kDraftFusedMaxK;
     for (int j = 0; j < in->L; ++j) {
         a.j = j;
-        hipLaunchKernelGGL(sv::draft_nodes_kernel, dim3((in->B + 3) / 4), dim3(256), 0, stream, a);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (j == 0 || !fused) {
+            hipLaunchKernelGGL(sv::draft_nodes_kernel, dim3((in->B + 3) / 4), dim3(256), 0, stream,
+                               a);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
         hipLaunchKernelGGL((sv::draft_tiles_kernel<NT, RD, E>), dim3(tile_grid), dim3(NT), 0,
                            stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((sv::draft_pick_kernel<NT, RD, E>), dim3((bk + 3) / 4), dim3(NT), 0,
-                           stream, a);
+        if (fused)
+            hipLaunchKernelGGL((sv::draft_pick_next_kernel<RD, E>), dim3(in->B),
+                               dim3(in->K * sv::kWave), 0, stream, a);
+        else
+            hipLaunchKernelGGL((sv::draft_pick_kernel<NT, RD, E>), dim3((bk + 3) / 4), dim3(NT), 0,
+                               stream, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const long long n = static_cast<long long>(in->B) * in->K * in->L;

@@ -9,10 +9,12 @@
 // last token of positive weight if rounding leaves none.
 //
 // The node of a draft at position j depends on the tokens drawn before, so each
-// position takes three launches:
+// position takes up to three launches:
 //   1. draft_nodes_kernel -- one wave per request: the node of every draft, the
 //      list of node rows to read (one per node, appended with one atomic per
-//      wave) and, per draft, the list slot of its node's row;
+//      wave) and, per draft, the list slot of its node's row.  The list has one
+//      buffer per position parity, so position j+1 can be listed while
+//      position j's draws still read theirs;
 //   2. draft_tiles_kernel -- grid-stride over (listed row, tile of 512 chunks),
 //      one 64-lane wave per tile (8 chunks per lane): the tile's maximum M_t and
 //      the sum of 2^(l c - K_t) over it (K_t = shift_term(M_t), the exponent
@@ -22,6 +24,9 @@
 //   3. draft_pick_kernel  -- one wave per draft: rescale the tile sums of its
 //      node's row to the row maximum, find the tile holding u Z and rescan it
 //      with the tiles kernel's own per-chunk arithmetic (wave reductions only).
+//      With K <= 16, draft_pick_next_kernel instead runs one workgroup per
+//      request (wave k = draft k): the draws of position j, a barrier, then the
+//      node rows of position j+1 -- one launch fewer per position.
 #pragma once
 
 #include "sv_device.hpp"
@@ -37,7 +42,7 @@ struct DraftArgs {
     int32_t *tok;           // [B][K][L]: drawn tokens (positions < j are read back)
     unsigned *bad;          // [B]: request data the rule cannot act on
     unsigned *count;        // [L]: node rows listed at each position
-    int32_t *list;          // [B*K]: listed node rows, b*K + k
+    int32_t *list;          // [2][B*K]: listed node rows, b*K + k (buffer j % 2)
     int32_t *slot;          // [B*K]: list slot of each draft's node row
     float *tmax;            // [B*K][ntiles]: shift of each tile (its maximum)
     double *tsum;           // [B*K][ntiles]: tile sums under their shift
@@ -65,12 +70,16 @@ __global__ void draft_fixup_kernel(const unsigned *bad, int32_t *tok, int32_t *f
     if (flags && i % KL == 0) flags[b] = bad[b] ? 2 : 0;
 }
 
-// 1. One 64-lane wave per request, lane k = draft k (K <= 64).
-__global__ __launch_bounds__(256) void draft_nodes_kernel(DraftArgs A) {
+// The list buffer of position j.
+__device__ __forceinline__ int32_t *draft_list(const DraftArgs &A, int j) {
+    return A.list + static_cast<long long>(j & 1) * A.B * A.K;
+}
+
+// 1. One 64-lane wave per request, lane k = draft k (K <= 64): the node rows
+// of request b at position j.
+__device__ void draft_nodes_wave(const DraftArgs &A, int b, int j) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (b >= A.B) return;                      // whole waves only
-    const int K = A.K, L = A.L, j = A.j;
+    const int K = A.K, L = A.L;
     const int32_t *X = A.tok + static_cast<long long>(b) * K * L;
     const float T = A.temp[b];
     if (!(T > 0.0f) || !isfinite(T)) {
@@ -92,10 +101,16 @@ __global__ __launch_bounds__(256) void draft_nodes_kernel(DraftArgs A) {
     base = __shfl(base, 0, kWave);
     const unsigned rank = __popcll(heads & ((1ull << lane) - 1ull));
     const int my_slot = static_cast<int>(base + rank);
-    if (head) A.list[my_slot] = b * K + lane;
+    if (head) draft_list(A, j)[my_slot] = b * K + lane;
     const int node_slot = __shfl(my_slot, canon, kWave);
     if (lane < K) A.slot[b * K + lane] = node_slot;
     if (head && A.rows) atomicAdd(A.rows + b, 1);
+}
+
+__global__ __launch_bounds__(256) void draft_nodes_kernel(DraftArgs A) {
+    const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (b >= A.B) return;                      // whole waves only
+    draft_nodes_wave(A, b, A.j);
 }
 
 // 2. Tile sums of the listed rows, one wave per tile.
@@ -112,7 +127,7 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
          it < nitems; it += static_cast<long long>(gridDim.x) * WPB) {
         const int slot = static_cast<int>(it / ntiles);
         const int t = static_cast<int>(it % ntiles);
-        const int bk = A.list[slot];
+        const int bk = draft_list(A, j)[slot];
         const int b = bk / K, k = bk % K;
         const RD P(base + ((static_cast<long long>(b) * K + k) * L + j) * V, V);
         // all eight loads are issued before any is used (addresses clamped into
@@ -154,17 +169,14 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
 }
 
 // 3. One 64-lane wave per draft: the inverse-CDF draw from its node row's tiles.
-template <int NT, typename RD, typename E>
-__global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
+template <typename RD, typename E>
+__device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     constexpr int kPerLane = kDraftTileChunks / kWave;   // rescanned chunks per lane
     const int lane = threadIdx.x & (kWave - 1);
-    const long long d = static_cast<long long>(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
     const int K = A.K, L = A.L, V = A.V, j = A.j;
-    if (d >= static_cast<long long>(A.B) * K) return;          // whole waves
-    const int b = static_cast<int>(d / K), k = static_cast<int>(d % K);
     if (A.bad[b]) return;     // one load for the wave; a flag set meanwhile changes nothing
     const int slot = A.slot[b * K + k];
-    const int c0 = A.list[slot] % K;           // the draft whose row is the node's
+    const int c0 = draft_list(A, j)[slot] % K;   // the draft whose row is the node's
     const int nch = (V + kChunk - 1) / kChunk;
     const int ntiles = A.ntiles;
     const float *tm = A.tmax + static_cast<long long>(slot) * ntiles;
@@ -278,6 +290,27 @@ __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     const int lastrow = wave_max_int(lastp);
     if (lane == 0)
         A.tok[(static_cast<long long>(b) * K + k) * L + j] = cand == 0x7fffffff ? lastrow : cand;
+}
+
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
+    const long long d = static_cast<long long>(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
+    if (d >= static_cast<long long>(A.B) * A.K) return;        // whole waves
+    draft_pick_wave<RD, E>(A, static_cast<int>(d / A.K), static_cast<int>(d % A.K));
+}
+
+// 3'. One workgroup of K waves per request (K <= 16): the draws of position j,
+// then (j + 1 < L) the node rows of position j + 1 from the tokens just drawn;
+// the barrier makes every wave's token visible to wave 0.
+constexpr int kDraftFusedMaxK = 16;
+template <typename RD, typename E>
+__global__ __launch_bounds__(kDraftFusedMaxK * kWave) void draft_pick_next_kernel(DraftArgs A) {
+    const int b = blockIdx.x, k = threadIdx.x / kWave;
+    draft_pick_wave<RD, E>(A, b, k);
+    if (A.j + 1 < A.L) {
+        __syncthreads();
+        if (k == 0) draft_nodes_wave(A, b, A.j + 1);
+    }
 }
 
 }  // namespace sv

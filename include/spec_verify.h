@@ -233,9 +233,11 @@ typedef struct sv_draft_outputs {
 size_t sv_draft_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
 
 /* Draw the K draft blocks of every request.  Asynchronous on ln->stream:
- * 3L + 2 launches (per position: list the node rows, stream them into tile
- * sums, draw; plus a clear and a final pass that marks invalid requests).  ln->phase_events[0] and [1], when non-null, are recorded before
- * and after them; [2..4] are not used.  The tokens of position j are written by
+ * per position, list the node rows, stream them into tile sums and draw (with
+ * K <= 16 the draw of position j also lists the node rows of position j + 1:
+ * 2L + 3 launches in all, else 3L + 2), plus a clear and a final pass that
+ * marks invalid requests.  ln->phase_events[0] and [1], when non-null, are
+ * recorded before and after them; [2..4] are not used.  The tokens of position j are written by
  * the launch for j and read back by the later ones, so draft_tokens must not
  * alias the other arguments. */
 int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,

@@ -103,6 +103,15 @@ def test_single_token_vocabulary():
     assert (g["draft_tokens"] == 0).all()
 
 
+@pytest.mark.parametrize("K", [16, 17])
+def test_draws_and_listing_in_one_launch_or_two(K):
+    """K <= 16: one workgroup per request draws position j and lists the node
+    rows of position j + 1; K = 17 takes a launch for each."""
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=24, K=K, L=5, V=3000,
+                      temperature=0.5)
+    _parity(*_inputs(ws, 6), f"K{K}")
+
+
 def test_largest_k_and_l():
     ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=6, K=64, L=16, V=96, temperature=1.5)
     _parity(*_inputs(ws, 5), "K64_L16")
