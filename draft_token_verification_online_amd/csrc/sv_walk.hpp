@@ -8,7 +8,10 @@
 //   * inverse CDF     y = min{v : C_v > u Z} in token-id order.
 // p and q are rebuilt per element from the row statistics: p(v) =
 // 2^((l_v - M) c) / S.  Drafted-token probabilities come from one gathered
-// logit per row and are kept in log2 form in fp64.
+// logit per row and are kept in log2 form in fp64.  Repeated mass sweeps at
+// one node, and the correction draw there, read a node list instead of the
+// rows when one was built (NodeList below): the few thousand tokens whose
+// residual weight can still matter, with a bound on the weight left out.
 //
 // Rules (see the header spec_verify.h for the full statement):
 //  token level   -- standard speculative sampling: accept X_j iff
