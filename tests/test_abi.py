@@ -190,7 +190,8 @@ def test_draft_host_validation(lib):
     assert f(ins, outs, ln) == sv.SV_EWORKSPACE
     ins, outs, ln = _fake_draft(B=0)
     assert f(ins, outs, ln) == sv.SV_OK
-    # flags, list lengths, list and slots, then per node row 38 tile shifts and tile sums
+    # flags, list lengths, two list buffers (by position parity) and slots, then per node
+    # row 38 tile shifts and tile sums
     big = lib.sv_draft_workspace_size(512, 8, 8, 151936, sv.SV_BF16)
     assert big % 256 == 0 and 4096 * 38 * 12 <= big < 4096 * 38 * 12 + 65536
     assert lib.sv_draft_workspace_size(1, 0, 8, 16, sv.SV_BF16) == 0
