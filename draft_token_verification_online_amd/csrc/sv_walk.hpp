@@ -246,58 +246,66 @@ __device__ double sweep_mass_build(const RD &P, const RD &Q, int nch, const Swee
     for (int t0 = 0; t0 < ntile; t0 += 2) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int ch = (t0 + i) * NT + tid;
-            float xp[8], xq[8];
-            RD::unpack(rp[i], xp);
-            RD::unpack(rq[i], xq);
-            const int cl = min(ch + 2 * NT, nch - 1);   // refill with the tile two on
-            rp[i] = P.raw(cl);
-            rq[i] = Q.raw(cl);
             if (t0 + i >= ntile) break;                 // wave-uniform
+            const int ch = (t0 + i) * NT + tid;
             const bool valid = ch < nch;
-            float ep[8], eq[8], w[8];
+            float w[8];
+            {
+                float xp[8], xq[8];
+                RD::unpack(rp[i], xp);
+                RD::unpack(rq[i], xq);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                ep[e] = fast_exp2(expo(xp[e], c, s.MPc));
-                eq[e] = fast_exp2(expo(xq[e], c, s.MQc));
-                w[e] = valid ? fmaxf(fmaf(-s.r, eq[e], ep[e]), 0.0f) : 0.0f;
+                for (int e = 0; e < 8; ++e) {
+                    const float ep = fast_exp2(expo(xp[e], c, s.MPc));
+                    const float eq = fast_exp2(expo(xq[e], c, s.MQc));
+                    w[e] = valid ? fmaxf(fmaf(-s.r, eq, ep), 0.0f) : 0.0f;
+                }
             }
             h_zero8(ch, H, nH, hl, w);
             acc += static_cast<double>(sum8(w));
-            if (n > kWaveList) continue;   // this wave's list is full: a plain sweep from here
-            float ex = 0.0f;
-            unsigned long long any = 0;
-            unsigned long long m[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool k = w[e] > keep;
-                if (!k) ex += w[e];
-                m[e] = __ballot(k);
-                any |= m[e];
-            }
-            exc += static_cast<double>(ex);
-            if (any) {
-                // slot of (lane, e): the wave's entries so far, the kept tokens
-                // of lower lanes in this tile, then this lane's kept tokens before e
-                int slot = n, tot = 0;
+            if (n <= kWaveList) {   // else this wave's list is full: a plain sweep from here
+                float ex = 0.0f;
+                unsigned long long any = 0;
+                unsigned long long m[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    slot += lanes_below(m[e]);
-                    tot += __popcll(m[e]);
+                    const bool k = w[e] > keep;
+                    if (!k) ex += w[e];
+                    m[e] = __ballot(k);
+                    any |= m[e];
                 }
+                exc += static_cast<double>(ex);
+                if (any) {
+                    // slot of (lane, e): the wave's entries so far, the kept tokens
+                    // of lower lanes in this tile, then this lane's kept tokens
+                    // before e.  The exponentials are recomputed here from the
+                    // chunk still held raw, so the sweep keeps none of them live.
+                    int slot = n, tot = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (w[e] > keep) {
-                        if (slot < kWaveList) {
-                            nl.idx[slot] = kChunk * ch + e;
-                            nl.ep[slot] = ep[e];
-                            nl.eq[slot] = eq[e];
-                        }
-                        ++slot;
+                    for (int e = 0; e < 8; ++e) {
+                        slot += lanes_below(m[e]);
+                        tot += __popcll(m[e]);
                     }
+                    float xp[8], xq[8];
+                    RD::unpack(rp[i], xp);
+                    RD::unpack(rq[i], xq);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (w[e] > keep) {
+                            if (slot < kWaveList) {
+                                nl.idx[slot] = kChunk * ch + e;
+                                nl.ep[slot] = fast_exp2(expo(xp[e], c, s.MPc));
+                                nl.eq[slot] = fast_exp2(expo(xq[e], c, s.MQc));
+                            }
+                            ++slot;
+                        }
+                    }
+                    n += tot;
                 }
-                n += tot;
             }
+            const int cl = min(ch + 2 * NT, nch - 1);   // refill with the tile two on
+            rp[i] = P.raw(cl);
+            rq[i] = Q.raw(cl);
         }
     }
     *cnt = n;
