@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libspec_verify.so")
 
 SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EHIP, SV_EWORKSPACE = range(5)
 SV_F32, SV_BF16 = 0, 1
-SV_FLAG_DEGENERATE, SV_FLAG_INVALID = 1, 2
+SV_FLAG_DEGENERATE, SV_FLAG_INVALID, SV_FLAG_NEAR_TIE = 1, 2, 4
+SV_NEAR_TIE = 1e-5
 SV_MAX_K, SV_MAX_L, SV_MAX_V = 64, 16, 1 << 22
 
 _vp = ctypes.c_void_p

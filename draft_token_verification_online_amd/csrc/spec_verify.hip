@@ -39,6 +39,7 @@ static_assert(SV_MAX_L == sv::kMaxL, "L limit");
 static_assert(SV_MAX_V == sv::kMaxV, "V limit");
 static_assert(SV_FLAG_DEGENERATE == sv::kFlagDegenerate, "flag bits");
 static_assert(SV_FLAG_INVALID == sv::kFlagInvalid, "flag bits");
+static_assert(SV_FLAG_NEAR_TIE == sv::kFlagNearTie && SV_NEAR_TIE == sv::kNearTie, "flag bits");
 static_assert(sizeof(sv::RowStat) == 16, "row statistics layout");
 static_assert(sizeof(sv_row_stat) == sizeof(sv::RowStat) && offsetof(sv_row_stat, sum) == 8,
               "sv_row_stat is the library's row statistics layout");

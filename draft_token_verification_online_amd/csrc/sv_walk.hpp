@@ -54,6 +54,8 @@ constexpr int kMethodBlockWalk = 1;
 constexpr int kMethodSpecTr = 2;
 constexpr int kFlagDegenerate = 1;
 constexpr int kFlagInvalid = 2;
+constexpr int kFlagNearTie = 4;
+constexpr double kNearTie = 1e-5;   // decisions closer than this to their threshold are flagged
 // Node lists: entries per wave, and the cutoff 2^-kListCut below which a
 // token's residual weight omega(v) / alpha leaves the list.
 constexpr int kWaveList = 2048;
@@ -363,7 +365,8 @@ constexpr int kListTiles = 64;
 template <int NT>
 __device__ int sweep_icdf_list(const NodeList<NT> &nl, int cnt, const SweepRows &s, const int *H,
                                int nH, double u, int ntile, double *Z, double *seg, int *segstart,
-                               int *ired, double *red) {
+                               int *ired, double *red, double *margin) {
+    *margin = 0.0;   // distance of u Z to the nearest boundary of the draw, over Z
     constexpr int NW = NT / kWave;
     constexpr int kTileTokens = kChunk * NT;
     const int lane = threadIdx.x & (kWave - 1);
@@ -463,7 +466,10 @@ __device__ int sweep_icdf_list(const NodeList<NT> &nl, int cnt, const SweepRows 
             const double inc = wave_exclusive_scan(v) + v + carry;
             const unsigned long long mc = __ballot(in && inc > thr);
             if (!past && mc) {
-                found = __shfl(x, __ffsll(static_cast<long long>(mc)) - 1, kWave);
+                const int fl = __ffsll(static_cast<long long>(mc)) - 1;
+                found = __shfl(x, fl, kWave);
+                const double hi = __shfl(inc, fl, kWave), lo = hi - __shfl(v, fl, kWave);
+                if (lane == 0) red[2] = fmin(hi - thr, thr - lo);
                 break;
             }
             const unsigned long long mp = __ballot(in && v > 0.0);
@@ -471,10 +477,14 @@ __device__ int sweep_icdf_list(const NodeList<NT> &nl, int cnt, const SweepRows 
             carry = __shfl(inc, kWave - 1, kWave);
             if (__ballot(in) != ~0ull) break;   // the run ends in this batch
         }
-        if (lane == 0) ired[2] = found >= 0 ? found : lastpos;
+        if (lane == 0) {
+            ired[2] = found >= 0 ? found : lastpos;
+            if (found < 0) red[2] = 0.0;
+        }
     }
     __syncthreads();
     const int y = ired[2];
+    *margin = red[2] / z;
     __syncthreads();
     return y;
 }
@@ -489,7 +499,8 @@ __device__ int sweep_icdf_list(const NodeList<NT> &nl, int cnt, const SweepRows 
 template <int NT, typename RD, bool HAS_Q, bool FLOOR = false>
 __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s, const Scale &c,
                           const int *H, int nH, double u, double *Z, double *tile, double *red,
-                          double *red4, int *ired) {
+                          double *red4, int *ired, double *margin) {
+    *margin = 0.0;   // distance of u Z to the nearest boundary of the draw, over Z
     const HLanes hl = h_lanes<NT>(H, nH);
     const int ntile = (nch + NT - 1) / NT;
     int lastc = -1;
@@ -586,6 +597,7 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
     }
     const double pre = base + block_exclusive_scan<NT>(cs, red);
     int cand = 0x7fffffff;
+    double cm = 0.0;
     if (ch < nch && pre <= thr && pre + cs > thr) {
         double C = pre;
         int last = -1;
@@ -593,14 +605,26 @@ __device__ int sweep_icdf(const RD &P, const RD &Q, int nch, const SweepRows &s,
         for (int e = 0; e < 8; ++e) {
             if (cand == 0x7fffffff) {
                 if (w[e] > 0.0f) last = kChunk * ch + e;
+                const double before = C;
                 C += static_cast<double>(w[e]);
-                if (C > thr) cand = kChunk * ch + e;
+                if (C > thr) {
+                    cand = kChunk * ch + e;
+                    cm = fmin(C - thr, thr - before);
+                }
             }
         }
         if (cand == 0x7fffffff && last >= 0) cand = last;
     }
+    const int mine = cand;
     cand = block_min_int<NT>(cand, ired);
-    return cand == 0x7fffffff ? last_positive() : cand;
+    if (cand == 0x7fffffff) return last_positive();
+    // the margin from the lane that drew (the block reductions that read red[]
+    // are done: block_min_int's barriers passed them)
+    if (mine == cand) red[0] = cm;
+    __syncthreads();
+    *margin = red[0] / z;
+    __syncthreads();
+    return cand;
 }
 
 // Block-wide maximum of a row (NaN entries are ignored here; they surface as a
@@ -654,6 +678,7 @@ struct WalkState {
     int tau, own, kstar, nH, flags, rows;
     int list_tries;         // node lists the request may still build
     double alpha, beta, N;
+    double tie;             // smallest |u - threshold| over the decisions so far
     int H[kMaxK];
 };
 constexpr int kStateDone = 0;
@@ -836,7 +861,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     double rho = 1.0, cc = 1.0;   // SpecTr: scaling factor and tries at the last node
     bool suspend = false;
     int own = 0, nH = 0, k0 = 0, list_tries = 1;
-    double alpha = 1.0, beta = 0.0, N = 1.0;
+    double alpha = 1.0, beta = 0.0, N = 1.0, tie = INFINITY;
     if (A.round == 2) {
         k0 = ws->k_next;
         tau = ws->tau;
@@ -846,6 +871,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         flags = ws->flags;
         rows = ws->rows;
         list_tries = ws->list_tries;
+        tie = ws->tie;
         alpha = ws->alpha;
         beta = ws->beta;
         N = ws->N;
@@ -899,6 +925,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     const double u = static_cast<double>(A.ua[bKL + k * L + j]);
                     if (tid == 0 && A.accept_prob)
                         A.accept_prob[bKL + k * L + j] = static_cast<float>(h);
+                    tie = fmin(tie, fabs(u - h));
                     if (u < h) acc = k;
                 }
                 if (acc < 0) break;
@@ -916,6 +943,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 if (a > 1.0) a = 1.0;
                 const double u = static_cast<double>(A.ua[bKL + j]);
                 if (tid == 0 && A.accept_prob) A.accept_prob[bKL + j] = static_cast<float>(a);
+                tie = fmin(tie, fabs(u - a));
                 if (!(u < a)) { tau = j; break; }
             }
             kstar = tau > 0 ? 0 : -1;
@@ -959,7 +987,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                         if (m == L) {
                             h = wm;
                         } else {
-                            if (!(u < wm)) continue;      // h_m <= w_m: rejects without a sweep
+                            if (!(u < wm)) {              // h_m <= w_m: rejects without a sweep
+                                tie = fmin(tie, u - wm);
+                                continue;
+                            }
                             const int cm = s_can[k * L1 + m];
                             const SweepRows sr = node_sweep(cm, m, wm, 1.0);
                             const RD P(trow(cm, m), V), Q(drow(cm, m), V);
@@ -971,6 +1002,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                         }
                         if (tid == 0 && A.accept_prob)
                             A.accept_prob[bKL + k * L + m - 1] = static_cast<float>(h);
+                        tie = fmin(tie, fabs(u - h));
                         if (u < h) { acc = m; break; }
                     }
                     if (acc > 0) {
@@ -1090,6 +1122,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             ws->flags = flags;
             ws->rows = rows;
             ws->list_tries = list_tries;
+            ws->tie = tie;
             ws->alpha = alpha;
             ws->beta = beta;
             ws->N = N;
@@ -1099,6 +1132,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     }
 
     // 5. correction token
+    double dm = INFINITY;   // the draw's margin (distance of u Z to a boundary, over Z)
     if (!bad) {
         const double u = static_cast<double>(ucf);
         if (tau == L) {
@@ -1113,7 +1147,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             double Z;
             y = (M > -INFINITY && M < INFINITY)
                     ? sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
-                                                s_red4, s_ired)
+                                                s_red4, s_ired, &dm)
                     : -1;
             Zp = 1.0;
             if (y < 0) bad = 1;   // the target row after the block is not a distribution
@@ -1127,7 +1161,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 sr = node_sweep(cn, tau, 1.0, cc);
                 sr.g = static_cast<float>(fmax(1.0 - cc / rho, 0.0));   // over a = 1 / S_P
                 y = sweep_icdf<NT, RD, true, true>(P, Q, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
-                                                   s_red4, s_ired);
+                                                   s_red4, s_ired, &dm);
             } else {
                 // from the node's list when it has one, its left-out weight is below
                 // 2^-30 of the mass and the row fits the draw's segment table
@@ -1135,12 +1169,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 y = -1;
                 if (list_node == cn * L1 + tau && ntile <= kListTiles) {
                     y = sweep_icdf_list<NT>(nl, lcnt, sr, s_H, nH, u, ntile, &Z, s_lseg,
-                                            s_lstart, s_ired, s_red);
+                                            s_lstart, s_ired, s_red, &dm);
                     if (!(list_out <= 0x1p-30 * Z)) y = -1;
                 }
                 if (y < 0)
                     y = sweep_icdf<NT, RD, true>(P, Q, nch, sr, sc, s_H, nH, u, &Z, s_tile, s_red,
-                                                 s_red4, s_ired);
+                                                 s_red4, s_ired, &dm);
             }
             Zp = Z;
             if (y < 0) {
@@ -1148,12 +1182,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 sr.a = 1.0 / s_S[cn * RS + tau];
                 sr.r = 0.0f;
                 y = sweep_icdf<NT, RD, false>(P, P, nch, sr, sc, s_H, 0, u, &Z, s_tile, s_red,
-                                              s_red4, s_ired);
+                                              s_red4, s_ired, &dm);
                 Zp = Z;
             }
         }
     }
 
+    tie = fmin(tie, dm);
+    if (tie < kNearTie) flags |= kFlagNearTie;
     if (tid == 0) {
         if (bad) {
             tau = -1;

@@ -111,6 +111,14 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
                                  a uniform outside [0, 1), or a node row that the
                                  rules read and that is not a distribution (NaN,
                                  +inf, all -inf) */
+#define SV_FLAG_NEAR_TIE 4    /* a decision came within SV_NEAR_TIE of its
+                                 threshold: an acceptance test with |u - h| <
+                                 SV_NEAR_TIE, or the correction draw with u Z
+                                 within SV_NEAR_TIE Z of a boundary of the
+                                 cumulative weights.  The exponentials are fp32,
+                                 so such a decision may differ from one taken in
+                                 exact arithmetic; every other decision cannot */
+#define SV_NEAR_TIE 1e-5
 
 /* Inputs.  All pointers are DEVICE pointers owned by the caller, row-major,
  * read-only for the library, and must stay valid until the stream reaches the

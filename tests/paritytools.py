@@ -42,6 +42,9 @@ def compare(method, gpu_out, ref, requests, *, diagnostics=True, label=""):
         rep["invalid"] += bool(oflags & oracle.FLAG_INVALID)
         rep["degenerate"] += bool((oflags | gflags) & oracle.FLAG_DEGENERATE)
         near_tie = ref["margin"][i] < TIE_BAND or ((oflags | gflags) & oracle.FLAG_DEGENERATE)
+        # the library flags every decision within 1e-5 of its threshold (SV_FLAG_NEAR_TIE = 4)
+        if ref["margin"][i] < TIE_BAND and "flags" in g and not (oflags & oracle.FLAG_INVALID):
+            assert gflags & 4, (label, int(b), "a near tie the library did not flag")
         if not same or (gflags & oracle.FLAG_INVALID) != (oflags & oracle.FLAG_INVALID):
             if near_tie and not ((gflags ^ oflags) & oracle.FLAG_INVALID):
                 rep["excused"] += 1

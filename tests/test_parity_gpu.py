@@ -258,6 +258,41 @@ def test_repeated_root_rejections(flat, V, B):
     assert (out["accept_len"] == 0).all(), "every draft is rejected at the root"
 
 
+def test_near_tie_decisions_are_flagged():
+    """Every request gets a near tie by construction: draft 0's test at the last
+    position (the first decision of the walk, h = w_L) gets u = h +- delta with
+    delta from 2e-7 to 6e-6, h taken from the oracle.  The library must flag every
+    request whose oracle decision log holds a decision within 5e-6 of its threshold
+    (its own margin is that within the fp32 error of h), every request whose
+    integer outputs differ from the oracle's must be flagged, and every unflagged
+    request must match exactly."""
+    from draft_token_verification_online_amd import SV_FLAG_NEAR_TIE
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=64, V=4096)
+    batch = pt.gpu_batch(ws, 12)
+    ref0 = pt.run_oracle("multidraft", synth.to_host(batch))
+    L = ws.L
+    ua = batch["u_accept"].clone()
+    deltas = [3e-6, -3e-6, 8e-7, -8e-7, 2e-7, -2e-7, 6e-6, -6e-6]
+    placed = 0
+    for b in range(ws.B):
+        h = float(ref0["accept_prob"][b, 0, L - 1])
+        if 0.01 < h < 0.99:
+            ua[b, 0, L - 1] = float(np.float32(h + deltas[b % len(deltas)]))
+            placed += 1
+    assert placed >= 16
+    batch2 = dict(batch, u_accept=ua.contiguous())
+    out = _verify("multidraft", batch2)
+    ref = pt.run_oracle("multidraft", synth.to_host(batch2))
+    near = (out["flags"].cpu().numpy() & SV_FLAG_NEAR_TIE) != 0
+    print(f"[near-tie] placed={placed} flagged={int(near.sum())} "
+          f"oracle<5e-6={int((ref['margin'] < 5e-6).sum())}", flush=True)
+    assert near[ref["margin"] < 5e-6].all()
+    same = np.ones(ws.B, dtype=bool)
+    for key in ("accept_len", "draft_index", "correction"):
+        same &= out[key].cpu().numpy() == ref[key]
+    assert near[~same].all(), "an unflagged request differs from the oracle"
+
+
 def test_misaligned_rows_take_the_scalar_path():
     ws = synth.scaled(W["gbv_bf16_b64_k1_l5_v32000"], B=16, V=2048)
     batch = pt.gpu_batch(ws, 11)
