@@ -174,6 +174,10 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     constexpr int kPerLane = kDraftTileChunks / kWave;   // rescanned chunks per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int K = A.K, L = A.L, V = A.V, j = A.j;
+    // the draft's uniform and the request's temperature do not depend on the
+    // node: their loads are issued before the chain of dependent ones
+    const float u = A.ud[(static_cast<long long>(b) * K + k) * L + j];
+    const Scale sc = temp_scale(A.temp[b]);
     if (A.bad[b]) return;     // one load for the wave; a flag set meanwhile changes nothing
     const int slot = A.slot[b * K + k];
     const int c0 = draft_list(A, j)[slot] % K;   // the draft whose row is the node's
@@ -181,7 +185,6 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     const int ntiles = A.ntiles;
     const float *tm = A.tmax + static_cast<long long>(slot) * ntiles;
     const double *ts = A.tsum + static_cast<long long>(slot) * ntiles;
-    const Scale sc = temp_scale(A.temp[b]);
 
     // row maximum over the tile shifts; each tile's weight in the row's scale
     float m = -INFINITY;
@@ -204,7 +207,6 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     const double pre = wave_exclusive_scan(own);
     const double Z = wave_sum(own);
     last_tile = wave_max_int(last_tile);
-    const float u = A.ud[(static_cast<long long>(b) * K + k) * L + j];
     if (!(Z > 0.0) || !isfinite(Z) || !(u >= 0.0f && u < 1.0f)) {
         if (lane == 0) A.bad[b] = 1u;
         return;
@@ -237,49 +239,47 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     const float Mgc = shift_term(tm[tc], sc);
     const double f = exp2(static_cast<double>(Mgc) - Mcd);
     const int c1 = tc * kDraftTileChunks + lane * kPerLane;
-    auto weights = [&](int c, float (&e)[8]) {
-        float x[8];
-        P.load(c, x);
+    // the lane's eight chunks are loaded before any is used (clamped addresses;
+    // chunks past the row are not counted) and kept for the crossing lane's
+    // in-order recount, so no chunk is read twice
+    typename RD::Raw r[kPerLane];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
-    };
+    for (int i = 0; i < kPerLane; ++i) r[i] = P.raw(min(c1 + i, nch - 1));
     double cs = 0.0;
     int lastp = -1;
-    {
-        // the lane's eight chunks are loaded before any is used (clamped
-        // addresses; chunks past the row are not counted)
-        typename RD::Raw r[kPerLane];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) r[i] = P.raw(min(c1 + i, nch - 1));
+    for (int i = 0; i < kPerLane; ++i) {
+        const int c = c1 + i;
+        if (c < nch) {
+            float x[8], e[8];
+            RD::unpack(r[i], x);
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int c = c1 + i;
-            if (c < nch) {
-                float x[8], e[8];
-                RD::unpack(r[i], x);
+            for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
 #pragma unroll
-                for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (e[q] > 0.0f) lastp = 8 * c + q;
-                cs += static_cast<double>(sum8(e));
-            }
+            for (int q = 0; q < 8; ++q)
+                if (e[q] > 0.0f) lastp = 8 * c + q;
+            cs += static_cast<double>(sum8(e));
         }
     }
     const double cpre = wave_exclusive_scan(cs);
     int cand = 0x7fffffff;
     if (!fallback && c1 < nch) {
         const double lo = tbase + f * cpre, hi = tbase + f * (cpre + cs);
-        if (lo <= thr && hi > thr) {   // the crossing lane: recompute its weights in order
+        if (lo <= thr && hi > thr) {   // the crossing lane: its weights again, in order
             double C = cpre;
-            for (int i = 0; i < kPerLane && c1 + i < nch && cand == 0x7fffffff; ++i) {
-                float e[8];
-                weights(c1 + i, e);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (cand == 0x7fffffff) {
-                        C += static_cast<double>(e[q]);
-                        if (tbase + f * C > thr) cand = 8 * (c1 + i) + q;
+            for (int i = 0; i < kPerLane; ++i) {
+                if (c1 + i < nch && cand == 0x7fffffff) {
+                    float x[8], e[8];
+                    RD::unpack(r[i], x);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) e[q] = fast_exp2(expo(x[q], sc, Mgc));
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (cand == 0x7fffffff) {
+                            C += static_cast<double>(e[q]);
+                            if (tbase + f * C > thr) cand = 8 * (c1 + i) + q;
+                        }
                     }
                 }
             }
