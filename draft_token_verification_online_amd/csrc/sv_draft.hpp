@@ -75,8 +75,27 @@ __device__ __forceinline__ int32_t *draft_list(const DraftArgs &A, int j) {
     return A.list + static_cast<long long>(j & 1) * A.B * A.K;
 }
 
+// The node rows of request b at position j, given in lane k < K the lowest
+// draft index whose prefix X[0..j-1] equals draft k's (the node's own draft):
+// one list slot per node (one atomic per wave), and each draft's slot.
+__device__ void draft_list_nodes(const DraftArgs &A, int b, int j, int canon) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int K = A.K;
+    const bool head = lane < K && canon == lane;
+    const unsigned long long heads = __ballot(head);
+    unsigned base = 0;
+    if (lane == 0) base = atomicAdd(A.count + j, static_cast<unsigned>(__popcll(heads)));
+    base = __shfl(base, 0, kWave);
+    const unsigned rank = __popcll(heads & ((1ull << lane) - 1ull));
+    const int my_slot = static_cast<int>(base + rank);
+    if (head) draft_list(A, j)[my_slot] = b * K + lane;
+    const int node_slot = __shfl(my_slot, canon, kWave);
+    if (lane < K) A.slot[b * K + lane] = node_slot;
+    if (head && A.rows) atomicAdd(A.rows + b, 1);
+}
+
 // 1. One 64-lane wave per request, lane k = draft k (K <= 64): the node rows
-// of request b at position j.
+// of request b at position j, from the drawn prefixes.
 __device__ void draft_nodes_wave(const DraftArgs &A, int b, int j) {
     const int lane = threadIdx.x & (kWave - 1);
     const int K = A.K, L = A.L;
@@ -94,17 +113,7 @@ __device__ void draft_nodes_wave(const DraftArgs &A, int b, int j) {
             if (same) { canon = c; break; }
         }
     }
-    const bool head = lane < K && canon == lane;
-    const unsigned long long heads = __ballot(head);
-    unsigned base = 0;
-    if (lane == 0) base = atomicAdd(A.count + j, static_cast<unsigned>(__popcll(heads)));
-    base = __shfl(base, 0, kWave);
-    const unsigned rank = __popcll(heads & ((1ull << lane) - 1ull));
-    const int my_slot = static_cast<int>(base + rank);
-    if (head) draft_list(A, j)[my_slot] = b * K + lane;
-    const int node_slot = __shfl(my_slot, canon, kWave);
-    if (lane < K) A.slot[b * K + lane] = node_slot;
-    if (head && A.rows) atomicAdd(A.rows + b, 1);
+    draft_list_nodes(A, b, j, canon);
 }
 
 __global__ __launch_bounds__(256) void draft_nodes_kernel(DraftArgs A) {
@@ -169,8 +178,10 @@ __global__ __launch_bounds__(NT) void draft_tiles_kernel(DraftArgs A) {
 }
 
 // 3. One 64-lane wave per draft: the inverse-CDF draw from its node row's tiles.
+// Returns, in every lane, the draft whose row is the node's and the token drawn
+// (token -1 - k where the request is invalid and nothing was drawn).
 template <typename RD, typename E>
-__device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
+__device__ int2 draft_pick_wave(const DraftArgs &A, int b, int k) {
     constexpr int kPerLane = kDraftTileChunks / kWave;   // rescanned chunks per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int K = A.K, L = A.L, V = A.V, j = A.j;
@@ -178,7 +189,8 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     // node: their loads are issued before the chain of dependent ones
     const float u = A.ud[(static_cast<long long>(b) * K + k) * L + j];
     const Scale sc = temp_scale(A.temp[b]);
-    if (A.bad[b]) return;     // one load for the wave; a flag set meanwhile changes nothing
+    const int2 none = make_int2(k, -1 - k);
+    if (A.bad[b]) return none;   // one load for the wave; a flag set meanwhile changes nothing
     const int slot = A.slot[b * K + k];
     const int c0 = draft_list(A, j)[slot] % K;   // the draft whose row is the node's
     const int nch = (V + kChunk - 1) / kChunk;
@@ -209,7 +221,7 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     last_tile = wave_max_int(last_tile);
     if (!(Z > 0.0) || !isfinite(Z) || !(u >= 0.0f && u < 1.0f)) {
         if (lane == 0) A.bad[b] = 1u;
-        return;
+        return none;
     }
     const double thr = static_cast<double>(u) * Z;
     int tc = 0x7fffffff;
@@ -288,28 +300,42 @@ __device__ void draft_pick_wave(const DraftArgs &A, int b, int k) {
     }
     cand = wave_min_int(cand);
     const int lastrow = wave_max_int(lastp);
-    if (lane == 0)
-        A.tok[(static_cast<long long>(b) * K + k) * L + j] = cand == 0x7fffffff ? lastrow : cand;
+    const int y = cand == 0x7fffffff ? lastrow : cand;
+    if (lane == 0) A.tok[(static_cast<long long>(b) * K + k) * L + j] = y;
+    return make_int2(c0, y);
 }
 
 template <int NT, typename RD, typename E>
 __global__ __launch_bounds__(NT) void draft_pick_kernel(DraftArgs A) {
     const long long d = static_cast<long long>(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
     if (d >= static_cast<long long>(A.B) * A.K) return;        // whole waves
-    draft_pick_wave<RD, E>(A, static_cast<int>(d / A.K), static_cast<int>(d % A.K));
+    (void)draft_pick_wave<RD, E>(A, static_cast<int>(d / A.K), static_cast<int>(d % A.K));
 }
 
 // 3'. One workgroup of K waves per request (K <= 16): the draws of position j,
-// then (j + 1 < L) the node rows of position j + 1 from the tokens just drawn;
-// the barrier makes every wave's token visible to wave 0.
+// then (j + 1 < L) the node rows of position j + 1.  Drafts share a node at
+// j + 1 exactly when they share one at j and drew the same token there, so
+// wave 0 finds each draft's node from the K (node draft, token) pairs the waves
+// leave in LDS, without reading the prefixes back.
 constexpr int kDraftFusedMaxK = 16;
 template <typename RD, typename E>
 __global__ __launch_bounds__(kDraftFusedMaxK * kWave) void draft_pick_next_kernel(DraftArgs A) {
-    const int b = blockIdx.x, k = threadIdx.x / kWave;
-    draft_pick_wave<RD, E>(A, b, k);
+    __shared__ int s_node[kDraftFusedMaxK], s_tok[kDraftFusedMaxK];
+    const int b = blockIdx.x, k = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int2 r = draft_pick_wave<RD, E>(A, b, k);
     if (A.j + 1 < A.L) {
+        if (lane == 0) { s_node[k] = r.x; s_tok[k] = r.y; }
         __syncthreads();
-        if (k == 0) draft_nodes_wave(A, b, A.j + 1);
+        if (k == 0 && !A.bad[b]) {   // an invalid request lists no more rows
+            const int K = A.K;
+            const int pn = lane < K ? s_node[lane] : -1, pt = lane < K ? s_tok[lane] : -1;
+            int canon = lane;
+            for (int c = K - 1; c >= 0; --c) {
+                const int cn = __shfl(pn, c, kWave), ct = __shfl(pt, c, kWave);
+                if (c < lane && cn == pn && ct == pt) canon = c;
+            }
+            draft_list_nodes(A, b, A.j + 1, canon);
+        }
     }
 }
 
