@@ -185,13 +185,14 @@ __device__ int2 draft_pick_wave(const DraftArgs &A, int b, int k) {
     constexpr int kPerLane = kDraftTileChunks / kWave;   // rescanned chunks per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int K = A.K, L = A.L, V = A.V, j = A.j;
-    // the draft's uniform and the request's temperature do not depend on the
-    // node: their loads are issued before the chain of dependent ones
+    // the draft's uniform, the request's temperature and the draft's list slot
+    // are loaded together with the request's flag; the slot (stale once a
+    // request is invalid) is used only after the flag is checked
     const float u = A.ud[(static_cast<long long>(b) * K + k) * L + j];
     const Scale sc = temp_scale(A.temp[b]);
+    const int slot = A.slot[b * K + k];
     const int2 none = make_int2(k, -1 - k);
     if (A.bad[b]) return none;   // one load for the wave; a flag set meanwhile changes nothing
-    const int slot = A.slot[b * K + k];
     const int c0 = draft_list(A, j)[slot] % K;   // the draft whose row is the node's
     const int nch = (V + kChunk - 1) / kChunk;
     const int ntiles = A.ntiles;
