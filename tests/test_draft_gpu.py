@@ -206,12 +206,13 @@ FULL = ["multi_bf16_b256_k4_l4_v128256", "multi_zipf_bf16_b512_k8_l8_v151936",
         "multi_mixedT_bf16_b1024_k4_l8_v151936"]
 
 
+@pytest.mark.parametrize("seed,n", [(1234, 24), (4321, 64)], ids=["seed1234", "seed4321"])
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_sampled_parity(name, seed, n):
     w = W[name]
-    d, temps, u = _inputs(w, 1234)
-    rng = np.random.default_rng(5)
-    req = sorted(rng.choice(w.B, size=min(w.B, 24), replace=False).tolist())
-    _parity(d, temps, u, f"full/{name}", requests=req)
+    d, temps, u = _inputs(w, seed)
+    rng = np.random.default_rng(seed + 1)
+    req = sorted(rng.choice(w.B, size=min(w.B, n), replace=False).tolist())
+    _parity(d, temps, u, f"full/{name}/seed{seed}", requests=req)
     del d
     torch.cuda.empty_cache()

@@ -313,15 +313,17 @@ def test_misaligned_rows_take_the_scalar_path():
 FULL = list(W)
 
 
+@pytest.mark.parametrize("seed,n", [(1234, 24), (4321, 64)], ids=["seed1234", "seed4321"])
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_sampled_parity(name, seed, n):
+    """The whole batch at its full size on the GPU, n requests of it sampled
+    for the oracle."""
     w = W[name]
-    batch = pt.gpu_batch(w, 1234)
-    rng = np.random.default_rng(5)
-    n = min(w.B, 24)
-    req = sorted(rng.choice(w.B, size=n, replace=False).tolist())
+    batch = pt.gpu_batch(w, seed)
+    rng = np.random.default_rng(seed + 1)
+    req = sorted(rng.choice(w.B, size=min(w.B, n), replace=False).tolist())
     for method in w.methods + (("spectr",) if w.K > 1 else ()):
-        _parity(method, batch, f"full/{name}", requests=req, diagnostics=False)
+        _parity(method, batch, f"full/{name}/seed{seed}", requests=req, diagnostics=False)
     del batch
     torch.cuda.empty_cache()
 
