@@ -149,6 +149,53 @@ def test_python_binding_refuses_host_tensors(lib):
                              torch.zeros(B, K, L), torch.zeros(B))
 
 
+class _Arg:
+    """What the binding inspects of a tensor argument before it passes a pointer
+    on: shape, dtype, layout and device (no GPU is needed to check them)."""
+
+    def __init__(self, shape, dtype, contiguous=True, device="cuda"):
+        import types
+        self.shape, self.dtype, self._c = tuple(shape), dtype, contiguous
+        self.device = types.SimpleNamespace(type=device)
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_python_binding_checks_every_argument(lib):
+    """Shape, dtype, layout and device are checked for every argument of the
+    three callable objects before anything reaches the library."""
+    import torch
+    f32, bf16, i32 = torch.float32, torch.bfloat16, torch.int32
+    B, K, L, V = 2, 2, 3, 16
+    v = sv.Verifier.__new__(sv.Verifier)
+    v.method, v.shape, v.dtype = "multidraft", (B, K, L, V), f32
+    vargs = [((B, K, L + 1, V), f32), ((B, K, L, V), f32), ((B, K, L), i32), ((B,), f32),
+             ((B, K, L), f32), ((B,), f32)]
+    d = sv.Drafter.__new__(sv.Drafter)
+    d.shape, d.dtype = (B, K, L, V), bf16
+    dargs = [((B, K, L, V), bf16), ((B,), f32), ((B, K, L), f32)]
+    R, dm = 4, 64
+    h = sv.LmHead.__new__(sv.LmHead)
+    h.shape = (R, dm, V)
+    hargs = [((R, dm), bf16), ((V, dm), bf16), ((R,), f32)]
+    for obj, spec in ((v, vargs), (d, dargs), (h, hargs)):
+        # good arguments pass every check: the call goes on to take their pointers
+        with pytest.raises(AttributeError, match="data_ptr"):
+            type(obj).__call__(obj, *[_Arg(s_, t_) for s_, t_ in spec])
+        for i, (shp, dt) in enumerate(spec):
+            other = torch.float64 if dt != torch.float64 else f32
+            bad = [(_Arg(shp[:-1] + (shp[-1] + 1,), dt), "expected contiguous"),
+                   (_Arg(shp, other), "expected contiguous"),
+                   (_Arg(shp, dt, contiguous=False), "expected contiguous"),
+                   (_Arg(shp, dt, device="cpu"), "GPU memory")]
+            for b, msg in bad:
+                a = [_Arg(s_, t_) for s_, t_ in spec]
+                a[i] = b
+                with pytest.raises(ValueError, match=msg):
+                    type(obj).__call__(obj, *a)
+
+
 def test_missing_library_fails_loudly(tmp_path):
     saved = sv._lib
     try:
