@@ -81,6 +81,9 @@ SMALL = [
     # drafts close together at low T: many drafts share prefixes
     ("bf16_shared_k8_l8_v6000", W["multi_zipf_bf16_b512_k8_l8_v151936"],
      dict(B=48, V=6000, temperature=0.25)),
+    # the widest one-launch draw (K = 16) with prefixes shared to deep positions
+    ("bf16_shared_k16_l8_v3000", W["multi_zipf_bf16_b512_k8_l8_v151936"],
+     dict(B=32, K=16, V=3000, temperature=0.1)),
 ]
 
 
@@ -88,7 +91,9 @@ SMALL = [
 def test_small_parity(name, w, over):
     ws = synth.scaled(w, **over)
     for seed in (1, 2):
-        _parity(*_inputs(ws, seed), f"{name}/seed{seed}")
+        g, ref = _parity(*_inputs(ws, seed), f"{name}/seed{seed}")
+        if "shared" in name:   # the case is only worth its name if drafts do meet at nodes
+            assert int(g["rows_streamed"].sum()) < ws.B * ws.K * ws.L
 
 
 def test_temperatures():
