@@ -130,6 +130,17 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _check_bytes(t, nbytes: int, what: str):
+    """A raw device buffer argument: a contiguous uint8 tensor in GPU memory of
+    at least `nbytes` bytes (the library writes or reads that many)."""
+    if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 1:
+        raise ValueError(f"{what} must be a contiguous 1-D uint8 tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must live in GPU memory")
+    if t.numel() < nbytes:
+        raise ValueError(f"{what} holds {t.numel()} bytes, {nbytes} needed")
+
+
 class Verifier:
     """Holds outputs and workspace for repeated calls on inputs of one shape.
 
@@ -182,10 +193,8 @@ class Verifier:
                                  f"got {t.dtype} {tuple(t.shape)}")
             if t.device.type != "cuda":
                 raise ValueError("inputs must live in GPU memory")
-        if row_stats is not None and (row_stats.device.type != "cuda" or
-                                      row_stats.numel() * row_stats.element_size()
-                                      < B * K * (2 * L + 1) * 16):
-            raise ValueError("row_stats must be a device buffer of B*K*(2L+1) statistics")
+        if row_stats is not None:
+            _check_bytes(row_stats, B * K * (2 * L + 1) * 16, "row_stats")
         ins = SvInputs(B, K, L, V, _dtype_code(target), target.data_ptr(), draft.data_ptr(),
                        tokens.data_ptr(), temperature.data_ptr(), u_accept.data_ptr(),
                        u_correct.data_ptr(), _ptr(row_stats))
@@ -274,6 +283,11 @@ class LmHead:
                                  f"got {t.dtype} {tuple(t.shape)}")
             if t.device.type != "cuda":
                 raise ValueError("inputs must live in GPU memory")
+        if stats is not None:
+            if not (group >= 1 and stride >= group and offset >= 0):
+                raise ValueError("stats slots need group >= 1, stride >= group, offset >= 0")
+            last = ((R - 1) // group) * stride + offset + (R - 1) % group if R > 0 else -1
+            _check_bytes(stats, (last + 1) * self.STAT_BYTES, "stats")
         ins = SvLmInputs(R, d, V, hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr())
         outs = SvLmOutputs(self.logits.data_ptr(), _ptr(stats), group, stride, offset)
         if stream is None:

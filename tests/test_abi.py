@@ -161,6 +161,15 @@ class _Arg:
     def is_contiguous(self):
         return self._c
 
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
 
 def test_python_binding_checks_every_argument(lib):
     """Shape, dtype, layout and device are checked for every argument of the
@@ -194,6 +203,28 @@ def test_python_binding_checks_every_argument(lib):
                 a[i] = b
                 with pytest.raises(ValueError, match=msg):
                     type(obj).__call__(obj, *a)
+    # the raw statistics buffers: dtype, layout, device and size
+    u8 = torch.uint8
+    good_h = [_Arg(s_, t_) for s_, t_ in hargs]
+    need = ((R - 1) // 2 * 5 + 1 + (R - 1) % 2 + 1) * 16     # group 2, stride 5, offset 1
+    with pytest.raises(AttributeError, match="data_ptr"):
+        h(*good_h, stats=_Arg((need,), u8), group=2, stride=5, offset=1)
+    for b, msg in [(_Arg((need - 1,), u8), "bytes"), (_Arg((need,), f32), "uint8"),
+                   (_Arg((need,), u8, contiguous=False), "uint8"),
+                   (_Arg((need,), u8, device="cpu"), "GPU memory")]:
+        with pytest.raises(ValueError, match=msg):
+            h(*good_h, stats=b, group=2, stride=5, offset=1)
+    for grp, strd, off in [(0, 5, 1), (3, 2, 0), (2, 5, -1)]:
+        with pytest.raises(ValueError, match="group"):
+            h(*good_h, stats=_Arg((1 << 20,), u8), group=grp, stride=strd, offset=off)
+    good_v = [_Arg(s_, t_) for s_, t_ in vargs]
+    nst = B * K * (2 * L + 1) * 16
+    with pytest.raises(AttributeError, match="data_ptr"):
+        v(*good_v, row_stats=_Arg((nst,), u8))
+    for b, msg in [(_Arg((nst - 16,), u8), "bytes"), (_Arg((nst,), i32), "uint8"),
+                   (_Arg((nst,), u8, device="cpu"), "GPU memory")]:
+        with pytest.raises(ValueError, match=msg):
+            v(*good_v, row_stats=b)
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -93,7 +93,14 @@ def test_small_parity(name, w, over):
     for seed in (1, 2):
         g, ref = _parity(*_inputs(ws, seed), f"{name}/seed{seed}")
         if "shared" in name:   # the case is only worth its name if drafts do meet at nodes
-            assert int(g["rows_streamed"].sum()) < ws.B * ws.K * ws.L
+            # at j = 0 every draft stands on the root, so without any sharing below
+            # it a request reads 1 + K (L - 1) node rows; fewer means deeper nodes met
+            assert int(g["rows_streamed"].sum()) < ws.B * (1 + ws.K * (ws.L - 1))
+            # and the oracle's tokens put two drafts on one node at depth >= 2
+            tok = ref["tokens"]
+            deep = sum(len({tuple(tok[b, k, :j]) for k in range(ws.K)}) < ws.K
+                       for b in range(ws.B) for j in range(2, ws.L))
+            assert deep > 0, "no node at depth >= 2 is shared"
 
 
 def test_temperatures():

@@ -435,18 +435,73 @@ def test_rows_never_read_cannot_invalidate():
     assert (c["flags"] == oracle.FLAG_INVALID).all()
 
 
-def test_golden_worked_examples():
+def _golden_examples():
     with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
-        ex = json.load(f)["examples"]
+        return json.load(f)["examples"]
+
+
+def _golden_inputs(e):
+    K, L, V = e["K"], e["L"], e["V"]
+    tgt = np.log(np.array(e["target_probs"], np.float64)).astype(np.float32)[None]
+    drf = np.log(np.array(e["draft_probs"], np.float64)).astype(np.float32)[None]
+    assert tgt.shape == (1, K, L + 1, V) and drf.shape == (1, K, L, V)
+    return (tgt, drf, np.array(e["tokens"], np.int32)[None],
+            np.array([e["T"]], np.float32), np.array(e["u_accept"], np.float32)[None],
+            np.array([e["u_correct"]], np.float32))
+
+
+def distinct_node_rows(tok, L):
+    """Upper bound on the rows any rule may read for one request: the number of
+    distinct nodes of its draft tree (prefixes of length 0..L for target rows,
+    0..L-1 for draft rows), counted from the tokens alone."""
+    K = tok.shape[0]
+    t = sum(len({tuple(tok[k, :j]) for k in range(K)}) for j in range(L + 1))
+    d = sum(len({tuple(tok[k, :j]) for k in range(K)}) for j in range(L))
+    return t + d
+
+
+def _shared_prefix_batch(rng, B=300, K=4, L=3, V=5, identical=False):
+    """Drafts that share prefixes often (V = 5, peaked rows) and target rows close
+    to the draft rows, so acceptances are frequent and later drafts are examined
+    below an accepted node.  identical: every draft repeats draft 0, so the tree
+    is one chain of 2L + 1 node rows."""
+    tgt, drf, tok, temps, ua, uc = _random_batch(rng, B, K, L, V, T=0.5, same_rows=False)
+    drf = (tgt[:, :, :L] + 0.1 * rng.standard_normal(drf.shape)).astype(np.float32)
+    tok[:, 1] = tok[:, 0]                       # draft 1 repeats draft 0
+    tok[:, 3, :2] = tok[:, 2, :2]               # draft 3 shares two tokens with draft 2
+    if identical:
+        tok[:] = tok[:, :1]
+    for b in range(B):                          # rows follow the node rule
+        for k in range(K):
+            for j in range(L + 1):
+                for c in range(k):
+                    if (tok[b, c, :j] == tok[b, k, :j]).all():
+                        tgt[b, k, j] = tgt[b, c, j]
+                        if j < L:
+                            drf[b, k, j] = drf[b, c, j]
+                        break
+    return tgt, drf, tok, temps, ua, uc
+
+
+def test_rows_read_within_distinct_nodes():
+    """The rows-read counter (the method's algorithmic bytes) never exceeds the
+    number of distinct node rows of the request's draft tree."""
+    rng = np.random.default_rng(31)
+    for identical in (False, True):
+        tgt, drf, tok, temps, ua, uc = _shared_prefix_batch(rng, identical=identical)
+        bound = np.array([distinct_node_rows(tok[b], tok.shape[2]) for b in range(len(tok))])
+        if identical:
+            assert (bound == 2 * tok.shape[2] + 1).all()
+        for method in ("multidraft", "spectr"):
+            o = oracle.verify(method, tgt, drf, tok, temps, ua, uc)
+            assert (o["counters"][:, 2] <= bound).all(), method
+            assert (o["counters"][:, 2] >= 2).all(), method       # the root pair at least
+
+
+def test_golden_worked_examples():
+    ex = _golden_examples()
     for e in ex:
-        K, L, V = e["K"], e["L"], e["V"]
-        tgt = np.log(np.array(e["target_probs"], np.float64)).astype(np.float32)[None]
-        drf = np.log(np.array(e["draft_probs"], np.float64)).astype(np.float32)[None]
-        assert tgt.shape == (1, K, L + 1, V) and drf.shape == (1, K, L, V)
-        tok = np.array(e["tokens"], np.int32)[None]
-        ua = np.array(e["u_accept"], np.float32)[None]
-        uc = np.array([e["u_correct"]], np.float32)
-        temps = np.array([e["T"]], np.float32)
+        tgt, drf, tok, temps, ua, uc = _golden_inputs(e)
         for method in e["methods"]:
             o = oracle.verify(method, tgt, drf, tok, temps, ua, uc, diagnostics=True)
             exp = e["expect"]
@@ -454,6 +509,8 @@ def test_golden_worked_examples():
             assert o["draft_index"][0] == exp["draft_index"], (e["name"], method)
             assert o["correction"][0] == exp["correction"], (e["name"], method)
             assert abs(o["resid_mass"][0] - exp["resid_mass"]) < 1e-6, (e["name"], method)
+            if "rows_read" in exp:   # distinct node rows whose logits the rules read
+                assert o["counters"][0, 2] == exp["rows_read"][method], (e["name"], method)
             want = np.array([[np.nan if v is None else v for v in row]
                              for row in exp["accept_prob"]])
             got = o["accept_prob"][0]
@@ -574,12 +631,20 @@ SPECTR_NUMERIC_MUTANTS = {
 }
 
 
+# the rows-read counter keyed by the reading draft instead of the node's owner
+ROWS_MUTANTS = {
+    "rows_counted_per_draft": ("r->touched[(target ? j : r->L + 1 + j) * r->K + c] = 1;",
+                               "r->touched[(target ? j : r->L + 1 + j) * r->K + k] = 1;"),
+}
+
+
 @pytest.fixture(scope="module")
 def mutant_libs(tmp_path_factory):
     d = tmp_path_factory.mktemp("mutants")
     src = open(oracle.SRC).read()
     libs = {}
-    for name, (old, new) in {**MUTANTS, **SPECTR_MUTANTS, **SPECTR_NUMERIC_MUTANTS}.items():
+    for name, (old, new) in {**MUTANTS, **SPECTR_MUTANTS, **SPECTR_NUMERIC_MUTANTS,
+                             **ROWS_MUTANTS}.items():
         assert src.count(old) == 1, name
         p = d / f"{name}.c"
         p.write_text(src.replace(old, new))
@@ -636,3 +701,25 @@ def test_planted_spectr_numeric_mistake_fails_a_pin(mutant_libs, name):
     lib = mutant_libs[name]
     assert not (spectr_near_identical_ok(lib) and spectr_near_disjoint_ok(lib)
                 and spectr_many_candidates_ok(lib)), name
+
+
+@pytest.mark.parametrize("name", sorted(ROWS_MUTANTS))
+def test_planted_rows_read_mistake_fails_a_pin(mutant_libs, name):
+    """A rows-read counter that counts the node rows of shared nodes once per
+    reading draft must miss a hand-derived count or the distinct-node bound."""
+    lib = mutant_libs[name]
+    caught = False
+    for e in _golden_examples():
+        args = _golden_inputs(e)
+        for method in e["methods"]:
+            exp = e["expect"].get("rows_read", {})
+            if method in exp:
+                o = oracle.verify(method, *args, lib_path=lib)
+                caught |= o["counters"][0, 2] != exp[method]
+    rng = np.random.default_rng(31)
+    for identical in (False, True):
+        tgt, drf, tok, temps, ua, uc = _shared_prefix_batch(rng, identical=identical)
+        o = oracle.verify("multidraft", tgt, drf, tok, temps, ua, uc, lib_path=lib)
+        bound = np.array([distinct_node_rows(tok[b], tok.shape[2]) for b in range(len(tok))])
+        caught |= bool((o["counters"][:, 2] > bound).any())
+    assert caught, name

@@ -308,20 +308,38 @@ def test_misaligned_rows_take_the_scalar_path():
 
 # ---------------------------------------------------------------- full sizes
 # The five workloads at their full shapes, in the launch configuration the
-# benchmark times (no diagnostics); the oracle checks a sample of requests.
+# benchmark times (no diagnostics).  Every request of the batch is checked
+# against the oracle, which runs over host copies of 64 requests at a time.
 
 FULL = list(W)
+FULL_CASES = [(n, m) for n in FULL for m in W[n].methods + (("spectr",) if W[n].K > 1 else ())]
 
 
-@pytest.mark.parametrize("seed,n", [(1234, 24), (4321, 64)], ids=["seed1234", "seed4321"])
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name, seed, n):
-    """The whole batch at its full size on the GPU, n requests of it sampled
-    for the oracle."""
+@pytest.mark.parametrize("name,method", FULL_CASES, ids=[f"{n}-{m}" for n, m in FULL_CASES])
+def test_full_size_full_batch_parity(name, method):
+    """The whole batch at its full size on the GPU and every request of it
+    through the oracle."""
     w = W[name]
+    batch = pt.gpu_batch(w, 1234)
+    print(f"[case] full/{name} method={method} shape={tuple(batch['target'].shape)}", flush=True)
+    out = _verify(method, batch, diagnostics=False)
+    ref = pt.oracle_on_device_batch(method, batch)
+    rep = pt.compare(method, out, ref, list(range(w.B)), diagnostics=False,
+                     label=f"full/{name}/{method}")
+    pt.check(rep)
+    assert rep["n"] == w.B
+    del batch
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity_second_seed(name):
+    """A second full-size batch, 64 requests of it sampled for the oracle."""
+    w = W[name]
+    seed = 4321
     batch = pt.gpu_batch(w, seed)
     rng = np.random.default_rng(seed + 1)
-    req = sorted(rng.choice(w.B, size=min(w.B, n), replace=False).tolist())
+    req = sorted(rng.choice(w.B, size=min(w.B, 64), replace=False).tolist())
     for method in w.methods + (("spectr",) if w.K > 1 else ()):
         _parity(method, batch, f"full/{name}/seed{seed}", requests=req, diagnostics=False)
     del batch
