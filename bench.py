@@ -16,12 +16,19 @@ of MineDraft's two-batch schedule: each step verifies one batch on one HIP
 stream while the other batch is drafted on a second stream, roles alternating.
 
 The roofline object describes the row-statistics kernel (the one that streams
-the logits): achieved = bytes of the rows it streams per step (rows_streamed *
-V * sizeof(logit), reported by the library) / its time per step (its one or two
-launches), timed with HIP events recorded on the launch stream around those
-launches in every timed step.  The cpu_baseline object times the CPU oracle (unmodified,
-single-threaded per request) on a bounded sample of the same batch across the
-host's cores.
+the logits), timed with HIP events recorded on the launch stream around its
+launches in every timed step.  achieved = the method's algorithmic bytes per
+step -- the node rows the method itself reads (the oracle's count over the
+whole batch, each row once, V * sizeof(logit) bytes) -- over that kernel's
+time per step; roofline.sustained holds the bytes it actually streamed (its
+speculative over-read included) over the same time.  The cpu_baseline object
+times the CPU oracle (unmodified, single-threaded per request) on a bounded
+sample of the same batch across the host's cores; the oracle then runs over the
+rest of the batch untimed, and the parity object counts the requests of the
+timed batch whose integer outputs or flag bits differ from it (mismatches),
+apart from those the oracle puts within 1e-6 of a threshold (excused).
+Batches smaller than 1 GiB are rotated through enough copies that every step
+reads its logits from HBM, not from the memory-side cache.
 """
 from __future__ import annotations
 
@@ -114,40 +121,94 @@ def read_traffic(workload: str, method: str):
     return float(d["bytes_per_step"])
 
 
-def cpu_baseline(method, batch, w, target_cpu_s: float):
+def host_threads():
+    """Oracle worker threads: the host cores this process may run on, at most 16
+    (the host share of one GPU on the benchmark machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(method, batch, w, out, target_cpu_s: float, chunk: int = 64):
+    """The CPU oracle on the benchmark's own batch: timed on a bounded sample (the
+    first requests, about target_cpu_s of CPU work), then run untimed over the
+    rest of the batch, so that every request of the timed batch is checked
+    against the GPU's outputs `out` and the rows the method reads (A_visit)
+    are counted over the whole batch."""
     import numpy as np
     import oracle
     import synth
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     host1 = synth.to_host(batch, [0])
     t = time.perf_counter()
     oracle.verify(method, host1["target"], host1["draft"], host1["tokens"],
                   host1["temperature"], host1["u_accept"], host1["u_correct"])
     t_one = max(time.perf_counter() - t, 1e-4)
-    m = int(np.clip(round(target_cpu_s / t_one), threads, w.B))
-    reqs = list(range(m))
-    host = synth.to_host(batch, reqs)
-    t = time.perf_counter()
-    res = oracle.verify(method, host["target"], host["draft"], host["tokens"],
-                        host["temperature"], host["u_accept"], host["u_correct"], threads=threads)
-    wall = time.perf_counter() - t
-    # rows whose logits the method reads, as the oracle counts them (A_visit)
-    visit_rows = float(res["counters"][:m, 2].mean())
-    return {
+    m = int(np.clip(round(target_cpu_s / t_one), min(threads, w.B), w.B))
+
+    wall = 0.0
+
+    def run(reqs, timed):
+        nonlocal wall
+        host = synth.to_host(batch, reqs)          # the host copy is not timed
+        t = time.perf_counter()
+        r = oracle.verify(method, host["target"], host["draft"], host["tokens"],
+                          host["temperature"], host["u_accept"], host["u_correct"],
+                          threads=threads)
+        if timed:
+            wall += time.perf_counter() - t
+        return r
+
+    parts = []
+    for i in range(0, w.B, chunk):
+        reqs = list(range(i, min(i + chunk, w.B)))
+        head = [r for r in reqs if r < m]
+        if head:
+            parts.append(run(head, True))
+        if len(head) < len(reqs):
+            parts.append(run(reqs[len(head):], False))
+        if (i // chunk) % 4 == 3:
+            log(f"[bench] oracle: {min(i + chunk, w.B)} of {w.B} requests")
+    ref = {k: np.concatenate([p[k] for p in parts], axis=0) for k in parts[0]}
+    cpu = {
         "value": m * w.K * w.L / wall,
         "unit": "verified draft tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {m} of {w.B} requests of the same batch ({m * w.K * w.L} draft "
-                  f"tokens), fp64 C oracle, one request per thread, {wall:.2f} s wall",
-    }, {"requests": m, "oracle_rows_per_request": visit_rows}
+        "sample": f"first {m} of {w.B} requests of the timed batch ({m * w.K * w.L} draft "
+                  f"tokens), fp64 C oracle, one request per thread on {threads} threads "
+                  f"(host reports {os.cpu_count()} cores), {wall:.2f} s wall",
+    }
+    # the timed batch against the oracle: integers and flag bits bit-exact, except
+    # requests the oracle itself puts within 1e-6 of a threshold (or degenerate)
+    g = {k: out[k].cpu().numpy() for k in ("accept_len", "draft_index", "correction", "flags")}
+    mism = excused = ties = 0
+    for b in range(w.B):
+        of = int(ref["flags"][b])
+        tie = not (of & 2) and (ref["margin"][b] < 1e-6 or bool(of & 1))
+        ties += tie
+        same = all(int(g[k][b]) == int(ref[k][b]) for k in ("accept_len", "draft_index",
+                                                              "correction"))
+        same &= (int(g["flags"][b]) & 3) == (of & 3)
+        if not same:
+            if tie:
+                excused += 1
+            else:
+                mism += 1
+    parity = {"n": w.B, "mismatches": mism, "excused": excused, "oracle_ties": ties,
+              "near_tie_flagged_by_gpu": int(((g["flags"] & 4) != 0).sum())}
+    visit = {"requests": w.B, "oracle_rows_per_request": float(ref["counters"][:, 2].mean()),
+             "oracle_rows": int(ref["counters"][:, 2].sum())}
+    return cpu, parity, visit
 
 
 def cpu_baseline_draft(batch, u, w, target_cpu_s: float):
     import numpy as np
     import oracle
     import synth
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     host = lambda reqs: (synth.to_host(batch, reqs)["draft"],
                          batch["temperature"][reqs].cpu().numpy(), u[reqs].cpu().numpy())
     t = time.perf_counter()
@@ -464,6 +525,9 @@ def main():
     ap.add_argument("--d-draft", type=int, default=896, help="hidden size of the draft LM head")
     ap.add_argument("--pipeline", action="store_true",
                     help="time the two-batch verify/draft overlap on two streams")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies to cycle through (0: enough for 1 GiB, at least 8, "
+                         "when one batch is smaller than 1 GiB)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this many MiB (a "
                          "reference kernel of known traffic for rocprofv3 PMC runs)")
@@ -506,14 +570,27 @@ def main():
     torch.cuda.synchronize()
     es = 2 if w.dtype == torch.bfloat16 else 4
     dense = synth.dense_bytes(w)
+    # Inputs smaller than the memory-side cache would be served from it on every
+    # step after the first: rotate through copies at different addresses, at
+    # least 8 and at least 1 GiB of logits in all, so each step reads from HBM.
+    copies = args.rotate if args.rotate else (1 if dense >= (1 << 30)
+                                              else max(8, -(-(1 << 30) // dense)))
+    inputs = [batch] + [{k: v.clone() for k, v in batch.items()} for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    if copies > 1:
+        log(f"[bench] rotating {copies} input copies ({copies * dense / 2**30:.2f} GiB of logits)")
 
     ver = sv.Verifier(method, w.B, w.K, w.L, w.V, w.dtype)
-    args_in = (batch["target"], batch["draft"], batch["tokens"], batch["temperature"],
-               batch["u_accept"], batch["u_correct"])
+
+    def args_of(i):
+        bt = inputs[i % copies]
+        return (bt["target"], bt["draft"], bt["tokens"], bt["temperature"], bt["u_accept"],
+                bt["u_correct"])
+
     hip = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(args.warmup):
-        ver(*args_in, stream=stream)
+    for i in range(args.warmup):
+        ver(*args_of(i), stream=stream)
     torch.cuda.synchronize()
     evs = [[hip.create() for _ in range(sv.N_PHASE_EVENTS)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps of {method} on {name}")
@@ -521,7 +598,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ver(*args_in, stream=stream, events=evs[i])
+        ver(*args_of(i), stream=stream, events=evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -538,32 +615,37 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     st_mean = sum(stats_ms) / len(stats_ms)
     wk_mean = sum(walk_ms) / len(walk_ms)
-    achieved = stats_bytes / (st_mean * 1e-3) / 1e9
+    streamed_gbps = stats_bytes / (st_mean * 1e-3) / 1e9
     flags = ver.out["flags"].cpu()
     log(f"[bench] {ms_per_step:.3f} ms/step, stats {st_mean:.3f} ms, walk {wk_mean:.3f} ms, "
-        f"{achieved:.0f} GB/s node-row stream, {value / 1e6:.2f} M tokens/s")
+        f"{streamed_gbps:.0f} GB/s node-row stream, {value / 1e6:.2f} M tokens/s")
 
     copy_calibration(torch, args.copy_calibration_mib)
 
     traffic = read_traffic(name, method)
-    cpu = None
+    cpu = parity = None
+    roofline = {"bound": "hbm", "kernel": "rowstats_kernel", "achieved": None,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": None, "traffic": traffic}
     a_visit = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
-        cpu, visit = cpu_baseline(method, batch, w, args.cpu_seconds)
-        log(f"[bench] cpu baseline {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
-        # the method's own floor: the rows it must read (oracle count on the sample, scaled
-        # to the batch) over the step time, next to the rows the GPU streamed for the same
-        # requests
-        m = visit["requests"]
-        gpu_rows = float(ver.out["rows_streamed"][:m].float().mean())
-        est = visit["oracle_rows_per_request"] * w.B * w.V * es
-        a_visit = {"sample_requests": m,
+        log("[bench] cpu baseline and parity of the timed batch (oracle) ...")
+        cpu, parity, visit = cpu_baseline(method, batch, w, ver.out, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.0f} tokens/s on {cpu['cores']} threads; "
+            f"parity {parity}")
+        # algorithmic bytes: the rows the method itself reads (oracle count over the
+        # whole batch), each once
+        a_bytes = visit["oracle_rows"] * w.V * es
+        achieved = a_bytes / (st_mean * 1e-3) / 1e9
+        roofline.update(achieved=achieved, frac=achieved / HBM_PEAK_GBPS)
+        a_visit = {"requests": visit["requests"],
                    "oracle_rows_per_request": visit["oracle_rows_per_request"],
-                   "gpu_rows_streamed_per_request": gpu_rows,
-                   "est_bytes_per_step": est,
-                   "est_GBps": est / (ms_per_step * 1e-3) / 1e9,
-                   "frac_of_peak": est / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                   "gpu_rows_streamed_per_request": rows / w.B,
+                   "bytes_per_step": a_bytes,
+                   "step_GBps": a_bytes / (ms_per_step * 1e-3) / 1e9,
+                   "step_frac_of_peak": a_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    # what the statistics kernel streamed (its speculative over-read included)
+    roofline["sustained"] = {"achieved": streamed_gbps, "frac": streamed_gbps / HBM_PEAK_GBPS,
+                             "bytes_per_step": stats_bytes}
 
     line = {
         "metric": "verified draft tokens/s (B*K*L) + achieved HBM GB/s of verify kernel",
@@ -580,17 +662,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "method": method, "B": w.B, "K": w.K, "L": w.L,
                    "V": w.V, "logits": "bf16" if es == 2 else "fp32",
-                   "seed": args.seed},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "rowstats_kernel",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-        },
+                   "seed": args.seed, "input_copies": copies},
+        "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "detail": {
             "rowstats_ms": st_mean,
             "walk_ms": wk_mean,
