@@ -25,6 +25,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_FLAG_DEGENERATE, SV_FLAG_INVALID, SV_FLAG_NEAR_TIE = 1, 2, 4
 SV_NEAR_TIE = 1e-5
 SV_MAX_K, SV_MAX_L, SV_MAX_V = 64, 16, 1 << 22
+SV_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _vp = ctypes.c_void_p
 
@@ -96,6 +97,9 @@ def load_library(path: str = LIB_PATH):
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(SvInputs), ctypes.POINTER(SvOutputs),
                       ctypes.POINTER(SvLaunch)]
+    lib.spec_verify_multidraft_noalloc.restype = ctypes.c_int
+    lib.spec_verify_multidraft_noalloc.argtypes = [ctypes.POINTER(SvInputs),
+                                                   ctypes.POINTER(SvOutputs), _vp]
     lib.sv_draft_workspace_size.restype = ctypes.c_size_t
     lib.sv_draft_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.spec_draft_sample.restype = ctypes.c_int
@@ -145,19 +149,26 @@ class Verifier:
     """Holds outputs and workspace for repeated calls on inputs of one shape.
 
     method: "token", "block", "multidraft" or "spectr".  diagnostics=True also returns
-    row_lse [B][K][2L+1], accept_prob [B][K][L] and resid_mass [B]."""
+    row_lse [B][K][2L+1], accept_prob [B][K][L] and resid_mass [B].  noalloc=True
+    (multidraft only) calls spec_verify_multidraft_noalloc, which takes its
+    workspace from scratch memory the library holds, so no workspace tensor is
+    made here."""
 
     _ENTRY = {"token": "spec_verify_token", "block": "spec_verify_block",
               "multidraft": "spec_verify_multidraft", "spectr": "spec_verify_spectr"}
 
     def __init__(self, method, B, K, L, V, dtype, device="cuda", diagnostics=False,
-                 with_flags=True):
+                 with_flags=True, noalloc=False):
         lib = load_library()
         if method not in self._ENTRY:
             raise ValueError(f"unknown method {method!r}")
+        if noalloc and method != "multidraft":
+            raise ValueError("noalloc is a variant of spec_verify_multidraft only")
         self.method, self.shape = method, (B, K, L, V)
         self.dtype = dtype
-        self._fn = getattr(lib, self._ENTRY[method])
+        self.noalloc = noalloc
+        self._fn = getattr(lib, "spec_verify_multidraft_noalloc" if noalloc
+                           else self._ENTRY[method])
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.out = {"accept_len": torch.empty(B, **i32),
@@ -174,7 +185,7 @@ class Verifier:
         nbytes = workspace_size(B, K, L, V, _dtype_code(torch.empty((), dtype=dtype)))
         if nbytes == 0:
             raise ValueError(f"sizes out of range: B={B} K={K} L={L} V={V}")
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.workspace = None if noalloc else torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self._outs = SvOutputs(*[_ptr(self.out.get(k)) for k in
                                  ("accept_len", "draft_index", "correction", "flags",
                                   "row_lse", "accept_prob", "resid_mass", "rows_streamed")])
@@ -200,12 +211,17 @@ class Verifier:
                        u_correct.data_ptr(), _ptr(row_stats))
         if stream is None:
             stream = torch.cuda.current_stream(target.device).cuda_stream
-        ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
-        ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
-        rc = self._fn(ctypes.byref(ins), ctypes.byref(self._outs), ctypes.byref(ln))
+        if self.noalloc:
+            rc = self._fn(ctypes.byref(ins), ctypes.byref(self._outs), stream)
+            name = "spec_verify_multidraft_noalloc"
+        else:
+            ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))
+            ln = SvLaunch(stream, self.workspace.data_ptr(), self.workspace.numel(), ev)
+            rc = self._fn(ctypes.byref(ins), ctypes.byref(self._outs), ctypes.byref(ln))
+            name = self._ENTRY[self.method]
         if rc != SV_OK:
             msg = load_library().sv_status_string(rc).decode()
-            raise SpecVerifyError(f"{self._ENTRY[self.method]} failed: {msg} ({rc})")
+            raise SpecVerifyError(f"{name} failed: {msg} ({rc})")
         return self.out
 
 

@@ -19,6 +19,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/spec_verify.h"
 #include "sv_draft.hpp"
@@ -338,6 +339,40 @@ size_t draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
 
 }  // namespace
 
+// Scratch of spec_verify_multidraft_noalloc: the workspace of a multi-draft call,
+// held by the library in device memory of its own (one copy on every device the
+// library is used on, for the life of the process), for callers that cannot
+// allocate.  In host code `scratch` names a host-side stand-in, not the device
+// array: kernels receive the address hipGetSymbolAddress reports for the
+// current device, kept per device below.
+static_assert(SV_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on device `dev`, looked up once per device
+// with that device current.  nullptr if the lookup fails.
+void *scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void *ptr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (err != hipSuccess || !ptr || reinterpret_cast<uintptr_t>(ptr) % 256) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+    return ptr;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t sv_lm_workspace_size(int32_t R, int32_t d, int32_t V) {
@@ -443,6 +478,28 @@ int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_
 
 int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
     return verify(sv::kMethodSpecTr, in, out, ln, false);
+}
+
+int spec_verify_multidraft_noalloc(const sv_inputs *in, const sv_outputs *out, void *stream) {
+    if (!in || !out) return SV_EINVAL;
+    if (!sizes_ok(in->B, in->K, in->L, in->V, in->dtype)) return SV_EINVAL;
+    if (layout(in->B, in->K, in->L).total > SV_NOALLOC_SCRATCH_BYTES) return SV_EUNSUPPORTED;
+    if (in->B == 0) return SV_OK;
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess)
+            return SV_EHIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SV_EHIP;
+    }
+    void *ws = scratch_on(dev);
+    if (!ws) return SV_EHIP;
+    sv_launch ln;
+    std::memset(&ln, 0, sizeof ln);
+    ln.stream = stream;
+    ln.workspace = ws;
+    ln.workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
+    return verify(sv::kMethodBlockWalk, in, out, &ln, false);
 }
 
 const char *sv_status_string(int status) {

@@ -32,7 +32,8 @@
  * Every call is asynchronous on the caller's HIP stream: it validates its
  * arguments on the host, launches kernels and returns without synchronising.
  * The library never allocates device memory; scratch comes from the caller's
- * workspace.  Calls that share a workspace must be ordered on one stream.
+ * workspace (spec_verify_multidraft_noalloc uses scratch the library holds
+ * itself).  Calls that share a workspace must be ordered on one stream.
  *
  * Work done per request: the softmax statistics of the rows the walk reads
  * first (the root pair and the rows of each draft with a new first token) are
@@ -207,6 +208,24 @@ int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_
  * inputs, outputs, workspace and events as spec_verify_multidraft; accept_prob
  * holds h of every test made (NaN for drafts not tested). */
 int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): spec_verify_multidraft
+ * with the workspace taken from scratch memory the library holds itself, a
+ * static device array of SV_NOALLOC_SCRATCH_BYTES on each device it is used on
+ * (held until the process ends).  The call allocates nothing.  The caller still
+ * passes inputs and outputs (device memory, as for spec_verify_multidraft);
+ * `stream` is the hipStream_t to launch on (NULL = the null stream of the
+ * current device), and the scratch of that stream's device is used.  Results
+ * equal spec_verify_multidraft's.  Sizes whose workspace
+ * (sv_workspace_size) exceeds SV_NOALLOC_SCRATCH_BYTES return SV_EUNSUPPORTED
+ * before any launch; B = 512, K = L = 8 still fits, B = 1024, K = 4, L = 8 does
+ * not.  Every call on one device shares that device's scratch: calls that can
+ * overlap on one device (different streams, or different threads without
+ * ordering) race and must not be issued; calls ordered on one stream are safe.
+ * Phase events are not recorded. */
+#define SV_NOALLOC_SCRATCH_BYTES (128u << 20)
+int spec_verify_multidraft_noalloc(const sv_inputs *in, const sv_outputs *out, void *stream);
 
 /* ------------------------------------------------------------- drafting */
 

@@ -329,3 +329,20 @@ def test_lm_head_host_validation(lib):
     # partial (max, sum) per row and 128-column block
     assert lib.sv_lm_workspace_size(36864, 3584, 151936) >= 36864 * 1187 * 12
     assert lib.sv_lm_workspace_size(4, 100, 16) == 0
+
+
+def test_noalloc_entry_checks_sizes_on_the_host(lib):
+    """spec_verify_multidraft_noalloc refuses null arguments and sizes whose
+    workspace exceeds its scratch before any device call."""
+    f = lib.spec_verify_multidraft_noalloc
+    ins, outs, _ = _fake(B=2, K=4, L=4, V=64)
+    assert f(None, ctypes.byref(outs), None) == sv.SV_EINVAL
+    assert f(ctypes.byref(ins), None, None) == sv.SV_EINVAL
+    ins.K = 0
+    assert f(ctypes.byref(ins), ctypes.byref(outs), None) == sv.SV_EINVAL
+    big = sv.SvInputs(1024, 4, 8, 151936, sv.SV_BF16, 1, 1, 1, 1, 1, 1, None)
+    assert sv.workspace_size(1024, 4, 8, 151936, sv.SV_BF16) > sv.SV_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), ctypes.byref(outs), None) == sv.SV_EUNSUPPORTED
+    text = open(HEADER).read()
+    m = re.search(r"^#define SV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text, flags=re.M)
+    assert m and int(m.group(1)) << int(m.group(2)) == sv.SV_NOALLOC_SCRATCH_BYTES
