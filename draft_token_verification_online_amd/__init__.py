@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libspec_verify.so")
 
 SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EHIP, SV_EWORKSPACE = range(5)
 SV_F32, SV_BF16 = 0, 1
-SV_FLAG_DEGENERATE, SV_FLAG_INVALID, SV_FLAG_NEAR_TIE = 1, 2, 4
+SV_FLAG_DEGENERATE, SV_FLAG_INVALID, SV_FLAG_NEAR_TIE, SV_FLAG_REDONE = 1, 2, 4, 8
 SV_NEAR_TIE = 1e-5
 SV_MAX_K, SV_MAX_L, SV_MAX_V = 64, 16, 1 << 22
 SV_NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -92,7 +92,7 @@ def load_library(path: str = LIB_PATH):
     lib.sv_workspace_size.restype = ctypes.c_size_t
     lib.sv_workspace_size.argtypes = [ctypes.c_int32] * 5
     for name in ("spec_verify_token", "spec_verify_block", "spec_verify_multidraft",
-                 "spec_verify_spectr"):
+                 "spec_verify_spectr", "spec_verify_spectr_bisect"):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(SvInputs), ctypes.POINTER(SvOutputs),
@@ -148,14 +148,16 @@ def _check_bytes(t, nbytes: int, what: str):
 class Verifier:
     """Holds outputs and workspace for repeated calls on inputs of one shape.
 
-    method: "token", "block", "multidraft" or "spectr".  diagnostics=True also returns
+    method: "token", "block", "multidraft", "spectr" or "spectr_bisect" (SpecTr with its
+    scaling factor found by plain bisection).  diagnostics=True also returns
     row_lse [B][K][2L+1], accept_prob [B][K][L] and resid_mass [B].  noalloc=True
     (multidraft only) calls spec_verify_multidraft_noalloc, which takes its
     workspace from scratch memory the library holds, so no workspace tensor is
     made here."""
 
     _ENTRY = {"token": "spec_verify_token", "block": "spec_verify_block",
-              "multidraft": "spec_verify_multidraft", "spectr": "spec_verify_spectr"}
+              "multidraft": "spec_verify_multidraft", "spectr": "spec_verify_spectr",
+              "spectr_bisect": "spec_verify_spectr_bisect"}
 
     def __init__(self, method, B, K, L, V, dtype, device="cuda", diagnostics=False,
                  with_flags=True, noalloc=False):

@@ -24,7 +24,9 @@
 #include "../../include/spec_verify.h"
 #include "sv_draft.hpp"
 #include "sv_lmhead.hpp"
+#include "sv_redo.hpp"
 #include "sv_rowstats.hpp"
+#include "sv_single.hpp"
 #include "sv_walk.hpp"
 
 namespace {
@@ -34,6 +36,8 @@ constexpr int kWalkThreads = 512;
 constexpr long long kMaxStatsGrid = 1LL << 22;
 constexpr long long kListGrid = 4096;
 constexpr int kMaxB = 1 << 24;
+constexpr int kRedoThreads = 512;
+constexpr int kMaxRedoGrid = 1 << 16;
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
 static_assert(SV_MAX_L == sv::kMaxL, "L limit");
@@ -41,6 +45,7 @@ static_assert(SV_MAX_V == sv::kMaxV, "V limit");
 static_assert(SV_FLAG_DEGENERATE == sv::kFlagDegenerate, "flag bits");
 static_assert(SV_FLAG_INVALID == sv::kFlagInvalid, "flag bits");
 static_assert(SV_FLAG_NEAR_TIE == sv::kFlagNearTie && SV_NEAR_TIE == sv::kNearTie, "flag bits");
+static_assert(SV_FLAG_REDONE == sv::kFlagRedone, "flag bits");
 static_assert(sizeof(sv::RowStat) == 16, "row statistics layout");
 static_assert(sizeof(sv_row_stat) == sizeof(sv::RowStat) && offsetof(sv_row_stat, sum) == 8,
               "sv_row_stat is the library's row statistics layout");
@@ -58,13 +63,31 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
 }
 
 // Workspace: row statistics | walk states | node rows flagged for the second
-// round (bytes, then the same rows as a list) | list length | node lists of
-// the walk (K >= 3 only: a node sees a second mass sweep only with three or
-// more drafts).
+// round (bytes, then the same rows as a list) | list length | requests marked
+// for re-evaluation in fp64 | node lists of the walk (K >= 3 only: a node sees
+// a second mass sweep only with three or more drafts).
 struct Layout {
-    size_t stats, state, need, list, count, nodes, total;
+    size_t stats, state, need, list, count, redo, nodes, total;
     bool has_nodes;
 };
+
+// Single-draft workspace (K = 1 without given statistics): slice statistics
+// of every row | residual slice sums per position.
+struct SingleLayout {
+    size_t part, rpart, total;
+    int NS;
+};
+
+SingleLayout single_layout(int32_t B, int32_t L, int32_t V) {
+    SingleLayout l;
+    const int nch = (V + sv::kChunk - 1) / sv::kChunk;
+    l.NS = (nch + sv::kSliceChunks - 1) / sv::kSliceChunks;
+    const size_t bs = static_cast<size_t>(B) * l.NS;
+    l.part = 0;
+    l.rpart = align_up(bs * (2 * L + 1) * sizeof(sv::SliceStat), 256);
+    l.total = l.rpart + align_up(bs * (L + 1) * sizeof(double), 256);
+    return l;
+}
 
 Layout layout(int32_t B, int32_t K, int32_t L) {
     Layout l;
@@ -74,7 +97,8 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.need = l.state + align_up(static_cast<size_t>(B) * sizeof(sv::WalkState), 256);
     l.list = l.need + align_up(bkl, 256);
     l.count = l.list + align_up(2 * bkl * sizeof(sv::RowRef), 256);
-    l.nodes = l.count + 256;
+    l.redo = l.count + 256;
+    l.nodes = l.redo + align_up(static_cast<size_t>(B), 256);
     l.has_nodes = K >= 3;
     l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
                                            static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
@@ -95,6 +119,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     const bool given = in->row_stats != nullptr;
     // a second round only pays when several drafts can share an accepted prefix
     const bool two_round = method != sv::kMethodToken && in->K > 1 && !diagnostics && !given;
+    const bool spectr = method == sv::kMethodSpecTr || method == sv::kMethodSpecTrBisect;
     const Layout lay = layout(in->B, in->K, in->L);
     char *ws = static_cast<char *>(ln->workspace);
 
@@ -117,7 +142,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     // through acceptances at every position before it: with several drafts it
     // streams the root pair and the position-1 node of every first token, and
     // a walk that gets further stops and lists the rest (the second round).
-    sa.depth = (method == sv::kMethodSpecTr && two_round) ? (in->L < 2 ? in->L : 2) : in->L;
+    sa.depth = (spectr && two_round) ? (in->L < 2 ? in->L : 2) : in->L;
     auto grid_for = [&](int rows_per_draft) {
         const long long n = static_cast<long long>(in->B) * in->K * rows_per_draft;
         return static_cast<unsigned>(n < kMaxStatsGrid ? n : kMaxStatsGrid);
@@ -135,7 +160,8 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.K = in->K;
     wa.L = in->L;
     wa.V = in->V;
-    wa.method = method;
+    wa.method = spectr ? sv::kMethodSpecTr : method;
+    wa.rho_bisect = method == sv::kMethodSpecTrBisect ? 1 : 0;
     wa.all_nodes = (diagnostics || given) ? 1 : 0;
     wa.fv_depth = sa.depth;
     wa.stats_given = given ? 1 : 0;
@@ -154,6 +180,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.row_lse = out->row_lse;
     wa.accept_prob = out->accept_prob;
     wa.resid_mass = out->resid_mass;
+    wa.redo = reinterpret_cast<unsigned char *>(ws + lay.redo);
 
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
@@ -165,7 +192,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     }
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
     auto walk = [&]() {
-        if (method == sv::kMethodSpecTr)
+        if (spectr)
             hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E, true>), dim3(in->B),
                                dim3(kWalkThreads), 0, stream, wa);
         else
@@ -190,7 +217,95 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         wa.round = 2;   // only the stopped walks run
         if ((err = walk()) != hipSuccess) return err;
     }
+    // requests with a decision within the fp32 error of its threshold, again in fp64
+    sv::RedoArgs ra;
+    ra.tgt = in->target_logits;
+    ra.drf = in->draft_logits;
+    ra.tok = in->draft_tokens;
+    ra.temp = in->temperature;
+    ra.ua = in->u_accept;
+    ra.uc = in->u_correct;
+    ra.redo = wa.redo;
+    ra.B = in->B;
+    ra.K = in->K;
+    ra.L = in->L;
+    ra.V = in->V;
+    ra.method = wa.method;
+    ra.accept_len = out->accept_len;
+    ra.draft_index = out->draft_index;
+    ra.correction = out->correction;
+    ra.flags = out->flags;
+    ra.accept_prob = out->accept_prob;
+    ra.resid_mass = out->resid_mass;
+    const unsigned rgrid = static_cast<unsigned>(in->B < kMaxRedoGrid ? in->B : kMaxRedoGrid);
+    hipLaunchKernelGGL((sv::redo_kernel<kRedoThreads, RD, E>), dim3(rgrid), dim3(kRedoThreads), 0,
+                       stream, ra);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     return record(ln, 4, stream);
+}
+
+// Bytes of workspace a call needs: the walk's layout, or for one draft the
+// single-draft layout when it is larger (the two are never used together).
+size_t workspace_total(int32_t B, int32_t K, int32_t L, int32_t V) {
+    size_t n = layout(B, K, L).total;
+    if (K == 1) {
+        const size_t s = single_layout(B, L, V).total;
+        if (s > n) n = s;
+    }
+    return n;
+}
+
+constexpr long long kMaxSingleGrid = 1LL << 20;
+
+template <typename E, bool VEC>
+hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
+                         int method) {
+    using RD = typename sv::RowOf<E, VEC>::type;
+    constexpr int NT = sv::kSingleThreads;
+    hipStream_t stream = static_cast<hipStream_t>(ln->stream);
+    const SingleLayout lay = single_layout(in->B, in->L, in->V);
+    char *ws = static_cast<char *>(ln->workspace);
+    sv::SingleArgs a;
+    a.tgt = in->target_logits;
+    a.drf = in->draft_logits;
+    a.tok = in->draft_tokens;
+    a.temp = in->temperature;
+    a.ua = in->u_accept;
+    a.uc = in->u_correct;
+    a.part = reinterpret_cast<sv::SliceStat *>(ws + lay.part);
+    a.rpart = reinterpret_cast<double *>(ws + lay.rpart);
+    a.B = in->B;
+    a.L = in->L;
+    a.V = in->V;
+    a.NS = lay.NS;
+    a.method = method;
+    a.accept_len = out->accept_len;
+    a.draft_index = out->draft_index;
+    a.correction = out->correction;
+    a.flags = out->flags;
+    a.rows_streamed = out->rows_streamed;
+    a.row_lse = out->row_lse;
+    a.accept_prob = out->accept_prob;
+    a.resid_mass = out->resid_mass;
+    auto grid = [](long long n) {
+        return static_cast<unsigned>(n < kMaxSingleGrid ? n : kMaxSingleGrid);
+    };
+    const long long n1 = static_cast<long long>(in->B) * (2 * in->L + 1) * lay.NS;
+    const long long n2 = static_cast<long long>(in->B) * (in->L + 1) * lay.NS;
+    hipError_t err;
+    if ((err = record(ln, 0, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL((sv::single_stats_kernel<NT, RD, E>), dim3(grid(n1)), dim3(NT), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record(ln, 1, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL((sv::single_partial_kernel<NT, RD, E>), dim3(grid(n2)), dim3(NT), 0, stream,
+                       a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((sv::single_final_kernel<NT, RD, E>), dim3(grid(in->B)), dim3(NT), 0, stream,
+                       a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    for (int i = 2; i < 5; ++i)
+        if ((err = record(ln, i, stream)) != hipSuccess) return err;
+    return hipSuccess;
 }
 
 int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
@@ -209,10 +324,23 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
     if (ta % es || da % es) return SV_EINVAL;
     if (in->row_stats && reinterpret_cast<uintptr_t>(in->row_stats) % 16) return SV_EINVAL;
     if (!ln->workspace || reinterpret_cast<uintptr_t>(ln->workspace) % 256) return SV_EWORKSPACE;
-    if (ln->workspace_bytes < layout(in->B, in->K, in->L).total) return SV_EWORKSPACE;
+    if (ln->workspace_bytes < workspace_total(in->B, in->K, in->L, in->V)) return SV_EWORKSPACE;
 
     const bool vec = (in->V % 8 == 0) && (ta % 16 == 0) && (da % 16 == 0);
     hipError_t err;
+    if (in->K == 1 && !in->row_stats) {
+        // one draft: split across the vocabulary (SpecTr with one candidate is the
+        // token-level rule)
+        const int m1 = (method == sv::kMethodSpecTr || method == sv::kMethodSpecTrBisect)
+                           ? sv::kMethodToken : method;
+        if (in->dtype == SV_BF16)
+            err = vec ? launch_single<uint16_t, true>(in, out, ln, m1)
+                      : launch_single<uint16_t, false>(in, out, ln, m1);
+        else
+            err = vec ? launch_single<float, true>(in, out, ln, m1)
+                      : launch_single<float, false>(in, out, ln, m1);
+        return err == hipSuccess ? SV_OK : SV_EHIP;
+    }
     if (in->dtype == SV_BF16)
         err = vec ? launch<uint16_t, true>(in, out, ln, method)
                   : launch<uint16_t, false>(in, out, ln, method);
@@ -460,7 +588,7 @@ int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
 
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype) {
     if (!sizes_ok(B, K, L, V, dtype)) return 0;
-    const size_t n = layout(B, K, L).total;
+    const size_t n = workspace_total(B, K, L, V);
     return n ? n : 256;
 }
 
@@ -480,10 +608,15 @@ int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_laun
     return verify(sv::kMethodSpecTr, in, out, ln, false);
 }
 
+int spec_verify_spectr_bisect(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln) {
+    return verify(sv::kMethodSpecTrBisect, in, out, ln, false);
+}
+
 int spec_verify_multidraft_noalloc(const sv_inputs *in, const sv_outputs *out, void *stream) {
     if (!in || !out) return SV_EINVAL;
     if (!sizes_ok(in->B, in->K, in->L, in->V, in->dtype)) return SV_EINVAL;
-    if (layout(in->B, in->K, in->L).total > SV_NOALLOC_SCRATCH_BYTES) return SV_EUNSUPPORTED;
+    if (workspace_total(in->B, in->K, in->L, in->V) > SV_NOALLOC_SCRATCH_BYTES)
+        return SV_EUNSUPPORTED;
     if (in->B == 0) return SV_OK;
     int dev = -1;
     if (stream) {

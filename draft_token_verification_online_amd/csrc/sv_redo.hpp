@@ -1,0 +1,474 @@
+// sv_redo.hpp -- requests re-evaluated in fp64.
+//
+// The fast kernels form every exponential in fp32 (one v_exp_f32 per element),
+// so an acceptance probability h or a residual mass carries a relative error
+// of order 1e-7, amplified by the conditioning of the rule (GBV's
+// h = R / (R + 1 - w) by ~1 / (R + 1 - w)).  A decision whose threshold lies
+// within that error of its uniform could come out differently in exact
+// arithmetic.  The fast walks therefore mark every request with such a decision
+// (the margin test of SV_FLAG_NEAR_TIE, widened by a first-order error estimate
+// for ill-conditioned tests), and this kernel takes each marked request again
+// from the start in fp64: row statistics M = max_v l_v and S = sum_v
+// exp((l_v - M) / T), every probability exp((l_v - M) / T) / S (the exponentials
+// in double precision), every residual
+// mass, weight chain, scaling-factor search and inverse-CDF draw in double, with
+// the rules stated in sv_walk.hpp (token level, GBV over K drafts, SpecTr).
+// Its integer outputs differ from exact arithmetic only where a decision lies
+// within double rounding (~1e-13) of its threshold.  One workgroup per marked
+// request; the others return at once.  It is written for clarity, not speed:
+// marked requests are rare (a decision within ~1e-5 of its threshold).
+#pragma once
+
+#include "sv_device.hpp"
+#include "sv_walk.hpp"
+
+namespace sv {
+
+constexpr int kFlagRedone = 8;
+
+struct RedoArgs {
+    const void *tgt;              // [B][K][L+1][V]
+    const void *drf;              // [B][K][L][V]
+    const int32_t *tok;           // [B][K][L]
+    const float *temp, *ua, *uc;  // [B], [B][K][L], [B]
+    const unsigned char *redo;    // [B]: re-evaluate request b when nonzero
+    int B, K, L, V;
+    int method;                   // kMethodToken, kMethodBlockWalk or kMethodSpecTr
+    int32_t *accept_len, *draft_index, *correction, *flags;
+    float *accept_prob, *resid_mass;
+};
+
+// LDS of one re-evaluation.
+struct RedoShared {
+    int x[kMaxK * kMaxL];
+    unsigned char can[kMaxK * (kMaxL + 1)];
+    unsigned char have[kMaxK * (2 * kMaxL + 1)];
+    unsigned char ok[kMaxK * (2 * kMaxL + 1)];
+    float M[kMaxK * (2 * kMaxL + 1)];
+    double S[kMaxK * (2 * kMaxL + 1)];
+    int H[kMaxK];
+    double red[16];
+    float fred[16];
+    int ired[16];
+    double pair[2];
+};
+
+// Re-evaluate request b in fp64 and overwrite its outputs (block-uniform call).
+template <int NT, typename RD, typename E>
+__device__ void redo_request(const RedoArgs &A, int b, RedoShared &sh) {
+    int *s_x = sh.x;
+    unsigned char *s_can = sh.can, *s_have = sh.have, *s_ok = sh.ok;
+    float *s_M = sh.M;
+    double *s_S = sh.S;
+    int *s_H = sh.H;
+    double *s_red = sh.red, *s_pair = sh.pair;
+    float *s_fred = sh.fred;
+    int *s_ired = sh.ired;
+    const int tid = threadIdx.x;
+    const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1;
+    const int nch = (V + kChunk - 1) / kChunk;
+    {
+        const long long bKL = static_cast<long long>(b) * K * L;
+        // exp((l - M) / T) taken as 2^((l - M) log2(e) / T)
+        const double cT = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+        const E *tgt = static_cast<const E *>(A.tgt);
+        const E *drf = static_cast<const E *>(A.drf);
+        for (int i = tid; i < K * L; i += NT) s_x[i] = A.tok[bKL + i];
+        for (int i = tid; i < K * RS; i += NT) s_have[i] = 0;
+        __syncthreads();
+        // node of (k, j): the lowest-index draft with the same first j tokens
+        for (int i = tid; i < K * L1; i += NT) {
+            const int k = i / L1, j = i % L1;
+            int c = k;
+            for (int cc = 0; cc < k; ++cc) {
+                int same = 1;
+                for (int t = 0; t < j; ++t) same &= (s_x[cc * L + t] == s_x[k * L + t]);
+                if (same) { c = cc; break; }
+            }
+            s_can[i] = static_cast<unsigned char>(c);
+        }
+        __syncthreads();
+        auto row = [&](bool target, int c, int j) {
+            return target ? RD(tgt + ((static_cast<long long>(b) * K + c) * L1 + j) * V, V)
+                          : RD(drf + ((static_cast<long long>(b) * K + c) * L + j) * V, V);
+        };
+        auto slot = [&](bool target, int c, int j) { return c * RS + (target ? j : L1 + j); };
+        int bad = 0;
+        // fp64 statistics of node row (target?, node of (k, j)); invalid rows mark
+        // the request
+        auto stats = [&](bool target, int k, int j) {
+            const int c = s_can[k * L1 + j];
+            const int sl = slot(target, c, j);
+            if (!s_have[sl]) {
+                const RD R = row(target, c, j);
+                float mx = -INFINITY;
+                int nan = 0;
+                for (int q = tid; q < nch; q += NT) {
+                    float x[8];
+                    R.load(q, x);
+                    for (int e = 0; e < 8; ++e) {
+                        nan |= isnan(x[e]) || x[e] == INFINITY;
+                        mx = fmaxf(mx, x[e]);
+                    }
+                }
+                nan = __syncthreads_or(nan);
+                mx = block_max<NT>(mx, s_fred);
+                double s = 0.0;
+                if (!nan && mx > -INFINITY) {
+                    for (int q = tid; q < nch; q += NT) {
+                        float x[8];
+                        R.load(q, x);
+                        for (int e = 0; e < 8; ++e)
+                            s += exp2((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT);
+                    }
+                }
+                s = block_sum<NT>(s, s_red);
+                if (tid == 0) {
+                    s_M[sl] = mx;
+                    s_S[sl] = s;
+                    s_ok[sl] = !nan && mx > -INFINITY && s > 0.0 && isfinite(s);
+                    s_have[sl] = 1;
+                }
+                __syncthreads();
+            }
+            bad |= !s_ok[sl];
+            return sl;
+        };
+        auto prob = [&](int sl, float x) {
+            return exp2((static_cast<double>(x) - static_cast<double>(s_M[sl])) * cT) / s_S[sl];
+        };
+        // one drafted token's probability under node row (target?, node of (k, j))
+        auto prob_at = [&](bool target, int k, int j, int x) {
+            const int sl = stats(target, k, j);
+            const int c = s_can[k * L1 + j];
+            return prob(sl, row(target, c, j).at(x));
+        };
+        // block-wide sum of f(v, p(v), q(v)) over node (k, j)'s row pair
+        auto sweep = [&](int k, int j, auto f) {
+            const int c = s_can[k * L1 + j];
+            const int sp = stats(true, k, j), sq = stats(false, k, j);
+            const RD P = row(true, c, j), Q = row(false, c, j);
+            double acc = 0.0;
+            for (int q = tid; q < nch; q += NT) {
+                float xp[8], xq[8];
+                P.load(q, xp);
+                Q.load(q, xq);
+                for (int e = 0; e < 8; ++e) {
+                    const int v = kChunk * q + e;
+                    if (v < V) acc += f(v, prob(sp, xp[e]), prob(sq, xq[e]));
+                }
+            }
+            return block_sum<NT>(acc, s_red);
+        };
+        // inverse-CDF draw in token-id order over weights w(v, p, q) of node (k, j)
+        // (q = 0 when only the target row is involved): y = min{v : C_v > u Z};
+        // the last v of positive weight when rounding leaves none.  Returns -1
+        // when Z is not a positive finite number; *Z and *margin (distance of u Z
+        // to the nearest boundary, over Z) are set.
+        auto icdf = [&](int k, int j, bool with_q, auto w, double u, double *Z, double *margin) {
+            const int c = s_can[k * L1 + j];
+            const int sp = stats(true, k, j);
+            const int sq = with_q ? stats(false, k, j) : sp;
+            const RD P = row(true, c, j), Q = row(false, c, j);
+            const int per = (nch + NT - 1) / NT;   // contiguous chunks per thread
+            const int q0 = tid * per, q1 = min(q0 + per, nch);
+            auto weight = [&](int q, int e, const float *xp, const float *xq) {
+                const int v = kChunk * q + e;
+                if (v >= V) return 0.0;
+                return w(v, prob(sp, xp[e]), with_q ? prob(sq, xq[e]) : 0.0);
+            };
+            double mine = 0.0;
+            int lastpos = -1;
+            for (int q = q0; q < q1; ++q) {
+                float xp[8], xq[8];
+                P.load(q, xp);
+                if (with_q) Q.load(q, xq);
+                for (int e = 0; e < 8; ++e) {
+                    const double wv = weight(q, e, xp, xq);
+                    mine += wv;
+                    if (wv > 0.0) lastpos = kChunk * q + e;
+                }
+            }
+            const double pre = block_exclusive_scan<NT>(mine, s_red);
+            const double z = block_sum<NT>(mine, s_red);
+            *Z = z;
+            *margin = 0.0;
+            if (!(z > 0.0) || !isfinite(z)) return -1;
+            const double thr = u * z;
+            int cand = 0x7fffffff;
+            double cm = 0.0;
+            if (pre <= thr && pre + mine > thr) {
+                double C = pre;
+                for (int q = q0; q < q1 && cand == 0x7fffffff; ++q) {
+                    float xp[8], xq[8];
+                    P.load(q, xp);
+                    if (with_q) Q.load(q, xq);
+                    for (int e = 0; e < 8 && cand == 0x7fffffff; ++e) {
+                        const double before = C;
+                        C += weight(q, e, xp, xq);
+                        if (C > thr) {
+                            cand = kChunk * q + e;
+                            cm = fmin(C - thr, thr - before);
+                        }
+                    }
+                }
+            }
+            const int got = cand;
+            cand = block_min_int<NT>(cand, s_ired);
+            if (cand != 0x7fffffff) {
+                if (got == cand) s_pair[0] = cm;
+                __syncthreads();
+                *margin = s_pair[0] / z;
+                __syncthreads();
+                return cand;
+            }
+            return block_max_int<NT>(lastpos, s_ired);
+        };
+        auto same_prefix = [&](int a, int c, int n) {
+            int same = 1;
+            for (int t = 0; t < n; ++t) same &= (s_x[a * L + t] == s_x[c * L + t]);
+            return same;
+        };
+        auto ratio = [](double num, double den) {   // a drafted token with q = 0
+            return den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
+        };
+        auto chain = [&](double w, double num, double den) {
+            if (w == 0.0) return 0.0;
+            const double t = w * ratio(num, den);
+            return t < 1.0 ? t : 1.0;
+        };
+
+        float *hout = A.accept_prob ? A.accept_prob + bKL : nullptr;
+        if (hout)
+            for (int i = tid; i < K * L; i += NT) hout[i] = NAN;
+        const float *ub = A.ua + bKL;
+        double tie = INFINITY;
+        int flags = 0;
+        auto test = [&](int k, int m, double h) {   // u < h for position m of draft k
+            const double u = static_cast<double>(ub[k * L + m - 1]);
+            if (tid == 0 && hout) hout[k * L + m - 1] = static_cast<float>(h);
+            tie = fmin(tie, fabs(u - h));
+            return u < h;
+        };
+        const double uc = static_cast<double>(A.uc[b]);
+        int tau = 0, kstar = -1, y = -1, own = 0;
+        double Z = NAN, dm = INFINITY;
+        auto draw_target = [&](int k, int j) {   // the node's target row itself
+            return icdf(k, j, false, [](int, double p, double) { return p; }, uc, &Z, &dm);
+        };
+
+        if (A.method == kMethodToken) {
+            tau = L;
+            for (int j = 0; j < L && !bad; ++j) {
+                const int x = s_x[j];
+                const double p = prob_at(true, 0, j, x), q = prob_at(false, 0, j, x);
+                double a = ratio(p, q);
+                if (a > 1.0) a = 1.0;
+                if (!test(0, j + 1, a)) { tau = j; break; }
+            }
+            kstar = tau > 0 ? 0 : -1;
+            if (!bad) {
+                if (tau == L) {
+                    y = draw_target(0, L);
+                } else {
+                    y = icdf(0, tau, true, [](int, double p, double q) { return fmax(p - q, 0.0); },
+                             uc, &Z, &dm);
+                    if (y < 0) {
+                        flags |= kFlagDegenerate;
+                        y = draw_target(0, tau);
+                    }
+                }
+            }
+        } else if (A.method == kMethodSpecTr) {
+            // SpecTr: rho* = the smallest rho in [1, n] with c(beta(rho)) <= rho,
+            // by bisection to adjacent doubles; the feasibility test is taken in
+            // the form rounding cannot flip (quotient form for beta <= 2^-10)
+            int kacc = -1;
+            bool done = false;
+            for (int j = 0; j < L && !bad && !done; ++j) {
+                stats(true, own, j);
+                stats(false, own, j);
+                if (bad) break;
+                int n = 0;
+                for (int k = 0; k < K; ++k) n += same_prefix(k, own, j);
+                auto c_of = [&](double beta) {
+                    double cc = 0.0, t = 1.0;
+                    for (int i = 0; i < n; ++i) { cc += t; t *= 1.0 - beta; }
+                    return cc;
+                };
+                auto feasible = [&](double rho) {
+                    const double beta = sweep(own, j, [&](int, double p, double q) {
+                        return fmin(q, p / rho);
+                    });
+                    if (beta <= kQuotientFormBeta) return c_of(beta) <= rho;
+                    double xn = 1.0;
+                    for (int i = 0; i < n; ++i) xn *= 1.0 - beta;
+                    const double D = sweep(own, j, [&](int, double p, double q) {
+                        return fmax(p - rho * q, 0.0);
+                    });
+                    return D <= xn;
+                };
+                double rho = 1.0;
+                if (n > 1 && !feasible(1.0)) {
+                    double lo = 1.0, hi = static_cast<double>(n);
+                    for (;;) {
+                        const double mid = 0.5 * (lo + hi);
+                        if (!(mid > lo && mid < hi)) break;
+                        if (feasible(mid)) hi = mid;
+                        else lo = mid;
+                    }
+                    rho = hi;
+                }
+                int acc = -1;
+                for (int k = 0; k < K && acc < 0; ++k) {
+                    if (!same_prefix(k, own, j)) continue;
+                    const int x = s_x[k * L + j];
+                    const double p = prob_at(true, own, j, x), q = prob_at(false, own, j, x);
+                    double a = ratio(p, rho * q);
+                    if (a > 1.0) a = 1.0;
+                    if (test(k, j + 1, a)) acc = k;
+                }
+                if (acc < 0) {
+                    const double beta = sweep(own, j, [&](int, double p, double q) {
+                        return fmin(q, p / rho);
+                    });
+                    const double cc = c_of(beta);
+                    y = icdf(own, j, true, [&](int, double p, double q) {
+                        return fmax(p - cc * fmin(q, p / rho), 0.0);
+                    }, uc, &Z, &dm);
+                    if (y < 0) {
+                        flags |= kFlagDegenerate;
+                        y = draw_target(own, j);
+                    }
+                    tau = j;
+                    kstar = kacc;
+                    done = true;
+                } else {
+                    own = acc;
+                    kacc = acc;
+                }
+            }
+            if (!bad && !done) {
+                tau = L;
+                kstar = kacc;
+                y = draw_target(own, L);
+            }
+        } else {
+            // GBV over K drafts: residual omega(v) = [v not in H] max(alpha p_s - beta q_s, 0)
+            double alpha = 1.0, beta = 0.0, N = 1.0;
+            int nH = 0;
+            double w[kMaxL + 1], R[kMaxL + 1];
+            auto in_H = [&](int v) {
+                for (int i = 0; i < nH; ++i)
+                    if (s_H[i] == v) return true;
+                return false;
+            };
+            auto node_mass = [&]() {
+                return sweep(own, tau, [&](int v, double p, double q) {
+                    return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
+                });
+            };
+            for (int k = 0; k < K && tau < L && !bad; ++k) {
+                if (!same_prefix(k, own, tau)) continue;
+                const int x = s_x[k * L + tau];
+                if (in_H(x)) {
+                    beta += N;
+                    N = node_mass();
+                } else {
+                    // first position: the node residual omega / N against q_s
+                    const double ps = prob_at(true, own, tau, x), qs = prob_at(false, own, tau, x);
+                    const double om = fmax(alpha * ps - beta * qs, 0.0);
+                    w[tau + 1] = chain(1.0, om / N, qs);
+                    for (int j = tau + 1; j < L; ++j) {
+                        const int xj = s_x[k * L + j];
+                        w[j + 1] = chain(w[j], prob_at(true, k, j, xj), prob_at(false, k, j, xj));
+                    }
+                    if (bad) break;
+                    int acc = 0;
+                    for (int m = L; m > tau; --m) {
+                        double h;
+                        if (m == L) {
+                            h = w[L];
+                        } else {
+                            const double wm = w[m];
+                            R[m] = sweep(k, m, [&](int, double p, double q) {
+                                return fmax(wm * p - q, 0.0);
+                            });
+                            if (bad) break;
+                            const double d = R[m] + 1.0 - wm;
+                            h = d > 0.0 ? R[m] / d : 1.0;
+                        }
+                        if (test(k, m, h)) { acc = m; break; }
+                    }
+                    if (bad) break;
+                    if (acc > 0) {
+                        tau = acc;
+                        own = k;
+                        kstar = k;
+                        nH = 0;
+                        if (tau < L) {
+                            alpha = w[tau];
+                            beta = 1.0;
+                            N = R[tau];
+                        }
+                    } else {
+                        if (tid == 0) s_H[nH] = x;
+                        __syncthreads();
+                        ++nH;
+                        beta += N;
+                        N = node_mass();
+                    }
+                }
+                if (tau < L && !(N > 0.0)) {   // only rounding empties a residual
+                    flags |= kFlagDegenerate;
+                    alpha = 1.0;
+                    beta = 0.0;
+                    N = 1.0;
+                    nH = 0;
+                }
+            }
+            if (!bad) {
+                if (tau == L) {
+                    y = draw_target(own, L);
+                } else {
+                    y = icdf(own, tau, true, [&](int v, double p, double q) {
+                        return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
+                    }, uc, &Z, &dm);
+                    if (y < 0) {
+                        flags |= kFlagDegenerate;
+                        y = draw_target(own, tau);
+                    }
+                }
+            }
+        }
+        if (!bad && y < 0) bad = 1;
+        tie = fmin(tie, dm);
+        if (tie < kNearTie) flags |= kFlagNearTie;
+        if (tid == 0) {
+            if (bad) {
+                tau = -1;
+                kstar = -1;
+                y = -1;
+                flags = kFlagInvalid;
+                Z = NAN;
+            }
+            A.accept_len[b] = tau;
+            A.draft_index[b] = kstar;
+            A.correction[b] = y;
+            if (A.flags) A.flags[b] = flags | kFlagRedone;
+            if (A.resid_mass) A.resid_mass[b] = static_cast<float>(Z);
+        }
+        if (bad && hout)
+            for (int i = tid; i < K * L; i += NT) hout[i] = NAN;
+        __syncthreads();
+    }
+}
+
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void redo_kernel(RedoArgs A) {
+    __shared__ RedoShared sh;
+    for (int b = blockIdx.x; b < A.B; b += gridDim.x)
+        if (A.redo[b]) redo_request<NT, RD, E>(A, b, sh);   // block-uniform
+}
+
+}  // namespace sv

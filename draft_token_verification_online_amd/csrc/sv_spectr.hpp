@@ -298,4 +298,48 @@ __device__ void spectr_scale(const RD &P, const RD &Q, int nch, float MPc, doubl
     c_out = c_fin;
 }
 
+// rho* and c as spectr_scale returns them, found the way the SpecTr-GBV page
+// costs SpecTr's selection step (section 3, O(|Omega| log K)): plain bisection
+// of [1, n], one sweep per halving, until the bracket is below kRhoTol of rho --
+// about 24 + log2(n) sweeps, each normalised like the Newton search's.
+template <int NT, typename RD>
+__device__ void spectr_scale_bisect(const RD &P, const RD &Q, int nch, float MPc, double SP,
+                                    float MQc, double SQ, const Scale &c2, int n,
+                                    double &rho_out, double &c_out, double *red) {
+    const float ap = static_cast<float>(1.0 / SP), aq = static_cast<float>(1.0 / SQ);
+    const double apd = ap, aqd = aq;
+    // the condition at rho (>= 0 iff feasible) and c there, from one sweep
+    auto probe = [&](double rho, double *c) {
+        double sw[5];
+        sweep_excess<NT, RD>(P, Q, nch, MPc, MQc, ap, static_cast<float>(rho / SQ), c2, sw, red);
+        const double EPt = sw[3] + sw[4], EQt = sw[1] + sw[2];
+        const double kap = (aqd * EQt) / (apd * EPt);
+        const double B1 = sw[1] / EQt, B2 = sw[4] / EPt, D = sw[0] / (apd * EPt);
+        double g, dg, x;
+        feasibility(rho * kap, D, B1, B2, n, &g, &dg, &x);
+        *c = tries(x, n) / kap;
+        return (sw[0] > 0.0) ? g : 1.0;   // D(rho) = 0: nothing left uncovered
+    };
+    double c1;
+    if (probe(1.0, &c1) >= 0.0) {   // p = q (or rho = 1 already feasible)
+        rho_out = 1.0;
+        c_out = 1.0;
+        return;
+    }
+    double lo = 1.0, hi = static_cast<double>(n), c_hi = -1.0;
+    while (hi - lo > kRhoTol * hi) {
+        const double mid = 0.5 * (lo + hi);
+        double cm;
+        if (probe(mid, &cm) < 0.0) {
+            lo = mid;
+        } else {
+            hi = mid;
+            c_hi = cm;
+        }
+    }
+    if (c_hi < 0.0) probe(hi, &c_hi);   // rho = n was never probed
+    rho_out = hi;
+    c_out = c_hi;
+}
+
 }  // namespace sv

@@ -52,10 +52,19 @@ constexpr int kMaxV = 1 << 22;
 constexpr int kMethodToken = 0;
 constexpr int kMethodBlockWalk = 1;
 constexpr int kMethodSpecTr = 2;
+constexpr int kMethodSpecTrBisect = 3;   // SpecTr with rho* found by plain bisection
 constexpr int kFlagDegenerate = 1;
 constexpr int kFlagInvalid = 2;
 constexpr int kFlagNearTie = 4;
 constexpr double kNearTie = 1e-5;   // decisions closer than this to their threshold are flagged
+// Relative error of one probability formed from fp32 exponentials (v_exp_f32 and
+// the rounding of its argument), the unit of the first-order error estimates
+// that mark ill-conditioned GBV tests for re-evaluation in fp64.
+constexpr double kExpEps = 0x1p-23;
+// With diagnostics requested, a request whose estimated error of some h exceeds
+// this (a quarter of the 1e-5 the acceptance probabilities are reported to) is
+// taken again in fp64 too, so the reported h hold to fp64 however ill-conditioned.
+constexpr double kDiagEh = 2.5e-6;
 // Node lists: entries per wave, and the cutoff 2^-kListCut below which a
 // token's residual weight omega(v) / alpha leaves the list.
 constexpr int kWaveList = 2048;
@@ -76,6 +85,7 @@ struct WalkArgs {
     int stats_given;        // they came from the caller: no row was streamed here
     int round;              // 1, or 2 to resume the walks the first round suspended
     int two_round;          // a second round follows: the first may suspend
+    int rho_bisect;         // SpecTr: find rho* by plain bisection instead of histogram + Newton
     struct WalkState *state;     // [B]
     unsigned char *need;    // [B][K][L]: node rows flagged for the second round
     RowRef *list;           // the same rows as a list for the statistics kernel
@@ -83,6 +93,7 @@ struct WalkArgs {
     void *nodes;            // [B] node lists (node_list_bytes each), or null
     int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
     float *row_lse, *accept_prob, *resid_mass;
+    unsigned char *redo;    // [B]: 1 where a decision came within its error of its threshold
 };
 
 // Likelihood ratio from log2-probabilities, with the drafted-token convention:
@@ -707,6 +718,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     __shared__ double s_tile[kMaxTiles];
     __shared__ int s_H[kMaxK];
     __shared__ double s_w[kMaxL + 1];
+    __shared__ double s_werr;   // relative error estimate of the first weight of the chain
     __shared__ unsigned s_hist[SPECTR ? 2 * kHistBins : 1];
     __shared__ double s_red6[SPECTR ? 6 * NW : 1];
     __shared__ double s_br[4];
@@ -909,7 +921,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                 }
                 rho = 1.0;
                 cc = 1.0;
-                if (n > 1)
+                if (n > 1 && A.rho_bisect)
+                    spectr_scale_bisect<NT, RD>(RD(trow(cn, j), V), RD(drow(cn, j), V), nch,
+                                                shift_term(s_M[cn * RS + j], sc), s_S[cn * RS + j],
+                                                shift_term(s_M[cn * RS + L1 + j], sc),
+                                                s_S[cn * RS + L1 + j], sc, n, rho, cc, s_red6);
+                else if (n > 1)
                     spectr_scale<NT, RD>(RD(trow(cn, j), V), RD(drow(cn, j), V), nch,
                                          shift_term(s_M[cn * RS + j], sc), s_S[cn * RS + j],
                                          shift_term(s_M[cn * RS + L1 + j], sc),
@@ -972,6 +989,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     if (tid == 0) {
                         double w = (qs > 0.0) ? fmin(om / N / qs, 1.0) : (om > 0.0 ? 1.0 : 0.0);
                         s_w[tau + 1] = w;
+                        // omega(x) cancels when alpha p ~ beta q; N and q add a sum's error
+                        s_werr = (om > 0.0 ? (alpha * ps + beta * qs) * 2.0 * kExpEps / om : 0.0) +
+                                 6.0 * kExpEps;
                         for (int j = tau + 1; j < L; ++j) {
                             w = chain_step(w, ratio_log2(lp2(k, j), lq2(k, j)));
                             s_w[j + 1] = w;
@@ -983,12 +1003,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     for (int m = L; m > tau; --m) {
                         const double u = static_cast<double>(A.ua[bKL + k * L + m - 1]);
                         const double wm = s_w[m];
-                        double h;
+                        // first-order error of w_m: the first weight's, plus two row
+                        // sums per further ratio of the chain
+                        const double dw = wm * (s_werr + 4.0 * kExpEps * (m - tau - 1));
+                        double h, eh = dw;
                         if (m == L) {
                             h = wm;
                         } else {
                             if (!(u < wm)) {              // h_m <= w_m: rejects without a sweep
                                 tie = fmin(tie, u - wm);
+                                if (u - wm < 4.0 * dw) tie = 0.0;   // within its error
                                 continue;
                             }
                             const int cm = s_can[k * L1 + m];
@@ -999,10 +1023,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                             const double d = R + 1.0 - wm;
                             h = d > 0.0 ? R / d : 1.0;
                             Racc = R;
+                            // h = R / (R + 1 - w): dh = ((1 - w) dR + R dw) / d^2
+                            const double dR = dw + (wm + 1.0) * 2.0 * kExpEps;
+                            eh = d > 0.0 ? ((1.0 - wm) * dR + R * dw) / (d * d) : INFINITY;
                         }
                         if (tid == 0 && A.accept_prob)
                             A.accept_prob[bKL + k * L + m - 1] = static_cast<float>(h);
                         tie = fmin(tie, fabs(u - h));
+                        if (fabs(u - h) < 4.0 * eh) tie = 0.0;   // within its error estimate
+                        if (A.accept_prob && eh > kDiagEh) tie = 0.0;   // h reported to 1e-5
                         if (u < h) { acc = m; break; }
                     }
                     if (acc > 0) {
@@ -1199,6 +1228,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             Zp = NAN;
         }
         ws->status = kStateDone;
+        if (A.redo) A.redo[b] = (!bad && (flags & kFlagNearTie)) ? 1 : 0;
         A.accept_len[b] = tau;
         A.draft_index[b] = kstar;
         A.correction[b] = y;

@@ -74,8 +74,10 @@
  *    success extends the prefix (draft_index = that draft), no success ends the
  *    walk with tau = j and a correction from max(p_s - c min(q_s, p_s/rho*), 0).
  *    rho* is found to about 1e-7 relative (fp32 evaluation of the rows).
- * Integer outputs match the CPU oracle bit for bit except where a decision lies
- * within floating-point error of its threshold (|u - h| of order 1e-6).
+ * Every probability is formed from fp32 exponentials with fp64 sums; a request
+ * with a decision within the fp32 error of its threshold is taken again in fp64
+ * (SV_FLAG_REDONE), so integer outputs match exact arithmetic except where a
+ * decision lies within fp64 rounding of its threshold.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -120,6 +122,13 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
                                  so such a decision may differ from one taken in
                                  exact arithmetic; every other decision cannot */
 #define SV_NEAR_TIE 1e-5
+#define SV_FLAG_REDONE 8      /* the request was taken again in fp64 because one of
+                                 its decisions came within SV_NEAR_TIE, or within a
+                                 first-order estimate of the fp32 error (GBV tests
+                                 whose h = R / (R + 1 - w) is ill-conditioned), of
+                                 its threshold; its outputs, SV_FLAG_NEAR_TIE (from
+                                 the fp64 margins), accept_prob and resid_mass are
+                                 the fp64 evaluation's */
 
 /* Inputs.  All pointers are DEVICE pointers owned by the caller, row-major,
  * read-only for the library, and must stay valid until the stream reaches the
@@ -208,6 +217,14 @@ int spec_verify_multidraft(const sv_inputs *in, const sv_outputs *out, const sv_
  * inputs, outputs, workspace and events as spec_verify_multidraft; accept_prob
  * holds h of every test made (NaN for drafts not tested). */
 int spec_verify_spectr(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
+
+/* SpecTr with rho* found by plain bisection of [1, n] (one sweep per halving,
+ * to 1e-7 relative), the O(V log K) selection step the SpecTr-GBV page puts on
+ * SpecTr (section 3) and measures its method against (section 4, time
+ * efficiency).  Same rule, arguments and results as spec_verify_spectr, whose
+ * search (a histogram sweep, then a few Newton sweeps) reaches the same rho* in
+ * fewer sweeps. */
+int spec_verify_spectr_bisect(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): spec_verify_multidraft

@@ -34,8 +34,12 @@ def host_threads():
     return max(1, min(16, n))
 
 
+# the oracle method that states the rule each library method implements
+ORACLE_METHOD = {"spectr_bisect": "spectr"}
+
+
 def run_oracle(method, host, diagnostics=True, requests=None):
-    return oracle.verify(method, host["target"], host["draft"], host["tokens"],
+    return oracle.verify(ORACLE_METHOD.get(method, method), host["target"], host["draft"], host["tokens"],
                          host["temperature"], host["u_accept"], host["u_correct"],
                          diagnostics=diagnostics, threads=host_threads(), requests=requests)
 

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
 
 def test_flag_bits_match_the_header():
     text = open(HEADER).read()
-    for name in ("SV_FLAG_DEGENERATE", "SV_FLAG_INVALID", "SV_FLAG_NEAR_TIE", "SV_NEAR_TIE"):
+    for name in ("SV_FLAG_DEGENERATE", "SV_FLAG_INVALID", "SV_FLAG_NEAR_TIE", "SV_FLAG_REDONE",
+                 "SV_NEAR_TIE"):
         m = re.search(rf"^#define {name} (\S+)", text, flags=re.M)
         assert m, name
         assert float(m.group(1)) == float(getattr(sv, name)), name
