@@ -8,7 +8,7 @@ the per-request walk).  Prints ONE JSON line on stdout; progress goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--method M]
 
 M is a verification method (token, block, multidraft -- the default for
-multi-draft workloads --, spectr), "draft" to time the drafting kernel
+multi-draft workloads --, spectr, spectr_bisect), "draft" to time the drafting kernel
 instead (drafted tokens per second), or "lmhead" to time the fused LM heads
 (synthetic target and draft projections, --d-target and --d-draft) feeding
 verification, against the same with the statistics left to the verifier.  --pipeline times the one-GPU emulation
@@ -28,8 +28,9 @@ sample of the same batch across the host's cores; the oracle then runs over the
 rest of the batch untimed, and the parity object counts the requests of the
 timed batch whose integer outputs or flag bits differ from it (mismatches),
 apart from those the oracle puts within 1e-6 of a threshold (excused).
-Batches smaller than 1 GiB are rotated through enough copies that every step
-reads its logits from HBM, not from the memory-side cache.
+Batches smaller than 1 GiB are rotated through enough copies (8 to 64, 1 GiB in
+all where that fits) that every step reads its logits from HBM, not from the
+memory-side cache.
 """
 from __future__ import annotations
 
@@ -56,7 +57,8 @@ def log(*a):
 
 # sources of each profiled kernel family (besides the shared device helpers, the
 # launch code and the C header): a summary stays valid while these are unchanged
-KERNEL_SOURCES = {"rowstats": ("sv_rowstats.hpp", "sv_walk.hpp", "sv_spectr.hpp"),
+KERNEL_SOURCES = {"rowstats": ("sv_rowstats.hpp", "sv_walk.hpp", "sv_spectr.hpp", "sv_single.hpp",
+                               "sv_redo.hpp"),
                   "draft": ("sv_draft.hpp",),
                   "lmhead": ("sv_lmhead.hpp",)}
 
@@ -142,6 +144,7 @@ def cpu_baseline(method, batch, w, out, target_cpu_s: float, chunk: int = 64):
     import oracle
     import synth
     threads = host_threads()
+    method = {"spectr_bisect": "spectr"}.get(method, method)   # the rule it implements
     host1 = synth.to_host(batch, [0])
     t = time.perf_counter()
     oracle.verify(method, host1["target"], host1["draft"], host1["tokens"],
@@ -189,7 +192,7 @@ def cpu_baseline(method, batch, w, out, target_cpu_s: float, chunk: int = 64):
     for b in range(w.B):
         of = int(ref["flags"][b])
         tie = not (of & 2) and (ref["margin"][b] < 1e-6 or bool(of & 1))
-        ties += tie
+        ties += int(tie)
         same = all(int(g[k][b]) == int(ref[k][b]) for k in ("accept_len", "draft_index",
                                                               "correction"))
         same &= (int(g["flags"][b]) & 3) == (of & 3)
@@ -199,7 +202,9 @@ def cpu_baseline(method, batch, w, out, target_cpu_s: float, chunk: int = 64):
             else:
                 mism += 1
     parity = {"n": w.B, "mismatches": mism, "excused": excused, "oracle_ties": ties,
-              "near_tie_flagged_by_gpu": int(((g["flags"] & 4) != 0).sum())}
+              "oracle_within_1e-5": int(((ref["margin"] < 1e-5) & ((ref["flags"] & 2) == 0)).sum()),
+              "near_tie_flagged_by_gpu": int(((g["flags"] & 4) != 0).sum()),
+              "redone_in_fp64": int(((g["flags"] & 8) != 0).sum())}
     visit = {"requests": w.B, "oracle_rows_per_request": float(ref["counters"][:, 2].mean()),
              "oracle_rows": int(ref["counters"][:, 2].sum())}
     return cpu, parity, visit
@@ -303,29 +308,33 @@ def run_draft(args, w, name):
 
 
 def run_pipeline(args, w, name, method):
-    """MineDraft's two-batch schedule on one GPU: step i verifies batch i%2 on
-    one stream while batch (i+1)%2 is drafted on another.  Verification of a
-    batch waits for its drafting in the previous step, and drafting waits for
-    that batch's verification in the previous step."""
+    """MineDraft's two-batch schedule on one GPU (TwoBatchPipeline): step i
+    verifies batch i%2 on one stream while batch (i+1)%2 is drafted on another.
+    Verification of a batch waits for its drafting in the previous step, and
+    drafting waits for that batch's verification in the previous step."""
     import torch
     import synth
-    import draft_token_verification_online_amd as sv
+    from draft_token_verification_online_amd.pipeline import TwoBatchPipeline
     log(f"[bench] generating two batches of {name} on cuda:0")
     batches = [synth.generate(w, args.seed + i, device="cuda") for i in range(2)]
-    us = [synth.draft_uniforms(w, args.seed + i, device="cuda") for i in range(2)]
+    # a pool of uniforms made before timing, cycled through by step
+    pool = [[(synth.draft_uniforms(w, args.seed + 10 * j + b, device="cuda"),
+              synth.generate(synth.scaled(w, V=8), args.seed + 10 * j + b,
+                             device="cuda")["u_accept"],
+              synth.generate(synth.scaled(w, V=8), args.seed + 10 * j + b,
+                             device="cuda")["u_correct"]) for b in range(2)] for j in range(4)]
     torch.cuda.synchronize()
-    drs = [sv.Drafter(w.B, w.K, w.L, w.V, w.dtype) for _ in range(2)]
-    vers = [sv.Verifier(method, w.B, w.K, w.L, w.V, w.dtype) for _ in range(2)]
-    s_ver, s_dra = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    pipe = TwoBatchPipeline(method, batches, lambda i, b: pool[i % 4][b])
+    s = pipe.s_verify
 
-    def draft(i, stream):
-        b = batches[i]
-        drs[i](b["draft"], b["temperature"], us[i], stream=stream.cuda_stream)
+    def draft(b):
+        bt = batches[b]
+        pipe.drafters[b](bt["draft"], bt["temperature"], pool[0][b][0], stream=s.cuda_stream)
 
-    def verify(i, stream):
-        b = batches[i]
-        vers[i](b["target"], b["draft"], drs[i].out["draft_tokens"], b["temperature"],
-                b["u_accept"], b["u_correct"], stream=stream.cuda_stream)
+    def verify(b):
+        bt = batches[b]
+        pipe.verifiers[b](bt["target"], bt["draft"], pipe.drafters[b].out["draft_tokens"],
+                          bt["temperature"], pool[0][b][1], pool[0][b][2], stream=s.cuda_stream)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -336,41 +345,19 @@ def run_pipeline(args, w, name, method):
         return (time.perf_counter() - t) * 1e3 / n
 
     # each piece alone, on one stream
-    for i in range(2):
-        draft(i, s_ver)
-    torch.cuda.synchronize()
+    for b in range(2):
+        draft(b)
     for _ in range(args.warmup):
-        verify(0, s_ver)
-    t_verify = timed(lambda: verify(0, s_ver), args.steps)
-    t_draft = timed(lambda: draft(1, s_ver), args.steps)
+        verify(0)
+    t_verify = timed(lambda: verify(0), args.steps)
+    t_draft = timed(lambda: draft(1), args.steps)
     # serial schedule: verify A, then draft B, on one stream
-    t_serial = timed(lambda: (verify(0, s_ver), draft(1, s_ver)), args.steps)
-
-    # overlapped: two streams, cross-stream events carry the dependencies
-    ev_drafted = [torch.cuda.Event(), torch.cuda.Event()]
-    ev_verified = [torch.cuda.Event(), torch.cuda.Event()]
-
-    def step(i):
-        a, b = i % 2, (i + 1) % 2
-        s_ver.wait_event(ev_drafted[a])
-        verify(a, s_ver)
-        ev_verified[a].record(s_ver)
-        s_dra.wait_event(ev_verified[b])
-        draft(b, s_dra)
-        ev_drafted[b].record(s_dra)
-
-    for i in range(2):
-        draft(i, s_dra)
-        ev_drafted[i].record(s_dra)
-        ev_verified[i].record(s_ver)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t_over = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_serial = timed(lambda: (verify(0), draft(1)), args.steps)
+    # overlapped: the two-batch schedule on two streams
+    pipe.prime()
+    for _ in range(args.warmup):
+        pipe.step()
+    t_over = timed(pipe.step, args.steps)
     tokens = synth.tokens_per_step(w)
     log(f"[bench] pipeline: verify {t_verify:.3f} ms, draft {t_draft:.3f} ms, serial "
         f"{t_serial:.3f} ms/step, overlapped {t_over:.3f} ms/step "
@@ -573,9 +560,10 @@ def main():
     dense = synth.dense_bytes(w)
     # Inputs smaller than the memory-side cache would be served from it on every
     # step after the first: rotate through copies at different addresses, at
-    # least 8 and at least 1 GiB of logits in all, so each step reads from HBM.
+    # least 8 and 1 GiB of logits in all, so each step reads from HBM (at most 64:
+    # a batch of a few KB is bound by launch latency, not by where it is read from).
     copies = args.rotate if args.rotate else (1 if dense >= (1 << 30)
-                                              else max(8, -(-(1 << 30) // dense)))
+                                              else min(64, max(8, -(-(1 << 30) // dense))))
     inputs = [batch] + [{k: v.clone() for k, v in batch.items()} for _ in range(copies - 1)]
     torch.cuda.synchronize()
     if copies > 1:

@@ -69,7 +69,8 @@ class SvLmInputs(ctypes.Structure):
 
 class SvLmOutputs(ctypes.Structure):
     _fields_ = [("logits", _vp), ("row_stats", _vp), ("stats_group", ctypes.c_int32),
-                ("stats_stride", ctypes.c_int32), ("stats_offset", ctypes.c_int32)]
+                ("stats_stride", ctypes.c_int32), ("stats_offset", ctypes.c_int32),
+                ("logits_dtype", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -272,17 +273,19 @@ class Drafter:
 
 
 class LmHead:
-    """The LM head logits = h W^T (bf16 in, fp32 logits out) with every row's
-    temperature-softmax statistics computed in the same kernel (spec_lm_head in
-    include/spec_verify.h).  Holds the logits output and the workspace."""
+    """The LM head logits = h W^T (bf16 in, fp32 or bf16 logits out) with every
+    row's temperature-softmax statistics computed in the same kernel
+    (spec_lm_head in include/spec_verify.h).  Holds the logits output and the
+    workspace."""
 
     STAT_BYTES = 16
 
-    def __init__(self, R, d, V, device="cuda"):
+    def __init__(self, R, d, V, device="cuda", logits_dtype=torch.float32):
         lib = load_library()
         self.shape = (R, d, V)
         dev = torch.device(device)
-        self.logits = torch.empty((R, V), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((R, V), dtype=logits_dtype, device=dev)
+        self._dt = _dtype_code(self.logits)
         nbytes = int(lib.sv_lm_workspace_size(R, d, V))
         if nbytes == 0:
             raise ValueError(f"sizes out of range: R={R} d={d} V={V} (d a multiple of 64)")
@@ -307,7 +310,7 @@ class LmHead:
             last = ((R - 1) // group) * stride + offset + (R - 1) % group if R > 0 else -1
             _check_bytes(stats, (last + 1) * self.STAT_BYTES, "stats")
         ins = SvLmInputs(R, d, V, hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr())
-        outs = SvLmOutputs(self.logits.data_ptr(), _ptr(stats), group, stride, offset)
+        outs = SvLmOutputs(self.logits.data_ptr(), _ptr(stats), group, stride, offset, self._dt)
         if stream is None:
             stream = torch.cuda.current_stream(hidden.device).cuda_stream
         ev = (_vp * N_PHASE_EVENTS)(*(events or (None,) * N_PHASE_EVENTS))

@@ -12,7 +12,8 @@ LIB = os.path.join(PKG, "libspec_verify.so")
 SOURCES = [os.path.join(CSRC, "spec_verify.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("sv_device.hpp", "sv_rowstats.hpp",
                                                   "sv_walk.hpp", "sv_spectr.hpp",
-                                                  "sv_draft.hpp", "sv_lmhead.hpp")] + \
+                                                  "sv_draft.hpp", "sv_lmhead.hpp",
+                                                  "sv_single.hpp", "sv_redo.hpp")] + \
     [os.path.join(ROOT, "include", "spec_verify.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -36,8 +36,10 @@ constexpr int kWalkThreads = 512;
 constexpr long long kMaxStatsGrid = 1LL << 22;
 constexpr long long kListGrid = 4096;
 constexpr int kMaxB = 1 << 24;
-constexpr int kRedoThreads = 512;
-constexpr int kMaxRedoGrid = 1 << 16;
+// Re-evaluation launches: workgroups over (listed request, node row) and over
+// listed requests.  With none listed every workgroup returns after one load.
+constexpr long long kRedoStatsGrid = 1024;
+constexpr int kRedoWalkGrid = 64;
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
 static_assert(SV_MAX_L == sv::kMaxL, "L limit");
@@ -47,6 +49,8 @@ static_assert(SV_FLAG_INVALID == sv::kFlagInvalid, "flag bits");
 static_assert(SV_FLAG_NEAR_TIE == sv::kFlagNearTie && SV_NEAR_TIE == sv::kNearTie, "flag bits");
 static_assert(SV_FLAG_REDONE == sv::kFlagRedone, "flag bits");
 static_assert(sizeof(sv::RowStat) == 16, "row statistics layout");
+static_assert(sizeof(sv::RedoStat) == sizeof(sv::RowStat) && sizeof(sv::SliceStat) == sizeof(sv::RowStat),
+              "the re-evaluation's fp64 statistics reuse the row-statistics region");
 static_assert(sizeof(sv_row_stat) == sizeof(sv::RowStat) && offsetof(sv_row_stat, sum) == 8,
               "sv_row_stat is the library's row statistics layout");
 
@@ -62,19 +66,23 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
            sizeof(sv::RowStat);
 }
 
-// Workspace: row statistics | walk states | node rows flagged for the second
-// round (bytes, then the same rows as a list) | list length | requests marked
-// for re-evaluation in fp64 | node lists of the walk (K >= 3 only: a node sees
-// a second mass sweep only with three or more drafts).
+// Workspace: row statistics (after the walk, the fp64 statistics of the requests
+// listed for re-evaluation) | walk states | node rows flagged for the second
+// round (bytes, then the same rows as a list) | list length | number of
+// requests listed for re-evaluation in fp64 | their indices | node lists of the
+// walk (K >= 3 only: a node sees a second mass sweep only with three or more
+// drafts).
 struct Layout {
-    size_t stats, state, need, list, count, redo, nodes, total;
+    size_t stats, state, need, list, count, rcount, rlist, nodes, total;
     bool has_nodes;
 };
 
-// Single-draft workspace (K = 1 without given statistics): slice statistics
-// of every row | residual slice sums per position.
+// Single-draft workspace (K = 1 without given statistics): slice statistics of
+// every row (after the final launch, the re-evaluation's fp64 statistics) |
+// residual slice sums per position | each request's combined statistics and
+// weight chain | number of requests listed for re-evaluation | their indices.
 struct SingleLayout {
-    size_t part, rpart, total;
+    size_t part, rpart, prep, rcount, rlist, total;
     int NS;
 };
 
@@ -85,7 +93,10 @@ SingleLayout single_layout(int32_t B, int32_t L, int32_t V) {
     const size_t bs = static_cast<size_t>(B) * l.NS;
     l.part = 0;
     l.rpart = align_up(bs * (2 * L + 1) * sizeof(sv::SliceStat), 256);
-    l.total = l.rpart + align_up(bs * (L + 1) * sizeof(double), 256);
+    l.prep = l.rpart + align_up(bs * (L + 1) * sizeof(double), 256);
+    l.rcount = l.prep + align_up(static_cast<size_t>(B) * sizeof(sv::SinglePrep), 256);
+    l.rlist = l.rcount + 256;
+    l.total = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
     return l;
 }
 
@@ -97,8 +108,9 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.need = l.state + align_up(static_cast<size_t>(B) * sizeof(sv::WalkState), 256);
     l.list = l.need + align_up(bkl, 256);
     l.count = l.list + align_up(2 * bkl * sizeof(sv::RowRef), 256);
-    l.redo = l.count + 256;
-    l.nodes = l.redo + align_up(static_cast<size_t>(B), 256);
+    l.rcount = l.count + 256;
+    l.rlist = l.rcount + 256;
+    l.nodes = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
     l.has_nodes = K >= 3;
     l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
                                            static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
@@ -109,6 +121,51 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
 hipError_t record(const sv_launch *ln, int i, hipStream_t stream) {
     return ln->phase_events[i] ? hipEventRecord(static_cast<hipEvent_t>(ln->phase_events[i]), stream)
                                : hipSuccess;
+}
+
+__global__ void reset_count_kernel(unsigned *count) {
+    if (threadIdx.x == 0) *count = 0u;
+}
+
+// Requests the fast path listed (a decision within the fp32 error of its
+// threshold), taken again in fp64: their node rows' statistics over the whole
+// chip, then one workgroup per request.  `stats` is a region of at least
+// B * K * (2L + 1) * 16 bytes that the fast path no longer reads.
+template <typename E, bool VEC>
+hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t stream, int method,
+                       const unsigned *count, const int32_t *list, void *stats) {
+    using RD = typename sv::RowOf<E, VEC>::type;
+    sv::RedoArgs ra;
+    ra.tgt = in->target_logits;
+    ra.drf = in->draft_logits;
+    ra.tok = in->draft_tokens;
+    ra.temp = in->temperature;
+    ra.ua = in->u_accept;
+    ra.uc = in->u_correct;
+    ra.count = count;
+    ra.list = list;
+    ra.stats = static_cast<sv::RedoStat *>(stats);
+    ra.B = in->B;
+    ra.K = in->K;
+    ra.L = in->L;
+    ra.V = in->V;
+    ra.method = method;
+    ra.accept_len = out->accept_len;
+    ra.draft_index = out->draft_index;
+    ra.correction = out->correction;
+    ra.flags = out->flags;
+    ra.accept_prob = out->accept_prob;
+    ra.resid_mass = out->resid_mass;
+    const long long rows = static_cast<long long>(in->B) * in->K * (2 * in->L + 1);
+    const unsigned g1 = static_cast<unsigned>(rows < kRedoStatsGrid ? rows : kRedoStatsGrid);
+    hipLaunchKernelGGL((sv::redo_stats_kernel<sv::kRedoStatsThreads, RD, E>), dim3(g1),
+                       dim3(sv::kRedoStatsThreads), 0, stream, ra);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const unsigned g2 = static_cast<unsigned>(in->B < kRedoWalkGrid ? in->B : kRedoWalkGrid);
+    hipLaunchKernelGGL((sv::redo_walk_kernel<sv::kRedoThreads, RD, E>), dim3(g2),
+                       dim3(sv::kRedoThreads), 0, stream, ra);
+    return hipGetLastError();
 }
 
 template <typename E, bool VEC>
@@ -131,6 +188,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     sa.stats = reinterpret_cast<sv::RowStat *>(ws + lay.stats);
     sa.list = reinterpret_cast<const sv::RowRef *>(ws + lay.list);
     sa.list_count = reinterpret_cast<unsigned *>(ws + lay.count);
+    sa.redo_count = reinterpret_cast<unsigned *>(ws + lay.rcount);
     sa.B = in->B;
     sa.K = in->K;
     sa.L = in->L;
@@ -180,7 +238,8 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.row_lse = out->row_lse;
     wa.accept_prob = out->accept_prob;
     wa.resid_mass = out->resid_mass;
-    wa.redo = reinterpret_cast<unsigned char *>(ws + lay.redo);
+    wa.redo_count = sa.redo_count;
+    wa.redo_list = reinterpret_cast<int32_t *>(ws + lay.rlist);
 
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
@@ -188,6 +247,9 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         hipLaunchKernelGGL((sv::rowstats_kernel<kStatsThreads, RD, E>),
                            dim3(grid_for(diagnostics ? 2 * in->L + 1 : 2 * sa.depth)), dim3(kStatsThreads),
                            0, stream, sa);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else {
+        hipLaunchKernelGGL(reset_count_kernel, dim3(1), dim3(64), 0, stream, sa.redo_count);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
@@ -217,30 +279,9 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         wa.round = 2;   // only the stopped walks run
         if ((err = walk()) != hipSuccess) return err;
     }
-    // requests with a decision within the fp32 error of its threshold, again in fp64
-    sv::RedoArgs ra;
-    ra.tgt = in->target_logits;
-    ra.drf = in->draft_logits;
-    ra.tok = in->draft_tokens;
-    ra.temp = in->temperature;
-    ra.ua = in->u_accept;
-    ra.uc = in->u_correct;
-    ra.redo = wa.redo;
-    ra.B = in->B;
-    ra.K = in->K;
-    ra.L = in->L;
-    ra.V = in->V;
-    ra.method = wa.method;
-    ra.accept_len = out->accept_len;
-    ra.draft_index = out->draft_index;
-    ra.correction = out->correction;
-    ra.flags = out->flags;
-    ra.accept_prob = out->accept_prob;
-    ra.resid_mass = out->resid_mass;
-    const unsigned rgrid = static_cast<unsigned>(in->B < kMaxRedoGrid ? in->B : kMaxRedoGrid);
-    hipLaunchKernelGGL((sv::redo_kernel<kRedoThreads, RD, E>), dim3(rgrid), dim3(kRedoThreads), 0,
-                       stream, ra);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_redo<E, VEC>(in, out, stream, wa.method, wa.redo_count, wa.redo_list,
+                                   ws + lay.stats)) != hipSuccess)
+        return err;
     return record(ln, 4, stream);
 }
 
@@ -274,6 +315,9 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
     a.uc = in->u_correct;
     a.part = reinterpret_cast<sv::SliceStat *>(ws + lay.part);
     a.rpart = reinterpret_cast<double *>(ws + lay.rpart);
+    a.prep = reinterpret_cast<sv::SinglePrep *>(ws + lay.prep);
+    a.redo_count = reinterpret_cast<unsigned *>(ws + lay.rcount);
+    a.redo_list = reinterpret_cast<int32_t *>(ws + lay.rlist);
     a.B = in->B;
     a.L = in->L;
     a.V = in->V;
@@ -297,12 +341,18 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
     hipLaunchKernelGGL((sv::single_stats_kernel<NT, RD, E>), dim3(grid(n1)), dim3(NT), 0, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL((sv::single_prep_kernel<NT, RD, E>), dim3(grid(in->B)), dim3(NT), 0, stream,
+                       a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((sv::single_partial_kernel<NT, RD, E>), dim3(grid(n2)), dim3(NT), 0, stream,
                        a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((sv::single_final_kernel<NT, RD, E>), dim3(grid(in->B)), dim3(NT), 0, stream,
                        a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_redo<E, VEC>(in, out, stream, method, a.redo_count, a.redo_list,
+                                   ws + lay.part)) != hipSuccess)
+        return err;
     for (int i = 2; i < 5; ++i)
         if ((err = record(ln, i, stream)) != hipSuccess) return err;
     return hipSuccess;
@@ -513,6 +563,7 @@ int spec_lm_head(const sv_lm_inputs *in, const sv_lm_outputs *out, const sv_laun
     if (!lm_sizes_ok(in->R, in->d, in->V)) return SV_EINVAL;
     if (in->R == 0) return SV_OK;
     if (!in->hidden || !in->weight || !in->temperature || !out->logits) return SV_EINVAL;
+    if (out->logits_dtype != SV_F32 && out->logits_dtype != SV_BF16) return SV_EINVAL;
     if (reinterpret_cast<uintptr_t>(in->hidden) % 16 || reinterpret_cast<uintptr_t>(in->weight) % 16)
         return SV_EINVAL;
     if (out->row_stats && (out->stats_group < 1 || out->stats_stride < out->stats_group ||
@@ -529,6 +580,7 @@ int spec_lm_head(const sv_lm_inputs *in, const sv_lm_outputs *out, const sv_laun
     a.w = static_cast<const uint16_t *>(in->weight);
     a.temp = in->temperature;
     a.logits = out->logits;
+    a.bf16_out = out->logits_dtype == SV_BF16 ? 1 : 0;
     a.pmax = reinterpret_cast<float *>(ws + lay.pmax);
     a.psum = reinterpret_cast<double *>(ws + lay.psum);
     a.R = in->R;

@@ -8,8 +8,9 @@
 // statistics (shift M, sum S = sum_v 2^(l_v c - K), c = log2(e)/T, K the row
 // constant of the shift, in the exponent convention of every kernel here) -- is computed
 // while the row is still in registers, so the statistics pass over the logits
-// disappears.  The logits are still written (fp32): the walk's residual sweeps
-// and correction draws read whole rows.
+// disappears.  The logits are still written, fp32 or rounded to bf16 (half the
+// bytes; the statistics are then those of the rounded values): the walk's
+// residual sweeps and correction draws read whole rows.
 //
 // lm_head_kernel: one 256-thread workgroup per 128 x 128 output tile, four waves
 // in a 2 x 2 arrangement each owning 64 x 64 (4 x 4 MFMA 16x16x32 bf16 tiles),
@@ -47,11 +48,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *m, i
         const_cast<uint16_t *>(m + static_cast<long long>(r0) * d), 0, n, 0x00020000);
 }
 
+// fp32 to bf16, round to nearest even (finite values; the LM head's logits are
+// finite sums of finite products).
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 struct LmArgs {
     const uint16_t *h;      // [R][d] bf16 bits
     const uint16_t *w;      // [V][d] bf16 bits
     const float *temp;      // [R]: temperature of each row
-    float *logits;          // [R][V]
+    void *logits;           // [R][V] fp32, or bf16 bits when bf16_out
+    int bf16_out;           // round the logits to bf16 (statistics from the rounded values)
     float *pmax;            // [R][nbn]: per column block, the row's maximum
     double *psum;           // [R][nbn]: and sum_v 2^((l_v - max) c) over the block
     int R, d, V, nbm, nbn;
@@ -207,8 +216,16 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int col = col0 + wn * 64 + b * 16 + (lane & 15);
-                v[b] = col < V ? acc[a][b][i] : -INFINITY;
-                if (rok && col < V) A.logits[static_cast<long long>(row) * V + col] = v[b];
+                const long long at = static_cast<long long>(row) * V + col;
+                if (A.bf16_out) {
+                    // the statistics describe the logits as stored
+                    const uint16_t hb = bf16_rne(acc[a][b][i]);
+                    v[b] = col < V ? __uint_as_float(static_cast<uint32_t>(hb) << 16) : -INFINITY;
+                    if (rok && col < V) static_cast<uint16_t *>(A.logits)[at] = hb;
+                } else {
+                    v[b] = col < V ? acc[a][b][i] : -INFINITY;
+                    if (rok && col < V) static_cast<float *>(A.logits)[at] = v[b];
+                }
                 m = fmaxf(m, v[b]);
             }
 #pragma unroll

@@ -5,18 +5,29 @@
 // of order 1e-7, amplified by the conditioning of the rule (GBV's
 // h = R / (R + 1 - w) by ~1 / (R + 1 - w)).  A decision whose threshold lies
 // within that error of its uniform could come out differently in exact
-// arithmetic.  The fast walks therefore mark every request with such a decision
+// arithmetic.  The fast walks therefore list every request with such a decision
 // (the margin test of SV_FLAG_NEAR_TIE, widened by a first-order error estimate
-// for ill-conditioned tests), and this kernel takes each marked request again
-// from the start in fp64: row statistics M = max_v l_v and S = sum_v
-// exp((l_v - M) / T), every probability exp((l_v - M) / T) / S (the exponentials
-// in double precision), every residual
-// mass, weight chain, scaling-factor search and inverse-CDF draw in double, with
-// the rules stated in sv_walk.hpp (token level, GBV over K drafts, SpecTr).
-// Its integer outputs differ from exact arithmetic only where a decision lies
-// within double rounding (~1e-13) of its threshold.  One workgroup per marked
-// request; the others return at once.  It is written for clarity, not speed:
-// marked requests are rare (a decision within ~1e-5 of its threshold).
+// for ill-conditioned tests), and two launches take each listed request again
+// from the start in fp64:
+//
+//   redo_stats_kernel  one workgroup per (listed request, node row), over the
+//                      whole chip: M = max_v l_v and log2 S with
+//                      S = sum_v exp((l_v - M) / T), in one pass (a running
+//                      maximum, the sum rescaled when it grows);
+//   redo_walk_kernel   one workgroup per listed request: every probability
+//                      exp((l_v - M) / T) / S, residual mass, weight chain,
+//                      scaling-factor search and inverse-CDF draw in double,
+//                      with the rules stated in sv_walk.hpp (token level, GBV
+//                      over K drafts, SpecTr).
+//
+// Double exponentials come from exp2_tang (Tang's table-driven method, ACM
+// TOMS 15(2), 1989: 2^a = 2^n 2^(j/256) 2^(r/256) with a 256-entry table in LDS
+// and a degree-4 polynomial; ~3 ulp).  The outputs differ from exact arithmetic
+// only where a decision lies within double rounding (~1e-13, times the rule's
+// conditioning) of its threshold.  Listed requests are rare -- about one in a
+// hundred on flat residuals, where the correction draw lands within 1e-5 Z of a
+// boundary of the cumulative weights -- and with none listed both launches
+// return after reading the count.
 #pragma once
 
 #include "sv_device.hpp"
@@ -25,27 +36,140 @@
 namespace sv {
 
 constexpr int kFlagRedone = 8;
+constexpr int kRedoThreads = 512;        // per listed request
+constexpr int kRedoStatsThreads = 512;   // per (listed request, node row)
+
+// 2^a in double precision.  a = (256 n + j + r) / 256 with n, j integers,
+// 0 <= j < 256, |r| <= 1/2: 2^a = 2^n * tab[j] * 2^(r/256), tab[j] = 2^(j/256),
+// and 2^(r/256) = exp(r ln2/256) is its Taylor polynomial of degree 4
+// (truncation below 4e-17 for |r ln2/256| <= 1.36e-3).  0 for a below the
+// subnormal range and for NaN; +inf above the double range.
+__device__ __forceinline__ double exp2_tang(double a, const double *tab) {
+    if (!(a > -1080.0)) return 0.0;
+    if (a > 1030.0) return INFINITY;
+    const double t = a * 256.0;
+    const double k = rint(t);
+    const double r = t - k;   // exact
+    const int ki = static_cast<int>(k);
+    const int j = ki & 255;
+    const int n = ki >> 8;    // floor(ki / 256)
+    constexpr double c1 = 0x1.62e42fefa39efp-9, c2 = 0x1.ebfbdff82c58fp-19,
+                     c3 = 0x1.c6b08d704a0c0p-29, c4 = 0x1.3b2ab6fba4e77p-39;
+    const double p = fma(r, fma(r, fma(r, fma(r, c4, c3), c2), c1), 1.0);
+    return ldexp(tab[j] * p, n);
+}
+
+// tab[j] = 2^(j/256), j = 0..255 (block-wide; ends with a barrier)
+__device__ __forceinline__ void exp2_tang_table(double *tab) {
+    for (int j = threadIdx.x; j < 256; j += blockDim.x) tab[j] = exp2(static_cast<double>(j) / 256.0);
+    __syncthreads();
+}
+
+// fp64 statistics of one node row: pi(v) = 2^((l_v - M) cT - ls), cT = log2(e)/T,
+// ls = log2 sum_v 2^((l_v - M) cT).  ok = 0 for a row that is not a distribution.
+struct RedoStat {
+    double ls;
+    float M;
+    int ok;
+};
 
 struct RedoArgs {
     const void *tgt;              // [B][K][L+1][V]
     const void *drf;              // [B][K][L][V]
     const int32_t *tok;           // [B][K][L]
     const float *temp, *ua, *uc;  // [B], [B][K][L], [B]
-    const unsigned char *redo;    // [B]: re-evaluate request b when nonzero
+    const unsigned *count;        // listed requests
+    const int32_t *list;          // [count]: their indices
+    RedoStat *stats;              // [count][K][2L+1]: node rows of listed request i at i*K*(2L+1)
     int B, K, L, V;
     int method;                   // kMethodToken, kMethodBlockWalk or kMethodSpecTr
     int32_t *accept_len, *draft_index, *correction, *flags;
     float *accept_prob, *resid_mass;
 };
 
+// One workgroup per (listed request, node row), grid-stride: the fp64
+// statistics of the row when it is the node's own (no earlier draft shares its
+// prefix; the walk reads only those).
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
+    __shared__ double s_tab[256];
+    __shared__ double s_red[NT / kWave];
+    __shared__ float s_fred[NT / kWave];
+    const unsigned n = *A.count;
+    if (n == 0) return;
+    exp2_tang_table(s_tab);
+    const int tid = threadIdx.x;
+    const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1, per = K * RS;
+    const int nch = (V + kChunk - 1) / kChunk;
+    const long long items = static_cast<long long>(n) * per;
+    for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+        const int i = static_cast<int>(it / per), r = static_cast<int>(it % per);
+        const int k = r / RS, s = r % RS;
+        const int b = A.list[i];
+        const bool target = s <= L;
+        const int j = target ? s : s - L1;
+        const int32_t *tk = A.tok + static_cast<long long>(b) * K * L;
+        int dup = 0;
+        for (int c = tid; c < k; c += NT) {
+            int same = 1;
+            for (int t = 0; t < j; ++t) same &= (tk[c * L + t] == tk[k * L + t]);
+            dup |= same;
+        }
+        if (__syncthreads_or(dup)) continue;   // block-uniform
+        const E *base = target
+            ? static_cast<const E *>(A.tgt) + ((static_cast<long long>(b) * K + k) * L1 + j) * V
+            : static_cast<const E *>(A.drf) + ((static_cast<long long>(b) * K + k) * L + j) * V;
+        const RD R(base, V);
+        const float T = A.temp[b];
+        const double cT = 1.4426950408889634 / static_cast<double>(T);
+        float mx = -INFINITY;
+        double sum = 0.0;
+        int nan = !(T > 0.0f) || !isfinite(T);
+        for (int q = tid; q < nch; q += NT) {
+            float x[8];
+            R.load(q, x);
+            float cm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                nan |= isnan(x[e]) || x[e] == INFINITY;
+                cm = fmaxf(cm, x[e]);
+            }
+            if (cm > mx) {   // rescale the sum to the new maximum
+                if (mx > -INFINITY)
+                    sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(cm)) * cT, s_tab);
+                mx = cm;
+            }
+            if (mx > -INFINITY && !nan) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sum += exp2_tang((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT, s_tab);
+            }
+        }
+        nan = __syncthreads_or(nan);
+        const float M = block_max<NT>(mx, s_fred);
+        if (mx > -INFINITY && !nan)
+            sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(M)) * cT, s_tab);
+        else
+            sum = 0.0;
+        sum = block_sum<NT>(sum, s_red);
+        if (tid == 0) {
+            RedoStat st;
+            st.ok = !nan && M > -INFINITY && sum > 0.0 && isfinite(sum);
+            st.M = M;
+            st.ls = st.ok ? log2(sum) : 0.0;
+            A.stats[it] = st;
+        }
+    }
+}
+
 // LDS of one re-evaluation.
 struct RedoShared {
+    double tab[256];
     int x[kMaxK * kMaxL];
     unsigned char can[kMaxK * (kMaxL + 1)];
-    unsigned char have[kMaxK * (2 * kMaxL + 1)];
     unsigned char ok[kMaxK * (2 * kMaxL + 1)];
     float M[kMaxK * (2 * kMaxL + 1)];
-    double S[kMaxK * (2 * kMaxL + 1)];
+    double ls[kMaxK * (2 * kMaxL + 1)];
     int H[kMaxK];
     double red[16];
     float fred[16];
@@ -53,39 +177,47 @@ struct RedoShared {
     double pair[2];
 };
 
-// Re-evaluate request b in fp64 and overwrite its outputs (block-uniform call).
+// Re-evaluate listed request i in fp64 and overwrite its outputs (block-uniform
+// call).
 template <int NT, typename RD, typename E>
-__device__ void redo_request(const RedoArgs &A, int b, RedoShared &sh) {
+__device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li, RedoShared &sh) {
     int *s_x = sh.x;
-    unsigned char *s_can = sh.can, *s_have = sh.have, *s_ok = sh.ok;
+    unsigned char *s_can = sh.can, *s_ok = sh.ok;
     float *s_M = sh.M;
-    double *s_S = sh.S;
+    double *s_ls = sh.ls;
+    const double *tab = sh.tab;
     int *s_H = sh.H;
     double *s_red = sh.red, *s_pair = sh.pair;
-    float *s_fred = sh.fred;
     int *s_ired = sh.ired;
     const int tid = threadIdx.x;
     const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
+    const int b = A.list[li];
     {
         const long long bKL = static_cast<long long>(b) * K * L;
         // exp((l - M) / T) taken as 2^((l - M) log2(e) / T)
         const double cT = 1.4426950408889634 / static_cast<double>(A.temp[b]);
         const E *tgt = static_cast<const E *>(A.tgt);
         const E *drf = static_cast<const E *>(A.drf);
-        for (int i = tid; i < K * L; i += NT) s_x[i] = A.tok[bKL + i];
-        for (int i = tid; i < K * RS; i += NT) s_have[i] = 0;
+        const RedoStat *st = A.stats + static_cast<long long>(li) * K * RS;
+        for (int q = tid; q < K * L; q += NT) s_x[q] = A.tok[bKL + q];
+        for (int q = tid; q < K * RS; q += NT) {
+            const RedoStat r = st[q];
+            s_ok[q] = static_cast<unsigned char>(r.ok);
+            s_M[q] = r.M;
+            s_ls[q] = r.ls;
+        }
         __syncthreads();
         // node of (k, j): the lowest-index draft with the same first j tokens
-        for (int i = tid; i < K * L1; i += NT) {
-            const int k = i / L1, j = i % L1;
+        for (int q = tid; q < K * L1; q += NT) {
+            const int k = q / L1, j = q % L1;
             int c = k;
             for (int cc = 0; cc < k; ++cc) {
                 int same = 1;
                 for (int t = 0; t < j; ++t) same &= (s_x[cc * L + t] == s_x[k * L + t]);
                 if (same) { c = cc; break; }
             }
-            s_can[i] = static_cast<unsigned char>(c);
+            s_can[q] = static_cast<unsigned char>(c);
         }
         __syncthreads();
         auto row = [&](bool target, int c, int j) {
@@ -94,50 +226,17 @@ __device__ void redo_request(const RedoArgs &A, int b, RedoShared &sh) {
         };
         auto slot = [&](bool target, int c, int j) { return c * RS + (target ? j : L1 + j); };
         int bad = 0;
-        // fp64 statistics of node row (target?, node of (k, j)); invalid rows mark
-        // the request
+        // node row (target?, node of (k, j)): its slot; an invalid row marks the
+        // request
         auto stats = [&](bool target, int k, int j) {
-            const int c = s_can[k * L1 + j];
-            const int sl = slot(target, c, j);
-            if (!s_have[sl]) {
-                const RD R = row(target, c, j);
-                float mx = -INFINITY;
-                int nan = 0;
-                for (int q = tid; q < nch; q += NT) {
-                    float x[8];
-                    R.load(q, x);
-                    for (int e = 0; e < 8; ++e) {
-                        nan |= isnan(x[e]) || x[e] == INFINITY;
-                        mx = fmaxf(mx, x[e]);
-                    }
-                }
-                nan = __syncthreads_or(nan);
-                mx = block_max<NT>(mx, s_fred);
-                double s = 0.0;
-                if (!nan && mx > -INFINITY) {
-                    for (int q = tid; q < nch; q += NT) {
-                        float x[8];
-                        R.load(q, x);
-                        for (int e = 0; e < 8; ++e)
-                            s += exp2((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT);
-                    }
-                }
-                s = block_sum<NT>(s, s_red);
-                if (tid == 0) {
-                    s_M[sl] = mx;
-                    s_S[sl] = s;
-                    s_ok[sl] = !nan && mx > -INFINITY && s > 0.0 && isfinite(s);
-                    s_have[sl] = 1;
-                }
-                __syncthreads();
-            }
+            const int sl = slot(target, s_can[k * L1 + j], j);
             bad |= !s_ok[sl];
             return sl;
         };
         auto prob = [&](int sl, float x) {
-            return exp2((static_cast<double>(x) - static_cast<double>(s_M[sl])) * cT) / s_S[sl];
+            return exp2_tang(fma(static_cast<double>(x) - static_cast<double>(s_M[sl]), cT, -s_ls[sl]),
+                             tab);
         };
-        // one drafted token's probability under node row (target?, node of (k, j))
         auto prob_at = [&](bool target, int k, int j, int x) {
             const int sl = stats(target, k, j);
             const int c = s_can[k * L1 + j];
@@ -391,6 +490,13 @@ __device__ void redo_request(const RedoArgs &A, int b, RedoShared &sh) {
                             h = w[L];
                         } else {
                             const double wm = w[m];
+                            const double u = static_cast<double>(ub[k * L + m - 1]);
+                            // h_m <= w_m: a uniform that far above w_m rejects without
+                            // R_m (its margin exceeds the near-tie band either way)
+                            if (u >= wm + kNearTie) {
+                                tie = fmin(tie, u - wm);
+                                continue;
+                            }
                             R[m] = sweep(k, m, [&](int, double p, double q) {
                                 return fmax(wm * p - q, 0.0);
                             });
@@ -464,11 +570,15 @@ __device__ void redo_request(const RedoArgs &A, int b, RedoShared &sh) {
     }
 }
 
+// One workgroup per listed request, grid-stride.
 template <int NT, typename RD, typename E>
-__global__ __launch_bounds__(NT) void redo_kernel(RedoArgs A) {
+__global__ __launch_bounds__(NT) void redo_walk_kernel(RedoArgs A) {
     __shared__ RedoShared sh;
-    for (int b = blockIdx.x; b < A.B; b += gridDim.x)
-        if (A.redo[b]) redo_request<NT, RD, E>(A, b, sh);   // block-uniform
+    const unsigned n = *A.count;
+    if (n == 0) return;
+    exp2_tang_table(sh.tab);
+    for (unsigned i = blockIdx.x; i < n; i += gridDim.x)
+        redo_request<NT, RD, E>(A, static_cast<int>(i), sh);   // block-uniform
 }
 
 }  // namespace sv

@@ -105,6 +105,8 @@ struct StatsArgs {
     RowStat *stats;         // [B][K][2L+1]: target rows 0..L, draft rows at L+1..2L
     const RowRef *list;     // rows the walk asked for (mode kSelectListed)
     unsigned *list_count;   // their number; the first-visit launch resets it to 0
+    unsigned *redo_count;   // requests listed for the fp64 re-evaluation; reset to 0 by
+                            // every launch that is not of listed rows
     int B, K, L, V;
     int mode;               // kSelectAllNodes, kSelectFirstVisit or kSelectListed
     int depth;              // first-visit rows are at positions j < depth (1 <= depth <= L)
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(NT) void rowstats_kernel(StatsArgs A) {
                                 : static_cast<long long>(A.B) * K * NR;
     const int nch = (V + kChunk - 1) / kChunk;
     if (A.mode == kSelectFirstVisit && blockIdx.x == 0 && tid == 0) *A.list_count = 0u;
+    if (A.mode != kSelectListed && blockIdx.x == 0 && tid == 0) *A.redo_count = 0u;
 
     for (long long r = blockIdx.x; r < nrows; r += gridDim.x) {
         int b, k, j, is_target, row_index;

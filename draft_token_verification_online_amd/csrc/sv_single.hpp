@@ -11,15 +11,19 @@
 //   single_stats_kernel   one workgroup per (request, row, slice): the slice's
 //                         maximum and sum of exponentials, from registers (one
 //                         HBM read of every logit);
+//   single_prep_kernel    one workgroup per request: combines the row statistics,
+//                         gathers the drafted tokens' logits, runs the weight
+//                         chain in fp64 and marks the positions the decision can
+//                         reach (SinglePrep, ~1 KB per request);
 //   single_partial_kernel one workgroup per (request, position m = 0..L, slice):
-//                         combines the row statistics, runs the weight chain in
-//                         fp64 and, if the decision can reach position m, sums
-//                         the slice of the residual at m (or, at m = L, of the
-//                         bonus row);
+//                         if the decision can reach position m, sums the slice
+//                         of the residual at m (or, at m = L, of the bonus row);
 //   single_final_kernel   one workgroup per request: the decision from those
 //                         sums, and the correction, found among the slice sums
 //                         and rescanned in the one slice that holds the
-//                         inverse-CDF crossing.
+//                         inverse-CDF crossing; a request with a decision within
+//                         its fp32 error of its threshold is listed for the fp64
+//                         re-evaluation (sv_redo.hpp, two launches after these).
 // (The launch boundaries publish each step's sums to the next.  Handing them
 // over inside one launch -- the last workgroup of a request to finish taking the
 // decision -- needs a device-scope fence per workgroup, which on this chip
@@ -39,15 +43,14 @@
 #pragma once
 
 #include "sv_device.hpp"
-#include "sv_redo.hpp"
 #include "sv_rowstats.hpp"
 #include "sv_walk.hpp"
 
 namespace sv {
 
 constexpr int kSingleThreads = 256;
-constexpr int kSliceChunksPerThread = 4;
-constexpr int kSliceChunks = kSliceChunksPerThread * kSingleThreads;   // 8192 tokens
+constexpr int kSliceChunksPerThread = 8;
+constexpr int kSliceChunks = kSliceChunksPerThread * kSingleThreads;   // 16384 tokens
 
 // Statistics of one slice of a row: its maximum and sum_v 2^(x c - K_s) with
 // K_s = shift_term(maximum).
@@ -66,6 +69,9 @@ struct SingleArgs {
     const float *uc;        // [B]
     SliceStat *part;        // [B][2L+1][NS]: rows in the order target 0..L, draft 0..L-1
     double *rpart;          // [B][L+1][NS]: residual (m < L) or bonus-row (m = L) slice sums
+    struct SinglePrep *prep;   // [B]: each request's combined statistics and chain
+    unsigned *redo_count;   // requests with a decision within its error of its threshold,
+    int32_t *redo_list;     // listed here for the fp64 re-evaluation (sv_redo.hpp)
     int B, L, V, NS;
     int method;             // kMethodToken (token level) or anything else (block)
     int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
@@ -97,6 +103,7 @@ __global__ __launch_bounds__(NT) void single_stats_kernel(SingleArgs A) {
     const int L = A.L, V = A.V, NS = A.NS, RS = 2 * L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
     const long long items = static_cast<long long>(A.B) * RS * NS;
+    if (blockIdx.x == 0 && tid == 0) *A.redo_count = 0u;   // the final launch lists
     for (long long it = blockIdx.x; it < items; it += gridDim.x) {
         const int s = static_cast<int>(it % NS);
         const long long br = it / NS;
@@ -113,13 +120,15 @@ __global__ __launch_bounds__(NT) void single_stats_kernel(SingleArgs A) {
 #pragma unroll
         for (int i = 0; i < kSliceChunksPerThread; ++i)
             if (i * NT + tid < nc) raw[i] = R.raw_once(c0 + i * NT + tid);
-        float x[kSliceChunksPerThread][8];
+        // the slice's maximum, then its exponentials (the chunks stay packed in
+        // registers and are unpacked for each pass)
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kSliceChunksPerThread; ++i) {
             if (i * NT + tid < nc) {
-                RD::unpack(raw[i], x[i]);
-                m = fmaxf(m, max8(x[i]));
+                float x[8];
+                RD::unpack(raw[i], x);
+                m = fmaxf(m, max8(x));
             }
         }
         const float M = block_max<NT>(m, s_fred);
@@ -128,9 +137,10 @@ __global__ __launch_bounds__(NT) void single_stats_kernel(SingleArgs A) {
 #pragma unroll
         for (int i = 0; i < kSliceChunksPerThread; ++i) {
             if (i * NT + tid < nc) {
-                float e[8];
+                float x[8], e[8];
+                RD::unpack(raw[i], x);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) e[k] = fast_exp2(expo(x[i][k], c, K));
+                for (int k = 0; k < 8; ++k) e[k] = fast_exp2(expo(x[k], c, K));
                 acc += static_cast<double>(sum8(e));
             }
         }
@@ -154,10 +164,13 @@ struct SinglePrep {
     float gp[16], gq[16];
     double lr[16];      // log2 p - log2 q of the drafted token at position j
     double w[17];       // GBV's weights w_0..w_L
+    double wrel[17];    // their relative error estimates (0 where clamped at 1 for certain)
     int need[17];       // positions whose slice sums the decision can use
     int tau;            // token level: the first rejected position (L: none)
     int bad;
+    int pad[1];
 };
+static_assert(sizeof(SinglePrep) % 16 == 0, "whole words");
 
 template <int NT, typename RD, typename E>
 __device__ void single_prepare(const SingleArgs &A, int b, const Scale &c, double scd,
@@ -231,12 +244,17 @@ __device__ void single_prepare(const SingleArgs &A, int b, const Scale &c, doubl
             if (!bad) {
                 // first position: the target itself is the residual (alpha = 1,
                 // beta = 0, N = 1); deeper ones the chain of likelihood ratios
-                double w = P.lr[0] == -INFINITY ? 0.0 : fmin(exp2(P.lr[0]), 1.0);
+                const double r0 = P.lr[0] == -INFINITY ? 0.0 : exp2(P.lr[0]);
+                double w = fmin(r0, 1.0), rel = clamp_err(r0, 4.0 * kExpEps);
                 P.w[0] = 1.0;
                 P.w[1] = w;
+                P.wrel[1] = rel;
                 for (int j = 1; j < L; ++j) {
-                    w = chain_step(w, P.lr[j] == -INFINITY ? 0.0 : exp2(P.lr[j]));
+                    const double r = P.lr[j] == -INFINITY ? 0.0 : exp2(P.lr[j]);
+                    rel = clamp_err(w * r, rel + 4.0 * kExpEps);   // two row sums per ratio
+                    w = chain_step(w, r);
                     P.w[j + 1] = w;
+                    P.wrel[j + 1] = rel;
                 }
                 if (static_cast<double>(u[L - 1]) < P.w[L]) {
                     P.need[L] = 1;
@@ -249,6 +267,31 @@ __device__ void single_prepare(const SingleArgs &A, int b, const Scale &c, doubl
         }
         P.bad = bad;
     }
+    __syncthreads();
+}
+
+// One workgroup per request: its SinglePrep, once, for the two launches after it.
+template <int NT, typename RD, typename E>
+__global__ __launch_bounds__(NT) void single_prep_kernel(SingleArgs A) {
+    __shared__ SinglePrep P;
+    for (int b = blockIdx.x; b < A.B; b += gridDim.x) {
+        const Scale c = temp_scale(A.temp[b]);
+        single_prepare<NT, RD, E>(A, b, c, scale64(c), P);
+        const unsigned *src = reinterpret_cast<const unsigned *>(&P);
+        unsigned *dst = reinterpret_cast<unsigned *>(A.prep + b);
+        for (int i = threadIdx.x; i < static_cast<int>(sizeof(SinglePrep) / 4); i += NT)
+            dst[i] = src[i];
+        __syncthreads();
+    }
+}
+
+// A request's SinglePrep into LDS (block-uniform call).
+template <int NT>
+__device__ __forceinline__ void load_prep(const SingleArgs &A, int b, SinglePrep &P) {
+    const unsigned *src = reinterpret_cast<const unsigned *>(A.prep + b);
+    unsigned *dst = reinterpret_cast<unsigned *>(&P);
+    for (int i = threadIdx.x; i < static_cast<int>(sizeof(SinglePrep) / 4); i += NT)
+        dst[i] = src[i];
     __syncthreads();
 }
 
@@ -269,9 +312,11 @@ __global__ __launch_bounds__(NT) void single_partial_kernel(SingleArgs A) {
         const int s = static_cast<int>(it % NS);
         const int m = static_cast<int>((it / NS) % L1);
         const int b = static_cast<int>(it / (static_cast<long long>(NS) * L1));
+        // most items are not needed: check the request's flags before anything else
+        const SinglePrep *G = A.prep + b;
+        if (G->bad || !G->need[m]) continue;   // block-uniform
         const Scale c = temp_scale(A.temp[b]);
-        single_prepare<NT, RD, E>(A, b, c, scale64(c), P);
-        if (P.bad || !P.need[m]) continue;   // block-uniform
+        load_prep<NT>(A, b, P);
         const E *tgt = static_cast<const E *>(A.tgt) + static_cast<long long>(b) * L1 * V;
         const E *drf = static_cast<const E *>(A.drf) + static_cast<long long>(b) * L * V;
         const int c0 = s * kSliceChunks;
@@ -330,35 +375,15 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
     __shared__ double s_red[NW];
     __shared__ int s_ired[NW];
     __shared__ double s_z[2];
-    __shared__ RedoShared s_redo;
     const int tid = threadIdx.x;
     const int L = A.L, V = A.V, NS = A.NS, RS = 2 * L + 1, L1 = L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
     const bool token = A.method == kMethodToken;
-    RedoArgs ra;
-    ra.tgt = A.tgt;
-    ra.drf = A.drf;
-    ra.tok = A.tok;
-    ra.temp = A.temp;
-    ra.ua = A.ua;
-    ra.uc = A.uc;
-    ra.redo = nullptr;
-    ra.B = A.B;
-    ra.K = 1;
-    ra.L = L;
-    ra.V = V;
-    ra.method = A.method;
-    ra.accept_len = A.accept_len;
-    ra.draft_index = A.draft_index;
-    ra.correction = A.correction;
-    ra.flags = A.flags;
-    ra.accept_prob = A.accept_prob;
-    ra.resid_mass = A.resid_mass;
     for (int b = blockIdx.x; b < A.B; b += gridDim.x) {
         const float T = A.temp[b];
         const Scale c = temp_scale(T);
         const double scd = scale64(c);
-        single_prepare<NT, RD, E>(A, b, c, scd, P);
+        load_prep<NT>(A, b, P);
         const E *tgt = static_cast<const E *>(A.tgt) + static_cast<long long>(b) * L1 * V;
         const E *drf = static_cast<const E *>(A.drf) + static_cast<long long>(b) * L * V;
         auto trow = [&](int j) { return RD(tgt + static_cast<long long>(j) * V, V); };
@@ -394,9 +419,9 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
                 for (int mm = L; mm >= 1; --mm) {
                     const double uu = static_cast<double>(u[mm - 1]);
                     const double wm = P.w[mm];
-                    // first-order error of w_m (two row sums per ratio of the chain)
-                    // and of h_m = R / (R + 1 - w_m)
-                    const double dw = wm * 4.0 * kExpEps * mm;
+                    // first-order error of w_m (exact where the chain clamped at 1
+                    // with room to spare) and of h_m = R / (R + 1 - w_m)
+                    const double dw = wm * P.wrel[mm];
                     double h, eh = dw;
                     if (mm == L) {
                         h = wm;
@@ -579,10 +604,10 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
         }
         if (bad && hout)
             for (int j = tid; j < L; j += NT) hout[j] = NAN;
+        // a decision within the fp32 error of its threshold: the request is taken
+        // again in fp64 (sv_redo.hpp)
+        if (tid == 0 && !bad && (flags & kFlagNearTie)) A.redo_list[atomicAdd(A.redo_count, 1u)] = b;
         __syncthreads();
-        // a decision within the fp32 error of its threshold: take the request
-        // again in fp64 (block-uniform)
-        if (!bad && (flags & kFlagNearTie)) redo_request<NT, RD, E>(ra, b, s_redo);
     }
 }
 

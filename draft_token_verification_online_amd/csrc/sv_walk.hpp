@@ -93,7 +93,8 @@ struct WalkArgs {
     void *nodes;            // [B] node lists (node_list_bytes each), or null
     int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
     float *row_lse, *accept_prob, *resid_mass;
-    unsigned char *redo;    // [B]: 1 where a decision came within its error of its threshold
+    unsigned *redo_count;   // requests with a decision within its error of its threshold,
+    int32_t *redo_list;     // listed here for the fp64 re-evaluation
 };
 
 // Likelihood ratio from log2-probabilities, with the drafted-token convention:
@@ -107,6 +108,13 @@ __device__ __forceinline__ double chain_step(double w, double r) {
     if (w == 0.0) return 0.0;
     const double t = w * r;
     return t < 1.0 ? t : 1.0;
+}
+
+// Relative error estimate of a weight after min(t, 1), t carrying relative error
+// rel: a value above 1 by more than four times its error clamps to exactly 1 in
+// exact arithmetic too (error 0); otherwise the clamp may not hold exactly.
+__device__ __forceinline__ double clamp_err(double t, double rel) {
+    return (t >= 1.0 && t * (1.0 - 4.0 * rel) >= 1.0) ? 0.0 : rel;
 }
 
 // The chunks of the rejected-token set H that this thread reads (chunk c is
@@ -718,7 +726,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
     __shared__ double s_tile[kMaxTiles];
     __shared__ int s_H[kMaxK];
     __shared__ double s_w[kMaxL + 1];
-    __shared__ double s_werr;   // relative error estimate of the first weight of the chain
+    __shared__ double s_wrel[kMaxL + 1];   // relative error estimates of the weights
     __shared__ unsigned s_hist[SPECTR ? 2 * kHistBins : 1];
     __shared__ double s_red6[SPECTR ? 6 * NW : 1];
     __shared__ double s_br[4];
@@ -987,14 +995,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     const double om = fmax(alpha * ps - beta * qs, 0.0);
                     __syncthreads();   // previous readers of s_w are done
                     if (tid == 0) {
-                        double w = (qs > 0.0) ? fmin(om / N / qs, 1.0) : (om > 0.0 ? 1.0 : 0.0);
+                        const double raw = (qs > 0.0) ? om / N / qs : (om > 0.0 ? INFINITY : 0.0);
+                        double w = fmin(raw, 1.0);
                         s_w[tau + 1] = w;
                         // omega(x) cancels when alpha p ~ beta q; N and q add a sum's error
-                        s_werr = (om > 0.0 ? (alpha * ps + beta * qs) * 2.0 * kExpEps / om : 0.0) +
-                                 6.0 * kExpEps;
+                        double rel = (om > 0.0 ? (alpha * ps + beta * qs) * 2.0 * kExpEps / om : 0.0) +
+                                     6.0 * kExpEps;
+                        rel = clamp_err(raw, rel);
+                        s_wrel[tau + 1] = rel;
                         for (int j = tau + 1; j < L; ++j) {
-                            w = chain_step(w, ratio_log2(lp2(k, j), lq2(k, j)));
+                            const double r = ratio_log2(lp2(k, j), lq2(k, j));
+                            rel = clamp_err(w * r, rel + 4.0 * kExpEps);   // two row sums per ratio
+                            w = chain_step(w, r);
                             s_w[j + 1] = w;
+                            s_wrel[j + 1] = rel;
                         }
                     }
                     __syncthreads();
@@ -1003,9 +1017,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     for (int m = L; m > tau; --m) {
                         const double u = static_cast<double>(A.ua[bKL + k * L + m - 1]);
                         const double wm = s_w[m];
-                        // first-order error of w_m: the first weight's, plus two row
-                        // sums per further ratio of the chain
-                        const double dw = wm * (s_werr + 4.0 * kExpEps * (m - tau - 1));
+                        // first-order error of w_m (exact where the chain clamped at 1
+                        // with room to spare)
+                        const double dw = wm * s_wrel[m];
                         double h, eh = dw;
                         if (m == L) {
                             h = wm;
@@ -1228,7 +1242,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             Zp = NAN;
         }
         ws->status = kStateDone;
-        if (A.redo) A.redo[b] = (!bad && (flags & kFlagNearTie)) ? 1 : 0;
+        if (!bad && (flags & kFlagNearTie)) A.redo_list[atomicAdd(A.redo_count, 1u)] = b;
         A.accept_len[b] = tau;
         A.draft_index[b] = kstar;
         A.correction[b] = y;

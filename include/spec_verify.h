@@ -198,10 +198,14 @@ typedef struct sv_launch {
 } sv_launch;
 
 /* Workspace bytes a call with these sizes needs (0 on invalid sizes): row
- * statistics (16 bytes per node row), one saved walk state per request, the
- * rows listed for the second round and, for K >= 3, one node list per request
+ * statistics (16 bytes per node row, reused after the walk for the fp64
+ * statistics of the requests taken again), one saved walk state per request,
+ * the rows listed for the second round, the list of requests taken again in
+ * fp64 (4 bytes per request) and, for K >= 3, one node list per request
  * (196 608 bytes: the tokens a node's repeated residual-mass sweeps still need,
- * so those sweeps read a few thousand entries instead of two rows of V). */
+ * so those sweeps read a few thousand entries instead of two rows of V).  With
+ * K = 1 the single-draft path's slice statistics, residual slice sums and
+ * per-request chains when they are larger. */
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t L, int32_t V, int32_t dtype);
 
 /* Token-level speculative sampling (K must be 1). */
@@ -292,7 +296,7 @@ int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
 /* The step that produces the verifier's inputs: logits = h W^T for bf16 hidden
  * states h [R][d] and a bf16 vocabulary projection W [V][d] (row-major, so both
  * operands are contiguous along d), fp32 accumulation on the matrix cores, fp32
- * logits out.  The temperature-softmax statistics of every row (the verifier's
+ * or bf16 logits out.  The temperature-softmax statistics of every row (the verifier's
  * first step) are computed in the same kernel while the row is in registers,
  * so passing them to a verification call (sv_inputs.row_stats) removes the
  * statistics pass over the logits.  Verification is a large share of a
@@ -307,13 +311,17 @@ typedef struct sv_lm_inputs {
 } sv_lm_inputs;
 
 typedef struct sv_lm_outputs {
-    float *logits;                /* [R][V] fp32, required */
+    void *logits;                 /* [R][V], required: fp32, or bf16 when logits_dtype is
+                                     SV_BF16 (rounded to nearest even; the statistics are
+                                     then those of the rounded values, as the verifier
+                                     reads them) */
     void *row_stats;              /* optional sv_row_stat array: row r is written to slot
                                      (r / stats_group) * stats_stride + stats_offset
                                      + r % stats_group.  Target rows [B][K][L+1] go to
                                      group L+1, stride 2L+1, offset 0; draft rows
                                      [B][K][L] to group L, stride 2L+1, offset L+1. */
     int32_t stats_group, stats_stride, stats_offset;
+    int32_t logits_dtype;         /* SV_F32 or SV_BF16 */
 } sv_lm_outputs;
 
 /* Workspace bytes spec_lm_head needs (0 on invalid sizes). */

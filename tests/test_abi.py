@@ -64,7 +64,8 @@ def test_status_strings_and_version(lib):
 def test_workspace_size(lib):
     ws = sv.workspace_size
     big = ws(512, 8, 8, 151936, sv.SV_BF16)
-    # row statistics (16 B per row) + per-request walk state + flag bytes, 256-aligned,
+    # row statistics (16 B per row) + per-request walk state, flag bytes and list entries,
+    # 256-aligned,
     # + a 196 608-byte node list per request when K >= 3
     node_lists = 512 * 196608
     assert big % 256 == 0
@@ -72,7 +73,7 @@ def test_workspace_size(lib):
     two = ws(512, 2, 8, 151936, sv.SV_BF16)
     assert two % 256 == 0 and 512 * 2 * 17 * 16 <= two < big - node_lists   # no node lists for K = 2
     assert ws(1, 1, 4, 32, sv.SV_F32) % 256 == 0 and ws(1, 1, 4, 32, sv.SV_F32) >= 9 * 16
-    assert ws(0, 1, 1, 1, sv.SV_F32) == 256
+    assert ws(0, 1, 1, 1, sv.SV_F32) == 512   # the two list counters
     for bad in [(1, 0, 4, 32), (1, 65, 4, 32), (1, 1, 0, 32), (1, 1, 17, 32), (1, 1, 4, 0),
                 (1, 1, 4, (1 << 22) + 1), (-1, 1, 4, 32)]:
         assert ws(*bad, sv.SV_F32) == 0, bad

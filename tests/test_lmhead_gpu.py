@@ -125,3 +125,73 @@ def test_lm_head_statistics_feed_verification(method):
           f"lse err {lse_err:.2e}", flush=True)
     assert not bad, bad
     assert lse_err <= bnd / float(Th.min()) + 1e-5
+
+
+@pytest.mark.parametrize("R,d,V,T", [(130, 64, 1000, 0.7), (257, 128, 4099, 0.4),
+                                     (128, 3584, 2048, 0.25)])
+def test_bf16_logits_and_their_statistics(R, d, V, T):
+    """bf16 logits: each is the fp32 accumulation rounded to nearest even, so it
+    lies within the accumulation bound plus half a bf16 ulp (2^-8 relative) of
+    the exact product; the statistics describe the stored (rounded) values."""
+    from scipy.special import logsumexp
+    print(f"[case] lm_head bf16 R={R} d={d} V={V} T={T}", flush=True)
+    h, w = _make(R, d, V, 300 + R)
+    temps = torch.full((R,), T, device="cuda") * (1 + 0.5 * (torch.arange(R, device="cuda") % 3))
+    stats = torch.zeros(R * 16, dtype=torch.uint8, device="cuda")
+    lm = LmHead(R, d, V, logits_dtype=torch.bfloat16)
+    logits = lm(h, w, temps, stats=stats)
+    torch.cuda.synchronize()
+    hb, wb, tt = _bits(h), _bits(w), temps.cpu().numpy().astype(np.float64)
+    ref, _ = oracle.lm_head(hb, wb, tt)
+    bound = _bound(hb, wb)
+    got = oracle.bf16_bits_to_f64(_bits(logits))
+    err = np.abs(got - ref)
+    assert (err <= bound + (np.abs(ref) + bound) * 2.0 ** -8).all()
+    lse_rounded = logsumexp(got / tt[:, None], axis=1)
+    lse_gpu = _stats_lse(stats, R, tt)
+    rel = np.abs(lse_gpu - lse_rounded) / np.maximum(1.0, np.abs(lse_rounded))
+    assert rel.max() <= 1e-6, rel.max()
+    print(f"[parity] lm_head bf16 R={R} d={d} V={V}: max logit err {err.max():.2e}, "
+          f"lse of the stored values rel {rel.max():.2e}", flush=True)
+
+
+@pytest.mark.parametrize("method", ["multidraft", "spectr"])
+def test_bf16_lm_head_feeds_verification(method):
+    """Target and draft LM heads write bf16 logits and the statistics of those
+    rounded values; verification given the statistics (no statistics pass) must
+    meet the parity bar against the oracle run on the same bf16 logits."""
+    B, K, L, V, d = 12, 4, 4, 4096, 256
+    print(f"[case] lm_head bf16->verify {method} B={B} K={K} L={L} V={V} d={d}", flush=True)
+    ht, wt = _make(B * K * (L + 1), d, V, 17)
+    g = torch.Generator(device="cuda").manual_seed(18)
+    hd = (ht.view(B, K, L + 1, d)[:, :, :L].float()
+          + 0.5 * torch.randn((B, K, L, d), generator=g, device="cuda")).to(torch.bfloat16)
+    hd = hd.reshape(B * K * L, d).contiguous()
+    wd = (wt.float() + 0.3 * (4 / d ** 0.5) * torch.randn((V, d), generator=g, device="cuda")
+          ).to(torch.bfloat16)
+    T = (0.5 + 0.5 * (torch.arange(B, device="cuda") % 3)).float()
+    stats = torch.zeros(B * K * (2 * L + 1) * 16, dtype=torch.uint8, device="cuda")
+    lt = LmHead(B * K * (L + 1), d, V, logits_dtype=torch.bfloat16)(
+        ht, wt, T.repeat_interleave(K * (L + 1)), stats=stats, group=L + 1, stride=2 * L + 1,
+        offset=0)
+    ld = LmHead(B * K * L, d, V, logits_dtype=torch.bfloat16)(
+        hd, wd, T.repeat_interleave(K * L), stats=stats, group=L, stride=2 * L + 1, offset=L + 1)
+    torch.cuda.synchronize()
+    tgt, drf = lt.view(B, K, L + 1, V), ld.view(B, K, L, V)
+    rng = np.random.default_rng(19)
+    Th = T.cpu().numpy()
+    tok = oracle.draft(_bits(drf).reshape(B, K, L, V), Th,
+                       rng.random((B, K, L)).astype(np.float32))["tokens"]
+    ua = rng.random((B, K, L)).astype(np.float32)
+    uc = rng.random(B).astype(np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    batch = {"target": tgt, "draft": drf, "tokens": dev(tok), "temperature": T,
+             "u_accept": dev(ua), "u_correct": dev(uc)}
+    v = Verifier(method, B, K, L, V, torch.bfloat16, diagnostics=True)
+    out = v(tgt, drf, batch["tokens"], T, batch["u_accept"], batch["u_correct"], row_stats=stats)
+    torch.cuda.synchronize()
+    assert (out["rows_streamed"] == 0).all()
+    ref = pt.run_oracle(method, {"target": _bits(tgt).reshape(B, K, L + 1, V),
+                                 "draft": _bits(drf).reshape(B, K, L, V), "tokens": tok,
+                                 "temperature": Th, "u_accept": ua, "u_correct": uc})
+    pt.check(pt.compare(method, out, ref, list(range(B)), label=f"lm_head_bf16/{method}"))
