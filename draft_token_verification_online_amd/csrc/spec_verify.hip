@@ -69,11 +69,11 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
 // Workspace: row statistics (after the walk, the fp64 statistics of the requests
 // listed for re-evaluation) | walk states | node rows flagged for the second
 // round (bytes, then the same rows as a list) | list length | number of
-// requests listed for re-evaluation in fp64 | their indices | node lists of the
-// walk (K >= 3 only: a node sees a second mass sweep only with three or more
-// drafts).
+// requests listed for re-evaluation in fp64 | their indices | the GBV walk's
+// test records (a byte per test) | node lists of the walk (K >= 3 only: a node
+// sees a second mass sweep only with three or more drafts).
 struct Layout {
-    size_t stats, state, need, list, count, rcount, rlist, nodes, total;
+    size_t stats, state, need, list, count, rcount, rlist, dec, nodes, total;
     bool has_nodes;
 };
 
@@ -110,7 +110,8 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.count = l.list + align_up(2 * bkl * sizeof(sv::RowRef), 256);
     l.rcount = l.count + 256;
     l.rlist = l.rcount + 256;
-    l.nodes = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
+    l.dec = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
+    l.nodes = l.dec + align_up(bkl, 256);
     l.has_nodes = K >= 3;
     l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
                                            static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
@@ -133,7 +134,8 @@ __global__ void reset_count_kernel(unsigned *count) {
 // B * K * (2L + 1) * 16 bytes that the fast path no longer reads.
 template <typename E, bool VEC>
 hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t stream, int method,
-                       const unsigned *count, const int32_t *list, void *stats) {
+                       const unsigned *count, const int32_t *list, void *stats,
+                       const unsigned char *dec) {
     using RD = typename sv::RowOf<E, VEC>::type;
     sv::RedoArgs ra;
     ra.tgt = in->target_logits;
@@ -145,6 +147,7 @@ hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t s
     ra.count = count;
     ra.list = list;
     ra.stats = static_cast<sv::RedoStat *>(stats);
+    ra.dec = dec;
     ra.B = in->B;
     ra.K = in->K;
     ra.L = in->L;
@@ -240,6 +243,8 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.resid_mass = out->resid_mass;
     wa.redo_count = sa.redo_count;
     wa.redo_list = reinterpret_cast<int32_t *>(ws + lay.rlist);
+    wa.dec = method == sv::kMethodBlockWalk ? reinterpret_cast<unsigned char *>(ws + lay.dec)
+                                            : nullptr;
 
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
@@ -280,7 +285,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         if ((err = walk()) != hipSuccess) return err;
     }
     if ((err = launch_redo<E, VEC>(in, out, stream, wa.method, wa.redo_count, wa.redo_list,
-                                   ws + lay.stats)) != hipSuccess)
+                                   ws + lay.stats, wa.dec)) != hipSuccess)
         return err;
     return record(ln, 4, stream);
 }
@@ -351,7 +356,7 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
                        a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_redo<E, VEC>(in, out, stream, method, a.redo_count, a.redo_list,
-                                   ws + lay.part)) != hipSuccess)
+                                   ws + lay.part, nullptr)) != hipSuccess)
         return err;
     for (int i = 2; i < 5; ++i)
         if ((err = record(ln, i, stream)) != hipSuccess) return err;

@@ -38,15 +38,17 @@ namespace sv {
 constexpr int kFlagRedone = 8;
 constexpr int kRedoThreads = 512;        // per listed request
 constexpr int kRedoStatsThreads = 512;   // per (listed request, node row)
+constexpr int kRedoDepth = 4;            // chunks per row in flight per thread
+
 
 // 2^a in double precision.  a = (256 n + j + r) / 256 with n, j integers,
 // 0 <= j < 256, |r| <= 1/2: 2^a = 2^n * tab[j] * 2^(r/256), tab[j] = 2^(j/256),
 // and 2^(r/256) = exp(r ln2/256) is its Taylor polynomial of degree 4
-// (truncation below 4e-17 for |r ln2/256| <= 1.36e-3).  0 for a below the
-// subnormal range and for NaN; +inf above the double range.
+// (truncation below 4e-17 for |r ln2/256| <= 1.36e-3).  Branch-free: a is
+// clamped to [-1080, 1030] (NaN to -1080), where ldexp gives 0 below the
+// subnormal range and +inf above the double range.
 __device__ __forceinline__ double exp2_tang(double a, const double *tab) {
-    if (!(a > -1080.0)) return 0.0;
-    if (a > 1030.0) return INFINITY;
+    a = fmin(fmax(a, -1080.0), 1030.0);
     const double t = a * 256.0;
     const double k = rint(t);
     const double r = t - k;   // exact
@@ -79,7 +81,8 @@ struct RedoArgs {
     const int32_t *tok;           // [B][K][L]
     const float *temp, *ua, *uc;  // [B], [B][K][L], [B]
     const unsigned *count;        // listed requests
-    const int32_t *list;          // [count]: their indices
+    const int32_t *list;          // [count]: their indices (| kListNoReplay)
+    const unsigned char *dec;     // [B][K][L] the fast GBV walk's test records, or null
     RedoStat *stats;              // [count][K][2L+1]: node rows of listed request i at i*K*(2L+1)
     int B, K, L, V;
     int method;                   // kMethodToken, kMethodBlockWalk or kMethodSpecTr
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
     for (long long it = blockIdx.x; it < items; it += gridDim.x) {
         const int i = static_cast<int>(it / per), r = static_cast<int>(it % per);
         const int k = r / RS, s = r % RS;
-        const int b = A.list[i];
+        const int b = A.list[i] & ~kListNoReplay;
         const bool target = s <= L;
         const int j = target ? s : s - L1;
         const int32_t *tk = A.tok + static_cast<long long>(b) * K * L;
@@ -125,24 +128,34 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
         float mx = -INFINITY;
         double sum = 0.0;
         int nan = !(T > 0.0f) || !isfinite(T);
-        for (int q = tid; q < nch; q += NT) {
-            float x[8];
-            R.load(q, x);
-            float cm = -INFINITY;
+        for (int q0 = tid; q0 < nch; q0 += kRedoDepth * NT) {   // loads issued ahead
+            typename RD::Raw raw[kRedoDepth];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                nan |= isnan(x[e]) || x[e] == INFINITY;
-                cm = fmaxf(cm, x[e]);
-            }
-            if (cm > mx) {   // rescale the sum to the new maximum
-                if (mx > -INFINITY)
-                    sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(cm)) * cT, s_tab);
-                mx = cm;
-            }
-            if (mx > -INFINITY && !nan) {
+            for (int d = 0; d < kRedoDepth; ++d)
+                if (q0 + d * NT < nch) raw[d] = R.raw(q0 + d * NT);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sum += exp2_tang((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT, s_tab);
+            for (int d = 0; d < kRedoDepth; ++d) {
+                if (q0 + d * NT >= nch) break;
+                float x[8];
+                RD::unpack(raw[d], x);
+                float cm = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    nan |= isnan(x[e]) || x[e] == INFINITY;
+                    cm = fmaxf(cm, x[e]);
+                }
+                if (cm > mx) {   // rescale the sum to the new maximum
+                    if (mx > -INFINITY)
+                        sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(cm)) * cT,
+                                         s_tab);
+                    mx = cm;
+                }
+                if (mx > -INFINITY && !nan) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sum += exp2_tang((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT,
+                                         s_tab);
+                }
             }
         }
         nan = __syncthreads_or(nan);
@@ -171,6 +184,7 @@ struct RedoShared {
     float M[kMaxK * (2 * kMaxL + 1)];
     double ls[kMaxK * (2 * kMaxL + 1)];
     int H[kMaxK];
+    unsigned char made[kMaxK * kMaxL];   // tests of the final path (accept_prob entries kept)
     double red[16];
     float fred[16];
     int ired[16];
@@ -192,7 +206,8 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
     const int tid = threadIdx.x;
     const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
-    const int b = A.list[li];
+    const int entry = A.list[li];
+    const int b = entry & ~kListNoReplay;
     {
         const long long bKL = static_cast<long long>(b) * K * L;
         // exp((l - M) / T) taken as 2^((l - M) log2(e) / T)
@@ -248,13 +263,26 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             const int sp = stats(true, k, j), sq = stats(false, k, j);
             const RD P = row(true, c, j), Q = row(false, c, j);
             double acc = 0.0;
-            for (int q = tid; q < nch; q += NT) {
-                float xp[8], xq[8];
-                P.load(q, xp);
-                Q.load(q, xq);
-                for (int e = 0; e < 8; ++e) {
-                    const int v = kChunk * q + e;
-                    if (v < V) acc += f(v, prob(sp, xp[e]), prob(sq, xq[e]));
+            for (int q0 = tid; q0 < nch; q0 += 2 * NT) {   // loads issued ahead
+                typename RD::Raw rp[2], rq[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    if (q0 + d * NT < nch) {
+                        rp[d] = P.raw(q0 + d * NT);
+                        rq[d] = Q.raw(q0 + d * NT);
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const int q = q0 + d * NT;
+                    if (q >= nch) break;
+                    float xp[8], xq[8];
+                    RD::unpack(rp[d], xp);
+                    RD::unpack(rq[d], xq);
+                    for (int e = 0; e < 8; ++e) {
+                        const int v = kChunk * q + e;
+                        if (v < V) acc += f(v, prob(sp, xp[e]), prob(sq, xq[e]));
+                    }
                 }
             }
             return block_sum<NT>(acc, s_red);
@@ -278,14 +306,27 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             };
             double mine = 0.0;
             int lastpos = -1;
-            for (int q = q0; q < q1; ++q) {
-                float xp[8], xq[8];
-                P.load(q, xp);
-                if (with_q) Q.load(q, xq);
-                for (int e = 0; e < 8; ++e) {
-                    const double wv = weight(q, e, xp, xq);
-                    mine += wv;
-                    if (wv > 0.0) lastpos = kChunk * q + e;
+            for (int qb = q0; qb < q1; qb += 2) {   // loads issued ahead
+                typename RD::Raw rp[2], rq[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    if (qb + d < q1) {
+                        rp[d] = P.raw(qb + d);
+                        if (with_q) rq[d] = Q.raw(qb + d);
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const int q = qb + d;
+                    if (q >= q1) break;
+                    float xp[8], xq[8];
+                    RD::unpack(rp[d], xp);
+                    if (with_q) RD::unpack(rq[d], xq);
+                    for (int e = 0; e < 8; ++e) {
+                        const double wv = weight(q, e, xp, xq);
+                        mine += wv;
+                        if (wv > 0.0) lastpos = kChunk * q + e;
+                    }
                 }
             }
             const double pre = block_exclusive_scan<NT>(mine, s_red);
@@ -337,15 +378,19 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             return t < 1.0 ? t : 1.0;
         };
 
+        // accept_prob: every test of the final path is written (or, replayed
+        // from the fast walk, kept); the others are set to NaN at the end
         float *hout = A.accept_prob ? A.accept_prob + bKL : nullptr;
-        if (hout)
-            for (int i = tid; i < K * L; i += NT) hout[i] = NAN;
+        unsigned char *s_made = sh.made;
+        for (int q = tid; q < K * L; q += NT) s_made[q] = 0;
+        __syncthreads();
         const float *ub = A.ua + bKL;
         double tie = INFINITY;
         int flags = 0;
         auto test = [&](int k, int m, double h) {   // u < h for position m of draft k
             const double u = static_cast<double>(ub[k * L + m - 1]);
             if (tid == 0 && hout) hout[k * L + m - 1] = static_cast<float>(h);
+            s_made[k * L + m - 1] = 1;
             tie = fmin(tie, fabs(u - h));
             return u < h;
         };
@@ -467,6 +512,11 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
                 });
             };
+            // While every decision so far agrees with the fast walk's, the walks
+            // are in the same state, and a test the fast walk recorded as certain
+            // is taken from its record without R_m (R_m is still summed where the
+            // test accepts: it is the next node's mass).
+            bool follow = A.dec != nullptr && !(entry & kListNoReplay);
             for (int k = 0; k < K && tau < L && !bad; ++k) {
                 if (!same_prefix(k, own, tau)) continue;
                 const int x = s_x[k * L + tau];
@@ -485,6 +535,21 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     if (bad) break;
                     int acc = 0;
                     for (int m = L; m > tau; --m) {
+                        const int dc = follow ? A.dec[bKL + k * L + m - 1] : 0;
+                        if (follow && !(dc & kDecMade)) follow = false;
+                        if (follow && (dc & kDecCertain)) {
+                            s_made[k * L + m - 1] = 1;
+                            if (!(dc & kDecAccept)) continue;
+                            if (m < L) {
+                                const double wm = w[m];
+                                R[m] = sweep(k, m, [&](int, double p, double q) {
+                                    return fmax(wm * p - q, 0.0);
+                                });
+                                if (bad) break;
+                            }
+                            acc = m;
+                            break;
+                        }
                         double h;
                         if (m == L) {
                             h = w[L];
@@ -495,6 +560,9 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                             // R_m (its margin exceeds the near-tie band either way)
                             if (u >= wm + kNearTie) {
                                 tie = fmin(tie, u - wm);
+                                if (tid == 0 && hout) hout[k * L + m - 1] = NAN;
+                                s_made[k * L + m - 1] = 1;
+                                if (dc & kDecAccept) follow = false;
                                 continue;
                             }
                             R[m] = sweep(k, m, [&](int, double p, double q) {
@@ -504,7 +572,9 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                             const double d = R[m] + 1.0 - wm;
                             h = d > 0.0 ? R[m] / d : 1.0;
                         }
-                        if (test(k, m, h)) { acc = m; break; }
+                        const bool a_m = test(k, m, h);
+                        if (a_m != ((dc & kDecAccept) != 0)) follow = false;
+                        if (a_m) { acc = m; break; }
                     }
                     if (bad) break;
                     if (acc > 0) {
@@ -531,6 +601,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     beta = 0.0;
                     N = 1.0;
                     nH = 0;
+                    follow = false;
                 }
             }
             if (!bad) {
@@ -564,8 +635,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             if (A.flags) A.flags[b] = flags | kFlagRedone;
             if (A.resid_mass) A.resid_mass[b] = static_cast<float>(Z);
         }
-        if (bad && hout)
-            for (int i = tid; i < K * L; i += NT) hout[i] = NAN;
+        __syncthreads();
+        if (hout)
+            for (int q = tid; q < K * L; q += NT)
+                if (bad || !s_made[q]) hout[q] = NAN;
         __syncthreads();
     }
 }

@@ -65,6 +65,13 @@ constexpr double kExpEps = 0x1p-23;
 // this (a quarter of the 1e-5 the acceptance probabilities are reported to) is
 // taken again in fp64 too, so the reported h hold to fp64 however ill-conditioned.
 constexpr double kDiagEh = 2.5e-6;
+// A GBV test's record for the fp64 re-evaluation (WalkArgs::dec).  Certain:
+// its margin is at least SV_NEAR_TIE plus four times its error estimate, so
+// the exact test agrees and its exact margin exceeds SV_NEAR_TIE.
+constexpr unsigned char kDecMade = 1, kDecAccept = 2, kDecCertain = 4;
+// A listed request whose walk met a degenerate residual, after which the fast
+// and the fp64 walk can be in different states: re-evaluated without the records.
+constexpr int kListNoReplay = 1 << 30;
 // Node lists: entries per wave, and the cutoff 2^-kListCut below which a
 // token's residual weight omega(v) / alpha leaves the list.
 constexpr int kWaveList = 2048;
@@ -95,6 +102,9 @@ struct WalkArgs {
     float *row_lse, *accept_prob, *resid_mass;
     unsigned *redo_count;   // requests with a decision within its error of its threshold,
     int32_t *redo_list;     // listed here for the fp64 re-evaluation
+    unsigned char *dec;     // [B][K][L] GBV tests made (kDecMade), accepted (kDecAccept) and
+                            // certain in exact arithmetic (kDecCertain); entries of tests
+                            // not made are left as they were
 };
 
 // Likelihood ratio from log2-probabilities, with the drafted-token convention:
@@ -1027,6 +1037,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                             if (!(u < wm)) {              // h_m <= w_m: rejects without a sweep
                                 tie = fmin(tie, u - wm);
                                 if (u - wm < 4.0 * dw) tie = 0.0;   // within its error
+                                if (tid == 0 && A.dec)
+                                    A.dec[bKL + k * L + m - 1] =
+                                        kDecMade | (u - wm >= kNearTie + 4.0 * dw ? kDecCertain : 0);
                                 continue;
                             }
                             const int cm = s_can[k * L1 + m];
@@ -1046,6 +1059,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                         tie = fmin(tie, fabs(u - h));
                         if (fabs(u - h) < 4.0 * eh) tie = 0.0;   // within its error estimate
                         if (A.accept_prob && eh > kDiagEh) tie = 0.0;   // h reported to 1e-5
+                        if (tid == 0 && A.dec)
+                            A.dec[bKL + k * L + m - 1] =
+                                kDecMade | (u < h ? kDecAccept : 0) |
+                                (fabs(u - h) >= kNearTie + 4.0 * eh &&
+                                         !(A.accept_prob && eh > kDiagEh)
+                                     ? kDecCertain
+                                     : 0);
                         if (u < h) { acc = m; break; }
                     }
                     if (acc > 0) {
@@ -1242,7 +1262,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
             Zp = NAN;
         }
         ws->status = kStateDone;
-        if (!bad && (flags & kFlagNearTie)) A.redo_list[atomicAdd(A.redo_count, 1u)] = b;
+        if (!bad && (flags & kFlagNearTie))
+            A.redo_list[atomicAdd(A.redo_count, 1u)] =
+                b | ((flags & kFlagDegenerate) ? kListNoReplay : 0);
         A.accept_len[b] = tau;
         A.draft_index[b] = kstar;
         A.correction[b] = y;
