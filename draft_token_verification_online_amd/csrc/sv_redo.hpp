@@ -20,9 +20,8 @@
 //                      with the rules stated in sv_walk.hpp (token level, GBV
 //                      over K drafts, SpecTr).
 //
-// Double exponentials come from exp2_tang (Tang's table-driven method, ACM
-// TOMS 15(2), 1989: 2^a = 2^n 2^(j/256) 2^(r/256) with a 256-entry table in LDS
-// and a degree-4 polynomial; ~3 ulp).  The outputs differ from exact arithmetic
+// Double exponentials come from exp2_d (range reduction to |f| <= 1/2 and a
+// degree-13 polynomial; within 1.4e-16).  The outputs differ from exact arithmetic
 // only where a decision lies within double rounding (~1e-13, times the rule's
 // conditioning) of its threshold.  Listed requests are rare -- about one in a
 // hundred on flat residuals, where the correction draw lands within 1e-5 Z of a
@@ -41,30 +40,32 @@ constexpr int kRedoStatsThreads = 512;   // per (listed request, node row)
 constexpr int kRedoDepth = 4;            // chunks per row in flight per thread
 
 
-// 2^a in double precision.  a = (256 n + j + r) / 256 with n, j integers,
-// 0 <= j < 256, |r| <= 1/2: 2^a = 2^n * tab[j] * 2^(r/256), tab[j] = 2^(j/256),
-// and 2^(r/256) = exp(r ln2/256) is its Taylor polynomial of degree 4
-// (truncation below 4e-17 for |r ln2/256| <= 1.36e-3).  Branch-free: a is
-// clamped to [-1080, 1030] (NaN to -1080), where ldexp gives 0 below the
-// subnormal range and +inf above the double range.
-__device__ __forceinline__ double exp2_tang(double a, const double *tab) {
+// 2^a in double precision: a = k + f with k = rint(a), |f| <= 1/2, and
+// 2^f = exp(f ln2) by its Taylor polynomial of degree 13 (truncation below
+// 5e-18 for |f ln2| <= 0.347), scaled by ldexp.  Within 1.4e-16 of 2^a over
+// the double range (checked against a long-double exp2 on 2e7 arguments).
+// No table: every exponential of a sweep is independent straight-line code.
+// Branch-free: a is clamped to [-1080, 1030] (NaN to -1080), where ldexp gives
+// 0 below the subnormal range and +inf above the double range.
+__device__ __forceinline__ double exp2_d(double a) {
     a = fmin(fmax(a, -1080.0), 1030.0);
-    const double t = a * 256.0;
-    const double k = rint(t);
-    const double r = t - k;   // exact
-    const int ki = static_cast<int>(k);
-    const int j = ki & 255;
-    const int n = ki >> 8;    // floor(ki / 256)
-    constexpr double c1 = 0x1.62e42fefa39efp-9, c2 = 0x1.ebfbdff82c58fp-19,
-                     c3 = 0x1.c6b08d704a0c0p-29, c4 = 0x1.3b2ab6fba4e77p-39;
-    const double p = fma(r, fma(r, fma(r, fma(r, c4, c3), c2), c1), 1.0);
-    return ldexp(tab[j] * p, n);
-}
-
-// tab[j] = 2^(j/256), j = 0..255 (block-wide; ends with a barrier)
-__device__ __forceinline__ void exp2_tang_table(double *tab) {
-    for (int j = threadIdx.x; j < 256; j += blockDim.x) tab[j] = exp2(static_cast<double>(j) / 256.0);
-    __syncthreads();
+    const double k = rint(a);
+    const double f = a - k;   // exact
+    double p = 0x1.816193166d0f9p-40;
+    p = fma(f, p, 0x1.c3bd650fc2986p-36);
+    p = fma(f, p, 0x1.e8cac7351bb25p-32);
+    p = fma(f, p, 0x1.e4cf5158b8ecap-28);
+    p = fma(f, p, 0x1.b5253d395e7c4p-24);
+    p = fma(f, p, 0x1.62c0223a5c824p-20);
+    p = fma(f, p, 0x1.ffcbfc588b0c7p-17);
+    p = fma(f, p, 0x1.430912f86c787p-13);
+    p = fma(f, p, 0x1.5d87fe78a6731p-10);
+    p = fma(f, p, 0x1.3b2ab6fba4e77p-7);
+    p = fma(f, p, 0x1.c6b08d704a0c0p-5);
+    p = fma(f, p, 0x1.ebfbdff82c58fp-3);
+    p = fma(f, p, 0x1.62e42fefa39efp-1);
+    p = fma(f, p, 1.0);
+    return ldexp(p, static_cast<int>(k));
 }
 
 // fp64 statistics of one node row: pi(v) = 2^((l_v - M) cT - ls), cT = log2(e)/T,
@@ -95,12 +96,10 @@ struct RedoArgs {
 // prefix; the walk reads only those).
 template <int NT, typename RD, typename E>
 __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
-    __shared__ double s_tab[256];
     __shared__ double s_red[NT / kWave];
     __shared__ float s_fred[NT / kWave];
     const unsigned n = *A.count;
     if (n == 0) return;
-    exp2_tang_table(s_tab);
     const int tid = threadIdx.x;
     const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1, per = K * RS;
     const int nch = (V + kChunk - 1) / kChunk;
@@ -146,22 +145,20 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
                 }
                 if (cm > mx) {   // rescale the sum to the new maximum
                     if (mx > -INFINITY)
-                        sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(cm)) * cT,
-                                         s_tab);
+                        sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(cm)) * cT);
                     mx = cm;
                 }
                 if (mx > -INFINITY && !nan) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        sum += exp2_tang((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT,
-                                         s_tab);
+                        sum += exp2_d((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT);
                 }
             }
         }
         nan = __syncthreads_or(nan);
         const float M = block_max<NT>(mx, s_fred);
         if (mx > -INFINITY && !nan)
-            sum *= exp2_tang((static_cast<double>(mx) - static_cast<double>(M)) * cT, s_tab);
+            sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(M)) * cT);
         else
             sum = 0.0;
         sum = block_sum<NT>(sum, s_red);
@@ -177,7 +174,6 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
 
 // LDS of one re-evaluation.
 struct RedoShared {
-    double tab[256];
     int x[kMaxK * kMaxL];
     unsigned char can[kMaxK * (kMaxL + 1)];
     unsigned char ok[kMaxK * (2 * kMaxL + 1)];
@@ -199,7 +195,6 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
     unsigned char *s_can = sh.can, *s_ok = sh.ok;
     float *s_M = sh.M;
     double *s_ls = sh.ls;
-    const double *tab = sh.tab;
     int *s_H = sh.H;
     double *s_red = sh.red, *s_pair = sh.pair;
     int *s_ired = sh.ired;
@@ -249,8 +244,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             return sl;
         };
         auto prob = [&](int sl, float x) {
-            return exp2_tang(fma(static_cast<double>(x) - static_cast<double>(s_M[sl]), cT, -s_ls[sl]),
-                             tab);
+            return exp2_d(fma(static_cast<double>(x) - static_cast<double>(s_M[sl]), cT, -s_ls[sl]));
         };
         auto prob_at = [&](bool target, int k, int j, int x) {
             const int sl = stats(target, k, j);
@@ -279,10 +273,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     float xp[8], xq[8];
                     RD::unpack(rp[d], xp);
                     RD::unpack(rq[d], xq);
-                    for (int e = 0; e < 8; ++e) {
-                        const int v = kChunk * q + e;
-                        if (v < V) acc += f(v, prob(sp, xp[e]), prob(sq, xq[e]));
-                    }
+                    // no test v < V: elements past the row read as -inf, so p = q = 0
+                    // there and every weight below is 0
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc += f(kChunk * q + e, prob(sp, xp[e]), prob(sq, xq[e]));
                 }
             }
             return block_sum<NT>(acc, s_red);
@@ -299,10 +293,9 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             const RD P = row(true, c, j), Q = row(false, c, j);
             const int per = (nch + NT - 1) / NT;   // contiguous chunks per thread
             const int q0 = tid * per, q1 = min(q0 + per, nch);
+            // (elements past the row read as -inf: weight 0)
             auto weight = [&](int q, int e, const float *xp, const float *xq) {
-                const int v = kChunk * q + e;
-                if (v >= V) return 0.0;
-                return w(v, prob(sp, xp[e]), with_q ? prob(sq, xq[e]) : 0.0);
+                return w(kChunk * q + e, prob(sp, xp[e]), with_q ? prob(sq, xq[e]) : 0.0);
             };
             double mine = 0.0;
             int lastpos = -1;
@@ -322,10 +315,11 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     float xp[8], xq[8];
                     RD::unpack(rp[d], xp);
                     if (with_q) RD::unpack(rq[d], xq);
+#pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const double wv = weight(q, e, xp, xq);
                         mine += wv;
-                        if (wv > 0.0) lastpos = kChunk * q + e;
+                        lastpos = wv > 0.0 ? kChunk * q + e : lastpos;
                     }
                 }
             }
@@ -335,21 +329,41 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             *margin = 0.0;
             if (!(z > 0.0) || !isfinite(z)) return -1;
             const double thr = u * z;
+            const int last = block_max_int<NT>(lastpos, s_ired);
+            // the first thread whose range ends past u Z holds the crossing
+            const int owner = block_min_int<NT>(pre + mine > thr ? tid : 0x7fffffff, s_ired);
+            if (owner == 0x7fffffff) return last;   // rounding: no C_v exceeds u Z
+            if (tid == owner) s_pair[1] = pre;
+            __syncthreads();
+            const double base = s_pair[1];
+            // the owner's elements, recounted by the whole block in token order:
+            // consecutive runs per thread, a block scan, then the run that
+            // crosses u Z element by element
+            const int e0 = kChunk * owner * per, e1 = min(e0 + kChunk * per, V);
+            const int cnt = e1 > e0 ? (e1 - e0 + NT - 1) / NT : 0;
+            const int a0 = min(e0 + tid * cnt, e1), a1 = min(a0 + cnt, e1);
+            auto wat = [&](int v) {
+                return w(v, prob(sp, P.at(v)), with_q ? prob(sq, Q.at(v)) : 0.0);
+            };
+            double part = 0.0;
+            int lastrun = -1;
+            for (int v = a0; v < a1; ++v) {
+                const double wv = wat(v);
+                part += wv;
+                lastrun = wv > 0.0 ? v : lastrun;
+            }
+            const double pre2 = base + block_exclusive_scan<NT>(part, s_red);
             int cand = 0x7fffffff;
             double cm = 0.0;
-            if (pre <= thr && pre + mine > thr) {
-                double C = pre;
-                for (int q = q0; q < q1 && cand == 0x7fffffff; ++q) {
-                    float xp[8], xq[8];
-                    P.load(q, xp);
-                    if (with_q) Q.load(q, xq);
-                    for (int e = 0; e < 8 && cand == 0x7fffffff; ++e) {
-                        const double before = C;
-                        C += weight(q, e, xp, xq);
-                        if (C > thr) {
-                            cand = kChunk * q + e;
-                            cm = fmin(C - thr, thr - before);
-                        }
+            if (pre2 + part > thr) {
+                double C = pre2;
+                for (int v = a0; v < a1; ++v) {
+                    const double before = C;
+                    C += wat(v);
+                    if (C > thr) {
+                        cand = v;
+                        cm = fmin(C - thr, thr - before);
+                        break;
                     }
                 }
             }
@@ -362,7 +376,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                 __syncthreads();
                 return cand;
             }
-            return block_max_int<NT>(lastpos, s_ired);
+            // the recount's rounding left u Z past the owner's elements (a tie
+            // at the level of double rounding): its last element of weight
+            lastrun = block_max_int<NT>(lastrun, s_ired);
+            return lastrun >= 0 ? lastrun : last;
         };
         auto same_prefix = [&](int a, int c, int n) {
             int same = 1;
@@ -502,10 +519,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
             double alpha = 1.0, beta = 0.0, N = 1.0;
             int nH = 0;
             double w[kMaxL + 1], R[kMaxL + 1];
-            auto in_H = [&](int v) {
-                for (int i = 0; i < nH; ++i)
-                    if (s_H[i] == v) return true;
-                return false;
+            auto in_H = [&](int v) {   // branch-free: nH is the same for every thread
+                bool r = false;
+                for (int i = 0; i < nH; ++i) r |= (s_H[i] == v);
+                return r;
             };
             auto node_mass = [&]() {
                 return sweep(own, tau, [&](int v, double p, double q) {
@@ -649,7 +666,6 @@ __global__ __launch_bounds__(NT) void redo_walk_kernel(RedoArgs A) {
     __shared__ RedoShared sh;
     const unsigned n = *A.count;
     if (n == 0) return;
-    exp2_tang_table(sh.tab);
     for (unsigned i = blockIdx.x; i < n; i += gridDim.x)
         redo_request<NT, RD, E>(A, static_cast<int>(i), sh);   // block-uniform
 }
