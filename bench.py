@@ -399,11 +399,12 @@ def run_lmhead(args, w, name):
     base = synth.generate(synth.scaled(w, V=8), args.seed, device="cuda")   # temperatures, uniforms
     T = base["temperature"]
     Tt, Td = T.repeat_interleave(K * (L + 1)), T.repeat_interleave(K * L)
-    lt, ld = sv.LmHead(Rt, dt, V), sv.LmHead(Rd, dd, V)
+    ldt = torch.bfloat16 if args.lm_logits == "bf16" else torch.float32
+    lt, ld = sv.LmHead(Rt, dt, V, logits_dtype=ldt), sv.LmHead(Rd, dd, V, logits_dtype=ldt)
     stats = torch.empty(B * K * (2 * L + 1) * 16, dtype=torch.uint8, device="cuda")
-    ver = sv.Verifier(method, B, K, L, V, torch.float32)
+    ver = sv.Verifier(method, B, K, L, V, ldt)
     ld(hd, wd, Td)
-    drafter = sv.Drafter(B, K, L, V, torch.float32)
+    drafter = sv.Drafter(B, K, L, V, ldt)
     tok = drafter(ld.logits.view(B, K, L, V), T,
                   synth.draft_uniforms(w, args.seed, device="cuda"))["draft_tokens"].clone()
     hip = HipEvents()
@@ -486,7 +487,8 @@ def run_lmhead(args, w, name):
         "ms_per_step": t_fused, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "method": "lmhead+" + method, "B": B, "K": K, "L": L,
-                   "V": V, "d_target": dt, "d_draft": dd, "seed": args.seed},
+                   "V": V, "d_target": dt, "d_draft": dd, "logits": args.lm_logits,
+                   "seed": args.seed},
         "roofline": {"bound": "mfma", "kernel": "lm_head_kernel (target)", "achieved": tflops,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
@@ -511,6 +513,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--d-target", type=int, default=3584, help="hidden size of the target LM head")
     ap.add_argument("--d-draft", type=int, default=896, help="hidden size of the draft LM head")
+    ap.add_argument("--lm-logits", choices=("f32", "bf16"), default="f32",
+                    help="element type of the logits the LM heads write (--method lmhead)")
     ap.add_argument("--pipeline", action="store_true",
                     help="time the two-batch verify/draft overlap on two streams")
     ap.add_argument("--rotate", type=int, default=0,

@@ -37,9 +37,11 @@ constexpr long long kMaxStatsGrid = 1LL << 22;
 constexpr long long kListGrid = 4096;
 constexpr int kMaxB = 1 << 24;
 // Re-evaluation launches: workgroups over (listed request, node row) and over
-// listed requests.  With none listed every workgroup returns after one load.
-constexpr long long kRedoStatsGrid = 1024;
-constexpr int kRedoWalkGrid = 64;
+// listed requests, grid-stride.  With none listed every workgroup returns after
+// one load, so the grids are kept small (one workgroup per CU at most): most
+// calls list nothing.
+constexpr long long kRedoStatsGrid = 256;
+constexpr int kRedoWalkGrid = 32;
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
 static_assert(SV_MAX_L == sv::kMaxL, "L limit");
@@ -69,11 +71,12 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
 // Workspace: row statistics (after the walk, the fp64 statistics of the requests
 // listed for re-evaluation) | walk states | node rows flagged for the second
 // round (bytes, then the same rows as a list) | list length | number of
-// requests listed for re-evaluation in fp64 | their indices | the GBV walk's
-// test records (a byte per test) | node lists of the walk (K >= 3 only: a node
-// sees a second mass sweep only with three or more drafts).
+// requests listed for re-evaluation in fp64 | their indices | the walk's test
+// records (a byte per test) | SpecTr's scaling factor per position | node lists
+// of the walk (K >= 3 only: a node sees a second mass sweep only with three or
+// more drafts).
 struct Layout {
-    size_t stats, state, need, list, count, rcount, rlist, dec, nodes, total;
+    size_t stats, state, need, list, count, rcount, rlist, dec, rho, nodes, total;
     bool has_nodes;
 };
 
@@ -111,7 +114,8 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.rcount = l.count + 256;
     l.rlist = l.rcount + 256;
     l.dec = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
-    l.nodes = l.dec + align_up(bkl, 256);
+    l.rho = l.dec + align_up(bkl, 256);
+    l.nodes = l.rho + align_up(static_cast<size_t>(B) * L * sizeof(double), 256);
     l.has_nodes = K >= 3;
     l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
                                            static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
@@ -135,7 +139,7 @@ __global__ void reset_count_kernel(unsigned *count) {
 template <typename E, bool VEC>
 hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t stream, int method,
                        const unsigned *count, const int32_t *list, void *stats,
-                       const unsigned char *dec) {
+                       const unsigned char *dec, const double *rho_rec) {
     using RD = typename sv::RowOf<E, VEC>::type;
     sv::RedoArgs ra;
     ra.tgt = in->target_logits;
@@ -148,6 +152,7 @@ hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t s
     ra.list = list;
     ra.stats = static_cast<sv::RedoStat *>(stats);
     ra.dec = dec;
+    ra.rho_rec = rho_rec;
     ra.B = in->B;
     ra.K = in->K;
     ra.L = in->L;
@@ -243,8 +248,10 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     wa.resid_mass = out->resid_mass;
     wa.redo_count = sa.redo_count;
     wa.redo_list = reinterpret_cast<int32_t *>(ws + lay.rlist);
-    wa.dec = method == sv::kMethodBlockWalk ? reinterpret_cast<unsigned char *>(ws + lay.dec)
-                                            : nullptr;
+    wa.dec = (method == sv::kMethodBlockWalk || spectr)
+                 ? reinterpret_cast<unsigned char *>(ws + lay.dec)
+                 : nullptr;
+    wa.rho_rec = spectr ? reinterpret_cast<double *>(ws + lay.rho) : nullptr;
 
     hipError_t err;
     if ((err = record(ln, 0, stream)) != hipSuccess) return err;
@@ -285,7 +292,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         if ((err = walk()) != hipSuccess) return err;
     }
     if ((err = launch_redo<E, VEC>(in, out, stream, wa.method, wa.redo_count, wa.redo_list,
-                                   ws + lay.stats, wa.dec)) != hipSuccess)
+                                   ws + lay.stats, wa.dec, wa.rho_rec)) != hipSuccess)
         return err;
     return record(ln, 4, stream);
 }
@@ -356,7 +363,7 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
                        a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_redo<E, VEC>(in, out, stream, method, a.redo_count, a.redo_list,
-                                   ws + lay.part, nullptr)) != hipSuccess)
+                                   ws + lay.part, nullptr, nullptr)) != hipSuccess)
         return err;
     for (int i = 2; i < 5; ++i)
         if ((err = record(ln, i, stream)) != hipSuccess) return err;

@@ -83,7 +83,8 @@ struct RedoArgs {
     const float *temp, *ua, *uc;  // [B], [B][K][L], [B]
     const unsigned *count;        // listed requests
     const int32_t *list;          // [count]: their indices (| kListNoReplay)
-    const unsigned char *dec;     // [B][K][L] the fast GBV walk's test records, or null
+    const unsigned char *dec;     // [B][K][L] the fast walk's test records, or null
+    const double *rho_rec;        // [B][L] the fast SpecTr walk's rho per position, or null
     RedoStat *stats;              // [count][K][2L+1]: node rows of listed request i at i*K*(2L+1)
     int B, K, L, V;
     int method;                   // kMethodToken, kMethodBlockWalk or kMethodSpecTr
@@ -441,9 +442,15 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                 }
             }
         } else if (A.method == kMethodSpecTr) {
-            // SpecTr: rho* = the smallest rho in [1, n] with c(beta(rho)) <= rho,
-            // by bisection to adjacent doubles; the feasibility test is taken in
-            // the form rounding cannot flip (quotient form for beta <= 2^-10)
+            // SpecTr: rho* = the smallest rho in [1, n] with c(beta(rho)) <= rho; the
+            // feasibility test is taken in the form rounding cannot flip (quotient
+            // form for beta <= 2^-10).  While every decision agrees with the fast
+            // walk's records, a position whose tests were all certain and where a
+            // candidate was accepted needs no rho*; elsewhere rho* is bracketed
+            // around the fast walk's rho (within 7.4e-7 of rho*) and narrowed by
+            // safeguarded secant steps on rho - c(beta(rho)) to 2^-42 relative.
+            const double *rrec = A.rho_rec ? A.rho_rec + static_cast<long long>(b) * L : nullptr;
+            bool follow = A.dec != nullptr && rrec != nullptr && !(entry & kListNoReplay);
             int kacc = -1;
             bool done = false;
             for (int j = 0; j < L && !bad && !done; ++j) {
@@ -457,28 +464,120 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     for (int i = 0; i < n; ++i) { cc += t; t *= 1.0 - beta; }
                     return cc;
                 };
-                auto feasible = [&](double rho) {
-                    const double beta = sweep(own, j, [&](int, double p, double q) {
-                        return fmin(q, p / rho);
-                    });
-                    if (beta <= kQuotientFormBeta) return c_of(beta) <= rho;
+                // beta(rho) = sum min(q, p/rho) and D(rho) = sum max(p - rho q, 0), one sweep
+                auto sums = [&](double rho, double &beta, double &D) {
+                    const int c = s_can[own * L1 + j];
+                    const int sp = stats(true, own, j), sq = stats(false, own, j);
+                    const RD P = row(true, c, j), Q = row(false, c, j);
+                    const double ir = 1.0 / rho;
+                    double v[2] = {0.0, 0.0};
+                    for (int q0 = tid; q0 < nch; q0 += 2 * NT) {
+                        typename RD::Raw rp[2], rq[2];
+#pragma unroll
+                        for (int d = 0; d < 2; ++d) {
+                            if (q0 + d * NT < nch) {
+                                rp[d] = P.raw(q0 + d * NT);
+                                rq[d] = Q.raw(q0 + d * NT);
+                            }
+                        }
+#pragma unroll
+                        for (int d = 0; d < 2; ++d) {
+                            if (q0 + d * NT >= nch) break;
+                            float xp[8], xq[8];
+                            RD::unpack(rp[d], xp);
+                            RD::unpack(rq[d], xq);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const double pp = prob(sp, xp[e]), qq = prob(sq, xq[e]);
+                                v[0] += fmin(qq, pp * ir);
+                                v[1] += fmax(pp - rho * qq, 0.0);
+                            }
+                        }
+                    }
+                    block_sum_n<NT, 2>(v, s_red);
+                    beta = v[0];
+                    D = v[1];
+                };
+                auto feasible = [&](double rho, double *g, double *bt) {
+                    double beta, D;
+                    sums(rho, beta, D);
+                    const double cc = c_of(beta);
+                    *g = rho - cc;
+                    *bt = beta;
+                    if (beta <= kQuotientFormBeta) return cc <= rho;
                     double xn = 1.0;
                     for (int i = 0; i < n; ++i) xn *= 1.0 - beta;
-                    const double D = sweep(own, j, [&](int, double p, double q) {
-                        return fmax(p - rho * q, 0.0);
-                    });
                     return D <= xn;
                 };
-                double rho = 1.0;
-                if (n > 1 && !feasible(1.0)) {
-                    double lo = 1.0, hi = static_cast<double>(n);
-                    for (;;) {
-                        const double mid = 0.5 * (lo + hi);
-                        if (!(mid > lo && mid < hi)) break;
-                        if (feasible(mid)) hi = mid;
-                        else lo = mid;
+                // the fast walk's records at this position: all certain, and accepted?
+                bool replay = follow && n > 1;
+                int rec_acc = -1;
+                if (replay) {
+                    for (int k = 0; k < K && rec_acc < 0 && replay; ++k) {
+                        if (!same_prefix(k, own, j)) continue;
+                        const int dc = A.dec[bKL + k * L + j];
+                        if (!(dc & kDecMade) || !(dc & kDecCertain)) replay = false;
+                        else if (dc & kDecAccept) rec_acc = k;
+                    }
+                    if (rec_acc < 0) replay = false;   // the draw is here: it needs rho*
+                }
+                if (replay) {
+                    for (int k = 0; k <= rec_acc; ++k)
+                        if (same_prefix(k, own, j)) s_made[k * L + j] = 1;
+                    own = rec_acc;
+                    kacc = rec_acc;
+                    continue;
+                }
+                // rho* and beta(rho*) (NAN: not swept at rho*)
+                double rho = 1.0, beta_rho = NAN;
+                double g, bt;
+                // the fast rho is within 7.4e-7 of rho*: one this far above 1 puts rho*
+                // above 1 without a sweep at 1
+                const double rf = follow ? rrec[j] : 0.0;
+                const bool above1 = rf > 1.0 + 8e-6;
+                bool at1 = false;
+                if (n > 1 && !above1) {
+                    at1 = feasible(1.0, &g, &bt);
+                    if (at1) beta_rho = bt;
+                }
+                if (n > 1 && !at1) {
+                    double lo = 1.0, hi = static_cast<double>(n);   // c <= n: n is feasible
+                    double glo = above1 ? NAN : g, ghi = NAN, bhi = NAN;
+                    int keep = 0;   // Illinois: the end retained on the last steps
+                    if (rf > lo && rf < hi) {
+                        const double t0 = fmax(rf * (1.0 - 4e-6), lo), t1 = fmin(rf * (1.0 + 4e-6), hi);
+                        if (t0 > lo) {
+                            if (feasible(t0, &g, &bt)) { hi = t0; ghi = g; bhi = bt; }
+                            else { lo = t0; glo = g; }
+                        }
+                        if (t1 < hi && t1 > lo) {
+                            if (feasible(t1, &g, &bt)) { hi = t1; ghi = g; bhi = bt; }
+                            else { lo = t1; glo = g; }
+                        }
+                    }
+                    for (int it = 0; it < 200 && hi - lo > 0x1p-42 * hi; ++it) {
+                        double t = 0.5 * (lo + hi);
+                        if (isfinite(ghi) && isfinite(glo) && ghi > glo) {
+                            const double sec = lo - glo * (hi - lo) / (ghi - glo);
+                            const double w = hi - lo;
+                            if (sec > lo + 1e-3 * w && sec < hi - 1e-3 * w) t = sec;
+                        }
+                        if (!(t > lo && t < hi)) break;
+                        if (feasible(t, &g, &bt)) {
+                            hi = t;
+                            ghi = g;
+                            bhi = bt;
+                            if (keep == -1) glo *= 0.5;
+                            keep = -1;
+                        } else {
+                            lo = t;
+                            glo = g;
+                            if (keep == 1) ghi *= 0.5;
+                            keep = 1;
+                        }
                     }
                     rho = hi;
+                    beta_rho = bhi;
                 }
                 int acc = -1;
                 for (int k = 0; k < K && acc < 0; ++k) {
@@ -487,12 +586,16 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
                     const double p = prob_at(true, own, j, x), q = prob_at(false, own, j, x);
                     double a = ratio(p, rho * q);
                     if (a > 1.0) a = 1.0;
-                    if (test(k, j + 1, a)) acc = k;
+                    const bool ak = test(k, j + 1, a);
+                    if (follow && n > 1) {
+                        const int dc = A.dec[bKL + k * L + j];
+                        if (!(dc & kDecMade) || ak != ((dc & kDecAccept) != 0)) follow = false;
+                    }
+                    if (ak) acc = k;
                 }
                 if (acc < 0) {
-                    const double beta = sweep(own, j, [&](int, double p, double q) {
-                        return fmin(q, p / rho);
-                    });
+                    double beta = beta_rho, D;
+                    if (!isfinite(beta)) sums(rho, beta, D);
                     const double cc = c_of(beta);
                     y = icdf(own, j, true, [&](int, double p, double q) {
                         return fmax(p - cc * fmin(q, p / rho), 0.0);

@@ -65,7 +65,7 @@ constexpr double kExpEps = 0x1p-23;
 // this (a quarter of the 1e-5 the acceptance probabilities are reported to) is
 // taken again in fp64 too, so the reported h hold to fp64 however ill-conditioned.
 constexpr double kDiagEh = 2.5e-6;
-// A GBV test's record for the fp64 re-evaluation (WalkArgs::dec).  Certain:
+// A test's record for the fp64 re-evaluation (WalkArgs::dec).  Certain:
 // its margin is at least SV_NEAR_TIE plus four times its error estimate, so
 // the exact test agrees and its exact margin exceeds SV_NEAR_TIE.
 constexpr unsigned char kDecMade = 1, kDecAccept = 2, kDecCertain = 4;
@@ -102,9 +102,10 @@ struct WalkArgs {
     float *row_lse, *accept_prob, *resid_mass;
     unsigned *redo_count;   // requests with a decision within its error of its threshold,
     int32_t *redo_list;     // listed here for the fp64 re-evaluation
-    unsigned char *dec;     // [B][K][L] GBV tests made (kDecMade), accepted (kDecAccept) and
+    unsigned char *dec;     // [B][K][L] tests made (kDecMade), accepted (kDecAccept) and
                             // certain in exact arithmetic (kDecCertain); entries of tests
                             // not made are left as they were
+    double *rho_rec;        // [B][L] SpecTr's scaling factor at each position it reached
 };
 
 // Likelihood ratio from log2-probabilities, with the drafted-token convention:
@@ -950,6 +951,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                                          shift_term(s_M[cn * RS + L1 + j], sc),
                                          s_S[cn * RS + L1 + j], sc, n, rho, cc, s_hist, s_red6,
                                          s_br, s_ired);
+                if (tid == 0 && A.rho_rec) A.rho_rec[static_cast<long long>(b) * L + j] = rho;
                 int acc = -1;
                 for (int k = 0; k < K && acc < 0; ++k) {
                     int m2 = 1;
@@ -961,6 +963,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
                     if (tid == 0 && A.accept_prob)
                         A.accept_prob[bKL + k * L + j] = static_cast<float>(h);
                     tie = fmin(tie, fabs(u - h));
+                    // h's error: two row sums and rho (within 7.4e-7 relative of the
+                    // fp64 search), four times over
+                    if (tid == 0 && A.dec)
+                        A.dec[bKL + k * L + j] =
+                            kDecMade | (u < h ? kDecAccept : 0) |
+                            (fabs(u - h) >= kNearTie + 4.0 * h * (4.0 * kExpEps + 1e-6) ? kDecCertain
+                                                                                      : 0);
                     if (u < h) acc = k;
                 }
                 if (acc < 0) break;
