@@ -61,6 +61,11 @@ def _load(path=None):
                                    vp, vp, vp, vp, vp, vp,
                                    i32, i32,
                                    vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.svo_verify_exact.restype = ctypes.c_int
+        lib.svo_verify_exact.argtypes = [i32, i32, i32, i32, i32, i32,
+                                         vp, vp, vp, vp, vp, vp,
+                                         i32, i32,
+                                         vp, vp, vp, vp, vp, vp, vp]
         _libs[key] = lib
         return lib
 
@@ -141,6 +146,49 @@ def verify(method, target, draft, tokens, temperature, u_accept, u_correct, *,
     else:
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda b: run(b, b + 1), reqs))
+    return out
+
+
+def verify_exact(method, target, draft, tokens, temperature, u_accept, u_correct, *,
+                 lib_path=None) -> dict:
+    """svo_verify_exact: the oracle with float64 uniforms, returning accept_len,
+    draft_index, correction, flags, accept_prob [B][K][L] and resid_mass [B]
+    like verify(..., diagnostics=True), plus corr_law [B][V]: the distribution
+    the correction token is drawn from.  For enumerating the output law exactly:
+    u = 0 takes the accepting branch of a test with h > 0, u = h the rejecting
+    one, and the correction's law is read off corr_law."""
+    lib = _load(lib_path)
+    m = METHODS[method] if isinstance(method, str) else int(method)
+    target, dt = _as_logits(target)
+    draft, dt2 = _as_logits(draft)
+    if dt != dt2:
+        raise TypeError("target and draft logits must share a dtype")
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    u_accept = np.ascontiguousarray(u_accept, dtype=np.float64)
+    u_correct = np.ascontiguousarray(u_correct, dtype=np.float64)
+    B, K, L1, V = target.shape
+    L = L1 - 1
+    if draft.shape != (B, K, L, V) or tokens.shape != (B, K, L) or \
+            u_accept.shape != (B, K, L) or temperature.shape != (B,) or u_correct.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    out = {
+        "accept_len": np.full(B, -2, np.int32),
+        "draft_index": np.full(B, -2, np.int32),
+        "correction": np.full(B, -2, np.int32),
+        "flags": np.zeros(B, np.int32),
+        "accept_prob": np.full((B, K, L), np.nan, np.float64),
+        "resid_mass": np.full(B, np.nan, np.float64),
+        "corr_law": np.full((B, V), np.nan, np.float64),
+    }
+    rc = lib.svo_verify_exact(m, B, K, L, V, dt, _ptr(target), _ptr(draft), _ptr(tokens),
+                              _ptr(temperature), _ptr(u_accept), _ptr(u_correct), 0, B,
+                              _ptr(out["accept_len"]), _ptr(out["draft_index"]),
+                              _ptr(out["correction"]), _ptr(out["flags"]),
+                              _ptr(out["accept_prob"]), _ptr(out["resid_mass"]),
+                              _ptr(out["corr_law"]))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return out
 
 

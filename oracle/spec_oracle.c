@@ -80,8 +80,10 @@ typedef struct {
     const void *drf;        /* this request's draft rows  [K][L][V]   */
     const int32_t *X;       /* draft tokens [K][L] */
     double T;
-    const float *ua;        /* acceptance uniforms [K][L] */
+    const float *ua;        /* acceptance uniforms [K][L] (fp32 entry point) */
+    const double *ua_d;     /* ... or as doubles (exact-law entry point); one is NULL */
     double uc;              /* correction uniform */
+    double *law;            /* [V]: the distribution the correction is drawn from, or NULL */
     double *p, *q, *om;     /* scratch, V doubles each */
     double *h_out;          /* [K][L] evaluated acceptance probabilities, or NULL */
     double margin;          /* min |u - threshold| over every decision taken */
@@ -203,6 +205,12 @@ static double svo_chain(double w, double num, double den)
     return t < 1.0 ? t : 1.0;
 }
 
+/* Acceptance uniform i of the request, as a double. */
+static double svo_ua(const svo_req *r, int i)
+{
+    return r->ua_d ? r->ua_d[i] : (double)r->ua[i];
+}
+
 static void svo_note_margin(svo_req *r, double m)
 {
     if (m < r->margin)
@@ -212,7 +220,7 @@ static void svo_note_margin(svo_req *r, double m)
 /* One acceptance test: accepted iff u < h. */
 static int svo_test(svo_req *r, int k, int m, double h)
 {
-    double u = (double)r->ua[k * r->L + (m - 1)];
+    double u = svo_ua(r, k * r->L + (m - 1));
     r->tests += 1;
     if (r->h_out)
         r->h_out[k * r->L + (m - 1)] = h;
@@ -233,6 +241,9 @@ static int svo_icdf(svo_req *r, const double *om, double *Z_out)
     *Z_out = Z;
     if (!(Z > 0.0) || !isfinite(Z))
         return -1;
+    if (r->law)   /* a uniform u gives v with probability om(v)/Z */
+        for (int v = 0; v < r->V; ++v)
+            r->law[v] = om[v] / Z;
     double t = r->uc * Z;
     double C = 0.0;
     for (int v = 0; v < r->V; ++v) {
@@ -655,7 +666,8 @@ static int svo_request_valid(const svo_req *r)
     for (int i = 0; i < r->K * r->L; ++i) {
         if (r->X[i] < 0 || r->X[i] >= r->V)
             return 0;
-        if (!(r->ua[i] >= 0.0f && r->ua[i] < 1.0f))
+        double u = svo_ua(r, i);
+        if (!(u >= 0.0 && u < 1.0))
             return 0;
     }
     if (!(r->uc >= 0.0 && r->uc < 1.0))
@@ -770,13 +782,15 @@ int svo_draft(int B, int K, int L, int V, int dtype, const void *draft,
  * distinct logit rows read).
  * Returns 0, or -1 for arguments outside the supported ranges.
  */
-int svo_verify(int method, int B, int K, int L, int V, int dtype,
-               const void *target, const void *draft, const int32_t *tokens,
-               const float *temperature, const float *u_accept, const float *u_correct,
-               int b_begin, int b_end,
-               int32_t *accept_len, int32_t *draft_index, int32_t *correction,
-               int32_t *flags, double *row_lse, double *accept_prob,
-               double *resid_mass, double *margin, int64_t *counters)
+static int svo_verify_any(int method, int B, int K, int L, int V, int dtype,
+                          const void *target, const void *draft, const int32_t *tokens,
+                          const float *temperature, const float *u_accept,
+                          const double *u_accept_d, const float *u_correct,
+                          const double *u_correct_d, int b_begin, int b_end,
+                          int32_t *accept_len, int32_t *draft_index, int32_t *correction,
+                          int32_t *flags, double *row_lse, double *accept_prob,
+                          double *resid_mass, double *margin, int64_t *counters,
+                          double *corr_law)
 {
     if (method < SVO_TOKEN || method > SVO_SPECTR || B < 0 || K < 1 || K > SVO_KMAX ||
         L < 1 || L > SVO_LMAX || V < 1 || (dtype != SVO_F32 && dtype != SVO_BF16))
@@ -807,8 +821,13 @@ int svo_verify(int method, int B, int K, int L, int V, int dtype,
         r.drf = (const char *)draft + (size_t)b * drow * es;
         r.X = tokens + (size_t)b * (size_t)K * (size_t)L;
         r.T = (double)temperature[b];
-        r.ua = u_accept + (size_t)b * (size_t)K * (size_t)L;
-        r.uc = (double)u_correct[b];
+        r.ua = u_accept ? u_accept + (size_t)b * (size_t)K * (size_t)L : NULL;
+        r.ua_d = u_accept_d ? u_accept_d + (size_t)b * (size_t)K * (size_t)L : NULL;
+        r.uc = u_correct_d ? u_correct_d[b] : (double)u_correct[b];
+        r.law = corr_law ? corr_law + (size_t)b * (size_t)V : NULL;
+        if (r.law)
+            for (int v = 0; v < V; ++v)
+                r.law[v] = NAN;
         r.p = scratch;
         r.q = scratch + V;
         r.om = scratch + 2 * (size_t)V;
@@ -875,4 +894,38 @@ int svo_verify(int method, int B, int K, int L, int V, int dtype,
     free(scratch);
     free(touched);
     return 0;
+}
+
+int svo_verify(int method, int B, int K, int L, int V, int dtype,
+               const void *target, const void *draft, const int32_t *tokens,
+               const float *temperature, const float *u_accept, const float *u_correct,
+               int b_begin, int b_end,
+               int32_t *accept_len, int32_t *draft_index, int32_t *correction,
+               int32_t *flags, double *row_lse, double *accept_prob,
+               double *resid_mass, double *margin, int64_t *counters)
+{
+    return svo_verify_any(method, B, K, L, V, dtype, target, draft, tokens, temperature,
+                          u_accept, NULL, u_correct, NULL, b_begin, b_end, accept_len,
+                          draft_index, correction, flags, row_lse, accept_prob, resid_mass,
+                          margin, counters, NULL);
+}
+
+/* svo_verify with the uniforms as doubles, for enumerating the oracle's output
+ * law exactly: a test is accepted iff u < h, so u = 0 takes the accepting branch
+ * of any test with h > 0 and u = h the rejecting one, with no float32 rounding
+ * in between.  corr_law [B][V] (optional) receives the distribution the
+ * correction is drawn from (om/Z of the final draw; NaN for an invalid request):
+ * the law of the correction token given everything else. */
+int svo_verify_exact(int method, int B, int K, int L, int V, int dtype,
+                     const void *target, const void *draft, const int32_t *tokens,
+                     const float *temperature, const double *u_accept,
+                     const double *u_correct, int b_begin, int b_end,
+                     int32_t *accept_len, int32_t *draft_index, int32_t *correction,
+                     int32_t *flags, double *accept_prob, double *resid_mass,
+                     double *corr_law)
+{
+    return svo_verify_any(method, B, K, L, V, dtype, target, draft, tokens, temperature,
+                          NULL, u_accept, NULL, u_correct, b_begin, b_end, accept_len,
+                          draft_index, correction, flags, NULL, accept_prob, resid_mass,
+                          NULL, NULL, corr_law);
 }

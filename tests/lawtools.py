@@ -11,8 +11,9 @@ The tools below
   * enumerate the oracle's *output law* exactly, treating the oracle as a black
     box: every draft realisation (K drafts in V^L) is weighted by its draft
     probability, every acceptance decision the oracle reports (its evaluated h)
-    is branched on by feeding it a uniform below / above h, and the correction
-    token's law is read off by bisecting the correction uniform over float32.
+    is branched on by feeding it the float64 uniforms 0 and h, and the
+    correction token's law is the distribution the oracle reports drawing it
+    from (pinned against its draws by bisecting the correction uniform).
 
 Nothing here imports or re-implements the oracle's walk; only the model's
 softmax (the definition of p and q) is computed in the test.
@@ -204,13 +205,20 @@ def _walk_order(method, K, L):
     return [(k, m - 1) for k in range(K) for m in range(L, 0, -1)]
 
 
-def output_law(m: TreeModel, K, method, lib_path=None, max_paths=400000):
+def output_law(m: TreeModel, K, method, lib_path=None, max_paths=4000000):
     """Exact law of the oracle's output (accepted prefix + correction token),
     marginalised over draft realisations and uniforms.
 
+    The oracle is driven through its float64-uniform entry point: every
+    acceptance decision it reports (its evaluated h) is branched on with u = 0
+    (accept, probability h) and u = h (reject, probability 1 - h, since a test
+    accepts iff u < h), and the correction token's law at each leaf is the
+    distribution the oracle reports drawing it from.  The only error is fp64
+    rounding.
+
     Returns (law, e_tau, dropped): law maps output tuples (prefix + (y,)) to
-    probabilities, e_tau is E[accept_len], dropped is the probability mass of
-    branches a float32 uniform cannot reach (h within one ulp of 1)."""
+    probabilities, e_tau is E[accept_len]; dropped (branches no uniform can
+    reach) is 0 here and kept for the callers' assertions."""
     L, V = m.L, m.V
     tgt, drf, tok, wq = realisations(m, K)
     R = len(wq)
@@ -219,21 +227,20 @@ def output_law(m: TreeModel, K, method, lib_path=None, max_paths=400000):
     flat_order = np.array([k * L + j for k, j in order])
 
     ridx = np.arange(R)
-    ua = np.full((R, K, L), 0.999, np.float32)
+    ua = np.full((R, K, L), 0.5, np.float64)   # placeholders until a test is branched on
     fixed = np.zeros((R, K, L), bool)
     prob = np.ones(R)
     leaves = []
-    dropped = 0.0
 
-    def run(ri, u, uc):
+    def run(ri, u):
         P = len(ri)
-        return oracle.verify(method, tgt[ri], drf[ri], tok[ri], np.repeat(temps, P),
-                             u, uc, diagnostics=True, lib_path=lib_path)
+        return oracle.verify_exact(method, tgt[ri], drf[ri], tok[ri], np.repeat(temps, P),
+                                   u, np.zeros(P), lib_path=lib_path)
 
     while len(ridx):
         if len(ridx) > max_paths:
             raise RuntimeError("too many paths")
-        out = run(ridx, ua, np.zeros(len(ridx), np.float32))
+        out = run(ridx, ua)
         if (out["flags"] & oracle.FLAG_INVALID).any():
             raise AssertionError("oracle flagged a valid tiny instance as invalid")
         h = out["accept_prob"].reshape(len(ridx), K * L)
@@ -241,63 +248,50 @@ def output_law(m: TreeModel, K, method, lib_path=None, max_paths=400000):
         has = pending.any(axis=1)
         done = ~has
         if done.any():
-            leaves.append((ridx[done], ua[done].copy(), prob[done],
-                           out["accept_len"][done], out["draft_index"][done]))
+            leaves.append((ridx[done], prob[done], out["accept_len"][done],
+                           out["draft_index"][done], out["corr_law"][done]))
         if not has.any():
             break
         sel = np.nonzero(has)[0]
         first = flat_order[np.argmax(pending[sel], axis=1)]
         hs = h[sel, first]
-        new_r, new_u, new_f, new_p = [], [], [], []
-        for i, d, hv in zip(sel, first, hs):
-            k, j = divmod(int(d), L)
-            base_u, base_f = ua[i].copy(), fixed[i].copy()
-            base_f[k, j] = True
-            if hv > 0.0:                            # accept branch: u < h
-                u = base_u.copy()
-                u[k, j] = _f32(hv * 0.5) if hv < 1.0 else _f32(0.5)
-                new_r.append(ridx[i]); new_u.append(u); new_f.append(base_f)
-                new_p.append(prob[i] * min(hv, 1.0))
-            if hv < 1.0:                            # reject branch: u >= h
-                u = base_u.copy()
-                cand = _f32((1.0 + hv) * 0.5) if hv > 0.0 else _f32(0.5)
-                if float(cand) < hv:
-                    cand = np.nextafter(cand, np.float32(1.0))
-                if float(cand) >= 1.0 or float(cand) < hv:
-                    dropped += prob[i] * wq[ridx[i]] * (1.0 - hv)
-                    continue
-                u[k, j] = cand
-                new_r.append(ridx[i]); new_u.append(u); new_f.append(base_f)
-                new_p.append(prob[i] * (1.0 - hv))
-        ridx = np.array(new_r, dtype=np.int64)
-        ua = np.array(new_u, dtype=np.float32).reshape(-1, K, L)
-        fixed = np.array(new_f, dtype=bool).reshape(-1, K, L)
-        prob = np.array(new_p)
+        k_, j_ = np.divmod(first, L)
+        acc = hs > 0.0
+        rej = hs < 1.0
+        ua_sel, fx_sel = ua[sel], fixed[sel]
+        fx_sel[np.arange(len(sel)), k_, j_] = True
+        ua_a = ua_sel[acc].copy()
+        ua_a[np.arange(acc.sum()), k_[acc], j_[acc]] = 0.0
+        ua_r = ua_sel[rej].copy()
+        ua_r[np.arange(rej.sum()), k_[rej], j_[rej]] = hs[rej]
+        ridx = np.concatenate([ridx[sel][acc], ridx[sel][rej]])
+        ua = np.concatenate([ua_a, ua_r])
+        fixed = np.concatenate([fx_sel[acc], fx_sel[rej]])
+        prob = np.concatenate([prob[sel][acc] * np.minimum(hs[acc], 1.0),
+                               prob[sel][rej] * (1.0 - hs[rej])])
 
     lr = np.concatenate([x[0] for x in leaves])
-    lu = np.concatenate([x[1] for x in leaves])
-    lp = np.concatenate([x[2] for x in leaves])
-    ltau = np.concatenate([x[3] for x in leaves])
-    lks = np.concatenate([x[4] for x in leaves])
-    py = correction_law(run, lr, lu, V)          # [leaves][V]
+    lp = np.concatenate([x[1] for x in leaves])
+    ltau = np.concatenate([x[2] for x in leaves])
+    lks = np.concatenate([x[3] for x in leaves])
+    py = np.concatenate([x[4] for x in leaves])   # [leaves][V]
 
     law = {}
-    e_tau = 0.0
+    w = wq[lr] * lp
+    e_tau = float(np.dot(w, ltau))
     for n in range(len(lr)):
-        w = wq[lr[n]] * lp[n]
         tau, ks = int(ltau[n]), int(lks[n])
         pre = tuple(int(t) for t in tok[lr[n], ks, :tau]) if tau > 0 else ()
-        e_tau += w * tau
-        for y in range(V):
-            if py[n, y] > 0:
-                key = pre + (y,)
-                law[key] = law.get(key, 0.0) + w * py[n, y]
-    return law, e_tau, dropped
+        for y in np.nonzero(py[n] > 0)[0]:
+            key = pre + (int(y),)
+            law[key] = law.get(key, 0.0) + w[n] * py[n, y]
+    return law, e_tau, 0.0
 
 
 def correction_law(run, lr, lu, V):
     """Law of the correction token at each leaf, read off by bisection over the
-    float32 correction uniform (the draw is non-decreasing in u)."""
+    float32 correction uniform (the draw is non-decreasing in u).  Used to pin
+    the law the oracle reports against the draws it makes."""
     n = len(lr)
     if V == 1:
         return np.ones((n, 1))

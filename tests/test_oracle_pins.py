@@ -29,15 +29,13 @@ import lawtools as lt
 import oracle
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LAW_TOL = 2e-6          # float32 bisection of the correction uniform: <= V ulps per leaf
+LAW_TOL = 1e-12         # fp64 rounding of the enumerated law (branch weights, reported laws)
 ETAU_TOL = 1e-10        # E[tau] from exact branch probabilities (fp64)
 
-# exhaustive grid (V, L, K): every corner of V <= 8, L <= 3, K <= 3 that enumerates
-# in seconds; (8, 3, 3) is covered statistically below.
-GRID = [(2, 1, 1), (2, 2, 1), (2, 3, 1), (2, 1, 2), (2, 2, 2), (2, 3, 2), (2, 1, 3),
-        (2, 2, 3), (2, 3, 3), (3, 1, 1), (3, 2, 1), (3, 1, 2), (3, 2, 2), (3, 1, 3),
-        (3, 2, 3), (4, 1, 3), (4, 2, 2), (8, 1, 1), (8, 1, 2), (8, 1, 3), (8, 2, 1),
-        (8, 3, 1), (8, 2, 2)]
+# exhaustive grid (V, L, K): every corner of V in {2, 3, 4, 8}, L <= 3, K <= 3
+# except (8, 3, 3), whose 512^3 draft realisations are covered statistically below.
+GRID = [(V, L, K) for V in (2, 3, 4, 8) for L in (1, 2, 3) for K in (1, 2, 3)
+        if (V, L, K) != (8, 3, 3)]
 
 
 def _model(V, L, seed, **kw):
@@ -63,9 +61,40 @@ def test_multidraft_keeps_target_law(V, L, K):
             assert abs(e_tau - lt.expected_tau_rrs_l1(m, K)) < ETAU_TOL
 
 
-# SpecTr enumerates like the K-draft walk; the two largest corners are left out
-# for time (each K-draft corner above is also run for SpecTr).
-SPECTR_GRID = [g for g in GRID if g not in ((2, 3, 3), (3, 2, 3))]
+# SpecTr enumerates like the K-draft walk, on the same corners.
+SPECTR_GRID = GRID
+
+
+def draws_follow_reported_law(method, K, lib_path=None):
+    """Whether the correction law the exact-law entry point reports (om/Z of the
+    final draw) is the law of the token the oracle draws: bisecting the float32
+    correction uniform over the draws must give the same distribution, to the
+    float32 resolution of the uniform."""
+    rng = np.random.default_rng(77)
+    V, L, B = 8, 3, 40
+    tgt = (rng.standard_normal((B, K, L + 1, V)) * 1.5).astype(np.float32)
+    drf = (tgt[:, :, :L] + rng.standard_normal((B, K, L, V))).astype(np.float32)
+    tok = rng.integers(0, V, (B, K, L)).astype(np.int32)
+    tok[:, 1:, 0] = tok[:, :1, 0]   # shared roots, so later drafts are tested too
+    T = np.full(B, 0.9, np.float32)
+    ua = rng.random((B, K, L)).astype(np.float32)
+    rep = oracle.verify_exact(method, tgt, drf, tok, T, ua.astype(np.float64), np.zeros(B),
+                              lib_path=lib_path)
+
+    def run(ri, u, uc):
+        return oracle.verify(method, tgt[ri], drf[ri], tok[ri], T[ri], u, uc, lib_path=lib_path)
+
+    drawn = lt.correction_law(run, np.arange(B), ua, V)
+    return bool(np.abs(rep["corr_law"].sum(axis=1) - 1.0).max() < 1e-14 and
+                np.abs(drawn - rep["corr_law"]).max() < V * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("method,K", [("multidraft", 3), ("spectr", 3), ("token", 1),
+                                      ("block", 1)])
+def test_reported_correction_law_matches_the_draws(method, K):
+    """The exact-law pins read the correction's law from what the oracle reports;
+    this pins that report to the oracle's own draws."""
+    assert draws_follow_reported_law(method, K)
 
 
 def spectr_l1_bracket(m, K, n_grid=4001):
@@ -657,10 +686,13 @@ def mutant_libs(tmp_path_factory):
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_fails_a_pin(mutant_libs, name):
-    """Each planted mistake must break the law, a closed form or the bound on
-    at least one tiny instance."""
-    caught = False
+    """Each planted mistake must break the law, a closed form, the bound on at
+    least one tiny instance, or the agreement of the draws with the law the
+    oracle reports for them."""
+    caught = not draws_follow_reported_law("multidraft", 3, lib_path=mutant_libs[name])
     for (V, L, K) in [(2, 2, 2), (3, 2, 2), (2, 3, 1), (3, 1, 3), (2, 3, 3)]:
+        if caught:
+            break
         for seed in range(2):
             m = _model(V, L, seed)
             law, e_tau, _ = lt.output_law(m, K, "multidraft", lib_path=mutant_libs[name])
@@ -678,8 +710,10 @@ def test_planted_mistake_fails_a_pin(mutant_libs, name):
 
 @pytest.mark.parametrize("name", sorted(SPECTR_MUTANTS))
 def test_planted_spectr_mistake_fails_a_pin(mutant_libs, name):
-    caught = False
+    caught = not draws_follow_reported_law("spectr", 3, lib_path=mutant_libs[name])
     for (V, L, K) in [(3, 1, 3), (2, 2, 2), (3, 2, 2), (8, 1, 3)]:
+        if caught:
+            break
         for seed in range(2):
             m = _model(V, L, seed)
             law, e_tau, _ = lt.output_law(m, K, "spectr", lib_path=mutant_libs[name])
