@@ -81,11 +81,10 @@ struct Layout {
 };
 
 // Single-draft workspace (K = 1 without given statistics): slice statistics of
-// every row (after the final launch, the re-evaluation's fp64 statistics) |
-// residual slice sums per position | each request's combined statistics and
-// weight chain | number of requests listed for re-evaluation | their indices.
+// every row | residual slice sums per position | each request's combined
+// statistics and weight chain.
 struct SingleLayout {
-    size_t part, rpart, prep, rcount, rlist, total;
+    size_t part, rpart, prep, total;
     int NS;
 };
 
@@ -97,9 +96,7 @@ SingleLayout single_layout(int32_t B, int32_t L, int32_t V) {
     l.part = 0;
     l.rpart = align_up(bs * (2 * L + 1) * sizeof(sv::SliceStat), 256);
     l.prep = l.rpart + align_up(bs * (L + 1) * sizeof(double), 256);
-    l.rcount = l.prep + align_up(static_cast<size_t>(B) * sizeof(sv::SinglePrep), 256);
-    l.rlist = l.rcount + 256;
-    l.total = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
+    l.total = l.prep + align_up(static_cast<size_t>(B) * sizeof(sv::SinglePrep), 256);
     return l;
 }
 
@@ -328,8 +325,6 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
     a.part = reinterpret_cast<sv::SliceStat *>(ws + lay.part);
     a.rpart = reinterpret_cast<double *>(ws + lay.rpart);
     a.prep = reinterpret_cast<sv::SinglePrep *>(ws + lay.prep);
-    a.redo_count = reinterpret_cast<unsigned *>(ws + lay.rcount);
-    a.redo_list = reinterpret_cast<int32_t *>(ws + lay.rlist);
     a.B = in->B;
     a.L = in->L;
     a.V = in->V;
@@ -362,9 +357,6 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
     hipLaunchKernelGGL((sv::single_final_kernel<NT, RD, E>), dim3(grid(in->B)), dim3(NT), 0, stream,
                        a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = launch_redo<E, VEC>(in, out, stream, method, a.redo_count, a.redo_list,
-                                   ws + lay.part, nullptr, nullptr)) != hipSuccess)
-        return err;
     for (int i = 2; i < 5; ++i)
         if ((err = record(ln, i, stream)) != hipSuccess) return err;
     return hipSuccess;

@@ -92,6 +92,58 @@ struct RedoArgs {
     float *accept_prob, *resid_mass;
 };
 
+// fp64 statistics of one row at temperature T, in one pass: each thread keeps
+// a running maximum and rescales its sum when it grows; the block combines them
+// (block-uniform call; every thread returns the result).
+template <int NT, typename RD>
+__device__ RedoStat redo_row_stat(const RD &R, int nch, float T, double *s_red, float *s_fred) {
+    const int tid = threadIdx.x;
+    const double cT = 1.4426950408889634 / static_cast<double>(T);
+    float mx = -INFINITY;
+    double sum = 0.0;
+    int nan = !(T > 0.0f) || !isfinite(T);
+    for (int q0 = tid; q0 < nch; q0 += kRedoDepth * NT) {   // loads issued ahead
+        typename RD::Raw raw[kRedoDepth];
+#pragma unroll
+        for (int d = 0; d < kRedoDepth; ++d)
+            if (q0 + d * NT < nch) raw[d] = R.raw(q0 + d * NT);
+#pragma unroll
+        for (int d = 0; d < kRedoDepth; ++d) {
+            if (q0 + d * NT >= nch) break;
+            float x[8];
+            RD::unpack(raw[d], x);
+            float cm = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                nan |= isnan(x[e]) || x[e] == INFINITY;
+                cm = fmaxf(cm, x[e]);
+            }
+            if (cm > mx) {   // rescale the sum to the new maximum
+                if (mx > -INFINITY)
+                    sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(cm)) * cT);
+                mx = cm;
+            }
+            if (mx > -INFINITY && !nan) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sum += exp2_d((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT);
+            }
+        }
+    }
+    nan = __syncthreads_or(nan);
+    const float M = block_max<NT>(mx, s_fred);
+    if (mx > -INFINITY && !nan)
+        sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(M)) * cT);
+    else
+        sum = 0.0;
+    sum = block_sum<NT>(sum, s_red);
+    RedoStat st;
+    st.ok = !nan && M > -INFINITY && sum > 0.0 && isfinite(sum);
+    st.M = M;
+    st.ls = st.ok ? log2(sum) : 0.0;
+    return st;
+}
+
 // One workgroup per (listed request, node row), grid-stride: the fp64
 // statistics of the row when it is the node's own (no earlier draft shares its
 // prefix; the walk reads only those).
@@ -124,52 +176,8 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
             : static_cast<const E *>(A.drf) + ((static_cast<long long>(b) * K + k) * L + j) * V;
         const RD R(base, V);
         const float T = A.temp[b];
-        const double cT = 1.4426950408889634 / static_cast<double>(T);
-        float mx = -INFINITY;
-        double sum = 0.0;
-        int nan = !(T > 0.0f) || !isfinite(T);
-        for (int q0 = tid; q0 < nch; q0 += kRedoDepth * NT) {   // loads issued ahead
-            typename RD::Raw raw[kRedoDepth];
-#pragma unroll
-            for (int d = 0; d < kRedoDepth; ++d)
-                if (q0 + d * NT < nch) raw[d] = R.raw(q0 + d * NT);
-#pragma unroll
-            for (int d = 0; d < kRedoDepth; ++d) {
-                if (q0 + d * NT >= nch) break;
-                float x[8];
-                RD::unpack(raw[d], x);
-                float cm = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    nan |= isnan(x[e]) || x[e] == INFINITY;
-                    cm = fmaxf(cm, x[e]);
-                }
-                if (cm > mx) {   // rescale the sum to the new maximum
-                    if (mx > -INFINITY)
-                        sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(cm)) * cT);
-                    mx = cm;
-                }
-                if (mx > -INFINITY && !nan) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sum += exp2_d((static_cast<double>(x[e]) - static_cast<double>(mx)) * cT);
-                }
-            }
-        }
-        nan = __syncthreads_or(nan);
-        const float M = block_max<NT>(mx, s_fred);
-        if (mx > -INFINITY && !nan)
-            sum *= exp2_d((static_cast<double>(mx) - static_cast<double>(M)) * cT);
-        else
-            sum = 0.0;
-        sum = block_sum<NT>(sum, s_red);
-        if (tid == 0) {
-            RedoStat st;
-            st.ok = !nan && M > -INFINITY && sum > 0.0 && isfinite(sum);
-            st.M = M;
-            st.ls = st.ok ? log2(sum) : 0.0;
-            A.stats[it] = st;
-        }
+        const RedoStat st = redo_row_stat<NT, RD>(R, nch, T, s_red, s_fred);
+        if (tid == 0) A.stats[it] = st;
     }
 }
 
@@ -178,6 +186,7 @@ struct RedoShared {
     int x[kMaxK * kMaxL];
     unsigned char can[kMaxK * (kMaxL + 1)];
     unsigned char ok[kMaxK * (2 * kMaxL + 1)];
+    unsigned char have[kMaxK * (2 * kMaxL + 1)];
     float M[kMaxK * (2 * kMaxL + 1)];
     double ls[kMaxK * (2 * kMaxL + 1)];
     int H[kMaxK];
@@ -188,12 +197,16 @@ struct RedoShared {
     double pair[2];
 };
 
-// Re-evaluate listed request i in fp64 and overwrite its outputs (block-uniform
-// call).
+// Re-evaluate request b in fp64 and overwrite its outputs (block-uniform call).
+// entry: its list entry (kListNoReplay: no records to replay); st: its node
+// rows' fp64 statistics [K][2L+1] from redo_stats_kernel, or null to compute
+// each one in this workgroup when the walk first reads it.
 template <int NT, typename RD, typename E>
-__device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li, RedoShared &sh) {
+__device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b, int entry,
+                                                       const RedoStat *st, RedoShared &sh) {
     int *s_x = sh.x;
-    unsigned char *s_can = sh.can, *s_ok = sh.ok;
+    unsigned char *s_can = sh.can, *s_ok = sh.ok, *s_have = sh.have;
+    float *s_fred = sh.fred;
     float *s_M = sh.M;
     double *s_ls = sh.ls;
     int *s_H = sh.H;
@@ -202,21 +215,21 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
     const int tid = threadIdx.x;
     const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
-    const int entry = A.list[li];
-    const int b = entry & ~kListNoReplay;
     {
         const long long bKL = static_cast<long long>(b) * K * L;
         // exp((l - M) / T) taken as 2^((l - M) log2(e) / T)
         const double cT = 1.4426950408889634 / static_cast<double>(A.temp[b]);
         const E *tgt = static_cast<const E *>(A.tgt);
         const E *drf = static_cast<const E *>(A.drf);
-        const RedoStat *st = A.stats + static_cast<long long>(li) * K * RS;
         for (int q = tid; q < K * L; q += NT) s_x[q] = A.tok[bKL + q];
         for (int q = tid; q < K * RS; q += NT) {
-            const RedoStat r = st[q];
-            s_ok[q] = static_cast<unsigned char>(r.ok);
-            s_M[q] = r.M;
-            s_ls[q] = r.ls;
+            if (st) {
+                const RedoStat r = st[q];
+                s_ok[q] = static_cast<unsigned char>(r.ok);
+                s_M[q] = r.M;
+                s_ls[q] = r.ls;
+            }
+            s_have[q] = st ? 1 : 0;
         }
         __syncthreads();
         // node of (k, j): the lowest-index draft with the same first j tokens
@@ -237,10 +250,22 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int li
         };
         auto slot = [&](bool target, int c, int j) { return c * RS + (target ? j : L1 + j); };
         int bad = 0;
-        // node row (target?, node of (k, j)): its slot; an invalid row marks the
-        // request
+        // node row (target?, node of (k, j)): its slot, its statistics computed
+        // here when not given; an invalid row marks the request
         auto stats = [&](bool target, int k, int j) {
-            const int sl = slot(target, s_can[k * L1 + j], j);
+            const int c = s_can[k * L1 + j];
+            const int sl = slot(target, c, j);
+            if (!s_have[sl]) {
+                const RedoStat r = redo_row_stat<NT, RD>(row(target, c, j), nch, A.temp[b], s_red,
+                                                        s_fred);
+                if (tid == 0) {
+                    s_ok[sl] = static_cast<unsigned char>(r.ok);
+                    s_M[sl] = r.M;
+                    s_ls[sl] = r.ls;
+                    s_have[sl] = 1;
+                }
+                __syncthreads();
+            }
             bad |= !s_ok[sl];
             return sl;
         };
@@ -769,8 +794,11 @@ __global__ __launch_bounds__(NT) void redo_walk_kernel(RedoArgs A) {
     __shared__ RedoShared sh;
     const unsigned n = *A.count;
     if (n == 0) return;
-    for (unsigned i = blockIdx.x; i < n; i += gridDim.x)
-        redo_request<NT, RD, E>(A, static_cast<int>(i), sh);   // block-uniform
+    for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {   // block-uniform
+        const int entry = A.list[i];
+        redo_request<NT, RD, E>(A, entry & ~kListNoReplay, entry,
+                                A.stats + static_cast<long long>(i) * A.K * (2 * A.L + 1), sh);
+    }
 }
 
 }  // namespace sv

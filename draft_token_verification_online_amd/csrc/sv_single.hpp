@@ -22,8 +22,8 @@
 //                         sums, and the correction, found among the slice sums
 //                         and rescanned in the one slice that holds the
 //                         inverse-CDF crossing; a request with a decision within
-//                         its fp32 error of its threshold is listed for the fp64
-//                         re-evaluation (sv_redo.hpp, two launches after these).
+//                         its fp32 error of its threshold is taken again in fp64
+//                         (sv_redo.hpp) by the same workgroup.
 // (The launch boundaries publish each step's sums to the next.  Handing them
 // over inside one launch -- the last workgroup of a request to finish taking the
 // decision -- needs a device-scope fence per workgroup, which on this chip
@@ -43,6 +43,7 @@
 #pragma once
 
 #include "sv_device.hpp"
+#include "sv_redo.hpp"
 #include "sv_rowstats.hpp"
 #include "sv_walk.hpp"
 
@@ -70,8 +71,6 @@ struct SingleArgs {
     SliceStat *part;        // [B][2L+1][NS]: rows in the order target 0..L, draft 0..L-1
     double *rpart;          // [B][L+1][NS]: residual (m < L) or bonus-row (m = L) slice sums
     struct SinglePrep *prep;   // [B]: each request's combined statistics and chain
-    unsigned *redo_count;   // requests with a decision within its error of its threshold,
-    int32_t *redo_list;     // listed here for the fp64 re-evaluation (sv_redo.hpp)
     int B, L, V, NS;
     int method;             // kMethodToken (token level) or anything else (block)
     int32_t *accept_len, *draft_index, *correction, *flags, *rows_streamed;
@@ -103,7 +102,6 @@ __global__ __launch_bounds__(NT) void single_stats_kernel(SingleArgs A) {
     const int L = A.L, V = A.V, NS = A.NS, RS = 2 * L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
     const long long items = static_cast<long long>(A.B) * RS * NS;
-    if (blockIdx.x == 0 && tid == 0) *A.redo_count = 0u;   // the final launch lists
     for (long long it = blockIdx.x; it < items; it += gridDim.x) {
         const int s = static_cast<int>(it % NS);
         const long long br = it / NS;
@@ -375,10 +373,29 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
     __shared__ double s_red[NW];
     __shared__ int s_ired[NW];
     __shared__ double s_z[2];
+    __shared__ RedoShared s_redo;
     const int tid = threadIdx.x;
     const int L = A.L, V = A.V, NS = A.NS, RS = 2 * L + 1, L1 = L + 1;
     const int nch = (V + kChunk - 1) / kChunk;
     const bool token = A.method == kMethodToken;
+    RedoArgs ra = {};
+    ra.tgt = A.tgt;
+    ra.drf = A.drf;
+    ra.tok = A.tok;
+    ra.temp = A.temp;
+    ra.ua = A.ua;
+    ra.uc = A.uc;
+    ra.B = A.B;
+    ra.K = 1;
+    ra.L = L;
+    ra.V = V;
+    ra.method = A.method;
+    ra.accept_len = A.accept_len;
+    ra.draft_index = A.draft_index;
+    ra.correction = A.correction;
+    ra.flags = A.flags;
+    ra.accept_prob = A.accept_prob;
+    ra.resid_mass = A.resid_mass;
     for (int b = blockIdx.x; b < A.B; b += gridDim.x) {
         const float T = A.temp[b];
         const Scale c = temp_scale(T);
@@ -604,10 +621,11 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
         }
         if (bad && hout)
             for (int j = tid; j < L; j += NT) hout[j] = NAN;
-        // a decision within the fp32 error of its threshold: the request is taken
-        // again in fp64 (sv_redo.hpp)
-        if (tid == 0 && !bad && (flags & kFlagNearTie)) A.redo_list[atomicAdd(A.redo_count, 1u)] = b;
         __syncthreads();
+        // a decision within the fp32 error of its threshold: the request is taken
+        // again in fp64 here, its 2L+1 rows' statistics computed by this
+        // workgroup (sv_redo.hpp; block-uniform)
+        if (!bad && (flags & kFlagNearTie)) redo_request<NT, RD, E>(ra, b, 0, nullptr, s_redo);
     }
 }
 
