@@ -373,6 +373,8 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
     __shared__ double s_red[NW];
     __shared__ int s_ired[NW];
     __shared__ double s_z[2];
+    __shared__ double s_zsum[kMaxL + 1];   // residual sum of each position
+    __shared__ float s_u[kMaxL];
     __shared__ RedoShared s_redo;
     const int tid = threadIdx.x;
     const int L = A.L, V = A.V, NS = A.NS, RS = 2 * L + 1, L1 = L + 1;
@@ -406,13 +408,18 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
         auto trow = [&](int j) { return RD(tgt + static_cast<long long>(j) * V, V); };
         auto drow = [&](int j) { return RD(drf + static_cast<long long>(j) * V, V); };
         auto ok = [&](int r) { return isfinite(P.M[r]) && P.S[r] > 0.0 && isfinite(P.S[r]); };
-        const float *u = A.ua + static_cast<long long>(b) * L;
         const double *rp = A.rpart + static_cast<long long>(b) * L1 * NS;
-        auto zsum = [&](int j) {   // slice sums of position j, in slice order
+        // every position's uniform and residual sum (its slice sums in slice
+        // order) into LDS at once, so the decision loop waits on no load
+        if (tid < L1) {
             double z = 0.0;
-            for (int q = 0; q < NS; ++q) z += rp[j * NS + q];
-            return z;
-        };
+            for (int q = 0; q < NS; ++q) z += rp[tid * NS + q];
+            s_zsum[tid] = z;
+        } else if (tid >= kWave && tid < kWave + L) {
+            s_u[tid - kWave] = A.ua[static_cast<long long>(b) * L + (tid - kWave)];
+        }
+        const float *u = s_u;
+        auto zsum = [&](int j) { return s_zsum[j]; };
         float *hout = A.accept_prob ? A.accept_prob + static_cast<long long>(b) * L : nullptr;
         if (hout)
             for (int j = tid; j < L; j += NT) hout[j] = NAN;
@@ -522,32 +529,50 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
             if (sc < 0) {   // no slice of positive weight (cannot happen for a valid row)
                 bad = 1;
             } else {
-                // rescan slice sc: thread t takes chunks 4t..4t+3 of it, in order
+                // rescan slice sc: thread t takes its kSliceChunksPerThread
+                // consecutive chunks, all loads issued at once, and keeps their
+                // weights in registers for the recount
                 const int q0 = sc * kSliceChunks, qn = min(kSliceChunks, nch - q0);
                 const RD Pr = trow(jd), Qr = has_q ? drow(jd) : trow(jd);
                 const float KP = P.K[jd], KQ = has_q ? P.K[L1 + jd] : 0.0f;
-                // omega / a of chunk q of the slice (the sweeps' own arithmetic)
-                auto weights = [&](int q, float w[8]) {
-                    float xp[8], xq[8];
-                    Pr.load(q0 + q, xp);
-                    if (has_q) {
-                        Qr.load(q0 + q, xq);
-                        resid8<true>(xp, xq, KP, KQ, r, c, w);
-                    } else {
-                        resid8<false>(xp, xp, KP, 0.0f, 0.0f, c, w);
+                float wv[kSliceChunksPerThread][8];   // omega / a (the sweeps' own arithmetic)
+                {
+                    typename RD::Raw rp[kSliceChunksPerThread], rq[kSliceChunksPerThread];
+#pragma unroll
+                    for (int i = 0; i < kSliceChunksPerThread; ++i) {
+                        const int q = kSliceChunksPerThread * tid + i;
+                        if (q < qn) {
+                            rp[i] = Pr.raw(q0 + q);
+                            if (has_q) rq[i] = Qr.raw(q0 + q);
+                        }
                     }
-                };
+#pragma unroll
+                    for (int i = 0; i < kSliceChunksPerThread; ++i) {
+                        const int q = kSliceChunksPerThread * tid + i;
+                        if (q < qn) {
+                            float xp[8], xq[8];
+                            RD::unpack(rp[i], xp);
+                            if (has_q) {
+                                RD::unpack(rq[i], xq);
+                                resid8<true>(xp, xq, KP, KQ, r, c, wv[i]);
+                            } else {
+                                resid8<false>(xp, xp, KP, 0.0f, 0.0f, c, wv[i]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) wv[i][e] = 0.0f;
+                        }
+                    }
+                }
                 double tsum = 0.0;
                 int lastpos = -1;
+#pragma unroll
                 for (int i = 0; i < kSliceChunksPerThread; ++i) {
                     const int q = kSliceChunksPerThread * tid + i;
-                    if (q < qn) {
-                        float w[8];
-                        weights(q, w);
-                        tsum += static_cast<double>(sum8(w));
-                        for (int e = 0; e < 8; ++e)
-                            if (w[e] > 0.0f) lastpos = kChunk * (q0 + q) + e;
-                    }
+                    tsum += static_cast<double>(sum8(wv[i]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        lastpos = (wv[i][e] > 0.0f && q < qn) ? kChunk * (q0 + q) + e : lastpos;
                 }
                 const double pre = base + block_exclusive_scan<NT>(tsum, s_red);
                 int cand = 0x7fffffff;
@@ -555,17 +580,18 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
                 if (!past && pre <= thr && pre + tsum > thr) {
                     // the crossing lies in this thread's chunks: recount them in order
                     double C = pre;
-                    for (int i = 0; i < kSliceChunksPerThread && cand == 0x7fffffff; ++i) {
+#pragma unroll
+                    for (int i = 0; i < kSliceChunksPerThread; ++i) {
                         const int q = kSliceChunksPerThread * tid + i;
-                        if (q >= qn) break;
-                        float w[8];
-                        weights(q, w);
-                        for (int e = 0; e < 8 && cand == 0x7fffffff; ++e) {
-                            const double before = C;
-                            C += static_cast<double>(w[e]);
-                            if (C > thr) {
-                                cand = kChunk * (q0 + q) + e;
-                                cm = fmin(C - thr, thr - before);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if (cand == 0x7fffffff && q < qn) {
+                                const double before = C;
+                                C += static_cast<double>(wv[i][e]);
+                                if (C > thr) {
+                                    cand = kChunk * (q0 + q) + e;
+                                    cm = fmin(C - thr, thr - before);
+                                }
                             }
                         }
                     }
