@@ -191,6 +191,7 @@ struct RedoShared {
     double ls[kMaxK * (2 * kMaxL + 1)];
     int H[kMaxK];
     unsigned char made[kMaxK * kMaxL];   // tests of the final path (accept_prob entries kept)
+    double w[kMaxL + 1], R[kMaxL + 1];   // GBV's weight chain and residual sums
     double red[16];
     float fred[16];
     int ired[16];
@@ -646,7 +647,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
             // GBV over K drafts: residual omega(v) = [v not in H] max(alpha p_s - beta q_s, 0)
             double alpha = 1.0, beta = 0.0, N = 1.0;
             int nH = 0;
-            double w[kMaxL + 1], R[kMaxL + 1];
+            double *w = sh.w, *R = sh.R;   // weight chain, residual sums (LDS: no scratch)
             auto in_H = [&](int v) {   // branch-free: nH is the same for every thread
                 bool r = false;
                 for (int i = 0; i < nH; ++i) r |= (s_H[i] == v);
