@@ -288,7 +288,7 @@ class LmHead:
         self._dt = _dtype_code(self.logits)
         nbytes = int(lib.sv_lm_workspace_size(R, d, V))
         if nbytes == 0:
-            raise ValueError(f"sizes out of range: R={R} d={d} V={V} (d a multiple of 64)")
+            raise ValueError(f"sizes out of range: R={R} d={d} V={V} (d a multiple of 64, at least 128)")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def __call__(self, hidden, weight, temperature, *, stats=None, group=1, stride=1, offset=0,

@@ -511,7 +511,7 @@ LmLayout lm_layout(int32_t R, int32_t V) {
 }
 
 bool lm_sizes_ok(int32_t R, int32_t d, int32_t V) {
-    return R >= 0 && R <= (1 << 26) && d >= sv::kLmBK && d <= 65536 && d % sv::kLmBK == 0 &&
+    return R >= 0 && R <= (1 << 26) && d >= sv::kLmDMin && d <= 65536 && d % sv::kLmDStep == 0 &&
            V >= 1 && V <= SV_MAX_V;
 }
 

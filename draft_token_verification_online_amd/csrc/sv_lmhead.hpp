@@ -12,15 +12,26 @@
 // bytes; the statistics are then those of the rounded values): the walk's
 // residual sweeps and correction draws read whole rows.
 //
-// lm_head_kernel: one 256-thread workgroup per 128 x 128 output tile, four waves
-// in a 2 x 2 arrangement each owning 64 x 64 (4 x 4 MFMA 16x16x32 bf16 tiles),
-// K stepped by 64 through double-buffered LDS (rows padded by 16 bytes against
-// bank conflicts), with the global loads three steps ahead in registers.
+// lm_head_kernel: one 256-thread workgroup (one per CU: 128 KB of LDS, 256
+// AGPRs per lane) per 256 x 256 output tile, four waves in a 2 x 2 arrangement
+// each owning a 128 x 128 quarter (8 x 8 MFMA 16x16x32 bf16 tiles, 256 fp32
+// accumulators per lane).  At that size a wave reads 16 KB of fragments from
+// LDS per 64 MFMAs, half the LDS and L2 traffic per flop of a 64 x 64 wave
+// tile.  The k dimension runs in regions of 32 columns between barriers; a
+// wave computes region s from fragments it read during region s-1 while it
+// reads those of region s+1, one read per four MFMAs.  Tiles reach LDS through
+// buffer loads that write LDS directly (no registers, no LDS store
+// instructions), 64 columns -- one 128-byte line per row -- at a time, into
+// two stages: the loads of a stage are issued two regions before its first
+// fragments are read.  The MFMA operand A is the vocabulary tile and B the
+// hidden-state tile, so a lane's four accumulators of a 16 x 16 tile are four
+// consecutive vocabulary entries of one output row: the epilogue stores them
+// as one 8- or 16-byte write and reduces a row with two cross-lane steps.
 // Blocks are ordered in groups of row-blocks so a group reuses each vocabulary
 // tile from L2, and remapped so that consecutive blocks of the order land on
-// the same XCD.  The epilogue writes the fp32
-// tile and, per row, the partial (max, sum) over its 128 columns; a combine
-// kernel folds the partials of a row into (M, S).
+// the same XCD.  The epilogue writes the tile and, per row, the partial
+// (max, sum) over its 256 columns; a combine kernel folds the partials of a
+// row into (M, S).
 #pragma once
 
 #include "sv_device.hpp"
@@ -30,23 +41,50 @@ namespace sv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLmBM = 128, kLmBN = 128, kLmBK = 64;
+constexpr int kLmBM = 256, kLmBN = 256, kLmBK = 32;   // kLmBK: columns per region
 constexpr int kLmThreads = 256;
-constexpr int kLmStride = kLmBK + 8;     // LDS row stride in bf16 elements
-constexpr int kLmGroupM = 16;            // row-blocks per group of the block order
+constexpr int kLmStageK = 64;            // columns per LDS stage: one 128-byte line per row
+constexpr int kLmStages = 2;             // 2 x (two 256 x 64 tiles) = 128 KB
+constexpr int kLmTileElems = kLmBM * kLmStageK;
+constexpr int kLmDStep = kLmStageK;      // d must be a multiple
+constexpr int kLmDMin = 2 * kLmStageK;   // and at least the pipeline's last two stages
+constexpr int kLmGroupM = 8;             // row-blocks per group of the block order
 constexpr int kXcds = 8;
 
-template <int N> struct Stage { static constexpr int value = N; };
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+__device__ __forceinline__ lds_void_ptr lds_ptr(uint16_t *p) { return (lds_void_ptr)p; }
 
-// Buffer resource over rows r0.. of a [rows][d] bf16 matrix (byte range clamped
-// to 32 bits; the kernel's offsets within a tile stay below 128 rows).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *m, int r0, int rows,
-                                                            int d) {
+// Buffer descriptor (as four words) over rows r0.. of a [rows][d] bf16 matrix:
+// base, no stride, byte range clamped to 32 bits, raw 32-bit data format.
+typedef int intx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ intx4 lm_desc(const uint16_t *m, int r0, int rows, int d) {
     const long long bytes = static_cast<long long>(rows - r0) * d * 2;
-    const int n = static_cast<int>(bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(m + static_cast<long long>(r0) * d), 0, n, 0x00020000);
+    const uint64_t base = reinterpret_cast<uint64_t>(m + static_cast<long long>(r0) * d);
+    return intx4{static_cast<int>(base & 0xffffffffu), static_cast<int>((base >> 32) & 0xffffu),
+                 static_cast<int>(bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL), 0x00020000};
 }
+
+// 16 bytes per lane from global memory (buffer range checked: zeros past the
+// range) straight into LDS: lane l's bytes land at LDS address lds + 16 l.
+// Issued as inline assembly so that the compiler, which cannot tell the stage
+// a load writes from the stage a fragment read reads, does not wait for every
+// such load before each LDS read; the kernel orders them itself with explicit
+// vector-memory waits before its barriers.
+// (m0 is reserved to the compiler, which warns that a clobber of it may not be
+// honoured; nothing else in the LM-head kernel uses m0, each load sets it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(uint32_t lds, int voff, intx4 desc, int soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(desc), "s"(soff)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 
 // fp32 to bf16, round to nearest even (finite values; the LM head's logits are
 // finite sums of finite products).
@@ -81,172 +119,229 @@ __device__ __forceinline__ void lm_block_coords(int pid, int nbm, int nbn, int *
     *bn = r / gsize;
 }
 
-__global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_kernel(
-    LmArgs A) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kLmBM * kLmStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kLmBN * kLmStride];
-    __shared__ float s_m[2][kLmBM];
-    __shared__ double s_s[2][kLmBM];
+// acc += A B^T for one 16 x 16 x 32 step, the accumulator pinned to an AGPR
+// quad.  (With 256 accumulators per lane and 128 fragment registers live, the
+// compiler's own choice spreads accumulators over both register files and
+// copies them between MFMAs.)  As volatile assembly the MFMAs keep the order
+// they are written in, relative to each other and to the LDS reads between
+// them, which is the interleave the kernel spells out.  The compiler still
+// places the waits for the LDS reads an MFMA's operands come from; what it
+// does not see: (a) an accumulator is read by ordinary instructions only after
+// the wait states that follow the last MFMAs (below); (b) an LDS read may
+// reuse the registers of a fragment whose last MFMA was issued a few
+// instructions earlier -- the MFMA takes its A and B operands when it starts,
+// and the read's data arrives tens of cycles after the read issues, by which
+// time the earlier MFMA has finished.
+__device__ __forceinline__ void mfma_acc(floatx4 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+template <int N> struct Par { static constexpr int value = N; };
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+__global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_kernel(
+    LmArgs A) {
+    // [stage][0: hidden tile, 1: vocabulary tile][256 rows x 64 columns]; the
+    // 16-byte chunk c (k = 8c .. 8c+7) of row r sits in slot c ^ (r % 8) of the
+    // row's 128 bytes, so the 8 rows that 8 lanes of a fragment read touch at one
+    // c fall in 8 distinct bank groups.
+    __shared__ __attribute__((aligned(1024))) uint16_t sT[kLmStages][2][kLmTileElems];
+    // the epilogue's per-row partials reuse stage 0 once the loop is done
+    float(*s_m)[kLmBM] = reinterpret_cast<float(*)[kLmBM]>(&sT[0][0][0]);
+    double(*s_s)[kLmBM] = reinterpret_cast<double(*)[kLmBM]>(&sT[0][1][0]);
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wv = wave & 1, wh = wave >> 1;   // vocabulary half, hidden-row half
     int bm, bn;
     lm_block_coords(blockIdx.x, A.nbm, A.nbn, &bm, &bn);
     const int row0 = bm * kLmBM, col0 = bn * kLmBN;
     const int R = A.R, d = A.d, V = A.V;
 
-    // a 128 x 64 bf16 tile is 1024 chunks of 16 bytes: 4 per thread.  The loads
-    // are buffer loads over the rows from the tile's first row to the end of the
-    // matrix: the hardware range check returns zeros past the end, so partial
-    // tiles need no branch in the loop.
-    const __amdgpu_buffer_rsrc_t rsA = tile_rsrc(A.h, row0, R, d);
-    const __amdgpu_buffer_rsrc_t rsB = tile_rsrc(A.w, col0, V, d);
-    auto load_tile = [&](const __amdgpu_buffer_rsrc_t &rs, int k0, uint4 (&buf)[4]) {
+    // Tiles reach LDS by buffer loads that write LDS directly: one instruction
+    // moves 64 lanes x 16 bytes to 1 KB of consecutive LDS, here 8 whole tile
+    // rows (128-byte lines).  Wave w fills rows w*64 .. w*64+63 of both tiles,
+    // 8 instructions each; lane l loads the chunk that belongs in slot l % 8 of
+    // row l / 8.  Rows past the matrix read as zeros (hardware range check of
+    // the buffer resource).
+    int voff[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + kLmThreads * i;
-            const int r = q >> 3, kc = q & 7;
-            buf[i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r * d + k0 + kc * 8) * 2, 0, 0));
+    for (int i = 0; i < 8; ++i) {
+        const int r = wave * 64 + i * 8 + (lane >> 3);
+        voff[i] = (r * d + (((lane & 7) ^ (r & 7)) * 8)) * 2;
+    }
+    const intx4 dH = lm_desc(A.h, row0, R, d), dW = lm_desc(A.w, col0, V, d);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(&sT[0][0][0]))) +
+                          wave * 64 * kLmStageK * 2;
+    auto load_stage = [&](int k0, int buf) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + buf * (2 * kLmTileElems * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lds_dma16(base + i * 8 * kLmStageK * 2, voff[i], dH, k0 * 2);
+            lds_dma16(base + kLmTileElems * 2 + i * 8 * kLmStageK * 2, voff[i], dW, k0 * 2);
         }
     };
-    auto store_tile = [&](uint16_t *s, const uint4 (&buf)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + kLmThreads * i;
-            const int r = q >> 3, kc = q & 7;
-            *reinterpret_cast<uint4 *>(s + r * kLmStride + kc * 8) = buf[i];
-        }
+    // fragment t of matrix m (0 hidden, 1 vocabulary) for the wave's half
+    // `half`, of region step s: rows half*128 + t*16 + lane%16, k = 8*(lane/16)
+    // within the step's 32 columns (chunk 4*(s%2) + lane/16 of the stage)
+    const int fo0 = (lane & 15) * kLmStageK + ((((lane >> 4)) ^ (lane & 7)) * 8);
+    const int fo1 = (lane & 15) * kLmStageK + (((4 + (lane >> 4)) ^ (lane & 7)) * 8);
+    auto read_frag = [&](int buf, int h, int m, int half, int t) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8 *>(&sT[buf][m][(half * 128 + t * 16) * kLmStageK] +
+                                                 (h ? fo1 : fo0));
     };
 
-    floatx4 acc[4][4];
+    floatx4 acc[8][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // three register stages: tile t lives in stage t % 3 from its load until it is
-    // stored to LDS, two compute steps later, so each load has two steps to land
-    // (stage indices are compile-time constants, so the stages stay in registers)
-    const int nk = d / kLmBK;
-    uint4 ra[3][4], rb[3][4];
-    load_tile(rsA, 0, ra[0]);
-    load_tile(rsB, 0, rb[0]);
-    if (nk > 1) {
-        load_tile(rsA, kLmBK, ra[1]);
-        load_tile(rsB, kLmBK, rb[1]);
-    }
-    if (nk > 2) {
-        load_tile(rsA, 2 * kLmBK, ra[2]);
-        load_tile(rsB, 2 * kLmBK, rb[2]);
-    }
-    store_tile(sA[0], ra[0]);
-    store_tile(sB[0], rb[0]);
+    // Regions of 32 columns between barriers: region s computes step s from
+    // fragments read during region s-1 (register set s % 2) and reads step
+    // s+1's.  Stage J % 2 holds columns 64J .. 64J+63 (steps 2J, 2J+1).  Odd
+    // region 2J+1 starts the loads of stage-step J+2 into the stage step J used
+    // (whose last fragments were read before the previous barrier); even region
+    // 2J+2 ends by waiting for them, before step 2J+4's fragments are read.
+    const int nk = d / kLmBK;     // even
+    const int nj = d / kLmStageK; // >= 2
+    bf16x8 wf[2][8], hf[2][8];
+    load_stage(0, 0);
+    load_stage(kLmStageK, 1);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage-step 0
     __syncthreads();
-
-    auto compute = [&](int buf) {
+    wf[0][0] = read_frag(0, 0, 1, wv, 0);
 #pragma unroll
-        for (int kk = 0; kk < kLmBK; kk += 32) {
-            bf16x8 af[4], bfr[4];
-            const int ko = kk + (lane >> 4) * 8;
+    for (int t = 0; t < 8; ++t) hf[0][t] = read_frag(0, 0, 0, wh, t);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = wm * 64 + t * 16 + (lane & 15);
-                af[t] = *reinterpret_cast<const bf16x8 *>(sA[buf] + r * kLmStride + ko);
-                const int c = wn * 64 + t * 16 + (lane & 15);
-                bfr[t] = *reinterpret_cast<const bf16x8 *>(sB[buf] + c * kLmStride + ko);
-            }
+    for (int t = 1; t < 8; ++t) wf[0][t] = read_frag(0, 0, 1, wv, t);
+    auto region = [&](int r, auto par, auto load, auto read) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value, Q = P ^ 1;   // P = r % 2
+        constexpr bool LOAD = decltype(load)::value, READ = decltype(read)::value;
+        if constexpr (LOAD) load_stage(((r + 3) >> 1) * kLmStageK, ((r + 3) >> 1) & 1);
+        const int sn = ((r + 1) >> 1) & 1;   // stage of step r+1 (its half is Q)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 8; ++a) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], acc[a][b], 0,
-                                                                       0, 0);
-        }
-    };
-    // step t (stage S = t % 3): compute tile t, store tile t+1 (stage S+1), load
-    // tile t+3 into stage S
-    auto step = [&](int t, auto stage) {
-        constexpr int S = decltype(stage)::value, S1 = (S + 1) % 3;
-        compute(t & 1);
-        if (t + 1 < nk) {
-            store_tile(sA[(t + 1) & 1], ra[S1]);
-            store_tile(sB[(t + 1) & 1], rb[S1]);
-        }
-        if (t + 3 < nk) {
-            load_tile(rsA, (t + 3) * kLmBK, ra[S]);
-            load_tile(rsB, (t + 3) * kLmBK, rb[S]);
-        }
-        __syncthreads();
-    };
-    // the same step where the next tile and the load three ahead both exist:
-    // no condition, so the steps of the main loop form one scheduling region
-    // apart from their barriers
-    auto full_step = [&](int t, auto stage) {
-        constexpr int S = decltype(stage)::value, S1 = (S + 1) % 3;
-        compute(t & 1);
-        store_tile(sA[(t + 1) & 1], ra[S1]);
-        store_tile(sB[(t + 1) & 1], rb[S1]);
-        load_tile(rsA, (t + 3) * kLmBK, ra[S]);
-        load_tile(rsB, (t + 3) * kLmBK, rb[S]);
-        __syncthreads();
-    };
-    int t = 0;
-    for (; t + 5 < nk; t += 3) {
-        full_step(t, Stage<0>{});
-        full_step(t + 1, Stage<1>{});
-        full_step(t + 2, Stage<2>{});
-    }
-    for (; t < nk; t += 3) {
-        step(t, Stage<0>{});
-        if (t + 1 < nk) step(t + 1, Stage<1>{});
-        if (t + 2 < nk) step(t + 2, Stage<2>{});
-    }
-
-    // epilogue: lane holds C[4*(lane/16) + i][lane%16] of each 16 x 16 tile
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rloc = wm * 64 + a * 16 + 4 * (lane >> 4) + i;
-            const int row = row0 + rloc;
-            const bool rok = row < R;
-            float v[4];
-            float m = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = col0 + wn * 64 + b * 16 + (lane & 15);
-                const long long at = static_cast<long long>(row) * V + col;
-                if (A.bf16_out) {
-                    // the statistics describe the logits as stored
-                    const uint16_t hb = bf16_rne(acc[a][b][i]);
-                    v[b] = col < V ? __uint_as_float(static_cast<uint32_t>(hb) << 16) : -INFINITY;
-                    if (rok && col < V) static_cast<uint16_t *>(A.logits)[at] = hb;
-                } else {
-                    v[b] = col < V ? acc[a][b][i] : -INFINITY;
-                    if (rok && col < V) static_cast<float *>(A.logits)[at] = v[b];
+            for (int b = 0; b < 8; ++b) {
+                mfma_acc(acc[a][b], wf[P][a], hf[P][b]);
+                if constexpr (READ) {
+                    if ((b & 3) == 3) {
+                        // step r+1's reads in the order its MFMAs use them
+                        const int t = a * 2 + (b >> 2);
+                        if (t == 0)
+                            wf[Q][0] = read_frag(sn, Q, 1, wv, 0);
+                        else if (t <= 8)
+                            hf[Q][t - 1] = read_frag(sn, Q, 0, wh, t - 1);
+                        else
+                            wf[Q][t - 8] = read_frag(sn, Q, 1, wv, t - 8);
+                    }
                 }
-                m = fmaxf(m, v[b]);
-            }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-            const Scale sc = temp_scale(rok ? A.temp[row] : 1.0f);
-            const float msc = shift_term(m, sc);
-            float e = 0.0f;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) e += fast_exp2(expo(v[b], sc, msc));
-            double s = static_cast<double>(e);
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
-            if ((lane & 15) == 0) {
-                s_m[wn][rloc] = m;
-                s_s[wn][rloc] = s;
             }
         }
+        if constexpr (P == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    using T = Flag<true>;
+    using F = Flag<false>;
+    // pairs of regions (2J, 2J+1) while stage-step J+2 exists, then the last two pairs
+    int r = 0;
+    for (; (r >> 1) + 2 < nj; r += 2) {
+        region(r, Par<0>{}, F{}, T{});
+        region(r + 1, Par<1>{}, T{}, T{});
     }
+    region(r, Par<0>{}, F{}, T{});
+    region(r + 1, Par<1>{}, F{}, T{});
+    region(r + 2, Par<0>{}, F{}, T{});
+    region(r + 3, Par<1>{}, F{}, F{});
+    (void)nk;
+    // wait states before the accumulators are read: the last MFMAs issued are
+    // those of row a = 7, ordered before the reads through their operands
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                   "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
+
+    // epilogue: lane holds, of tile (a, b), the vocabulary entries
+    // a*16 + 4*(lane/16) + i (i = 0..3) of hidden row b*16 + lane%16.  The
+    // statistics describe the logits as stored (rounded to bf16 when they are).
+    const bool vec = (V & 3) == 0;
+    auto stored = [&](float x) __attribute__((always_inline)) {
+        return A.bf16_out ? __uint_as_float(static_cast<uint32_t>(bf16_rne(x)) << 16) : x;
+    };
+    // (b is a template constant: a loop this large is not unrolled, and any
+    // runtime index into acc would put it in scratch memory)
+    auto epilogue_rows = [&](auto bc) __attribute__((always_inline)) {
+        constexpr int b = decltype(bc)::value;
+        const int rloc = wh * 128 + b * 16 + (lane & 15);
+        const int row = row0 + rloc;
+        const bool rok = row < R;
+        float m = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            const int col = col0 + wv * 128 + a * 16 + 4 * (lane >> 4);
+            const long long at = static_cast<long long>(row) * V + col;
+            if (A.bf16_out) {
+                uint16_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hb[i] = bf16_rne(acc[a][b][i]);
+                if (rok) {
+                    uint16_t *o = static_cast<uint16_t *>(A.logits) + at;
+                    if (vec && col + 3 < V) {
+                        *reinterpret_cast<uint2 *>(o) =
+                            make_uint2(hb[0] | (static_cast<uint32_t>(hb[1]) << 16),
+                                       hb[2] | (static_cast<uint32_t>(hb[3]) << 16));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (col + i < V) o[i] = hb[i];
+                    }
+                }
+            } else if (rok) {
+                float *o = static_cast<float *>(A.logits) + at;
+                if (vec && col + 3 < V) {
+                    *reinterpret_cast<float4 *>(o) =
+                        make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (col + i < V) o[i] = acc[a][b][i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (col + i < V) m = fmaxf(m, stored(acc[a][b][i]));
+        }
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const Scale sc = temp_scale(rok ? A.temp[row] : 1.0f);
+        const float msc = shift_term(m, sc);
+        float e = 0.0f;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            const int col = col0 + wv * 128 + a * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (col + i < V) e += fast_exp2(expo(stored(acc[a][b][i]), sc, msc));
+        }
+        double s = static_cast<double>(e);
+        s += __shfl_xor(s, 16, kWave);
+        s += __shfl_xor(s, 32, kWave);
+        if (lane < 16) {
+            s_m[wv][rloc] = m;
+            s_s[wv][rloc] = s;
+        }
+    };
+    epilogue_rows(Par<0>{});
+    epilogue_rows(Par<1>{});
+    epilogue_rows(Par<2>{});
+    epilogue_rows(Par<3>{});
+    epilogue_rows(Par<4>{});
+    epilogue_rows(Par<5>{});
+    epilogue_rows(Par<6>{});
+    epilogue_rows(Par<7>{});
     __syncthreads();
-    if (tid < kLmBM) {
-        const int row = row0 + tid;
+    {
+        const int row = row0 + tid;   // kLmThreads == kLmBM
         if (row < R) {
             const Scale sc = temp_scale(A.temp[row]);
             const float m0 = s_m[0][tid], m1 = s_m[1][tid];
@@ -260,6 +355,7 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
     }
 }
+static_assert(kLmThreads == kLmBM, "one epilogue thread per tile row");
 
 // The partials of row r folded into its statistics, written to slot
 // (r / group) * stride + offset + r % group of a 16-byte {float M; float pad;

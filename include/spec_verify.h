@@ -303,7 +303,7 @@ int spec_draft_sample(const sv_draft_inputs *in, const sv_draft_outputs *out,
  * speculative-decoding step (the performance study's page, section 1). */
 typedef struct sv_lm_inputs {
     int32_t R;                    /* rows, >= 0 */
-    int32_t d;                    /* hidden size, a positive multiple of 64, <= 65536 */
+    int32_t d;                    /* hidden size, a multiple of 64, 128 <= d <= 65536 */
     int32_t V;                    /* vocabulary size, 1..SV_MAX_V */
     const void *hidden;           /* [R][d] bf16, 16-byte aligned, device memory */
     const void *weight;           /* [V][d] bf16, 16-byte aligned, device memory */

@@ -306,7 +306,7 @@ def test_lm_head_host_validation(lib):
     ins, outs, ln = fake()
     assert f(None, outs, ln) == sv.SV_EINVAL and f(ins, None, ln) == sv.SV_EINVAL
     assert f(ins, outs, None) == sv.SV_EINVAL
-    for field, value in [("d", 0), ("d", 96), ("d", 70000), ("V", 0), ("R", -1)]:
+    for field, value in [("d", 0), ("d", 64), ("d", 96), ("d", 70000), ("V", 0), ("R", -1)]:
         ins, outs, ln = fake()
         setattr(ins, field, value)
         assert f(ins, outs, ln) == sv.SV_EINVAL, (field, value)
@@ -328,8 +328,8 @@ def test_lm_head_host_validation(lib):
     assert f(ins, outs, ln) == sv.SV_EWORKSPACE
     ins, outs, ln = fake(R=0)
     assert f(ins, outs, ln) == sv.SV_OK
-    # partial (max, sum) per row and 128-column block
-    assert lib.sv_lm_workspace_size(36864, 3584, 151936) >= 36864 * 1187 * 12
+    # partial (max, sum) per row and 256-column block
+    assert lib.sv_lm_workspace_size(36864, 3584, 151936) >= 36864 * 594 * 12
     assert lib.sv_lm_workspace_size(4, 100, 16) == 0
 
 

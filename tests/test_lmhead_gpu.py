@@ -42,7 +42,7 @@ def _stats_lse(buf, rows, temps):
     return shift / temps + np.log(ssum)
 
 
-@pytest.mark.parametrize("R,d,V,T", [(1, 64, 1, 1.0), (130, 64, 1000, 0.7), (257, 128, 4099, 0.4),
+@pytest.mark.parametrize("R,d,V,T", [(1, 128, 1, 1.0), (130, 192, 1000, 0.7), (257, 128, 4099, 0.4),
                                      (300, 896, 8192, 1.0), (128, 3584, 2048, 0.25)])
 def test_logits_and_statistics(R, d, V, T):
     print(f"[case] lm_head R={R} d={d} V={V} T={T}", flush=True)
@@ -127,7 +127,7 @@ def test_lm_head_statistics_feed_verification(method):
     assert lse_err <= bnd / float(Th.min()) + 1e-5
 
 
-@pytest.mark.parametrize("R,d,V,T", [(130, 64, 1000, 0.7), (257, 128, 4099, 0.4),
+@pytest.mark.parametrize("R,d,V,T", [(130, 192, 1000, 0.7), (257, 128, 4099, 0.4),
                                      (128, 3584, 2048, 0.25)])
 def test_bf16_logits_and_their_statistics(R, d, V, T):
     """bf16 logits: each is the fp32 accumulation rounded to nearest even, so it
