@@ -22,8 +22,9 @@
 // reads those of region s+1, one read per four MFMAs.  Tiles reach LDS through
 // buffer loads that write LDS directly (no registers, no LDS store
 // instructions), 64 columns -- one 128-byte line per row -- at a time, into
-// two stages: the loads of a stage are issued two regions before its first
-// fragments are read.  The MFMA operand A is the vocabulary tile and B the
+// two stages: a stage's 16 loads per wave are issued one per four MFMAs of the
+// region two regions before its first fragments are read (issued back to back
+// they stall the wave behind the load queue: 0.94 against 1.1 PFLOP/s).  The MFMA operand A is the vocabulary tile and B the
 // hidden-state tile, so a lane's four accumulators of a 16 x 16 tile are four
 // consecutive vocabulary entries of one output row: the epilogue stores them
 // as one 8- or 16-byte write and reduces a row with two cross-lane steps.
@@ -173,13 +174,15 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     const intx4 dH = lm_desc(A.h, row0, R, d), dW = lm_desc(A.w, col0, V, d);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(&sT[0][0][0]))) +
                           wave * 64 * kLmStageK * 2;
+    // load j (0..15) of a stage: rows 8(j % 8) .. of the wave's share of the
+    // hidden tile (j < 8) or of the vocabulary tile (j >= 8)
+    auto load_one = [&](int k0, int buf, int j) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + buf * (2 * kLmTileElems * 2) + (j >> 3) * (kLmTileElems * 2);
+        lds_dma16(base + (j & 7) * 8 * kLmStageK * 2, voff[j & 7], j < 8 ? dH : dW, k0 * 2);
+    };
     auto load_stage = [&](int k0, int buf) __attribute__((always_inline)) {
-        const uint32_t base = lds0 + buf * (2 * kLmTileElems * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            lds_dma16(base + i * 8 * kLmStageK * 2, voff[i], dH, k0 * 2);
-            lds_dma16(base + kLmTileElems * 2 + i * 8 * kLmStageK * 2, voff[i], dW, k0 * 2);
-        }
+        for (int j = 0; j < 16; ++j) load_one(k0, buf, j);
     };
     // fragment t of matrix m (0 hidden, 1 vocabulary) for the wave's half
     // `half`, of region step s: rows half*128 + t*16 + lane%16, k = 8*(lane/16)
@@ -197,12 +200,13 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Regions of 32 columns between barriers: region s computes step s from
-    // fragments read during region s-1 (register set s % 2) and reads step
-    // s+1's.  Stage J % 2 holds columns 64J .. 64J+63 (steps 2J, 2J+1).  Odd
-    // region 2J+1 starts the loads of stage-step J+2 into the stage step J used
-    // (whose last fragments were read before the previous barrier); even region
-    // 2J+2 ends by waiting for them, before step 2J+4's fragments are read.
+    // Regions of 32 columns: region s computes step s from fragments read
+    // during region s-1 (register set s % 2) and reads step s+1's.  Stage J % 2
+    // holds columns 64J .. 64J+63 (steps 2J, 2J+1).  Odd region 2J+1 issues the
+    // loads of stage-step J+2 into the stage stage-step J used (whose last
+    // fragments were read during region 2J, before the barrier that ends it);
+    // even region 2J+2 ends by waiting for them and a barrier, before step
+    // 2J+4's fragments are read in region 2J+3.
     const int nk = d / kLmBK;     // even
     const int nj = d / kLmStageK; // >= 2
     bf16x8 wf[2][8], hf[2][8];
@@ -218,13 +222,17 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     auto region = [&](int r, auto par, auto load, auto read) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value, Q = P ^ 1;   // P = r % 2
         constexpr bool LOAD = decltype(load)::value, READ = decltype(read)::value;
-        if constexpr (LOAD) load_stage(((r + 3) >> 1) * kLmStageK, ((r + 3) >> 1) & 1);
+        const int kl = ((r + 3) >> 1) * kLmStageK, sl = ((r + 3) >> 1) & 1;   // loads of stage-step (r+3)/2
         const int sn = ((r + 1) >> 1) & 1;   // stage of step r+1 (its half is Q)
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 mfma_acc(acc[a][b], wf[P][a], hf[P][b]);
+                // the stage's 16 loads spread over the region, one per four MFMAs
+                if constexpr (LOAD) {
+                    if ((b & 3) == 0) load_one(kl, sl, a * 2 + (b >> 2));
+                }
                 if constexpr (READ) {
                     if ((b & 3) == 3) {
                         // step r+1's reads in the order its MFMAs use them
@@ -239,8 +247,13 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
                 }
             }
         }
-        if constexpr (P == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // only even regions end in a barrier: it publishes stage-step (r+2)/2
+        // (loaded during region r-1) and frees the stage region r+1 loads into
+        // (its last fragments were read during region r)
+        if constexpr (P == 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     };
     using T = Flag<true>;
     using F = Flag<false>;
