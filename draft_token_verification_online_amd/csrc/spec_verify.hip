@@ -41,7 +41,6 @@ constexpr int kMaxB = 1 << 24;
 // one load, so the grids are kept small (one workgroup per CU at most): most
 // calls list nothing.
 constexpr long long kRedoStatsGrid = 256;
-constexpr int kRedoWalkGrid = 32;
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
 static_assert(SV_MAX_L == sv::kMaxL, "L limit");
@@ -76,7 +75,7 @@ size_t stats_bytes(int32_t B, int32_t K, int32_t L) {
 // of the walk (K >= 3 only: a node sees a second mass sweep only with three or
 // more drafts).
 struct Layout {
-    size_t stats, state, need, list, count, rcount, rlist, dec, rho, nodes, total;
+    size_t stats, state, need, list, count, rcount, rlist, dec, rho, team, nodes, total;
     bool has_nodes;
 };
 
@@ -112,7 +111,8 @@ Layout layout(int32_t B, int32_t K, int32_t L) {
     l.rlist = l.rcount + 256;
     l.dec = l.rlist + align_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
     l.rho = l.dec + align_up(bkl, 256);
-    l.nodes = l.rho + align_up(static_cast<size_t>(B) * L * sizeof(double), 256);
+    l.team = l.rho + align_up(static_cast<size_t>(B) * L * sizeof(double), 256);
+    l.nodes = l.team + align_up(sv::kRedoTeamSlots * (sizeof(sv::TeamCmd) + sizeof(sv::TeamPart)), 256);
     l.has_nodes = K >= 3;
     l.total = l.nodes + (l.has_nodes ? static_cast<size_t>(B) *
                                            static_cast<size_t>(sv::node_list_bytes<kWalkThreads>())
@@ -136,7 +136,7 @@ __global__ void reset_count_kernel(unsigned *count) {
 template <typename E, bool VEC>
 hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t stream, int method,
                        const unsigned *count, const int32_t *list, void *stats,
-                       const unsigned char *dec, const double *rho_rec) {
+                       const unsigned char *dec, const double *rho_rec, void *team) {
     using RD = typename sv::RowOf<E, VEC>::type;
     sv::RedoArgs ra;
     ra.tgt = in->target_logits;
@@ -161,13 +161,18 @@ hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t s
     ra.flags = out->flags;
     ra.accept_prob = out->accept_prob;
     ra.resid_mass = out->resid_mass;
+    ra.team_cmd = static_cast<sv::TeamCmd *>(team);
+    ra.team_part = reinterpret_cast<sv::TeamPart *>(static_cast<char *>(team) +
+                                                    sv::kRedoTeamSlots * sizeof(sv::TeamCmd));
     const long long rows = static_cast<long long>(in->B) * in->K * (2 * in->L + 1);
     const unsigned g1 = static_cast<unsigned>(rows < kRedoStatsGrid ? rows : kRedoStatsGrid);
     hipLaunchKernelGGL((sv::redo_stats_kernel<sv::kRedoStatsThreads, RD, E>), dim3(g1),
                        dim3(sv::kRedoStatsThreads), 0, stream, ra);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const unsigned g2 = static_cast<unsigned>(in->B < kRedoWalkGrid ? in->B : kRedoWalkGrid);
+    // teams of up to kTeamMax workgroups per listed request (at most B of them)
+    const long long want = static_cast<long long>(in->B) * sv::kTeamMax;
+    const unsigned g2 = static_cast<unsigned>(want < sv::kRedoTeamSlots ? want : sv::kRedoTeamSlots);
     hipLaunchKernelGGL((sv::redo_walk_kernel<sv::kRedoThreads, RD, E>), dim3(g2),
                        dim3(sv::kRedoThreads), 0, stream, ra);
     return hipGetLastError();
@@ -289,7 +294,7 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         if ((err = walk()) != hipSuccess) return err;
     }
     if ((err = launch_redo<E, VEC>(in, out, stream, wa.method, wa.redo_count, wa.redo_list,
-                                   ws + lay.stats, wa.dec, wa.rho_rec)) != hipSuccess)
+                                   ws + lay.stats, wa.dec, wa.rho_rec, ws + lay.team)) != hipSuccess)
         return err;
     return record(ln, 4, stream);
 }

@@ -76,6 +76,45 @@ struct RedoStat {
     int ok;
 };
 
+// Teams.  When few requests are listed, each gets a team of workgroups that
+// share its O(V) passes: the team's first workgroup runs the re-evaluation and,
+// for each pass, publishes a command (the node, the weight, its parameters);
+// every member sums the weights over its own contiguous range of the row's
+// chunks and publishes the partial sums, which the first workgroup adds in
+// member order (the same order whichever workgroup computed a range, so the
+// result does not depend on timing).  No wait is unbounded: a member that has
+// not answered within kTeamWaitTicks is computed by the first workgroup itself
+// (the team then works alone), and a member that has seen no command for
+// kTeamIdleTicks leaves.  Commands and partials go through device memory with
+// agent-scope release and acquire (relaxed polls).
+constexpr int kTeamMax = 16;                  // workgroups per team
+constexpr int kTeamDone = 0x7fffffff;         // command number that ends a team
+constexpr long long kTeamWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
+constexpr long long kTeamIdleTicks = 200000;  // 2 ms
+constexpr int kTeamRes = 0;    // [v not in H] max(a p - bq q, 0)   (q = 0 without the draft row)
+constexpr int kTeamSRes = 1;   // max(p - cc min(q, p / rho), 0)    (SpecTr residual)
+constexpr int kTeamSSums = 2;  // min(q, p / rho) and max(p - rho q, 0), two sums
+
+struct TeamBody {       // one pass: its node, weight and parameters
+    int kind, c, j, with_q, nH;
+    int H[kMaxK];
+    float Mp, Mq;       // node rows' fp64 statistics (see RedoStat)
+    double lsp, lsq;
+    double a, bq, cc, rho;
+};
+
+struct TeamCmd {
+    int seq;            // command number (0: none yet; kTeamDone: the team is finished)
+    int acks;           // partials published by the members, over all commands
+    TeamBody body;
+};
+
+struct TeamPart {
+    double s[2];        // partial sums over the member's range
+    int last;           // last token of positive weight in it (-1: none)
+    int seq;            // the command they answer
+};
+
 struct RedoArgs {
     const void *tgt;              // [B][K][L+1][V]
     const void *drf;              // [B][K][L][V]
@@ -90,7 +129,12 @@ struct RedoArgs {
     int method;                   // kMethodToken, kMethodBlockWalk or kMethodSpecTr
     int32_t *accept_len, *draft_index, *correction, *flags;
     float *accept_prob, *resid_mass;
+    TeamCmd *team_cmd;            // [kRedoTeamSlots]: one per team
+    TeamPart *team_part;          // [kRedoTeamSlots]: team t's members at t*T ..
 };
+
+// Slots of the team areas (the re-evaluation launch's grid bound).
+constexpr int kRedoTeamSlots = 256;
 
 // fp64 statistics of one row at temperature T, in one pass: each thread keeps
 // a running maximum and rescales its sum when it grows; the block combines them
@@ -154,6 +198,12 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
     const unsigned n = *A.count;
     if (n == 0) return;
     const int tid = threadIdx.x;
+    // the team areas start clean for this call's re-evaluation launch
+    for (int i = blockIdx.x * NT + tid; i < kRedoTeamSlots; i += gridDim.x * NT) {
+        A.team_cmd[i].seq = 0;
+        A.team_cmd[i].acks = 0;
+        A.team_part[i].seq = 0;
+    }
     const int K = A.K, L = A.L, V = A.V, L1 = L + 1, RS = 2 * L + 1, per = K * RS;
     const int nch = (V + kChunk - 1) / kChunk;
     const long long items = static_cast<long long>(n) * per;
@@ -181,6 +231,123 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
     }
 }
 
+// Weight of token v (probabilities p, q) under a team command.
+__device__ __forceinline__ double team_weight(const TeamBody &d, int v, double p, double q) {
+    if (d.kind == kTeamSRes) return fmax(p - d.cc * fmin(q, p / d.rho), 0.0);
+    bool inH = false;   // branch-free: nH is the same for every thread
+    for (int i = 0; i < d.nH; ++i) inH |= (d.H[i] == v);
+    return inH ? 0.0 : fmax(d.a * p - d.bq * q, 0.0);
+}
+
+// A team command's sums over chunks [q0, q1) of its node's rows (block-uniform;
+// every thread returns them): out[0] (and for kTeamSSums out[1]); *last the last
+// token of positive weight (-1: none).  Chunks are taken two per thread at a
+// time, strided by the block, the order of the single-workgroup sweep.
+template <int NT, typename RD, typename E>
+__device__ void team_slice(const RedoArgs &A, int b, const TeamBody &d, int q0, int q1,
+                           double out[2], int *last, double *s_red, int *s_ired) {
+    const int tid = threadIdx.x;
+    const int K = A.K, L = A.L, V = A.V, L1 = L + 1;
+    const double cT = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+    const RD P(static_cast<const E *>(A.tgt) + ((static_cast<long long>(b) * K + d.c) * L1 + d.j) * V,
+               V);
+    const RD Q(static_cast<const E *>(A.drf) +
+                   ((static_cast<long long>(b) * K + d.c) * L + (d.with_q ? d.j : 0)) * V,
+               V);
+    const double Mp = d.Mp, Mq = d.Mq, lsp = d.lsp, lsq = d.lsq;
+    const bool sums = d.kind == kTeamSSums;
+    const double ir = sums ? 1.0 / d.rho : 0.0;
+    double v0 = 0.0, v1 = 0.0;
+    int lp = -1;
+    for (int qa = q0 + tid; qa < q1; qa += 2 * NT) {   // loads issued ahead
+        typename RD::Raw rp[2], rq[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            if (qa + e2 * NT < q1) {
+                rp[e2] = P.raw(qa + e2 * NT);
+                if (d.with_q) rq[e2] = Q.raw(qa + e2 * NT);
+            }
+        }
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const int q = qa + e2 * NT;
+            if (q >= q1) break;
+            float xp[8], xq[8];
+            RD::unpack(rp[e2], xp);
+            if (d.with_q) RD::unpack(rq[e2], xq);
+            // elements past the row read as -inf: p = q = 0, weight 0
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double p = exp2_d(fma(static_cast<double>(xp[e]) - static_cast<double>(Mp), cT, -lsp));
+                const double qq =
+                    d.with_q ? exp2_d(fma(static_cast<double>(xq[e]) - static_cast<double>(Mq), cT, -lsq))
+                             : 0.0;
+                if (sums) {
+                    v0 += fmin(qq, p * ir);
+                    v1 += fmax(p - d.rho * qq, 0.0);
+                } else {
+                    const double w = team_weight(d, kChunk * q + e, p, qq);
+                    v0 += w;
+                    lp = w > 0.0 ? kChunk * q + e : lp;
+                }
+            }
+        }
+    }
+    out[0] = block_sum<NT>(v0, s_red);
+    out[1] = sums ? block_sum<NT>(v1, s_red) : 0.0;
+    *last = sums ? -1 : block_max_int<NT>(lp, s_ired);
+}
+
+// Chunk range of team member m of T over nch chunks.
+__device__ __forceinline__ int team_lo(int m, int T, int nch) {
+    return static_cast<int>(static_cast<long long>(nch) * m / T);
+}
+
+// A member (not the first) of request b's team: sums its range of every
+// command until the team is finished or no command comes for kTeamIdleTicks.
+template <int NT, typename RD, typename E>
+__device__ void team_member(const RedoArgs &A, int b, int team, int m, int T, TeamBody &cmd,
+                            double *s_red, int *s_ired, int *s_seq) {
+    const int tid = threadIdx.x;
+    const int nch = (A.V + kChunk - 1) / kChunk;
+    TeamCmd *gc = A.team_cmd + team;
+    TeamPart *gp = A.team_part + team * T + m;
+    int seen = 0;
+    while (true) {
+        if (tid == 0) {
+            const long long t0 = static_cast<long long>(__builtin_amdgcn_s_memrealtime());
+            int got = -1;
+            // relaxed polls (an acquire would drop this XCD's L2 at every poll), one
+            // acquire fence once the number moved
+            while (true) {
+                const int sq = __hip_atomic_load(&gc->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (sq != seen) { got = sq; break; }
+                if (static_cast<long long>(__builtin_amdgcn_s_memrealtime()) - t0 > kTeamIdleTicks) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (got > 0 && got != kTeamDone) cmd = gc->body;
+            *s_seq = got;
+        }
+        __syncthreads();
+        const int sq = *s_seq;
+        if (sq <= 0 || sq == kTeamDone) return;   // block-uniform
+        double out[2];
+        int last;
+        team_slice<NT, RD, E>(A, b, cmd, team_lo(m, T, nch), team_lo(m + 1, T, nch), out, &last, s_red,
+                              s_ired);
+        if (tid == 0) {
+            gp->s[0] = out[0];
+            gp->s[1] = out[1];
+            gp->last = last;
+            __hip_atomic_store(&gp->seq, sq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&gc->acks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        seen = sq;
+        __syncthreads();
+    }
+}
+
 // LDS of one re-evaluation.
 struct RedoShared {
     int x[kMaxK * kMaxL];
@@ -196,15 +363,21 @@ struct RedoShared {
     float fred[16];
     int ired[16];
     double pair[2];
+    TeamBody cmd;                         // the command being run (team of more than one)
+    double tp[2][kTeamMax];               // members' partial sums, in member order
+    int tlast[kTeamMax], tgot[kTeamMax];
+    int tseq;
 };
 
 // Re-evaluate request b in fp64 and overwrite its outputs (block-uniform call).
 // entry: its list entry (kListNoReplay: no records to replay); st: its node
 // rows' fp64 statistics [K][2L+1] from redo_stats_kernel, or null to compute
-// each one in this workgroup when the walk first reads it.
+// each one in this workgroup when the walk first reads it.  team, T: the
+// request's team (T = 1: this workgroup alone); this workgroup is its first.
 template <int NT, typename RD, typename E>
 __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b, int entry,
-                                                       const RedoStat *st, RedoShared &sh) {
+                                                       const RedoStat *st, RedoShared &sh, int team,
+                                                       int T) {
     int *s_x = sh.x;
     unsigned char *s_can = sh.can, *s_ok = sh.ok, *s_have = sh.have;
     float *s_fred = sh.fred;
@@ -408,6 +581,174 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
             lastrun = block_max_int<NT>(lastrun, s_ired);
             return lastrun >= 0 ? lastrun : last;
         };
+        // ---- team passes (T > 1): the command in sh.cmd over the members' ranges
+        int tseq = 0;        // commands published so far
+        bool solo = false;   // a member failed to answer: every range is summed here
+        auto team_run = [&]() {
+            TeamCmd *gc = A.team_cmd + team;
+            if (!solo) {
+                ++tseq;
+                if (tid == 0) {
+                    gc->body = sh.cmd;
+                    __hip_atomic_store(&gc->seq, tseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            double o[2];
+            int lst;
+            team_slice<NT, RD, E>(A, b, sh.cmd, team_lo(0, T, nch), team_lo(1, T, nch), o, &lst, s_red,
+                                  s_ired);
+            if (tid == 0) {
+                sh.tp[0][0] = o[0];
+                sh.tp[1][0] = o[1];
+                sh.tlast[0] = lst;
+                // every member's partial of this command counted (or the wait is over)
+                if (!solo) {
+                    const int want = tseq * (T - 1);
+                    const long long t0 = static_cast<long long>(__builtin_amdgcn_s_memrealtime());
+                    while (__hip_atomic_load(&gc->acks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want &&
+                           static_cast<long long>(__builtin_amdgcn_s_memrealtime()) - t0 <= kTeamWaitTicks)
+                        __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            __syncthreads();
+            // the members' partials, one thread each: a partial counts only if it
+            // answers this command (its number, published by a release after the
+            // sums, read here before an acquire fence)
+            if (tid > 0 && tid < T) {
+                int got = 0;
+                if (!solo) {
+                    const TeamPart *gp = A.team_part + team * T + tid;
+                    const int q = __hip_atomic_load(&gp->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    if (q == tseq) {
+                        sh.tp[0][tid] = gp->s[0];
+                        sh.tp[1][tid] = gp->s[1];
+                        sh.tlast[tid] = gp->last;
+                        got = 1;
+                    }
+                }
+                sh.tgot[tid] = got;
+            }
+            __syncthreads();
+            for (int m = 1; m < T; ++m) {   // block-uniform: ranges no member answered
+                if (sh.tgot[m]) continue;
+                team_slice<NT, RD, E>(A, b, sh.cmd, team_lo(m, T, nch), team_lo(m + 1, T, nch), o, &lst,
+                                      s_red, s_ired);
+                if (tid == 0) {
+                    sh.tp[0][m] = o[0];
+                    sh.tp[1][m] = o[1];
+                    sh.tlast[m] = lst;
+                }
+                solo = true;
+            }
+            __syncthreads();
+        };
+        // the command for node (k, j): kind, parameters, the node rows' statistics
+        auto team_cmd = [&](int k, int j, int kind, int with_q, double a, double bq, double cc,
+                            double rho, int nh) {
+            const int sp = stats(true, k, j);
+            const int sq = with_q ? stats(false, k, j) : sp;
+            if (tid == 0) {
+                sh.cmd.kind = kind;
+                sh.cmd.c = s_can[k * L1 + j];
+                sh.cmd.j = j;
+                sh.cmd.with_q = with_q;
+                sh.cmd.nH = nh;
+                for (int i = 0; i < nh; ++i) sh.cmd.H[i] = s_H[i];
+                sh.cmd.Mp = s_M[sp];
+                sh.cmd.lsp = s_ls[sp];
+                sh.cmd.Mq = s_M[sq];
+                sh.cmd.lsq = s_ls[sq];
+                sh.cmd.a = a;
+                sh.cmd.bq = bq;
+                sh.cmd.cc = cc;
+                sh.cmd.rho = rho;
+            }
+            __syncthreads();
+        };
+        // sum of the residual weight [v not in H] max(a p - bq q, 0) at node (k, j)
+        auto team_sweep = [&](int k, int j, double a, double bq, int nh) {
+            team_cmd(k, j, kTeamRes, 1, a, bq, 0.0, 1.0, nh);
+            team_run();
+            double z = 0.0;
+            for (int m = 0; m < T; ++m) z += sh.tp[0][m];
+            return z;
+        };
+        // the inverse-CDF draw of icdf over a team command set up by team_cmd
+        auto team_icdf = [&](double u, double *Z, double *margin) {
+            team_run();
+            double z = 0.0;
+            int last = -1;
+            for (int m = 0; m < T; ++m) {
+                z += sh.tp[0][m];
+                last = max(last, sh.tlast[m]);
+            }
+            *Z = z;
+            *margin = 0.0;
+            if (!(z > 0.0) || !isfinite(z)) return -1;
+            const double thr = u * z;
+            // the first member range whose end passes u Z
+            double base = 0.0;
+            int ms = -1;
+            for (int m = 0; m < T; ++m) {
+                if (base + sh.tp[0][m] > thr) { ms = m; break; }
+                base += sh.tp[0][m];
+            }
+            if (ms < 0) return last;   // rounding: no C_v exceeds u Z
+            // that range's elements, recounted by the whole block in token order:
+            // consecutive runs per thread, a block scan, then the run that crosses
+            // u Z element by element
+            const TeamBody &d = sh.cmd;
+            const RD P(static_cast<const E *>(A.tgt) + ((static_cast<long long>(b) * K + d.c) * L1 + d.j) * V,
+                       V);
+            const RD Q(static_cast<const E *>(A.drf) +
+                           ((static_cast<long long>(b) * K + d.c) * L + (d.with_q ? d.j : 0)) * V,
+                       V);
+            const double cT = 1.4426950408889634 / static_cast<double>(A.temp[b]);
+            auto wat = [&](int v) {
+                const double p = exp2_d(fma(static_cast<double>(P.at(v)) - static_cast<double>(d.Mp), cT, -d.lsp));
+                const double q =
+                    d.with_q ? exp2_d(fma(static_cast<double>(Q.at(v)) - static_cast<double>(d.Mq), cT, -d.lsq))
+                             : 0.0;
+                return team_weight(d, v, p, q);
+            };
+            const int e0 = kChunk * team_lo(ms, T, nch), e1 = min(kChunk * team_lo(ms + 1, T, nch), V);
+            const int cnt = e1 > e0 ? (e1 - e0 + NT - 1) / NT : 0;
+            const int a0 = min(e0 + tid * cnt, e1), a1 = min(a0 + cnt, e1);
+            double part = 0.0;
+            int lastrun = -1;
+            for (int v = a0; v < a1; ++v) {
+                const double wv = wat(v);
+                part += wv;
+                lastrun = wv > 0.0 ? v : lastrun;
+            }
+            const double pre2 = base + block_exclusive_scan<NT>(part, s_red);
+            int cand = 0x7fffffff;
+            double cm = 0.0;
+            if (pre2 + part > thr) {
+                double C = pre2;
+                for (int v = a0; v < a1; ++v) {
+                    const double before = C;
+                    C += wat(v);
+                    if (C > thr) {
+                        cand = v;
+                        cm = fmin(C - thr, thr - before);
+                        break;
+                    }
+                }
+            }
+            const int got = cand;
+            cand = block_min_int<NT>(cand, s_ired);
+            if (cand != 0x7fffffff) {
+                if (got == cand) s_pair[0] = cm;
+                __syncthreads();
+                *margin = s_pair[0] / z;
+                __syncthreads();
+                return cand;
+            }
+            lastrun = block_max_int<NT>(lastrun, s_ired);
+            return lastrun >= 0 ? lastrun : last;
+        };
         auto same_prefix = [&](int a, int c, int n) {
             int same = 1;
             for (int t = 0; t < n; ++t) same &= (s_x[a * L + t] == s_x[c * L + t]);
@@ -442,6 +783,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
         int tau = 0, kstar = -1, y = -1, own = 0;
         double Z = NAN, dm = INFINITY;
         auto draw_target = [&](int k, int j) {   // the node's target row itself
+            if (T > 1) {
+                team_cmd(k, j, kTeamRes, 0, 1.0, 0.0, 0.0, 1.0, 0);
+                return team_icdf(uc, &Z, &dm);
+            }
             return icdf(k, j, false, [](int, double p, double) { return p; }, uc, &Z, &dm);
         };
 
@@ -459,8 +804,13 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 if (tau == L) {
                     y = draw_target(0, L);
                 } else {
-                    y = icdf(0, tau, true, [](int, double p, double q) { return fmax(p - q, 0.0); },
-                             uc, &Z, &dm);
+                    if (T > 1) {
+                        team_cmd(0, tau, kTeamRes, 1, 1.0, 1.0, 0.0, 1.0, 0);
+                        y = team_icdf(uc, &Z, &dm);
+                    } else {
+                        y = icdf(0, tau, true, [](int, double p, double q) { return fmax(p - q, 0.0); },
+                                 uc, &Z, &dm);
+                    }
                     if (y < 0) {
                         flags |= kFlagDegenerate;
                         y = draw_target(0, tau);
@@ -492,6 +842,17 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 };
                 // beta(rho) = sum min(q, p/rho) and D(rho) = sum max(p - rho q, 0), one sweep
                 auto sums = [&](double rho, double &beta, double &D) {
+                    if (T > 1) {
+                        team_cmd(own, j, kTeamSSums, 1, 0.0, 0.0, 0.0, rho, 0);
+                        team_run();
+                        beta = 0.0;
+                        D = 0.0;
+                        for (int m = 0; m < T; ++m) {
+                            beta += sh.tp[0][m];
+                            D += sh.tp[1][m];
+                        }
+                        return;
+                    }
                     const int c = s_can[own * L1 + j];
                     const int sp = stats(true, own, j), sq = stats(false, own, j);
                     const RD P = row(true, c, j), Q = row(false, c, j);
@@ -623,9 +984,14 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                     double beta = beta_rho, D;
                     if (!isfinite(beta)) sums(rho, beta, D);
                     const double cc = c_of(beta);
-                    y = icdf(own, j, true, [&](int, double p, double q) {
-                        return fmax(p - cc * fmin(q, p / rho), 0.0);
-                    }, uc, &Z, &dm);
+                    if (T > 1) {
+                        team_cmd(own, j, kTeamSRes, 1, 0.0, 0.0, cc, rho, 0);
+                        y = team_icdf(uc, &Z, &dm);
+                    } else {
+                        y = icdf(own, j, true, [&](int, double p, double q) {
+                            return fmax(p - cc * fmin(q, p / rho), 0.0);
+                        }, uc, &Z, &dm);
+                    }
                     if (y < 0) {
                         flags |= kFlagDegenerate;
                         y = draw_target(own, j);
@@ -654,6 +1020,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 return r;
             };
             auto node_mass = [&]() {
+                if (T > 1) return team_sweep(own, tau, alpha, beta, nH);
                 return sweep(own, tau, [&](int v, double p, double q) {
                     return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
                 });
@@ -688,9 +1055,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                             if (!(dc & kDecAccept)) continue;
                             if (m < L) {
                                 const double wm = w[m];
-                                R[m] = sweep(k, m, [&](int, double p, double q) {
-                                    return fmax(wm * p - q, 0.0);
-                                });
+                                R[m] = T > 1 ? team_sweep(k, m, wm, 1.0, 0)
+                                             : sweep(k, m, [&](int, double p, double q) {
+                                                   return fmax(wm * p - q, 0.0);
+                                               });
                                 if (bad) break;
                             }
                             acc = m;
@@ -711,9 +1079,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                                 if (dc & kDecAccept) follow = false;
                                 continue;
                             }
-                            R[m] = sweep(k, m, [&](int, double p, double q) {
-                                return fmax(wm * p - q, 0.0);
-                            });
+                            R[m] = T > 1 ? team_sweep(k, m, wm, 1.0, 0)
+                                         : sweep(k, m, [&](int, double p, double q) {
+                                               return fmax(wm * p - q, 0.0);
+                                           });
                             if (bad) break;
                             const double d = R[m] + 1.0 - wm;
                             h = d > 0.0 ? R[m] / d : 1.0;
@@ -754,9 +1123,14 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 if (tau == L) {
                     y = draw_target(own, L);
                 } else {
-                    y = icdf(own, tau, true, [&](int v, double p, double q) {
-                        return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
-                    }, uc, &Z, &dm);
+                    if (T > 1) {
+                        team_cmd(own, tau, kTeamRes, 1, alpha, beta, 0.0, 1.0, nH);
+                        y = team_icdf(uc, &Z, &dm);
+                    } else {
+                        y = icdf(own, tau, true, [&](int v, double p, double q) {
+                            return in_H(v) ? 0.0 : fmax(alpha * p - beta * q, 0.0);
+                        }, uc, &Z, &dm);
+                    }
                     if (y < 0) {
                         flags |= kFlagDegenerate;
                         y = draw_target(own, tau);
@@ -789,16 +1163,36 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
     }
 }
 
-// One workgroup per listed request, grid-stride.
+// The listed requests: with at least two workgroups per request, a team of
+// T = min(grid / n, kTeamMax) per request (workgroup t*T runs it, the next T-1
+// sum ranges of its passes); otherwise one workgroup per request, grid-stride.
+// The grid is at most kRedoTeamSlots.
 template <int NT, typename RD, typename E>
 __global__ __launch_bounds__(NT) void redo_walk_kernel(RedoArgs A) {
     __shared__ RedoShared sh;
     const unsigned n = *A.count;
     if (n == 0) return;
-    for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {   // block-uniform
-        const int entry = A.list[i];
-        redo_request<NT, RD, E>(A, entry & ~kListNoReplay, entry,
-                                A.stats + static_cast<long long>(i) * A.K * (2 * A.L + 1), sh);
+    const int G = static_cast<int>(gridDim.x);
+    const int T = static_cast<long long>(n) * 2 <= G ? min(G / static_cast<int>(n), kTeamMax) : 1;
+    const long long per = static_cast<long long>(A.K) * (2 * A.L + 1);
+    if (T == 1) {
+        for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {   // block-uniform
+            const int entry = A.list[i];
+            redo_request<NT, RD, E>(A, entry & ~kListNoReplay, entry, A.stats + i * per, sh, 0, 1);
+        }
+        return;
+    }
+    const int team = blockIdx.x / T, m = blockIdx.x % T;
+    if (team >= static_cast<int>(n)) return;
+    const int entry = A.list[team];
+    const int b = entry & ~kListNoReplay;
+    if (m == 0) {
+        redo_request<NT, RD, E>(A, b, entry, A.stats + team * per, sh, team, T);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&A.team_cmd[team].seq, kTeamDone, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        team_member<NT, RD, E>(A, b, team, m, T, sh.cmd, sh.red, sh.ired, &sh.tseq);
     }
 }
 

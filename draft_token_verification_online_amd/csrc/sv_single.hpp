@@ -651,7 +651,7 @@ __global__ __launch_bounds__(NT) void single_final_kernel(SingleArgs A) {
         // a decision within the fp32 error of its threshold: the request is taken
         // again in fp64 here, its 2L+1 rows' statistics computed by this
         // workgroup (sv_redo.hpp; block-uniform)
-        if (!bad && (flags & kFlagNearTie)) redo_request<NT, RD, E>(ra, b, 0, nullptr, s_redo);
+        if (!bad && (flags & kFlagNearTie)) redo_request<NT, RD, E>(ra, b, 0, nullptr, s_redo, 0, 1);
     }
 }
 

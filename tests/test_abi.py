@@ -73,7 +73,9 @@ def test_workspace_size(lib):
     two = ws(512, 2, 8, 151936, sv.SV_BF16)
     assert two % 256 == 0 and 512 * 2 * 17 * 16 <= two < big - node_lists   # no node lists for K = 2
     assert ws(1, 1, 4, 32, sv.SV_F32) % 256 == 0 and ws(1, 1, 4, 32, sv.SV_F32) >= 9 * 16
-    assert ws(0, 1, 1, 1, sv.SV_F32) == 512   # the two list counters
+    # the two list counters, and 256 command (344 B) and partial (24 B) slots of the
+    # fp64 re-evaluation's teams
+    assert ws(0, 1, 1, 1, sv.SV_F32) == 512 + 256 * (344 + 24)
     for bad in [(1, 0, 4, 32), (1, 65, 4, 32), (1, 1, 0, 32), (1, 1, 17, 32), (1, 1, 4, 0),
                 (1, 1, 4, (1 << 22) + 1), (-1, 1, 4, 32)]:
         assert ws(*bad, sv.SV_F32) == 0, bad
