@@ -49,6 +49,7 @@ constexpr int kLmStages = 2;             // 2 x (two 256 x 64 tiles) = 128 KB
 constexpr int kLmTileElems = kLmBM * kLmStageK;
 constexpr int kLmDStep = kLmStageK;      // d must be a multiple
 constexpr int kLmDMin = 2 * kLmStageK;   // and at least the pipeline's last two stages
+constexpr int kLmPastEnd = 0x3ff80000;   // a column offset whose byte offset no buffer range covers
 constexpr int kLmGroupM = 8;             // row-blocks per group of the block order
 constexpr int kXcds = 8;
 
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     // the epilogue's per-row partials reuse stage 0 once the loop is done
     float(*s_m)[kLmBM] = reinterpret_cast<float(*)[kLmBM]>(&sT[0][0][0]);
     double(*s_s)[kLmBM] = reinterpret_cast<double(*)[kLmBM]>(&sT[0][1][0]);
+    __shared__ float s_temp[kLmBM];   // the tile rows' temperatures, read before the loop
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -165,6 +167,9 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     // 8 instructions each; lane l loads the chunk that belongs in slot l % 8 of
     // row l / 8.  Rows past the matrix read as zeros (hardware range check of
     // the buffer resource).
+    // (loaded here so the epilogue waits on no global load: a load there would
+    // also wait for every logits store before it)
+    s_temp[tid] = row0 + tid < R ? A.temp[row0 + tid] : 1.0f;   // kLmThreads == kLmBM
     int voff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -200,6 +205,23 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // Wait states after the MFMAs issued so far, before any accumulator is read
+    // or copied.  The compiler does not know the MFMAs are MFMAs, so it could
+    // place such a read (or a copy between registers, where it reshuffles them
+    // between the loop and the code after it) right behind the MFMA that writes
+    // it; every accumulator therefore passes through a volatile statement
+    // ordered after the wait states, and its later uses depend on that.
+    auto acc_fence = [&]() __attribute__((always_inline)) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                       "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
+#pragma unroll
+        for (int a = 0; a < 7; ++a)
+            asm volatile(""
+                         : "+a"(acc[a][0]), "+a"(acc[a][1]), "+a"(acc[a][2]), "+a"(acc[a][3]),
+                           "+a"(acc[a][4]), "+a"(acc[a][5]), "+a"(acc[a][6]), "+a"(acc[a][7]));
+    };
+
     // Regions of 32 columns: region s computes step s from fragments read
     // during region s-1 (register set s % 2) and reads step s+1's.  Stage J % 2
     // holds columns 64J .. 64J+63 (steps 2J, 2J+1).  Odd region 2J+1 issues the
@@ -222,7 +244,10 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     auto region = [&](int r, auto par, auto load, auto read) __attribute__((always_inline)) {
         constexpr int P = decltype(par)::value, Q = P ^ 1;   // P = r % 2
         constexpr bool LOAD = decltype(load)::value, READ = decltype(read)::value;
-        const int kl = ((r + 3) >> 1) * kLmStageK, sl = ((r + 3) >> 1) & 1;   // loads of stage-step (r+3)/2
+        // loads of stage-step (r+3)/2; past the last one, an offset no buffer
+        // reaches, so the loads return zeros without touching memory
+        const int kl = ((r + 3) >> 1) < nj ? ((r + 3) >> 1) * kLmStageK : kLmPastEnd;
+        const int sl = ((r + 3) >> 1) & 1;
         const int sn = ((r + 1) >> 1) & 1;   // stage of step r+1 (its half is Q)
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
@@ -257,23 +282,21 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     };
     using T = Flag<true>;
     using F = Flag<false>;
-    // pairs of regions (2J, 2J+1) while stage-step J+2 exists, then the last two pairs
-    int r = 0;
-    for (; (r >> 1) + 2 < nj; r += 2) {
+    // Every pair of regions is the same code, the last ones included: their loads
+    // past the last stage-step return zeros from outside every buffer, and their
+    // reads of fragments past the last step (into stages no MFMA then uses) read
+    // whatever is there.  (Separate code for the last regions would hold the
+    // accumulators in other registers, and the copies the compiler then makes
+    // cannot be kept clear of the MFMAs.)
+    for (int r = 0; r < nk; r += 2) {   // nk is even
         region(r, Par<0>{}, F{}, T{});
         region(r + 1, Par<1>{}, T{}, T{});
+        // wait states inside the loop, so that any copy the compiler places after
+        // it follows them (~1% of a pair of regions)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
-    region(r, Par<0>{}, F{}, T{});
-    region(r + 1, Par<1>{}, F{}, T{});
-    region(r + 2, Par<0>{}, F{}, T{});
-    region(r + 3, Par<1>{}, F{}, F{});
+    acc_fence();
     (void)nk;
-    // wait states before the accumulators are read: the last MFMAs issued are
-    // those of row a = 7, ordered before the reads through their operands
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
-                   "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7]));
-
     // epilogue: lane holds, of tile (a, b), the vocabulary entries
     // a*16 + 4*(lane/16) + i (i = 0..3) of hidden row b*16 + lane%16.  The
     // statistics describe the logits as stored (rounded to bf16 when they are).
@@ -283,59 +306,76 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     };
     // (b is a template constant: a loop this large is not unrolled, and any
     // runtime index into acc would put it in scratch memory)
+    // Column tests are selects, not branches (a branch per element costs more
+    // than the element's arithmetic); the stores are guarded only in tiles that
+    // reach past R or V (the test below is the same for the whole workgroup).
+    const bool full = vec && row0 + kLmBM <= R && col0 + kLmBN <= V;
     auto epilogue_rows = [&](auto bc) __attribute__((always_inline)) {
         constexpr int b = decltype(bc)::value;
         const int rloc = wh * 128 + b * 16 + (lane & 15);
         const int row = row0 + rloc;
         const bool rok = row < R;
         float m = -INFINITY;
+        float v[8][4];
+        bool ok[8][4];
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             const int col = col0 + wv * 128 + a * 16 + 4 * (lane >> 4);
-            const long long at = static_cast<long long>(row) * V + col;
-            if (A.bf16_out) {
-                uint16_t hb[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) hb[i] = bf16_rne(acc[a][b][i]);
-                if (rok) {
+            for (int i = 0; i < 4; ++i) {
+                ok[a][i] = col + i < V;
+                v[a][i] = stored(acc[a][b][i]);
+                m = fmaxf(m, ok[a][i] ? v[a][i] : -INFINITY);
+            }
+            const long long at = static_cast<long long>(row) * V + col;
+            if (full) {
+                if (A.bf16_out) {
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(A.logits) + at) =
+                        make_uint2((__float_as_uint(v[a][0]) >> 16) | (__float_as_uint(v[a][1]) & 0xffff0000u),
+                                   (__float_as_uint(v[a][2]) >> 16) | (__float_as_uint(v[a][3]) & 0xffff0000u));
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(A.logits) + at) =
+                        make_float4(v[a][0], v[a][1], v[a][2], v[a][3]);
+                }
+            } else if (rok) {
+                if (A.bf16_out) {
                     uint16_t *o = static_cast<uint16_t *>(A.logits) + at;
-                    if (vec && col + 3 < V) {
+                    uint16_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hb[i] = static_cast<uint16_t>(__float_as_uint(v[a][i]) >> 16);
+                    if (vec && ok[a][3]) {
                         *reinterpret_cast<uint2 *>(o) =
                             make_uint2(hb[0] | (static_cast<uint32_t>(hb[1]) << 16),
                                        hb[2] | (static_cast<uint32_t>(hb[3]) << 16));
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (col + i < V) o[i] = hb[i];
+                            if (ok[a][i]) o[i] = hb[i];
+                    }
+                } else {
+                    float *o = static_cast<float *>(A.logits) + at;
+                    if (vec && ok[a][3]) {
+                        *reinterpret_cast<float4 *>(o) = make_float4(v[a][0], v[a][1], v[a][2], v[a][3]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (ok[a][i]) o[i] = v[a][i];
                     }
                 }
-            } else if (rok) {
-                float *o = static_cast<float *>(A.logits) + at;
-                if (vec && col + 3 < V) {
-                    *reinterpret_cast<float4 *>(o) =
-                        make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (col + i < V) o[i] = acc[a][b][i];
-                }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (col + i < V) m = fmaxf(m, stored(acc[a][b][i]));
         }
         m = fmaxf(m, __shfl_xor(m, 16, kWave));
         m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const Scale sc = temp_scale(rok ? A.temp[row] : 1.0f);
+        const Scale sc = temp_scale(s_temp[rloc]);
         const float msc = shift_term(m, sc);
         float e = 0.0f;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            const int col = col0 + wv * 128 + a * 16 + 4 * (lane >> 4);
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (col + i < V) e += fast_exp2(expo(stored(acc[a][b][i]), sc, msc));
-        }
+            for (int i = 0; i < 4; ++i) {
+                const float x = fast_exp2(expo(v[a][i], sc, msc));
+                e += ok[a][i] ? x : 0.0f;
+            }
         double s = static_cast<double>(e);
         s += __shfl_xor(s, 16, kWave);
         s += __shfl_xor(s, 32, kWave);
@@ -356,7 +396,7 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     {
         const int row = row0 + tid;   // kLmThreads == kLmBM
         if (row < R) {
-            const Scale sc = temp_scale(A.temp[row]);
+            const Scale sc = temp_scale(s_temp[tid]);
             const float m0 = s_m[0][tid], m1 = s_m[1][tid];
             const float M = fmaxf(m0, m1);
             const double Mc = static_cast<double>(shift_term(M, sc));
