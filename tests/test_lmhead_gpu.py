@@ -195,3 +195,44 @@ def test_bf16_lm_head_feeds_verification(method):
                                  "draft": _bits(drf).reshape(B, K, L, V), "tokens": tok,
                                  "temperature": Th, "u_accept": ua, "u_correct": uc})
     pt.check(pt.compare(method, out, ref, list(range(B)), label=f"lm_head_bf16/{method}"))
+
+
+@pytest.mark.parametrize("ldt", [torch.float32, torch.bfloat16])
+def test_lm_head_at_the_bench_target_shape(ldt):
+    """The bench's target LM head (36 864 rows, d = 3 584, V = 151 936), in the launch
+    configuration bench.py times: sampled rows (first and last of the grid, the
+    last row-block, rows in the partial last column block) against the oracle's
+    float64 product over the whole vocabulary, and their statistics."""
+    from scipy.special import logsumexp
+    R, d, V, T = 36864, 3584, 151936, 0.4
+    print(f"[case] lm_head bench shape R={R} d={d} V={V} {ldt}", flush=True)
+    h, w = _make(R, d, V, 7)
+    temps = torch.full((R,), T, device="cuda") * (1 + 0.5 * (torch.arange(R, device="cuda") % 3))
+    stats = torch.zeros(R * 16, dtype=torch.uint8, device="cuda")
+    lm = LmHead(R, d, V, logits_dtype=ldt)
+    logits = lm(h, w, temps, stats=stats)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 18437, R - 257, R - 1])
+    hb = _bits(h[torch.as_tensor(rows, device="cuda")])
+    wb = _bits(w)
+    tt = temps.cpu().numpy().astype(np.float64)[rows]
+    ref, lse_ref = oracle.lm_head(hb, wb, tt)
+    acc_bound = _bound(hb, wb)
+    bound = acc_bound
+    got_t = logits[torch.as_tensor(rows, device="cuda")]
+    if ldt == torch.bfloat16:
+        got = oracle.bf16_bits_to_f64(_bits(got_t))
+        bound = bound + (np.abs(ref) + bound) * 2.0 ** -8
+        lse_want = logsumexp(got / tt[:, None], axis=1)   # statistics of the stored values
+        tol = 1e-6 * np.maximum(1.0, np.abs(lse_want))
+    else:
+        got = got_t.cpu().numpy().astype(np.float64)
+        lse_want = lse_ref
+        tol = acc_bound.max(axis=1) / tt + 1e-6 * np.maximum(1.0, np.abs(lse_ref))
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float((err / np.maximum(bound, 1e-300)).max())
+    raw = stats.view(-1, 16)[torch.as_tensor(rows, device="cuda")].reshape(-1)
+    lse_gpu = _stats_lse(raw, len(rows), tt)
+    assert (np.abs(lse_gpu - lse_want) <= tol).all(), float(np.abs(lse_gpu - lse_want).max())
+    print(f"[parity] lm_head bench shape {ldt}: max logit err {err.max():.2e}, "
+          f"max lse err {np.abs(lse_gpu - lse_want).max():.2e}", flush=True)
