@@ -40,7 +40,7 @@ constexpr int kMaxB = 1 << 24;
 // listed requests, grid-stride.  With none listed every workgroup returns after
 // one load, so the grids are kept small (one workgroup per CU at most): most
 // calls list nothing.
-constexpr long long kRedoStatsGrid = 256;
+constexpr long long kRedoStatsGrid = 1024;   // up to four 512-thread workgroups per CU
 
 static_assert(SV_MAX_K == sv::kMaxK, "K limit");
 static_assert(SV_MAX_L == sv::kMaxL, "L limit");

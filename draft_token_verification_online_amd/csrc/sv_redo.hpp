@@ -221,6 +221,20 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
             dup |= same;
         }
         if (__syncthreads_or(dup)) continue;   // block-uniform
+        // Only rows of drafts the fast walk tested (a draft sharing the row's
+        // prefix [0, j) that has a test record): while the fp64 walk agrees with
+        // the records those are the rows it reads; one it reaches after a
+        // disagreement is computed by the re-walk itself when first read.
+        if (A.dec && !(A.list[i] & kListNoReplay)) {
+            const unsigned char *dk = A.dec + static_cast<long long>(b) * K * L;
+            int used = 0;
+            for (int c = k + tid; c < K; c += NT) {
+                int same = 1;
+                for (int t = 0; t < j; ++t) same &= (tk[c * L + t] == tk[k * L + t]);
+                for (int m = 0; m < L && same; ++m) used |= (dk[c * L + m] & kDecMade) != 0;
+            }
+            if (!__syncthreads_or(used)) continue;   // block-uniform
+        }
         const E *base = target
             ? static_cast<const E *>(A.tgt) + ((static_cast<long long>(b) * K + k) * L1 + j) * V
             : static_cast<const E *>(A.drf) + ((static_cast<long long>(b) * K + k) * L + j) * V;

@@ -776,6 +776,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void wa
         bad |= !(u >= 0.0f && u < 1.0f);
         if (A.round == 1) {
             if (A.accept_prob) A.accept_prob[bKL + i] = NAN;
+            if (A.dec) A.dec[bKL + i] = 0;   // this call's tests only
             need[i] = 0;
         }
     }
