@@ -69,12 +69,15 @@ __device__ __forceinline__ double exp2_d(double a) {
 }
 
 // fp64 statistics of one node row: pi(v) = 2^((l_v - M) cT - ls), cT = log2(e)/T,
-// ls = log2 sum_v 2^((l_v - M) cT).  ok = 0 for a row that is not a distribution.
+// ls = log2 sum_v 2^((l_v - M) cT).  ok = 0 for a row that is not a distribution;
+// kRedoStatAbsent for a row the statistics launch left out (computed by the
+// re-walk if it reads the row).
 struct RedoStat {
     double ls;
     float M;
     int ok;
 };
+constexpr int kRedoStatAbsent = 2;
 
 // Teams.  When few requests are listed, each gets a team of workgroups that
 // share its O(V) passes: the team's first workgroup runs the re-evaluation and,
@@ -220,11 +223,25 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
             for (int t = 0; t < j; ++t) same &= (tk[c * L + t] == tk[k * L + t]);
             dup |= same;
         }
-        if (__syncthreads_or(dup)) continue;   // block-uniform
+        // a row left out is marked absent, never left with another call's bytes
+        auto absent = [&]() {
+            if (tid == 0) {
+                RedoStat st;
+                st.ls = 0.0;
+                st.M = 0.0f;
+                st.ok = kRedoStatAbsent;
+                A.stats[it] = st;
+            }
+        };
+        if (__syncthreads_or(dup)) {   // block-uniform
+            absent();
+            continue;
+        }
         // Only rows of drafts the fast walk tested (a draft sharing the row's
         // prefix [0, j) that has a test record): while the fp64 walk agrees with
         // the records those are the rows it reads; one it reaches after a
-        // disagreement is computed by the re-walk itself when first read.
+        // disagreement is marked absent and computed by the re-walk itself when
+        // first read.
         if (A.dec && !(A.list[i] & kListNoReplay)) {
             const unsigned char *dk = A.dec + static_cast<long long>(b) * K * L;
             int used = 0;
@@ -233,7 +250,10 @@ __global__ __launch_bounds__(NT) void redo_stats_kernel(RedoArgs A) {
                 for (int t = 0; t < j; ++t) same &= (tk[c * L + t] == tk[k * L + t]);
                 for (int m = 0; m < L && same; ++m) used |= (dk[c * L + m] & kDecMade) != 0;
             }
-            if (!__syncthreads_or(used)) continue;   // block-uniform
+            if (!__syncthreads_or(used)) {   // block-uniform
+                absent();
+                continue;
+            }
         }
         const E *base = target
             ? static_cast<const E *>(A.tgt) + ((static_cast<long long>(b) * K + k) * L1 + j) * V
@@ -411,13 +431,15 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
         const E *drf = static_cast<const E *>(A.drf);
         for (int q = tid; q < K * L; q += NT) s_x[q] = A.tok[bKL + q];
         for (int q = tid; q < K * RS; q += NT) {
+            int have = 0;
             if (st) {
                 const RedoStat r = st[q];
+                have = r.ok != kRedoStatAbsent;
                 s_ok[q] = static_cast<unsigned char>(r.ok);
                 s_M[q] = r.M;
                 s_ls[q] = r.ls;
             }
-            s_have[q] = st ? 1 : 0;
+            s_have[q] = static_cast<unsigned char>(have);
         }
         __syncthreads();
         // node of (k, j): the lowest-index draft with the same first j tokens

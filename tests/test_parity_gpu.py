@@ -24,6 +24,9 @@ def _verify(method, batch, diagnostics=True):
     t = batch["target"]
     B, K, L1, V = t.shape
     v = Verifier(method, B, K, L1 - 1, V, t.dtype, diagnostics=diagnostics)
+    # the workspace's contents need not be initialised: every byte starts as NaN
+    # bits, so a value read before this call wrote it shows in the outputs
+    v.workspace.fill_(0xFF)
     out = v(batch["target"], batch["draft"], batch["tokens"], batch["temperature"],
             batch["u_accept"], batch["u_correct"])
     torch.cuda.synchronize()
@@ -317,9 +320,76 @@ def test_near_ties_are_taken_again_in_fp64(name, over, method):
     redone = (fl & SV_FLAG_REDONE) != 0
     assert ((fl[redone] & SV_FLAG_NEAR_TIE) != 0)[ref["margin"][redone] < 9e-6].all()
     assert ((fl[redone] & SV_FLAG_NEAR_TIE) == 0)[ref["margin"][redone] > 1.1e-5].all()
+    # A request taken again in fp64 takes exact arithmetic's decisions, also where
+    # they differ from the fast walk's and lead to drafts it never tested: it
+    # equals the oracle wherever the oracle's margin is far above double rounding
+    # (the parity bar above excuses every request within 1e-6).
+    g = {k: out[k].cpu().numpy() for k in ("accept_len", "draft_index", "correction")}
+    strict = np.nonzero(redone & (ref["margin"] > 1e-9))[0]
+    off = [int(b) for b in strict if any(int(g[k][b]) != int(ref[k][b]) for k in g)]
+    print(f"[near-tie] {name}: redone with margin > 1e-9: {len(strict)}, differing: {off[:8]}",
+          flush=True)
+    assert not off, (name, off[:8])
 
 
 
+
+@pytest.mark.parametrize("diagnostics", [False, True], ids=["plain", "diagnostics"])
+def test_fp64_walk_reaches_drafts_the_fast_walk_never_tested(diagnostics):
+    """Two drafts of two tokens.  Draft 0's first token is less likely under the
+    target than under the draft (w_1 < 1), its test at position 1 rejects
+    (u = 1 - 2^-24 > h_1), and its test at the last position gets u = the float32
+    rounding of the exact w_2 (margins ~1e-8 of either sign), so every such
+    request is taken again in fp64 and about half of them reject draft 0 and go
+    on to draft 1.  Where the fast walk took the other side of such a test, the
+    fp64 walk reaches draft 1's node rows at position 1, which the fast walk
+    never needed and the fp64 statistics launch leaves out: the re-walk must
+    compute them rather than read the workspace (filled with NaN bits).  Every
+    request taken again equals the oracle exactly (its margins are far above
+    double rounding)."""
+    B, K, L, V = 96, 2, 2, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    tgt = torch.randn((B, K, L + 1, V), generator=g, device="cuda") * 2.0
+    drf = tgt[:, :, :L] + torch.randn((B, K, L, V), generator=g, device="cuda") * 0.5
+    tokens = torch.randint(0, V, (B, K, L), generator=g, device="cuda", dtype=torch.int32)
+    tokens[:, 1, 0] = (tokens[:, 0, 0] + 1 + torch.randint(0, V - 1, (B,), generator=g,
+                                                           device="cuda", dtype=torch.int32)) % V
+    # the root is one node: both drafts read the same row pair there
+    tgt[:, 1, 0] = tgt[:, 0, 0]
+    drf[:, 1, 0] = drf[:, 0, 0]
+    a = tokens[:, 0, 0].long()
+    idx = torch.arange(B, device="cuda")
+    drf[idx, 0, 0, a] = tgt[idx, 0, 0, a] + 1.0
+    drf[idx, 1, 0, a] = drf[idx, 0, 0, a]
+    ua = torch.rand((B, K, L), generator=g, device="cuda")
+    ua[:, 0, 0] = float(np.float32(1.0) - np.float32(2.0 ** -24))
+    batch = {"target": tgt.to(torch.bfloat16).contiguous(),
+             "draft": drf.to(torch.bfloat16).contiguous(), "tokens": tokens.contiguous(),
+             "temperature": torch.ones((B,), device="cuda"),
+             "u_accept": ua.contiguous(),
+             "u_correct": torch.rand((B,), generator=g, device="cuda")}
+    w2 = pt.run_oracle("multidraft", synth.to_host(batch), diagnostics=True)["accept_prob"][:, 0, L - 1]
+    placed, rejects = 0, 0
+    for b in range(B):
+        if 0.05 < w2[b] < 0.95:
+            ua[b, 0, L - 1] = float(np.float32(w2[b]))
+            placed += 1
+            rejects += float(np.float32(w2[b])) > w2[b]   # exact arithmetic rejects draft 0 there
+    assert placed >= 48 and rejects >= 16, (placed, rejects)
+    batch["u_accept"] = ua.contiguous()
+    rep, out, ref = _parity("multidraft", batch, f"fp64_reaches_untested/{diagnostics}",
+                            diagnostics=diagnostics)
+    from draft_token_verification_online_amd import SV_FLAG_REDONE
+    fl = out["flags"].cpu().numpy()
+    redone = (fl & SV_FLAG_REDONE) != 0
+    got = {k: out[k].cpu().numpy() for k in ("accept_len", "draft_index", "correction")}
+    strict = np.nonzero(redone & (ref["margin"] > 1e-10))[0]
+    off = [int(b) for b in strict if any(int(got[k][b]) != int(ref[k][b]) for k in got)]
+    print(f"[fp64-untested] placed={placed} exact rejects={rejects} redone={int(redone.sum())} "
+          f"strict={len(strict)} differing: {off[:8]}", flush=True)
+    assert len(strict) >= 16, len(strict)
+    assert not off, off[:8]
 
 # ------------------------------------------------------- one draft, split-V
 # With K = 1 every call runs the single-draft kernels: slices of 1024 chunks
