@@ -91,6 +91,7 @@ constexpr int kRedoStatAbsent = 2;
 // kTeamIdleTicks leaves.  Commands and partials go through device memory with
 // agent-scope release and acquire (relaxed polls).
 constexpr int kTeamMax = 16;                  // workgroups per team
+constexpr int kTeamDepth = 4;                 // chunks per thread in flight in a member's range
 constexpr int kTeamDone = 0x7fffffff;         // command number that ends a team
 constexpr long long kTeamWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
 constexpr long long kTeamIdleTicks = 200000;  // 2 ms
@@ -275,8 +276,9 @@ __device__ __forceinline__ double team_weight(const TeamBody &d, int v, double p
 
 // A team command's sums over chunks [q0, q1) of its node's rows (block-uniform;
 // every thread returns them): out[0] (and for kTeamSSums out[1]); *last the last
-// token of positive weight (-1: none).  Chunks are taken two per thread at a
-// time, strided by the block, the order of the single-workgroup sweep.
+// token of positive weight (-1: none).  Chunks are strided by the block, the
+// order of the single-workgroup sweep, with up to kTeamDepth per thread in
+// flight (a 16-member team's range of a 151 936-token row in one round).
 template <int NT, typename RD, typename E>
 __device__ void team_slice(const RedoArgs &A, int b, const TeamBody &d, int q0, int q1,
                            double out[2], int *last, double *s_red, int *s_ired) {
@@ -293,17 +295,17 @@ __device__ void team_slice(const RedoArgs &A, int b, const TeamBody &d, int q0, 
     const double ir = sums ? 1.0 / d.rho : 0.0;
     double v0 = 0.0, v1 = 0.0;
     int lp = -1;
-    for (int qa = q0 + tid; qa < q1; qa += 2 * NT) {   // loads issued ahead
-        typename RD::Raw rp[2], rq[2];
+    for (int qa = q0 + tid; qa < q1; qa += kTeamDepth * NT) {   // loads issued ahead
+        typename RD::Raw rp[kTeamDepth], rq[kTeamDepth];
 #pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
+        for (int e2 = 0; e2 < kTeamDepth; ++e2) {
             if (qa + e2 * NT < q1) {
                 rp[e2] = P.raw(qa + e2 * NT);
                 if (d.with_q) rq[e2] = Q.raw(qa + e2 * NT);
             }
         }
 #pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
+        for (int e2 = 0; e2 < kTeamDepth; ++e2) {
             const int q = qa + e2 * NT;
             if (q >= q1) break;
             float xp[8], xq[8];
@@ -392,6 +394,8 @@ struct RedoShared {
     double ls[kMaxK * (2 * kMaxL + 1)];
     int H[kMaxK];
     unsigned char made[kMaxK * kMaxL];   // tests of the final path (accept_prob entries kept)
+    float gp[kMaxK * kMaxL], gq[kMaxK * kMaxL];   // drafted tokens' logits in their nodes' rows
+    unsigned char dec[kMaxK * kMaxL];    // the fast walk's test records
     double w[kMaxL + 1], R[kMaxL + 1];   // GBV's weight chain and residual sums
     double red[16];
     float fred[16];
@@ -459,6 +463,22 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                           : RD(drf + ((static_cast<long long>(b) * K + c) * L + j) * V, V);
         };
         auto slot = [&](bool target, int c, int j) { return c * RS + (target ? j : L1 + j); };
+        // every drafted token's logit in its node's target and draft rows, and
+        // the fast walk's test records, in one round of loads (the walk below
+        // reads them one position at a time)
+        for (int q = tid; q < K * L; q += NT) {
+            const int k = q / L, j = q % L, x = s_x[q];
+            float gp = NAN, gq = NAN;
+            if (x >= 0 && x < V) {
+                const int c = s_can[k * L1 + j];
+                gp = row(true, c, j).at(x);
+                gq = row(false, c, j).at(x);
+            }
+            sh.gp[q] = gp;
+            sh.gq[q] = gq;
+            sh.dec[q] = A.dec ? A.dec[bKL + q] : 0;
+        }
+        __syncthreads();
         int bad = 0;
         // node row (target?, node of (k, j)): its slot, its statistics computed
         // here when not given; an invalid row marks the request
@@ -482,10 +502,10 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
         auto prob = [&](int sl, float x) {
             return exp2_d(fma(static_cast<double>(x) - static_cast<double>(s_M[sl]), cT, -s_ls[sl]));
         };
-        auto prob_at = [&](bool target, int k, int j, int x) {
+        // p or q of draft k's token at position j, in the row of its node (k, j)
+        auto prob_tok = [&](bool target, int k, int j) {
             const int sl = stats(target, k, j);
-            const int c = s_can[k * L1 + j];
-            return prob(sl, row(target, c, j).at(x));
+            return prob(sl, target ? sh.gp[k * L + j] : sh.gq[k * L + j]);
         };
         // block-wide sum of f(v, p(v), q(v)) over node (k, j)'s row pair
         auto sweep = [&](int k, int j, auto f) {
@@ -829,8 +849,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
         if (A.method == kMethodToken) {
             tau = L;
             for (int j = 0; j < L && !bad; ++j) {
-                const int x = s_x[j];
-                const double p = prob_at(true, 0, j, x), q = prob_at(false, 0, j, x);
+                const double p = prob_tok(true, 0, j), q = prob_tok(false, 0, j);
                 double a = ratio(p, q);
                 if (a > 1.0) a = 1.0;
                 if (!test(0, j + 1, a)) { tau = j; break; }
@@ -938,7 +957,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 if (replay) {
                     for (int k = 0; k < K && rec_acc < 0 && replay; ++k) {
                         if (!same_prefix(k, own, j)) continue;
-                        const int dc = A.dec[bKL + k * L + j];
+                        const int dc = sh.dec[k * L + j];
                         if (!(dc & kDecMade) || !(dc & kDecCertain)) replay = false;
                         else if (dc & kDecAccept) rec_acc = k;
                     }
@@ -1005,13 +1024,13 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                 int acc = -1;
                 for (int k = 0; k < K && acc < 0; ++k) {
                     if (!same_prefix(k, own, j)) continue;
-                    const int x = s_x[k * L + j];
-                    const double p = prob_at(true, own, j, x), q = prob_at(false, own, j, x);
+                    // draft k shares node (own, j): its token's p and q there
+                    const double p = prob_tok(true, k, j), q = prob_tok(false, k, j);
                     double a = ratio(p, rho * q);
                     if (a > 1.0) a = 1.0;
                     const bool ak = test(k, j + 1, a);
                     if (follow && n > 1) {
-                        const int dc = A.dec[bKL + k * L + j];
+                        const int dc = sh.dec[k * L + j];
                         if (!(dc & kDecMade) || ak != ((dc & kDecAccept) != 0)) follow = false;
                     }
                     if (ak) acc = k;
@@ -1074,17 +1093,16 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                     N = node_mass();
                 } else {
                     // first position: the node residual omega / N against q_s
-                    const double ps = prob_at(true, own, tau, x), qs = prob_at(false, own, tau, x);
+                    const double ps = prob_tok(true, k, tau), qs = prob_tok(false, k, tau);
                     const double om = fmax(alpha * ps - beta * qs, 0.0);
                     w[tau + 1] = chain(1.0, om / N, qs);
                     for (int j = tau + 1; j < L; ++j) {
-                        const int xj = s_x[k * L + j];
-                        w[j + 1] = chain(w[j], prob_at(true, k, j, xj), prob_at(false, k, j, xj));
+                        w[j + 1] = chain(w[j], prob_tok(true, k, j), prob_tok(false, k, j));
                     }
                     if (bad) break;
                     int acc = 0;
                     for (int m = L; m > tau; --m) {
-                        const int dc = follow ? A.dec[bKL + k * L + m - 1] : 0;
+                        const int dc = follow ? sh.dec[k * L + m - 1] : 0;
                         if (follow && !(dc & kDecMade)) follow = false;
                         if (follow && (dc & kDecCertain)) {
                             s_made[k * L + m - 1] = 1;
