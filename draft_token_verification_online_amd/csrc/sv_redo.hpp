@@ -90,7 +90,7 @@ constexpr int kRedoStatAbsent = 2;
 // (the team then works alone), and a member that has seen no command for
 // kTeamIdleTicks leaves.  Commands and partials go through device memory with
 // agent-scope release and acquire (relaxed polls).
-constexpr int kTeamMax = 16;                  // workgroups per team
+constexpr int kTeamMax = 32;                  // workgroups per team
 constexpr int kTeamDepth = 4;                 // chunks per thread in flight in a member's range
 constexpr int kTeamDone = 0x7fffffff;         // command number that ends a team
 constexpr long long kTeamWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
@@ -278,7 +278,7 @@ __device__ __forceinline__ double team_weight(const TeamBody &d, int v, double p
 // every thread returns them): out[0] (and for kTeamSSums out[1]); *last the last
 // token of positive weight (-1: none).  Chunks are strided by the block, the
 // order of the single-workgroup sweep, with up to kTeamDepth per thread in
-// flight (a 16-member team's range of a 151 936-token row in one round).
+// flight (a range of a 16th of a 151 936-token row, or less, in one round).
 template <int NT, typename RD, typename E>
 __device__ void team_slice(const RedoArgs &A, int b, const TeamBody &d, int q0, int q1,
                            double out[2], int *last, double *s_red, int *s_ired) {
