@@ -178,11 +178,8 @@ hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t s
     return hipGetLastError();
 }
 
-// after_stats: an event recorded on the stream once the first row-statistics
-// launch is queued (the batch-halves schedule below starts its second half there).
 template <typename E, bool VEC>
-hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln, int method,
-                  hipEvent_t after_stats = nullptr) {
+hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln, int method) {
     using RD = typename sv::RowOf<E, VEC>::type;
     hipStream_t stream = static_cast<hipStream_t>(ln->stream);
     const bool diagnostics = out->row_lse != nullptr;
@@ -270,7 +267,6 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = record(ln, 1, stream)) != hipSuccess) return err;
-    if (after_stats && (err = hipEventRecord(after_stats, stream)) != hipSuccess) return err;
     auto walk = [&]() {
         if (spectr)
             hipLaunchKernelGGL((sv::walk_kernel<kWalkThreads, RD, E, true>), dim3(in->B),
@@ -303,23 +299,10 @@ hipError_t launch(const sv_inputs *in, const sv_outputs *out, const sv_launch *l
     return record(ln, 4, stream);
 }
 
-// SpecTr over K > 1 drafts and at least kSplitMinB requests runs as two halves
-// of the batch on two streams (below), each half with a layout of its own: the
-// first half's at offset 0, the second's at split_offset.
-constexpr int kSplitMinB = 512;
-size_t split_offset(int32_t B, int32_t K, int32_t L) {
-    return align_up(layout(B / 2, K, L).total, 256);
-}
-
-// Bytes of workspace a call needs: the walk's layout (or the two halves' when
-// a SpecTr call of that size would split the batch, whichever is larger), or for
-// one draft the single-draft layout when it is larger (never used together).
+// Bytes of workspace a call needs: the walk's layout, or for one draft the
+// single-draft layout when it is larger (the two are never used together).
 size_t workspace_total(int32_t B, int32_t K, int32_t L, int32_t V) {
     size_t n = layout(B, K, L).total;
-    if (K > 1 && B >= kSplitMinB) {
-        const size_t s = split_offset(B, K, L) + layout(B - B / 2, K, L).total;
-        if (s > n) n = s;
-    }
     if (K == 1) {
         const size_t s = single_layout(B, L, V).total;
         if (s > n) n = s;
@@ -384,92 +367,6 @@ hipError_t launch_single(const sv_inputs *in, const sv_outputs *out, const sv_la
     return hipSuccess;
 }
 
-// The second stream and the two events of the batch-halves schedule, one set
-// per device, made on first use (a non-blocking stream of default priority);
-// `mu` keeps one caller's fork and join from interleaving with another's.
-struct SplitRes {
-    hipStream_t s1 = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool made = false;
-    std::mutex mu;
-};
-constexpr int kSplitDevices = 64;
-SplitRes g_split[kSplitDevices];
-std::mutex g_split_make_mu;
-
-SplitRes *split_res(hipStream_t stream) {
-    int dev = -1;
-    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    if (dev < 0 || dev >= kSplitDevices) return nullptr;
-    std::lock_guard<std::mutex> lock(g_split_make_mu);
-    SplitRes &r = g_split[dev];
-    if (r.made) return &r;
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
-    const bool ok = hipStreamCreateWithFlags(&r.s1, hipStreamNonBlocking) == hipSuccess &&
-                    hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) == hipSuccess &&
-                    hipEventCreateWithFlags(&r.join, hipEventDisableTiming) == hipSuccess;
-    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
-    if (!ok) return nullptr;
-    r.made = true;
-    return &r;
-}
-
-// SpecTr over a large batch: its two halves verified one after the other in
-// time but overlapped, the second half (on the library's second stream) starting
-// when the first half's row-statistics launch is queued, so that one half's walk
-// (arithmetic: its scaling-factor searches) runs beside the other half's row
-// statistics (HBM).  Every request's result is the one the whole-batch call
-// gives (requests are independent); the caller's stream waits for both halves.
-// Phase events [0]-[3] mark the first half's phases; [4] the end of both.
-template <typename E, bool VEC>
-hipError_t launch_split(const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
-                        int method) {
-    hipStream_t stream = static_cast<hipStream_t>(ln->stream);
-    SplitRes *r = split_res(stream);
-    if (!r) return launch<E, VEC>(in, out, ln, method);   // no second stream: one sequence
-    std::lock_guard<std::mutex> lock(r->mu);
-    const long long K = in->K, L = in->L, V = in->V;
-    const long long es = in->dtype == SV_F32 ? 4 : 2;
-    const int half[2][2] = {{0, in->B / 2}, {in->B / 2, in->B - in->B / 2}};
-    sv_inputs h[2] = {*in, *in};
-    sv_outputs o[2] = {*out, *out};
-    for (int i = 0; i < 2; ++i) {
-        const long long b = half[i][0];
-        h[i].B = half[i][1];
-        h[i].target_logits = static_cast<const char *>(in->target_logits) + b * K * (L + 1) * V * es;
-        h[i].draft_logits = static_cast<const char *>(in->draft_logits) + b * K * L * V * es;
-        h[i].draft_tokens = in->draft_tokens + b * K * L;
-        h[i].temperature = in->temperature + b;
-        h[i].u_accept = in->u_accept + b * K * L;
-        h[i].u_correct = in->u_correct + b;
-        o[i].accept_len = out->accept_len + b;
-        o[i].draft_index = out->draft_index + b;
-        o[i].correction = out->correction + b;
-        o[i].flags = out->flags ? out->flags + b : nullptr;
-        o[i].accept_prob = out->accept_prob ? out->accept_prob + b * K * L : nullptr;
-        o[i].resid_mass = out->resid_mass ? out->resid_mass + b : nullptr;
-        o[i].rows_streamed = out->rows_streamed ? out->rows_streamed + b : nullptr;
-    }
-    const size_t off = split_offset(in->B, in->K, in->L);
-    sv_launch l0 = *ln, l1 = *ln;
-    l0.workspace_bytes = off;
-    l0.phase_events[4] = nullptr;
-    l1.stream = r->s1;
-    l1.workspace = static_cast<char *>(ln->workspace) + off;
-    l1.workspace_bytes = ln->workspace_bytes - off;
-    for (int i = 0; i < 5; ++i) l1.phase_events[i] = nullptr;
-    hipError_t err;
-    if ((err = launch<E, VEC>(&h[0], &o[0], &l0, method, r->fork)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(r->s1, r->fork, 0)) != hipSuccess) return err;
-    if ((err = launch<E, VEC>(&h[1], &o[1], &l1, method)) != hipSuccess) return err;
-    if ((err = hipEventRecord(r->join, r->s1)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(stream, r->join, 0)) != hipSuccess) return err;
-    return record(ln, 4, stream);
-}
-
 int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_launch *ln,
            bool single_draft) {
     if (!in || !out || !ln) return SV_EINVAL;
@@ -503,14 +400,7 @@ int verify(int method, const sv_inputs *in, const sv_outputs *out, const sv_laun
                       : launch_single<float, false>(in, out, ln, m1);
         return err == hipSuccess ? SV_OK : SV_EHIP;
     }
-    const bool split = (method == sv::kMethodSpecTr || method == sv::kMethodSpecTrBisect) &&
-                       in->K > 1 && in->B >= kSplitMinB && !in->row_stats && !out->row_lse;
-    if (split)
-        err = in->dtype == SV_BF16 ? (vec ? launch_split<uint16_t, true>(in, out, ln, method)
-                                          : launch_split<uint16_t, false>(in, out, ln, method))
-                                   : (vec ? launch_split<float, true>(in, out, ln, method)
-                                          : launch_split<float, false>(in, out, ln, method));
-    else if (in->dtype == SV_BF16)
+    if (in->dtype == SV_BF16)
         err = vec ? launch<uint16_t, true>(in, out, ln, method)
                   : launch<uint16_t, false>(in, out, ln, method);
     else

@@ -391,23 +391,6 @@ def test_fp64_walk_reaches_drafts_the_fast_walk_never_tested(diagnostics):
     assert len(strict) >= 16, len(strict)
     assert not off, off[:8]
 
-SPLIT_CASES = [("v4096_vec", 4096), ("v4099_scalar", 4099)]
-
-
-@pytest.mark.parametrize("method", ["spectr", "spectr_bisect"])
-@pytest.mark.parametrize("name,V", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
-def test_spectr_batch_halves(name, V, method):
-    """SpecTr over at least 512 requests runs as two halves of the batch on two
-    streams; an odd batch gives halves of 256 and 257.  Every request equals
-    the oracle, and the call equals itself when repeated on a workspace filled
-    with NaN bits (the halves' layouts are disjoint)."""
-    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], B=513, V=V)
-    batch = pt.gpu_batch(ws, 77)
-    rep, out, ref = _parity(method, batch, f"spectr_halves/{name}", diagnostics=False)
-    again = _verify(method, batch, diagnostics=False)
-    for k in ("accept_len", "draft_index", "correction", "flags"):
-        assert torch.equal(out[k], again[k]), k
-
 # ------------------------------------------------------- one draft, split-V
 # With K = 1 every call runs the single-draft kernels: slices of 1024 chunks
 # (8192 tokens) per workgroup, residual sums per (position, slice), the draw's
