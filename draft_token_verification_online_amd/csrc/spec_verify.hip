@@ -18,6 +18,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -129,6 +130,18 @@ __global__ void reset_count_kernel(unsigned *count) {
     if (threadIdx.x == 0) *count = 0u;
 }
 
+// How long a team's first workgroup waits for its members' answers to a command
+// (real-time counter ticks, 100 MHz) before it sums their ranges itself: 200 us,
+// or SV_TEAM_WAIT_TICKS when that is set (tests set 0 to make every command take
+// the fallback; the results do not depend on it).
+long long team_wait_ticks() {
+    const char *e = std::getenv("SV_TEAM_WAIT_TICKS");
+    if (!e || !*e) return sv::kTeamWaitTicks;
+    char *end = nullptr;
+    const long long v = std::strtoll(e, &end, 10);
+    return (end && *end == '\0' && v >= 0 && v <= sv::kTeamWaitTicks) ? v : sv::kTeamWaitTicks;
+}
+
 // Requests the fast path listed (a decision within the fp32 error of its
 // threshold), taken again in fp64: their node rows' statistics over the whole
 // chip, then one workgroup per request.  `stats` is a region of at least
@@ -161,6 +174,7 @@ hipError_t launch_redo(const sv_inputs *in, const sv_outputs *out, hipStream_t s
     ra.flags = out->flags;
     ra.accept_prob = out->accept_prob;
     ra.resid_mass = out->resid_mass;
+    ra.team_wait = team_wait_ticks();
     ra.team_cmd = static_cast<sv::TeamCmd *>(team);
     ra.team_part = reinterpret_cast<sv::TeamPart *>(static_cast<char *>(team) +
                                                     sv::kRedoTeamSlots * sizeof(sv::TeamCmd));

@@ -94,6 +94,7 @@ constexpr int kTeamMax = 32;                  // workgroups per team
 constexpr int kTeamDepth = 4;                 // chunks per thread in flight in a member's range
 constexpr int kTeamDone = 0x7fffffff;         // command number that ends a team
 constexpr long long kTeamWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
+                                              // (the default of RedoArgs::team_wait)
 constexpr long long kTeamIdleTicks = 200000;  // 2 ms
 constexpr int kTeamRes = 0;    // [v not in H] max(a p - bq q, 0)   (q = 0 without the draft row)
 constexpr int kTeamSRes = 1;   // max(p - cc min(q, p / rho), 0)    (SpecTr residual)
@@ -135,6 +136,8 @@ struct RedoArgs {
     float *accept_prob, *resid_mass;
     TeamCmd *team_cmd;            // [kRedoTeamSlots]: one per team
     TeamPart *team_part;          // [kRedoTeamSlots]: team t's members at t*T ..
+    long long team_wait;          // ticks the first workgroup waits for its members'
+                                  // answers to a command before summing their ranges itself
 };
 
 // Slots of the team areas (the re-evaluation launch's grid bound).
@@ -662,7 +665,7 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                     const int want = tseq * (T - 1);
                     const long long t0 = static_cast<long long>(__builtin_amdgcn_s_memrealtime());
                     while (__hip_atomic_load(&gc->acks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want &&
-                           static_cast<long long>(__builtin_amdgcn_s_memrealtime()) - t0 <= kTeamWaitTicks)
+                           static_cast<long long>(__builtin_amdgcn_s_memrealtime()) - t0 <= A.team_wait)
                         __builtin_amdgcn_s_sleep(1);
                 }
             }

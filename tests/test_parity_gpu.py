@@ -391,6 +391,41 @@ def test_fp64_walk_reaches_drafts_the_fast_walk_never_tested(diagnostics):
     assert len(strict) >= 16, len(strict)
     assert not off, off[:8]
 
+@pytest.mark.parametrize("method", ["multidraft", "spectr"])
+def test_team_members_that_never_answer(method, monkeypatch):
+    """The fp64 re-walk's teams: with SV_TEAM_WAIT_TICKS=0 the first workgroup
+    of every team stops waiting for its members at once and sums their ranges
+    itself (the fallback for members that cannot start), for the rest of the
+    request.  Partial sums are added in member order either way, so every
+    output, diagnostics included, equals the normal run's bit for bit, and the
+    oracle's to the parity bar.  Uniforms at the oracle's threshold of draft 0's
+    first decision list about 50 of 64 requests (teams of five)."""
+    ws = synth.scaled(W["multi_bf16_b256_k4_l4_v128256"], V=4096, B=64)
+    batch = pt.gpu_batch(ws, 12)
+    L = ws.L
+    ref0 = pt.run_oracle(method, synth.to_host(batch))
+    ua = batch["u_accept"].clone()
+    deltas = [3e-6, -3e-6, 1.5e-6, -1.5e-6, 2e-7, -2e-7]
+    j = 0 if method == "spectr" else L - 1
+    for b in range(ws.B):
+        h = ref0["accept_prob"][b, 0, j]
+        if not np.isnan(h) and 0.01 < h < 0.99:
+            ua[b, 0, j] = float(np.float32(h + deltas[b % len(deltas)]))
+    batch = dict(batch, u_accept=ua.contiguous())
+    normal = _verify(method, batch)
+    monkeypatch.setenv("SV_TEAM_WAIT_TICKS", "0")
+    rep, alone, ref = _parity(method, batch, f"team_fallback/{method}")
+    from draft_token_verification_online_amd import SV_FLAG_REDONE
+    redone = int(((alone["flags"] & SV_FLAG_REDONE) != 0).sum())
+    print(f"[team-fallback] {method}: redone {redone}", flush=True)
+    assert redone >= 16, redone
+    for k in normal:
+        a, b = normal[k], alone[k]
+        if a.dtype.is_floating_point:
+            assert torch.equal(torch.isnan(a), torch.isnan(b)), k
+            a, b = torch.nan_to_num(a), torch.nan_to_num(b)
+        assert torch.equal(a, b), k
+
 # ------------------------------------------------------- one draft, split-V
 # With K = 1 every call runs the single-draft kernels: slices of 1024 chunks
 # (8192 tokens) per workgroup, residual sums per (position, slice), the draw's
