@@ -943,15 +943,23 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                     beta = v[0];
                     D = v[1];
                 };
+                // Feasibility of rho, and g = rho - c(beta) for the secant steps.
+                // Since rho beta + D = 1, (1 - beta)^n - D = beta (rho - c(beta)):
+                // where beta is not small the difference ((1 - beta)^n - D) / beta
+                // gives g without rho - c(beta)'s cancellation, whose noise near
+                // rho* would turn the secant steps into bisection (~25 sweeps).
                 auto feasible = [&](double rho, double *g, double *bt) {
                     double beta, D;
                     sums(rho, beta, D);
-                    const double cc = c_of(beta);
-                    *g = rho - cc;
                     *bt = beta;
-                    if (beta <= kQuotientFormBeta) return cc <= rho;
+                    if (beta <= kQuotientFormBeta) {
+                        const double cc = c_of(beta);
+                        *g = rho - cc;
+                        return cc <= rho;
+                    }
                     double xn = 1.0;
                     for (int i = 0; i < n; ++i) xn *= 1.0 - beta;
+                    *g = (xn - D) / beta;
                     return D <= xn;
                 };
                 // the fast walk's records at this position: all certain, and accepted?
@@ -1003,9 +1011,13 @@ __device__ __attribute__((noinline)) void redo_request(const RedoArgs &A, int b,
                     for (int it = 0; it < 200 && hi - lo > 0x1p-42 * hi; ++it) {
                         double t = 0.5 * (lo + hi);
                         if (isfinite(ghi) && isfinite(glo) && ghi > glo) {
+                            // the secant point, kept 1e-3 of the width inside the
+                            // bracket: where rho* lies that close to an end (an
+                            // earlier step landed next to it) the bracket then
+                            // shrinks a thousandfold a step instead of halving
                             const double sec = lo - glo * (hi - lo) / (ghi - glo);
                             const double w = hi - lo;
-                            if (sec > lo + 1e-3 * w && sec < hi - 1e-3 * w) t = sec;
+                            if (isfinite(sec)) t = fmin(fmax(sec, lo + 1e-3 * w), hi - 1e-3 * w);
                         }
                         if (!(t > lo && t < hi)) break;
                         if (feasible(t, &g, &bt)) {
